@@ -1,0 +1,113 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that a pin catches each.
+
+A pin that passes for a broken oracle pins nothing; every mutation below must
+make at least one of the pins in test_oracle.py fail.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.codec as codec
+import oracle.paged_attention as pa
+from tests import test_oracle as pins
+
+
+def _attention_gqa_modulo(q, K, V, scale, visible):
+    nq, hq, d = q.shape
+    hkv = K.shape[1]
+    out = np.zeros((nq, hq, d))
+    for h in range(hq):
+        kvh = h % hkv  # wrong grouping
+        s = scale * (q[:, h, :] @ K[:, kvh, :].T)
+        s = np.where(np.arange(len(K))[None, :] < np.asarray(visible)[:, None], s, -np.inf)
+        w = np.exp(s - s.max(1, keepdims=True))
+        out[:, h, :] = (w / w.sum(1, keepdims=True)) @ V[:, kvh, :]
+    return out
+
+
+def _attention_no_scale(q, K, V, scale, visible):
+    return pa.__dict__["_orig_attention_rows"](q, K, V, 1.0, visible)
+
+
+def _attention_transposed_v(q, K, V, scale, visible):
+    out = pa.__dict__["_orig_attention_rows"](q, K, V, scale, visible)
+    return out[:, ::-1, :].copy()  # heads' outputs permuted (operand mix-up)
+
+
+def _slot_off_by_one(row, pos, block_size=16):
+    return int(row[pos // block_size]) * block_size + (pos + 1) % block_size
+
+
+def _decode_excluding_current(q, k_pool, v_pool, bt, ctx, scale, k_scale=None, v_scale=None, codec=None):
+    ctx = [max(int(n) - 1, 1) for n in ctx]
+    return pa.__dict__["_orig_decode"](q, k_pool, v_pool, bt, ctx, scale, k_scale, v_scale, codec)
+
+
+def _prefill_causal_off_by_one(q, k_pool, v_pool, qsl, seq_lens, bt, scale, k_scale=None, v_scale=None, codec=None):
+    q = np.asarray(q, dtype=np.float64)
+    out = np.zeros_like(q)
+    for s in range(len(seq_lens)):
+        a, b = int(qsl[s]), int(qsl[s + 1])
+        n = int(seq_lens[s])
+        K = pa.gather_sequence(k_pool, bt[s], n, k_scale, codec)
+        V = pa.gather_sequence(v_pool, bt[s], n, v_scale, codec)
+        visible = [max(n - (b - a) + i, 1) for i in range(b - a)]  # misses its own key
+        out[a:b] = pa.attention_rows(q[a:b], K, V, scale, visible)
+    return out
+
+
+def _gather_ignores_scale(pool, row, n, scales=None, codec=None):
+    return pa.__dict__["_orig_gather"](pool, row, n, None, codec)
+
+
+def _gather_wrong_block_order(pool, row, n, scales=None, codec=None):
+    nb = -(-n // 16)
+    row = list(row[:nb])[::-1] + list(row[nb:])
+    return pa.__dict__["_orig_gather"](pool, row, n, scales, codec)
+
+
+_E4M3_WRONG_BIAS = np.array([
+    (-1.0 if c & 0x80 else 1.0) * ((1 + (c & 7) / 8) * 2.0 ** (((c >> 3) & 15) - 8) if (c >> 3) & 15
+                                   else (c & 7) / 8 * 2.0 ** -7)
+    for c in range(256)])
+
+
+MUTATIONS = {
+    "gqa_modulo": ("attention_rows", _attention_gqa_modulo,
+                   [lambda: pins.test_decode_matches_sdpa(4, 2, 64)]),
+    "scale_dropped": ("attention_rows", _attention_no_scale,
+                      [lambda: pins.test_decode_matches_sdpa(4, 2, 64)]),
+    "head_mixup": ("attention_rows", _attention_transposed_v,
+                   [lambda: pins.test_decode_matches_sdpa(8, 1, 32)]),
+    "slot_off_by_one": ("slot_for_position", _slot_off_by_one,
+                        [pins.test_token_by_token_decode_equals_recompute]),
+    "ctx_excludes_new_token": ("decode", _decode_excluding_current,
+                               [pins.test_token_by_token_decode_equals_recompute]),
+    "causal_off_by_one": ("prefill_chunk", _prefill_causal_off_by_one,
+                          [pins.test_prefill_matches_sdpa_causal,
+                           pins.test_chunked_prefill_mixed_batch_equals_recompute]),
+    "scale_not_applied": ("gather_sequence", _gather_ignores_scale,
+                          [pins.test_quantized_single_token_is_decoded_code_times_scale]),
+    "block_order": ("gather_sequence", _gather_wrong_block_order,
+                    [pins.test_token_by_token_decode_equals_recompute]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    attr, fn, checks = MUTATIONS[name]
+    monkeypatch.setitem(pa.__dict__, "_orig_attention_rows", pa.attention_rows)
+    monkeypatch.setitem(pa.__dict__, "_orig_decode", pa.decode)
+    monkeypatch.setitem(pa.__dict__, "_orig_gather", pa.gather_sequence)
+    monkeypatch.setattr(pa, attr, fn)
+    if hasattr(oracle, attr):
+        monkeypatch.setattr(oracle, attr, fn)
+    for check in checks:
+        with pytest.raises(AssertionError):
+            check()
+
+
+def test_fp8_wrong_bias_is_caught(monkeypatch):
+    monkeypatch.setattr(codec, "_E4M3_TABLE", _E4M3_WRONG_BIAS)
+    with pytest.raises(AssertionError):
+        pins.test_e4m3fn_decode_all_codes_match_torch()
