@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+A step is one pass of the whole path over one synthetic batch already resident
+in HBM: slot mapping -> (copy-on-write block copies) -> cache write of this
+step's K/V -> paged attention (decode, or the mixed prefill+decode launch).
+
+Default workload: the Llama-3-8B-shaped decode layer (64 sequences, contexts
+uniform in [128, 4096], 32 query / 8 KV heads, head_dim 128, fp16 KV, fp32
+accumulation).  `value` is the step's algorithmic bytes divided by the step
+time (effective GB/s); the roofline object prices the attention launch alone
+(its algorithmic bytes over its HIP-event-timed duration) against the 8 TB/s
+HBM peak.  The pools are rotated among several copies between steps so that
+the 256 MB Infinity Cache cannot serve a step from a previous step's reads.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--rotate R]
+"""
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode effective KV GB/s (% of HBM peak) and tokens/s at Llama-3-8B shape"
+HBM_PEAK_GBPS = 8000.0
+ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1, "i8": 1}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama3-decode",
+                    choices=["llama3-decode", "tiny", "prefix-cow", "mixed", "long-fp8", "long-i8"])
+    ap.add_argument("--rotate", type=int, default=4, help="pool copies cycled between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def make_batch(name):
+    from paged_kv_cache_455_amd import workloads as W
+    return {"llama3-decode": W.llama3_8b_decode, "tiny": W.tiny_fp32, "prefix-cow": W.prefix_cow,
+            "mixed": W.mixed_step, "long-fp8": lambda: W.long_quantised("fp8"),
+            "long-i8": lambda: W.long_quantised("i8")}[name]()
+
+
+# ---------------------------------------------------------------------------------------
+# algorithmic work (what the path must move / compute, independent of the kernels)
+# ---------------------------------------------------------------------------------------
+def attention_bytes(b, seqs=None):
+    """KV (+ scales, table entries) read once per (sequence, kv head), q read, out written."""
+    e = ELEM[b.kv_dtype]
+    eq = ELEM[b.q_dtype]
+    qsl = b.query_start_loc.tolist()
+    lens = b.seq_lens.tolist()
+    seqs = range(b.num_seqs) if seqs is None else seqs
+    tot = 0
+    for s in seqs:
+        n = lens[s]
+        q_len = qsl[s + 1] - qsl[s]
+        nblk = -(-n // 16)
+        tot += 2 * n * b.num_kv_heads * b.head_dim * e
+        if b.kv_dtype in ("fp8", "i8"):
+            tot += 2 * nblk * b.num_kv_heads * 4
+        tot += nblk * 4
+        tot += q_len * b.num_q_heads * b.head_dim * 2 * eq
+    return tot
+
+
+def attention_flops(b):
+    qsl = b.query_start_loc.tolist()
+    tot = 0
+    for s, n in enumerate(b.seq_lens.tolist()):
+        q_len = qsl[s + 1] - qsl[s]
+        c = n - q_len
+        tot += 4 * b.num_q_heads * b.head_dim * (q_len * c + q_len * (q_len + 1) // 2)
+    return tot
+
+
+def side_bytes(b):
+    """Cache write (read new K/V, write pool rows), slots, and CoW copies (read + write)."""
+    e = ELEM[b.kv_dtype]
+    tot = b.num_tokens * 8
+    if b.k_new is not None:
+        tot += 2 * 2 * b.num_tokens * b.num_kv_heads * b.head_dim * e
+    if b.copy_pairs is not None:
+        tot += 2 * 2 * int(b.copy_pairs.shape[0]) * b.num_kv_heads * 16 * b.head_dim * e
+    return tot
+
+
+# ---------------------------------------------------------------------------------------
+def cpu_baseline(b, budget_s):
+    """The oracle as it stands, timed on this host over a bounded sample of the batch."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    from tests.pa_testlib import np_of, oracle_pools
+
+    kp, vp, kw = oracle_pools(b)
+    q = np_of(b.q).astype(np.float64)
+    bt = b.block_tables.numpy()
+    lens = b.seq_lens.numpy()
+    qsl = b.query_start_loc.numpy()
+    done, t0 = [], time.perf_counter()
+    s = 0
+    while time.perf_counter() - t0 < budget_s:
+        i = s % b.num_seqs
+        a, e = int(qsl[i]), int(qsl[i + 1])
+        if b.kind == "decode":
+            oracle.decode(q[i:i + 1], kp, vp, bt[i:i + 1], lens[i:i + 1], b.scale, **kw)
+        else:
+            oracle.prefill_chunk(q[a:e], kp, vp, np.array([0, e - a]), lens[i:i + 1], bt[i:i + 1],
+                                 b.scale, **kw)
+        done.append(i)
+        s += 1
+    dt = time.perf_counter() - t0
+    nbytes = attention_bytes(b, done)
+    uniq = len(set(done))
+    return {
+        "value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"numpy fp64 oracle over {len(done)} sequence passes ({uniq} distinct of "
+                   f"{b.num_seqs}) of the same batch in {dt:.1f} s; attention only; "
+                   f"tokens/s {len(done) / dt:.2f}"),
+        "cpu_model": _cpu_model(), "host_cores": len(os.sched_getaffinity(0)),
+    }
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+# ---------------------------------------------------------------------------------------
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the paged-attention path here is a single-GPU build)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import paged_kv_cache_455_amd as pa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    pa.load_library()
+    dev = torch.device("cuda:0")
+    b = make_batch(args.workload)
+    to = lambda t: None if t is None else t.to(dev).contiguous()
+    q, bt, lens, qsl = to(b.q), to(b.block_tables), to(b.seq_lens), to(b.query_start_loc)
+    k_new, v_new, pairs = to(b.k_new), to(b.v_new), to(b.copy_pairs)
+    R = max(1, args.rotate)
+    pools = []
+    k0, v0 = to(b.k_pool), to(b.v_pool)
+    ks0, vs0 = to(b.k_scale), to(b.v_scale)
+    for r in range(R):
+        k = k0 if r == 0 else k0.clone()
+        v = v0 if r == 0 else v0.clone()
+        ks = ks0 if (r == 0 or ks0 is None) else ks0.clone()
+        vs = vs0 if (r == 0 or vs0 is None) else vs0.clone()
+        pools.append(pa.KVPool(k, v, ks, vs))
+    out = torch.empty_like(q)
+    slots = torch.empty(b.num_tokens, dtype=torch.int64, device=dev)
+    if b.kind == "decode":
+        ws_bytes = pa.pa_decode_workspace_size(b.num_seqs, b.num_q_heads, b.num_kv_heads,
+                                               b.head_dim, b.max_seq_len)
+    else:
+        ws_bytes = pa.pa_prefill_workspace_size(b.num_seqs, b.num_tokens, b.num_q_heads,
+                                                b.num_kv_heads, b.head_dim, b.max_query_len,
+                                                b.max_seq_len)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        pool = pools[i % R]
+        if pairs is not None:
+            pa.kv_block_copy(pool, pairs)
+        pa.pa_slot_mapping(bt, qsl, lens, b.num_tokens, out=slots)
+        if k_new is not None:
+            pa.kv_cache_write(pool, k_new, v_new, slots)
+        if ev is not None:
+            ev[0].record(stream)
+        if b.kind == "decode":
+            pa.pa_decode(pool, q, bt, lens, b.max_seq_len, b.scale, out=out, workspace=ws)
+        else:
+            pa.pa_prefill_chunk(pool, q, qsl, lens, bt, b.max_query_len, b.max_seq_len, b.scale,
+                                out=out, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attn_ms = [a.elapsed_time(e) for a, e in evs]
+    attn_ms_avg = sum(attn_ms) / len(attn_ms)
+    attn_ms_sorted = sorted(attn_ms)
+    ms_per_step = wall * 1e3 / args.steps
+
+    a_bytes = attention_bytes(b)
+    s_bytes = side_bytes(b)
+    flops = attention_flops(b)
+    step_gbps = (a_bytes + s_bytes) / (ms_per_step * 1e-3) / 1e9
+    attn_gbps = a_bytes / (attn_ms_avg * 1e-3) / 1e9
+    tokens = b.num_seqs if b.kind == "decode" else b.num_tokens
+    rec = {
+        "metric": METRIC,
+        "value": round(step_gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": b.kv_dtype,
+        "data": "synthetic (seeded N(0,1) draws; no dataset or weights)",
+        "config": {
+            "workload": b.name, "num_seqs": b.num_seqs, "num_q_tokens": b.num_tokens,
+            "q_heads": b.num_q_heads, "kv_heads": b.num_kv_heads, "head_dim": b.head_dim,
+            "block_size": 16, "kv_dtype": b.kv_dtype, "q_dtype": b.q_dtype, "accumulate": "f32",
+            "max_context": b.max_seq_len, "pool_copies_rotated": R,
+        },
+        "tokens_per_s": round(tokens / (ms_per_step * 1e-3), 1),
+        "pct_hbm_peak": round(100.0 * step_gbps / HBM_PEAK_GBPS, 2),
+        "attention_us": {"avg": round(attn_ms_avg * 1e3, 2),
+                         "p10": round(attn_ms_sorted[len(attn_ms) // 10] * 1e3, 2),
+                         "p50": round(attn_ms_sorted[len(attn_ms) // 2] * 1e3, 2),
+                         "p90": round(attn_ms_sorted[(9 * len(attn_ms)) // 10] * 1e3, 2)},
+        "algorithmic": {"attention_bytes": a_bytes, "side_bytes": s_bytes, "attention_flops": flops},
+        "roofline": {"bound": "hbm", "achieved": round(attn_gbps, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "pa_decode (partition + merge launches)" if b.kind == "decode"
+                     else "pa_prefill_chunk"},
+    }
+    if b.kind != "decode":
+        rec["attention_tflops"] = round(flops / (attn_ms_avg * 1e-3) / 1e12, 2)
+    if not args.no_cpu_baseline:
+        del pools, k0, v0
+        torch.cuda.synchronize()
+        rec["cpu_baseline"] = cpu_baseline(b, args.cpu_budget_s)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,180 @@
+/*
+ * pa.h -- paged KV-cache attention on one MI355X (gfx950): the C ABI.
+ *
+ * Sources for what each call computes (the pages are the authority):
+ *  [P1] "vLLM ... PagedAttention / Prefix Sharing / Continuous Batching"
+ *       (uml.org.cn), sections PagedAttention, Prefix Sharing, Continuous Batching.
+ *  [P2] "3、核心概念：LLM推理原理、KV Cache、PagedAttention、连续批处理"
+ *       (5688vip.com course, chapter 3), sections 3.1-3.3.
+ *  [P3] "从KV Cache到vLLM：大模型推理提速与显存优化实战" (xxqk.cn),
+ *       sections 1.1-1.2 (attention against the cache), 2.1-2.3 (KV size,
+ *       GQA, INT8/FP8 storage), 3.2 (16-token pages).
+ *
+ * Conventions shared by every call
+ *  - Every pointer is a DEVICE pointer unless its comment says "host".
+ *  - Calls validate their scalar arguments on the host, then only enqueue
+ *    work on `stream`; they never allocate, free or synchronise.  A non-OK
+ *    status means nothing was enqueued (PA_E_HIP: a launch was attempted and
+ *    failed; pa_last_error() holds the HIP message).
+ *  - The caller owns every buffer.  Scratch memory comes from the caller's
+ *    `workspace` (size from the matching *_workspace_size call).
+ *  - Contents of device arrays are NOT checked (that would need a sync):
+ *    block ids outside [0, num_blocks), negative or too-long lengths,
+ *    duplicate write slots or overlapping copy pairs are undefined behaviour.
+ *
+ * KV pool layout (the pages fix the paging, not the memory layout):
+ *    k, v : [num_blocks][num_kv_heads][block_size = 16][head_dim], kv_dtype
+ *    k_scale, v_scale : float32 [num_blocks][num_kv_heads] for 1-byte codes
+ *  so one (block, kv head) tile of 16 token rows is contiguous: 4 KiB for
+ *  fp16/bf16 at head_dim 128, 2 KiB for fp8/int8.
+ *
+ * GQA ([P3] 2.2): query head h reads kv head h / (num_q_heads / num_kv_heads).
+ */
+#ifndef PAGED_KV_PA_H
+#define PAGED_KV_PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_dtype {
+  PA_F32 = 0,
+  PA_F16 = 1,
+  PA_BF16 = 2,
+  PA_FP8_E4M3 = 3, /* OCP E4M3FN codes: bias 7, max 448, NaN = S.1111.111 */
+  PA_I8 = 4        /* symmetric int8 codes, value = code * scale */
+} pa_dtype_t;
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_E_ARG = 1,         /* a null pointer or an out-of-range scalar */
+  PA_E_UNSUPPORTED = 2, /* a valid but unimplemented shape or dtype combination */
+  PA_E_WORKSPACE = 3,   /* workspace missing or smaller than *_workspace_size */
+  PA_E_HIP = 4          /* a HIP launch failed */
+} pa_status_t;
+
+/* Host struct describing caller-owned device memory. */
+typedef struct pa_kv_pool {
+  void *k;          /* [num_blocks][num_kv_heads][16][head_dim] */
+  void *v;          /* same shape */
+  float *k_scale;   /* [num_blocks][num_kv_heads]; NULL unless kv_dtype is 1 byte */
+  float *v_scale;
+  int64_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t block_size; /* must be 16 ([P2] 3.2, [P3] 3.2) */
+  int32_t head_dim;   /* 64 or 128 */
+  int32_t kv_dtype;   /* pa_dtype_t */
+} pa_kv_pool_t;
+
+/* Version string of the library (static storage). */
+const char *pa_version(void);
+
+/* Text of a status code (static storage). */
+const char *pa_status_string(pa_status_t s);
+
+/* Detail of the last non-OK status returned on the calling thread. */
+const char *pa_last_error(void);
+
+/*
+ * pa_slot_mapping -- where each new token's K/V goes ([P2] 3.2: a decode
+ * step writes the new token at the end of the current block; a block that is
+ * full is followed by a new physical block from the block table).
+ *
+ * For sequence s, query rows t in [query_start_loc[s], query_start_loc[s+1])
+ * are the q_len newest tokens; row t sits at logical position
+ *     p = seq_lens[s] - q_len + (t - query_start_loc[s])
+ * and its slot is   block_tables[s][p / 16] * 16 + p % 16.
+ *   block_tables    int32 [num_seqs][max_blocks_per_seq]
+ *   query_start_loc int32 [num_seqs + 1], non-decreasing, [0] = 0,
+ *                   [num_seqs] = num_tokens
+ *   seq_lens        int32 [num_seqs], KV length including the new rows
+ *   slot_mapping    int64 [num_tokens] (output)
+ */
+pa_status_t pa_slot_mapping(const int32_t *block_tables, int32_t max_blocks_per_seq,
+                            const int32_t *query_start_loc, const int32_t *seq_lens,
+                            int32_t num_seqs, int32_t num_tokens, int64_t *slot_mapping,
+                            hipStream_t stream);
+
+/*
+ * kv_cache_write -- scatter new tokens' K and V into the pools by slot
+ * ([P2] 3.2 prefill writes every prompt token, decode appends one token).
+ *   k_new, v_new  [num_tokens][num_kv_heads][head_dim], dtype = pool kv_dtype
+ *   slot_mapping  int64 [num_tokens]; slot = block * 16 + offset; slot < 0
+ *                 means "no token" and is skipped.
+ * A pure bit copy.  Pools with 1-byte codes return PA_E_UNSUPPORTED (codes
+ * and their per-block scales are produced outside this library).
+ */
+pa_status_t kv_cache_write(const pa_kv_pool_t *pool, const void *k_new, const void *v_new,
+                           const int64_t *slot_mapping, int32_t num_tokens,
+                           hipStream_t stream);
+
+/*
+ * kv_block_copy -- copy-on-write duplication of physical blocks ([P1]
+ * Prefix Sharing: when a request that shares a page diverges, the shared page
+ * stays as it is and the new token goes into a copy of it).
+ *   src_dst int32 [num_pairs][2]: every kv head's K and V tile of block src
+ *           (and both scales, for 1-byte pools) is copied to block dst.
+ * Destinations must be unique and disjoint from the sources.
+ */
+pa_status_t kv_block_copy(const pa_kv_pool_t *pool, const int32_t *src_dst, int32_t num_pairs,
+                          hipStream_t stream);
+
+/* Workspace bytes pa_decode needs for these sizes (0 is a valid answer). */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_context_len);
+
+/*
+ * pa_decode -- one decode step: every sequence's single new query token
+ * attends to all of its cached tokens through its block table ([P2] 3.2: the
+ * kernel reads the scattered blocks by indirection through the block table;
+ * [P3] 1.1: dot the query with every cached key, softmax, weight the values).
+ *   q            [num_seqs][num_q_heads][head_dim], q_dtype
+ *   out          same shape and dtype as q (fp32 accumulation, rounded to
+ *                nearest even on store)
+ *   block_tables int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens int32 [num_seqs], >= 1: cached tokens including this step's
+ *                token, whose K/V must already be written
+ *   max_context_len  host upper bound of context_lens (sizes the split)
+ *   scale        softmax scale applied to q.k (1/sqrt(head_dim) usually)
+ * dtypes: kv f32/f16/bf16 need q_dtype == kv_dtype; fp8/int8 KV take f16 or
+ * bf16 queries.  num_q_heads / num_kv_heads must be 1, 2, 4 or 8.
+ */
+pa_status_t pa_decode(const pa_kv_pool_t *pool, const void *q, int32_t q_dtype, void *out,
+                      const int32_t *block_tables, int32_t max_blocks_per_seq,
+                      const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t max_context_len, float scale, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes pa_prefill_chunk needs for these sizes. */
+size_t pa_prefill_workspace_size(int32_t num_seqs, int32_t num_q_tokens, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t max_query_len,
+                                 int32_t max_seq_len);
+
+/*
+ * pa_prefill_chunk -- one continuous-batching step ([P1] Continuous
+ * Batching): chunked prefills and decodes of many sequences in one call.
+ *   q               [num_q_tokens][num_q_heads][head_dim], rows packed by
+ *                   sequence; out has the same shape and dtype
+ *   query_start_loc int32 [num_seqs + 1]; q_len = qsl[s+1] - qsl[s] >= 1
+ *                   (q_len == 1 is a decode)
+ *   seq_lens        int32 [num_seqs]: KV length including the q_len new
+ *                   tokens, whose K/V must already be written
+ * Causality ([P2] 3.1, autoregressive order): row i of sequence s sits at
+ * position seq_lens[s] - q_len + i and sees keys 0 .. that position.
+ */
+pa_status_t pa_prefill_chunk(const pa_kv_pool_t *pool, const void *q, int32_t q_dtype,
+                             void *out, const int32_t *query_start_loc, const int32_t *seq_lens,
+                             const int32_t *block_tables, int32_t max_blocks_per_seq,
+                             int32_t num_seqs, int32_t num_q_tokens, int32_t num_q_heads,
+                             int32_t max_query_len, int32_t max_seq_len, float scale,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_KV_PA_H */

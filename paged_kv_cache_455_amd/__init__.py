@@ -1,0 +1,226 @@
+"""Paged KV-cache attention for one MI355X (gfx950): Python binding.
+
+Thin ctypes marshalling over the C ABI in ``include/pa.h`` (``libpa.so``, built
+in-tree by ``paged_kv_cache_455_amd._build``).  Every step of the path runs in
+the HIP kernels; PyTorch only provides device memory and the current stream.
+There is no CPU fallback: without the built library every call raises.
+
+Entry points (same names as the C ABI): ``pa_slot_mapping``,
+``kv_cache_write``, ``kv_block_copy``, ``pa_decode``, ``pa_prefill_chunk``,
+``pa_decode_workspace_size``, ``pa_prefill_workspace_size``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "KVPool", "PagedAttentionError", "library_path", "load_library",
+    "pa_slot_mapping", "kv_cache_write", "kv_block_copy", "pa_decode", "pa_prefill_chunk",
+    "pa_decode_workspace_size", "pa_prefill_workspace_size", "PA_DTYPE",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3, PA_I8 = 0, 1, 2, 3, 4
+PA_DTYPE = {
+    torch.float32: PA_F32,
+    torch.float16: PA_F16,
+    torch.bfloat16: PA_BF16,
+    torch.uint8: PA_FP8_E4M3,          # E4M3FN bit patterns
+    torch.float8_e4m3fn: PA_FP8_E4M3,
+    torch.int8: PA_I8,
+}
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP error"}
+
+
+class PagedAttentionError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__(f"{fn}: {_STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+class _Pool(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("num_blocks", ctypes.c_int64), ("num_kv_heads", ctypes.c_int32),
+        ("block_size", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+    ]
+
+
+_c = ctypes
+_SIGS = {
+    "pa_version": (_c.c_char_p, []),
+    "pa_status_string": (_c.c_char_p, [_c.c_int]),
+    "pa_last_error": (_c.c_char_p, []),
+    "pa_slot_mapping": (_c.c_int, [_c.c_void_p, _c.c_int32, _c.c_void_p, _c.c_void_p, _c.c_int32,
+                                   _c.c_int32, _c.c_void_p, _c.c_void_p]),
+    "kv_cache_write": (_c.c_int, [_c.POINTER(_Pool), _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                  _c.c_int32, _c.c_void_p]),
+    "kv_block_copy": (_c.c_int, [_c.POINTER(_Pool), _c.c_void_p, _c.c_int32, _c.c_void_p]),
+    "pa_decode_workspace_size": (_c.c_size_t, [_c.c_int32] * 5),
+    "pa_decode": (_c.c_int, [_c.POINTER(_Pool), _c.c_void_p, _c.c_int32, _c.c_void_p, _c.c_void_p,
+                             _c.c_int32, _c.c_void_p, _c.c_int32, _c.c_int32, _c.c_int32,
+                             _c.c_float, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "pa_prefill_workspace_size": (_c.c_size_t, [_c.c_int32] * 7),
+    "pa_prefill_chunk": (_c.c_int, [_c.POINTER(_Pool), _c.c_void_p, _c.c_int32, _c.c_void_p,
+                                    _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int32, _c.c_int32,
+                                    _c.c_int32, _c.c_int32, _c.c_int32, _c.c_int32, _c.c_float,
+                                    _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+}
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def library_path() -> str:
+    return os.environ.get("PA_LIBRARY", os.path.join(_HERE, "libpa.so"))
+
+
+def load_library() -> ctypes.CDLL:
+    """Load ``libpa.so``; raise if it has not been built (no fallback exists)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library {path} is not built; run "
+                           "`python -m paged_kv_cache_455_amd._build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _LIB = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        detail = load_library().pa_last_error().decode(errors="replace")
+        raise PagedAttentionError(fn, status, detail)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the HIP library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor, stream=None) -> Optional[int]:
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dt(t: torch.Tensor) -> int:
+    try:
+        return PA_DTYPE[t.dtype]
+    except KeyError:
+        raise ValueError(f"unsupported dtype {t.dtype}") from None
+
+
+class KVPool:
+    """Device K/V pools ``[num_blocks][num_kv_heads][16][head_dim]`` (+ scales)."""
+
+    def __init__(self, k: torch.Tensor, v: torch.Tensor, k_scale: Optional[torch.Tensor] = None,
+                 v_scale: Optional[torch.Tensor] = None):
+        if k.shape != v.shape or k.dim() != 4 or k.dtype != v.dtype:
+            raise ValueError("k and v pools must share one 4-d shape and dtype")
+        self.k, self.v, self.k_scale, self.v_scale = k, v, k_scale, v_scale
+        nb, hkv, bs, d = k.shape
+        self._s = _Pool(_ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale), nb, hkv, bs, d, _dt(k))
+
+    @property
+    def num_kv_heads(self) -> int:
+        return int(self.k.shape[1])
+
+    @property
+    def head_dim(self) -> int:
+        return int(self.k.shape[3])
+
+    def ref(self):
+        return ctypes.byref(self._s)
+
+
+def pa_slot_mapping(block_tables, query_start_loc, seq_lens, num_tokens: int, out=None, stream=None):
+    lib = load_library()
+    if out is None:
+        out = torch.empty(num_tokens, dtype=torch.int64, device=block_tables.device)
+    S = int(seq_lens.shape[0])
+    _check("pa_slot_mapping", lib.pa_slot_mapping(
+        _ptr(block_tables), int(block_tables.shape[1]), _ptr(query_start_loc), _ptr(seq_lens), S,
+        int(num_tokens), _ptr(out), _stream(block_tables, stream)))
+    return out
+
+
+def kv_cache_write(pool: KVPool, k_new, v_new, slot_mapping, stream=None):
+    lib = load_library()
+    _check("kv_cache_write", lib.kv_cache_write(
+        pool.ref(), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), int(slot_mapping.shape[0]),
+        _stream(pool.k, stream)))
+
+
+def kv_block_copy(pool: KVPool, src_dst, stream=None):
+    lib = load_library()
+    _check("kv_block_copy", lib.kv_block_copy(
+        pool.ref(), _ptr(src_dst), int(src_dst.shape[0]), _stream(pool.k, stream)))
+
+
+def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len) -> int:
+    return int(load_library().pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads,
+                                                       head_dim, max_context_len))
+
+
+def pa_prefill_workspace_size(num_seqs, num_q_tokens, num_q_heads, num_kv_heads, head_dim,
+                              max_query_len, max_seq_len) -> int:
+    return int(load_library().pa_prefill_workspace_size(num_seqs, num_q_tokens, num_q_heads,
+                                                        num_kv_heads, head_dim, max_query_len,
+                                                        max_seq_len))
+
+
+def _workspace(nbytes: int, device, workspace):
+    if nbytes == 0:
+        return workspace
+    if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return workspace
+
+
+def pa_decode(pool: KVPool, q, block_tables, context_lens, max_context_len: int, scale: float,
+              out=None, workspace=None, stream=None):
+    lib = load_library()
+    S, hq, _ = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    need = pa_decode_workspace_size(S, hq, pool.num_kv_heads, pool.head_dim, max_context_len)
+    workspace = _workspace(need, q.device, workspace)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pa_decode", lib.pa_decode(
+        pool.ref(), _ptr(q), _dt(q), _ptr(out), _ptr(block_tables), int(block_tables.shape[1]),
+        _ptr(context_lens), int(S), int(hq), int(max_context_len), float(scale),
+        _ptr(workspace), wbytes, _stream(q, stream)))
+    return out
+
+
+def pa_prefill_chunk(pool: KVPool, q, query_start_loc, seq_lens, block_tables, max_query_len: int,
+                     max_seq_len: int, scale: float, out=None, workspace=None, stream=None):
+    lib = load_library()
+    T, hq, _ = q.shape
+    S = int(seq_lens.shape[0])
+    if out is None:
+        out = torch.empty_like(q)
+    need = pa_prefill_workspace_size(S, T, hq, pool.num_kv_heads, pool.head_dim, max_query_len,
+                                     max_seq_len)
+    workspace = _workspace(need, q.device, workspace)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pa_prefill_chunk", lib.pa_prefill_chunk(
+        pool.ref(), _ptr(q), _dt(q), _ptr(out), _ptr(query_start_loc), _ptr(seq_lens),
+        _ptr(block_tables), int(block_tables.shape[1]), S, int(T), int(hq), int(max_query_len),
+        int(max_seq_len), float(scale), _ptr(workspace), wbytes, _stream(q, stream)))
+    return out

@@ -1,0 +1,312 @@
+// C ABI of the paged-attention library: argument checks, workspace sizing,
+// split-context policy and kernel dispatch.  Declarations and contracts are in
+// include/pa.h.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "pa_launch.h"
+#include "../../include/pa.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+pa_status_t fail(pa_status_t st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+pa_status_t fail(pa_status_t st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+pa_status_t hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return PA_OK;
+  return fail(PA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kBlockTokens = 16;
+
+int elem_bytes(int dt) {
+  switch (dt) {
+    case PA_F32: return 4;
+    case PA_F16: case PA_BF16: return 2;
+    case PA_FP8_E4M3: case PA_I8: return 1;
+    default: return 0;
+  }
+}
+
+bool is_quantised(int dt) { return dt == PA_FP8_E4M3 || dt == PA_I8; }
+
+pa_status_t check_pool(const pa_kv_pool_t *pool, bool need_scales_if_quantised) {
+  if (pool == nullptr) return fail(PA_E_ARG, "pool is NULL");
+  if (pool->k == nullptr || pool->v == nullptr) return fail(PA_E_ARG, "pool k/v pointer is NULL");
+  if (pool->num_blocks <= 0) return fail(PA_E_ARG, "num_blocks must be > 0");
+  if (pool->num_kv_heads <= 0) return fail(PA_E_ARG, "num_kv_heads must be > 0");
+  if (pool->block_size != kBlockTokens)
+    return fail(PA_E_UNSUPPORTED, "block_size %d unsupported (must be 16)", pool->block_size);
+  if (pool->head_dim != 64 && pool->head_dim != 128)
+    return fail(PA_E_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", pool->head_dim);
+  if (elem_bytes(pool->kv_dtype) == 0) return fail(PA_E_ARG, "unknown kv_dtype %d", pool->kv_dtype);
+  if (need_scales_if_quantised && is_quantised(pool->kv_dtype) &&
+      (pool->k_scale == nullptr || pool->v_scale == nullptr))
+    return fail(PA_E_ARG, "1-byte kv_dtype needs k_scale and v_scale");
+  if (!is_quantised(pool->kv_dtype) && (pool->k_scale != nullptr || pool->v_scale != nullptr))
+    return fail(PA_E_ARG, "scales are only meaningful for 1-byte kv_dtype");
+  return PA_OK;
+}
+
+pa_status_t check_q_dtype(int kv, int q) {
+  if (is_quantised(kv)) {
+    if (q != PA_F16 && q != PA_BF16)
+      return fail(PA_E_UNSUPPORTED, "1-byte KV takes f16 or bf16 queries (got %d)", q);
+  } else if (q != kv) {
+    return fail(PA_E_UNSUPPORTED, "q_dtype %d must equal kv_dtype %d for float KV", q, kv);
+  }
+  return PA_OK;
+}
+
+pa_status_t check_heads(int num_q_heads, int num_kv_heads, int *group) {
+  if (num_q_heads <= 0) return fail(PA_E_ARG, "num_q_heads must be > 0");
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PA_E_ARG, "num_q_heads %d not a multiple of num_kv_heads %d", num_q_heads,
+                num_kv_heads);
+  const int g = num_q_heads / num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return fail(PA_E_UNSUPPORTED, "GQA group %d unsupported (1, 2, 4 or 8)", g);
+  *group = g;
+  return PA_OK;
+}
+
+// ---- split-context policy ---------------------------------------------------------------
+// A context of nblk blocks is cut into partitions of part_blocks blocks, each one
+// workgroup.  The default keeps partitions long (little merge traffic) and only
+// shortens them when there would be too few workgroups to fill 256 CUs.
+int env_int(const char *name, int dflt) {
+  const char *v = getenv(name);
+  if (v == nullptr || *v == 0) return dflt;
+  const int x = atoi(v);
+  return x > 0 ? x : dflt;
+}
+
+int decode_part_blocks(int64_t num_rows, int num_kv_heads, int max_blocks) {
+  const int forced = env_int("PA_PARTITION_BLOCKS", 0);
+  if (forced > 0) return forced;
+  int pb = 32;
+  const int64_t kMinGroups = 1024;
+  while (pb > 8) {
+    const int64_t parts = (max_blocks + pb - 1) / pb;
+    if (num_rows * num_kv_heads * parts >= kMinGroups) break;
+    pb /= 2;
+  }
+  return pb;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct WsLayout {
+  size_t acc_off, m_off, l_off, total;
+};
+
+WsLayout ws_layout(int64_t rows, int num_q_heads, int head_dim, int max_parts) {
+  WsLayout w{};
+  if (max_parts <= 1) return w;
+  const size_t n_ml = (size_t)rows * num_q_heads * max_parts;
+  w.acc_off = 0;
+  w.m_off = align256(n_ml * head_dim * sizeof(float));
+  w.l_off = w.m_off + align256(n_ml * sizeof(float));
+  w.total = w.l_off + align256(n_ml * sizeof(float));
+  return w;
+}
+
+int max_parts_for(int max_ctx, int part_blocks) {
+  const int max_blocks = (max_ctx + kBlockTokens - 1) / kBlockTokens;
+  return (max_blocks + part_blocks - 1) / part_blocks;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pa_version(void) { return "paged_kv_cache_455_amd 0.1 (gfx950)"; }
+
+const char *pa_status_string(pa_status_t s) {
+  switch (s) {
+    case PA_OK: return "ok";
+    case PA_E_ARG: return "invalid argument";
+    case PA_E_UNSUPPORTED: return "unsupported shape or dtype";
+    case PA_E_WORKSPACE: return "workspace too small";
+    case PA_E_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char *pa_last_error(void) { return g_last_error; }
+
+pa_status_t pa_slot_mapping(const int32_t *block_tables, int32_t max_blocks_per_seq,
+                            const int32_t *query_start_loc, const int32_t *seq_lens,
+                            int32_t num_seqs, int32_t num_tokens, int64_t *slot_mapping,
+                            hipStream_t stream) {
+  if (num_seqs < 0 || num_tokens < 0) return fail(PA_E_ARG, "negative num_seqs/num_tokens");
+  if (num_seqs == 0 || num_tokens == 0) return PA_OK;
+  if (!block_tables || !query_start_loc || !seq_lens || !slot_mapping)
+    return fail(PA_E_ARG, "NULL array argument");
+  if (max_blocks_per_seq <= 0) return fail(PA_E_ARG, "max_blocks_per_seq must be > 0");
+  return hip_status(pa::launch_slot_mapping(block_tables, max_blocks_per_seq, query_start_loc,
+                                            seq_lens, num_seqs, slot_mapping, stream),
+                    "pa_slot_mapping launch");
+}
+
+pa_status_t kv_cache_write(const pa_kv_pool_t *pool, const void *k_new, const void *v_new,
+                           const int64_t *slot_mapping, int32_t num_tokens, hipStream_t stream) {
+  pa_status_t st = check_pool(pool, false);
+  if (st != PA_OK) return st;
+  if (is_quantised(pool->kv_dtype))
+    return fail(PA_E_UNSUPPORTED, "kv_cache_write into 1-byte pools is not implemented");
+  if (num_tokens < 0) return fail(PA_E_ARG, "num_tokens must be >= 0");
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping) return fail(PA_E_ARG, "NULL array argument");
+  pa::CacheWriteArgs a{};
+  a.k = pool->k;
+  a.v = pool->v;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.slots = slot_mapping;
+  a.num_blocks = pool->num_blocks;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.row_bytes = pool->head_dim * elem_bytes(pool->kv_dtype);
+  return hip_status(pa::launch_cache_write(a, stream), "kv_cache_write launch");
+}
+
+pa_status_t kv_block_copy(const pa_kv_pool_t *pool, const int32_t *src_dst, int32_t num_pairs,
+                          hipStream_t stream) {
+  pa_status_t st = check_pool(pool, true);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0) return fail(PA_E_ARG, "num_pairs must be >= 0");
+  if (num_pairs == 0) return PA_OK;
+  if (!src_dst) return fail(PA_E_ARG, "src_dst is NULL");
+  pa::BlockCopyArgs a{};
+  a.k = pool->k;
+  a.v = pool->v;
+  a.k_scale = pool->k_scale;
+  a.v_scale = pool->v_scale;
+  a.pairs = src_dst;
+  a.num_pairs = num_pairs;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.tile_bytes = kBlockTokens * pool->head_dim * elem_bytes(pool->kv_dtype);
+  return hip_status(pa::launch_block_copy(a, stream), "kv_block_copy launch");
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_context_len) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_context_len <= 0)
+    return 0;
+  const int max_blocks = (max_context_len + kBlockTokens - 1) / kBlockTokens;
+  const int pb = decode_part_blocks(num_seqs, num_kv_heads, max_blocks);
+  return ws_layout(num_seqs, num_q_heads, head_dim, max_parts_for(max_context_len, pb)).total;
+}
+
+static pa_status_t fill_decode_args(const pa_kv_pool_t *pool, const void *q, int32_t q_dtype,
+                                    void *out, const int32_t *block_tables,
+                                    int32_t max_blocks_per_seq, const int32_t *lens,
+                                    int64_t rows, int32_t num_q_heads, int32_t max_len,
+                                    float scale, void *workspace, size_t workspace_bytes,
+                                    pa::DecodeArgs &a, int &group) {
+  pa_status_t st = check_pool(pool, true);
+  if (st != PA_OK) return st;
+  if ((st = check_q_dtype(pool->kv_dtype, q_dtype)) != PA_OK) return st;
+  if ((st = check_heads(num_q_heads, pool->num_kv_heads, &group)) != PA_OK) return st;
+  if (!q || !out || !block_tables || !lens) return fail(PA_E_ARG, "NULL array argument");
+  if (max_blocks_per_seq <= 0) return fail(PA_E_ARG, "max_blocks_per_seq must be > 0");
+  if (max_len <= 0) return fail(PA_E_ARG, "max length must be > 0");
+  if ((int64_t)max_len > (int64_t)max_blocks_per_seq * kBlockTokens)
+    return fail(PA_E_ARG, "max length %d exceeds max_blocks_per_seq * 16", max_len);
+  if (!(scale == scale)) return fail(PA_E_ARG, "scale is NaN");
+  const int max_blocks = (max_len + kBlockTokens - 1) / kBlockTokens;
+  const int pb = decode_part_blocks(rows, pool->num_kv_heads, max_blocks);
+  const int parts = max_parts_for(max_len, pb);
+  const WsLayout w = ws_layout(rows, num_q_heads, pool->head_dim, parts);
+  if (w.total > 0 && (workspace == nullptr || workspace_bytes < w.total))
+    return fail(PA_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
+                workspace ? workspace_bytes : (size_t)0);
+  a = pa::DecodeArgs{};
+  a.k = pool->k;
+  a.v = pool->v;
+  a.k_scale = pool->k_scale;
+  a.v_scale = pool->v_scale;
+  a.q = q;
+  a.out = out;
+  a.bt = block_tables;
+  a.ctx = lens;
+  char *ws = reinterpret_cast<char *>(workspace);
+  a.ws_acc = w.total ? reinterpret_cast<float *>(ws + w.acc_off) : nullptr;
+  a.ws_m = w.total ? reinterpret_cast<float *>(ws + w.m_off) : nullptr;
+  a.ws_l = w.total ? reinterpret_cast<float *>(ws + w.l_off) : nullptr;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.num_q_heads = num_q_heads;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.part_blocks = pb;
+  a.max_parts = parts;
+  a.qk_scale = scale * 1.4426950408889634f;
+  return PA_OK;
+}
+
+pa_status_t pa_decode(const pa_kv_pool_t *pool, const void *q, int32_t q_dtype, void *out,
+                      const int32_t *block_tables, int32_t max_blocks_per_seq,
+                      const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t max_context_len, float scale, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  if (num_seqs < 0) return fail(PA_E_ARG, "num_seqs must be >= 0");
+  if (num_seqs == 0) return PA_OK;
+  pa::DecodeArgs a;
+  int group = 0;
+  pa_status_t st = fill_decode_args(pool, q, q_dtype, out, block_tables, max_blocks_per_seq,
+                                    context_lens, num_seqs, num_q_heads, max_context_len, scale,
+                                    workspace, workspace_bytes, a, group);
+  if (st != PA_OK) return st;
+  return hip_status(pa::launch_decode(a, pool->kv_dtype, q_dtype, pool->head_dim, group, num_seqs,
+                                      stream),
+                    "pa_decode launch");
+}
+
+size_t pa_prefill_workspace_size(int32_t num_seqs, int32_t num_q_tokens, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t max_query_len,
+                                 int32_t max_seq_len) {
+  (void)max_query_len;
+  if (num_seqs <= 0 || num_q_tokens <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      head_dim <= 0 || max_seq_len <= 0)
+    return 0;
+  const int max_blocks = (max_seq_len + kBlockTokens - 1) / kBlockTokens;
+  const int pb = decode_part_blocks(num_q_tokens, num_kv_heads, max_blocks);
+  return ws_layout(num_q_tokens, num_q_heads, head_dim, max_parts_for(max_seq_len, pb)).total;
+}
+
+pa_status_t pa_prefill_chunk(const pa_kv_pool_t *pool, const void *q, int32_t q_dtype,
+                             void *out, const int32_t *query_start_loc, const int32_t *seq_lens,
+                             const int32_t *block_tables, int32_t max_blocks_per_seq,
+                             int32_t num_seqs, int32_t num_q_tokens, int32_t num_q_heads,
+                             int32_t max_query_len, int32_t max_seq_len, float scale,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (num_seqs < 0 || num_q_tokens < 0) return fail(PA_E_ARG, "negative num_seqs/num_q_tokens");
+  if (num_seqs == 0 || num_q_tokens == 0) return PA_OK;
+  if (!query_start_loc) return fail(PA_E_ARG, "query_start_loc is NULL");
+  if (max_query_len <= 0 || max_query_len > max_seq_len)
+    return fail(PA_E_ARG, "max_query_len %d must be in [1, max_seq_len]", max_query_len);
+  pa::PrefillArgs a;
+  int group = 0;
+  pa_status_t st = fill_decode_args(pool, q, q_dtype, out, block_tables, max_blocks_per_seq,
+                                    seq_lens, num_q_tokens, num_q_heads, max_seq_len, scale,
+                                    workspace, workspace_bytes, a.dec, group);
+  if (st != PA_OK) return st;
+  a.qsl = query_start_loc;
+  a.num_seqs = num_seqs;
+  return hip_status(pa::launch_prefill(a, pool->kv_dtype, q_dtype, pool->head_dim, group,
+                                       num_q_tokens, stream),
+                    "pa_prefill_chunk launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// Device-side helpers shared by the paged-attention kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pa.h"
+
+namespace pa {
+
+constexpr int kBlock = 16;            // tokens per physical block
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+// Running-max sentinel: finite so that exp2(sentinel - sentinel) = 1 keeps an
+// empty lane's (m, l, acc) = (sentinel, 0, 0) harmless in every merge.
+constexpr float kNegBig = -1.0e30f;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+
+__host__ __device__ constexpr int dtype_bytes(int dt) {
+  return dt == PA_F32 ? 4 : (dt == PA_F16 || dt == PA_BF16) ? 2 : 1;
+}
+
+// ---- scalar conversions -------------------------------------------------------------
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(h2_t, w)[0];
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(h2_t, w)[1];
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) {
+  return __builtin_bit_cast(float, w & 0xffff0000u);
+}
+
+// Load one query element of dtype QT as float.
+template <int QT>
+__device__ __forceinline__ float load_q(const void *p, int64_t i) {
+  if constexpr (QT == PA_F32) {
+    return reinterpret_cast<const float *>(p)[i];
+  } else if constexpr (QT == PA_F16) {
+    return (float)reinterpret_cast<const _Float16 *>(p)[i];
+  } else {
+    uint16_t b = reinterpret_cast<const uint16_t *>(p)[i];
+    return __builtin_bit_cast(float, (uint32_t)b << 16);
+  }
+}
+
+// Store a float as dtype OT, rounding to nearest even.
+template <int OT>
+__device__ __forceinline__ void store_out(void *p, int64_t i, float x) {
+  if constexpr (OT == PA_F32) {
+    reinterpret_cast<float *>(p)[i] = x;
+  } else if constexpr (OT == PA_F16) {
+    reinterpret_cast<_Float16 *>(p)[i] = (_Float16)x;
+  } else {
+    reinterpret_cast<__bf16 *>(p)[i] = (__bf16)x;
+  }
+}
+
+// E4M3FN pair -> two floats (gfx950 decodes the OCP format in hardware).
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float *f) {
+  auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  f[0] = lo[0];
+  f[1] = lo[1];
+  f[2] = hi[0];
+  f[3] = hi[1];
+}
+
+__device__ __forceinline__ void i8x4_to_f32(uint32_t w, float *f) {
+  f[0] = (float)(int8_t)(w & 0xff);
+  f[1] = (float)(int8_t)((w >> 8) & 0xff);
+  f[2] = (float)(int8_t)((w >> 16) & 0xff);
+  f[3] = (float)(int8_t)(w >> 24);
+}
+
+// ---- cross-lane sums inside groups of 2^k lanes (DPP, no LDS) ---------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within 8
+constexpr int kDppMirror = 0x140;     // lane i <- lane 15-i within 16
+
+// After the call every lane holds the sum over its aligned group of N lanes.
+// Lanes of one group must hold the same kind of value (a partial dot product).
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "N");
+  if constexpr (N >= 2) x += dpp_f<kDppXor1>(x);
+  if constexpr (N >= 4) x += dpp_f<kDppXor2>(x);
+  if constexpr (N >= 8) x += dpp_f<kDppHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp_f<kDppMirror>(x);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16, 64);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace pa

@@ -1,0 +1,69 @@
+// Kernel argument blocks and launchers shared between the C-ABI layer and the
+// kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct DecodeArgs {
+  const void *k;
+  const void *v;
+  const float *k_scale;
+  const float *v_scale;
+  const void *q;
+  void *out;
+  const int32_t *bt;   // [num_seqs][max_blocks_per_seq]
+  const int32_t *ctx;  // [num_seqs] context (KV) length per sequence
+  float *ws_acc;       // [num_seqs][num_q_heads][max_parts][head_dim]
+  float *ws_m;         // [num_seqs][num_q_heads][max_parts]
+  float *ws_l;
+  int32_t num_kv_heads;
+  int32_t num_q_heads;
+  int32_t max_blocks_per_seq;
+  int32_t part_blocks;  // blocks per context partition
+  int32_t max_parts;    // partitions of the longest context
+  float qk_scale;       // softmax scale * log2(e)
+};
+
+struct PrefillArgs {
+  DecodeArgs dec;        // decode rows (q_len == 1) reuse the decode partition path
+  const int32_t *qsl;    // [num_seqs + 1]
+  int32_t num_seqs;
+};
+
+struct CacheWriteArgs {
+  void *k;
+  void *v;
+  const void *k_new;
+  const void *v_new;
+  const int64_t *slots;
+  int64_t num_blocks;
+  int32_t num_tokens;
+  int32_t num_kv_heads;
+  int32_t row_bytes;  // head_dim * element bytes
+};
+
+struct BlockCopyArgs {
+  void *k;
+  void *v;
+  float *k_scale;
+  float *v_scale;
+  const int32_t *pairs;
+  int32_t num_pairs;
+  int32_t num_kv_heads;
+  int32_t tile_bytes;  // 16 * head_dim * element bytes
+};
+
+hipError_t launch_decode(const DecodeArgs &a, int kv_dtype, int q_dtype, int head_dim, int group,
+                         int num_seqs, hipStream_t st);
+hipError_t launch_prefill(const PrefillArgs &a, int kv_dtype, int q_dtype, int head_dim, int group,
+                          int num_rows, hipStream_t st);
+hipError_t launch_cache_write(const CacheWriteArgs &a, hipStream_t st);
+hipError_t launch_block_copy(const BlockCopyArgs &a, hipStream_t st);
+hipError_t launch_slot_mapping(const int32_t *bt, int32_t mbps, const int32_t *qsl,
+                               const int32_t *seq_lens, int32_t num_seqs, int64_t *slots,
+                               hipStream_t st);
+
+}  // namespace pa
