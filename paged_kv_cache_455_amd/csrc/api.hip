@@ -107,7 +107,7 @@ int decode_part_blocks(int64_t num_rows, int num_kv_heads, int max_blocks) {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsLayout {
-  size_t acc_off, m_off, l_off, total;
+  size_t acc_off, m_off, l_off, hdr_off, total;
 };
 
 WsLayout ws_layout(int64_t rows, int num_q_heads, int head_dim, int max_parts) {
@@ -118,6 +118,27 @@ WsLayout ws_layout(int64_t rows, int num_q_heads, int head_dim, int max_parts) {
   w.m_off = align256(n_ml * head_dim * sizeof(float));
   w.l_off = w.m_off + align256(n_ml * sizeof(float));
   w.total = w.l_off + align256(n_ml * sizeof(float));
+  return w;
+}
+
+// Balanced-split decode: every wave streams at least this many tiles, which bounds
+// how many waves (pieces) can share one (sequence, kv head) segment.
+constexpr int kMinTilesPerWave = 8;
+
+int stream_pieces(int max_ctx) {
+  const int max_blocks = (max_ctx + kBlockTokens - 1) / kBlockTokens;
+  return (max_blocks + kMinTilesPerWave - 1) / kMinTilesPerWave + 1;
+}
+
+WsLayout stream_layout(int64_t num_seqs, int num_q_heads, int head_dim, int max_ctx) {
+  const int pieces = stream_pieces(max_ctx);
+  WsLayout w{};
+  const size_t n_ml = (size_t)num_seqs * num_q_heads * pieces;
+  w.acc_off = 0;
+  w.m_off = align256(n_ml * head_dim * sizeof(float));
+  w.l_off = w.m_off + align256(n_ml * sizeof(float));
+  w.hdr_off = w.l_off + align256(n_ml * sizeof(float));
+  w.total = w.hdr_off + align256((size_t)(num_seqs + 1) * sizeof(int32_t));
   return w;
 }
 
@@ -205,9 +226,7 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       max_context_len <= 0)
     return 0;
-  const int max_blocks = (max_context_len + kBlockTokens - 1) / kBlockTokens;
-  const int pb = decode_part_blocks(num_seqs, num_kv_heads, max_blocks);
-  return ws_layout(num_seqs, num_q_heads, head_dim, max_parts_for(max_context_len, pb)).total;
+  return stream_layout(num_seqs, num_q_heads, head_dim, max_context_len).total;
 }
 
 static pa_status_t fill_decode_args(const pa_kv_pool_t *pool, const void *q, int32_t q_dtype,
@@ -215,7 +234,7 @@ static pa_status_t fill_decode_args(const pa_kv_pool_t *pool, const void *q, int
                                     int32_t max_blocks_per_seq, const int32_t *lens,
                                     int64_t rows, int32_t num_q_heads, int32_t max_len,
                                     float scale, void *workspace, size_t workspace_bytes,
-                                    pa::DecodeArgs &a, int &group) {
+                                    pa::DecodeArgs &a, int &group, bool partitioned = true) {
   pa_status_t st = check_pool(pool, true);
   if (st != PA_OK) return st;
   if ((st = check_q_dtype(pool->kv_dtype, q_dtype)) != PA_OK) return st;
@@ -229,7 +248,8 @@ static pa_status_t fill_decode_args(const pa_kv_pool_t *pool, const void *q, int
   const int max_blocks = (max_len + kBlockTokens - 1) / kBlockTokens;
   const int pb = decode_part_blocks(rows, pool->num_kv_heads, max_blocks);
   const int parts = max_parts_for(max_len, pb);
-  const WsLayout w = ws_layout(rows, num_q_heads, pool->head_dim, parts);
+  const WsLayout w =
+      partitioned ? ws_layout(rows, num_q_heads, pool->head_dim, parts) : WsLayout{};
   if (w.total > 0 && (workspace == nullptr || workspace_bytes < w.total))
     return fail(PA_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
                 workspace ? workspace_bytes : (size_t)0);
@@ -266,10 +286,22 @@ pa_status_t pa_decode(const pa_kv_pool_t *pool, const void *q, int32_t q_dtype, 
   int group = 0;
   pa_status_t st = fill_decode_args(pool, q, q_dtype, out, block_tables, max_blocks_per_seq,
                                     context_lens, num_seqs, num_q_heads, max_context_len, scale,
-                                    workspace, workspace_bytes, a, group);
+                                    nullptr, 0, a, group, /*partitioned=*/false);
   if (st != PA_OK) return st;
-  return hip_status(pa::launch_decode(a, pool->kv_dtype, q_dtype, pool->head_dim, group, num_seqs,
-                                      stream),
+  const WsLayout w = stream_layout(num_seqs, num_q_heads, pool->head_dim, max_context_len);
+  if (workspace == nullptr || workspace_bytes < w.total)
+    return fail(PA_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
+                workspace ? workspace_bytes : (size_t)0);
+  char *ws = reinterpret_cast<char *>(workspace);
+  a.ws_acc = reinterpret_cast<float *>(ws + w.acc_off);
+  a.ws_m = reinterpret_cast<float *>(ws + w.m_off);
+  a.ws_l = reinterpret_cast<float *>(ws + w.l_off);
+  a.hdr = reinterpret_cast<int32_t *>(ws + w.hdr_off);
+  a.max_parts = stream_pieces(max_context_len);
+  a.num_seqs = num_seqs;
+  a.min_tpw = kMinTilesPerWave;
+  return hip_status(pa::launch_decode_stream(a, pool->kv_dtype, q_dtype, pool->head_dim, group,
+                                             num_seqs, stream),
                     "pa_decode launch");
 }
 

@@ -204,11 +204,160 @@ __device__ __forceinline__ void tile_update(DecodeState<KV, QT, D, G> &st,
   }
 }
 
+// ---- fast path for 16-lane token rows (LPT == 16, 4 loads per tile) and G >= 4 ------
+// After the partial dot products every lane of a row holds NV = 4*G partial sums;
+// a reduce-scatter leaves each lane NV/16 finished scores, so each score's exp is
+// computed once.  The probabilities and rescale factors then go back to every lane
+// of the row by DPP row broadcasts for the P.V update.
+template <int KV, int D, int G>
+struct FastGeom {
+  static constexpr bool kOn = Geom<KV, D>::LPT == 16 && Geom<KV, D>::NL == 4 && (G == 4 || G == 8);
+  static constexpr int NV = 4 * G;    // partial values per lane before the reduce-scatter
+  static constexpr int NVL = NV / 16; // finished scores per lane after it
+};
+
+template <int KV, int D, int G>
+struct FastState {
+  static constexpr int NVL = FastGeom<KV, D, G>::NVL;
+  float m[NVL], l[NVL];  // running max / sum for this lane's heads, shared by its row
+};
+
+// Lane c of row r owns, after the reduce-scatter, value indices v = c*NVL + j, i.e.
+// load slot i = c/4 (token 4*(c/4) + r) and heads g = v % G.
+template <int KV, int QT, int D, int G, bool MASK>
+__device__ __forceinline__ void tile_update_fast(DecodeState<KV, QT, D, G> &st,
+                                                 FastState<KV, D, G> &fs,
+                                                 const Chunk<Geom<KV, D>::W32> *kc,
+                                                 const Chunk<Geom<KV, D>::W32> *vc,
+                                                 float qk_scale, float v_scale, int valid_rows,
+                                                 int r, int c) {
+  using Gm = Geom<KV, D>;
+  using Fg = FastGeom<KV, D, G>;
+  constexpr int NL = Gm::NL, EPC = Gm::EPC, W32 = Gm::W32, NV = Fg::NV, NVL = Fg::NVL;
+  constexpr bool kNeedKf = !(KV == PA_F16 || KV == PA_BF16);
+  constexpr bool kQuant = (KV == PA_FP8_E4M3 || KV == PA_I8);
+  float part[NV];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    float kf[kNeedKf ? EPC : 1];
+    if constexpr (kNeedKf) chunk_to_f32<KV, W32>(kc[i], kf);
+#pragma unroll
+    for (int g = 0; g < G; ++g) part[i * G + g] = st.q[g].dot(kc[i], kf);
+  }
+  row_reduce_scatter<NV>(part, c);
+
+  const bool valid = !MASK || (4 * (c >> 2) + r) < valid_rows;
+  float p[NVL];
+  bool changed = false;
+#pragma unroll
+  for (int j = 0; j < NVL; ++j) {
+    float s = part[j] * qk_scale;
+    if constexpr (MASK) s = valid ? s : kNegBig;
+    float mt = fmaxf(s, dpp_f<kDppRor4>(s));
+    mt = fmaxf(mt, dpp_f<kDppRor8>(mt));
+    const float mn = fmaxf(fs.m[j], mt);
+    changed |= mn > fs.m[j];
+    const float alpha = fast_exp2(fs.m[j] - mn);
+    float pj = fast_exp2(s - mn);
+    if constexpr (MASK) pj = valid ? pj : 0.f;
+    fs.l[j] = fs.l[j] * alpha + pj;
+    fs.m[j] = mn;
+    part[NVL + j] = alpha;       // park alpha next to the score slots
+    p[j] = kQuant ? pj * v_scale : pj;
+  }
+  if (__any(changed)) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float a;
+      // alpha of head g lives in lane g / NVL (token slot 0), slot g % NVL
+#define PA_BC(n) case n: a = row_bcast<n>(part[NVL + g % NVL]); break;
+      switch (g / NVL) { PA_BC(0) PA_BC(1) PA_BC(2) PA_BC(3) PA_BC(4) PA_BC(5) PA_BC(6) PA_BC(7) default: a = 1.f; }
+#undef PA_BC
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) st.acc[g][e] *= a;
+    }
+  }
+  float P[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+#define PA_BC(n) case n: P[v] = row_bcast<n>(p[v % NVL]); break;
+    switch (v / NVL) {
+      PA_BC(0) PA_BC(1) PA_BC(2) PA_BC(3) PA_BC(4) PA_BC(5) PA_BC(6) PA_BC(7)
+      PA_BC(8) PA_BC(9) PA_BC(10) PA_BC(11) PA_BC(12) PA_BC(13) PA_BC(14) PA_BC(15)
+    }
+#undef PA_BC
+  }
+
+  const int tg = r;
+  float vf[NL][EPC];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    Chunk<W32> cv = vc[i];
+    if constexpr (MASK) {
+      const bool ok = (i * Gm::TPI + tg) < valid_rows;
+#pragma unroll
+      for (int w = 0; w < W32; ++w) cv.w[w] = ok ? cv.w[w] : 0u;
+    }
+    chunk_to_f32<KV, W32>(cv, vf[i]);
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+      float a = st.acc[g][e];
+#pragma unroll
+      for (int i = 0; i < NL; ++i) a = __builtin_fmaf(P[i * G + g], vf[i][e], a);
+      st.acc[g][e] = a;
+    }
+}
+
+// Turn the fast per-lane state into the generic one (m[G], l[G] shared by a row).
+template <int KV, int QT, int D, int G>
+__device__ __forceinline__ void fast_to_generic(DecodeState<KV, QT, D, G> &st,
+                                                FastState<KV, D, G> &fs) {
+  constexpr int NVL = FastGeom<KV, D, G>::NVL;
+#pragma unroll
+  for (int j = 0; j < NVL; ++j) {  // sum the four token slots' partial l (same max)
+    fs.l[j] += dpp_f<kDppRor4>(fs.l[j]);
+    fs.l[j] += dpp_f<kDppRor8>(fs.l[j]);
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+#define PA_BC(n) case n: st.m[g] = row_bcast<n>(fs.m[g % NVL]); st.l[g] = row_bcast<n>(fs.l[g % NVL]); break;
+    switch (g / NVL) { PA_BC(0) PA_BC(1) PA_BC(2) PA_BC(3) PA_BC(4) PA_BC(5) PA_BC(6) PA_BC(7) }
+#undef PA_BC
+  }
+}
+
 // Combine two online-softmax states (m1, l1, a1) <- (m1, l1, a1) (+) (m2, l2, a2).
 __device__ __forceinline__ void merge_weights(float m1, float m2, float &w1, float &w2, float &mn) {
   mn = fmaxf(m1, m2);
   w1 = fast_exp2(m1 - mn);
   w2 = fast_exp2(m2 - mn);
+}
+
+// Merge the token groups of one wave (lanes that differ above the LPT lanes of a
+// row) so that every lane ends with the wave's (m, l, acc) for its column chunk.
+template <int KV, int QT, int D, int G>
+__device__ __forceinline__ void merge_token_groups(DecodeState<KV, QT, D, G> &st) {
+  constexpr int LPT = Geom<KV, D>::LPT, EPC = Geom<KV, D>::EPC;
+#pragma unroll
+  for (int mask = LPT; mask < kWave; mask <<= 1) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float mo = __shfl_xor(st.m[g], mask, kWave);
+      const float lo = __shfl_xor(st.l[g], mask, kWave);
+      float w1, w2, mn;
+      merge_weights(st.m[g], mo, w1, w2, mn);
+      st.m[g] = mn;
+      st.l[g] = st.l[g] * w1 + lo * w2;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        const float ao = __shfl_xor(st.acc[g][e], mask, kWave);
+        st.acc[g][e] = st.acc[g][e] * w1 + ao * w2;
+      }
+    }
+  }
 }
 
 constexpr int kDecodeWaves = 4;
@@ -274,12 +423,26 @@ __device__ __forceinline__ void decode_partition(const DecodeArgs &a, int s, int
       vs = a.v_scale[tile];
     }
   };
+  constexpr bool kFast = FastGeom<KV, D, G>::kOn;
+  FastState<KV, D, G> fs;
+#pragma unroll
+  for (int j = 0; j < FastGeom<KV, D, G>::NVL; ++j) {
+    fs.m[j] = kNegBig;
+    fs.l[j] = 0.f;
+  }
   auto compute = [&](int j, const Chunk<W32> *kc, const Chunk<W32> *vc, float ks, float vs) {
-    const float qs = a.qk_scale * ks;
-    if (j == last_blk && tail_rows < kBlock)
-      tile_update<KV, QT, D, G, true>(st, kc, vc, qs, vs, tail_rows, tg);
-    else
-      tile_update<KV, QT, D, G, false>(st, kc, vc, qs, vs, kBlock, tg);
+    const float qs = quant ? a.qk_scale * ks : a.qk_scale;
+    if constexpr (kFast) {
+      if (j == last_blk && tail_rows < kBlock)
+        tile_update_fast<KV, QT, D, G, true>(st, fs, kc, vc, qs, vs, tail_rows, tg, cidx);
+      else
+        tile_update_fast<KV, QT, D, G, false>(st, fs, kc, vc, qs, vs, kBlock, tg, cidx);
+    } else {
+      if (j == last_blk && tail_rows < kBlock)
+        tile_update<KV, QT, D, G, true>(st, kc, vc, qs, vs, tail_rows, tg);
+      else
+        tile_update<KV, QT, D, G, false>(st, kc, vc, qs, vs, kBlock, tg);
+    }
   };
 
   int j = jbeg + wave;
@@ -299,24 +462,9 @@ __device__ __forceinline__ void decode_partition(const DecodeArgs &a, int s, int
     }
   }
 
-  // ---- merge the token groups of this wave (lanes that differ in tg) ----
-#pragma unroll
-  for (int mask = LPT; mask < kWave; mask <<= 1) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float mo = __shfl_xor(st.m[g], mask, kWave);
-      const float lo = __shfl_xor(st.l[g], mask, kWave);
-      float w1, w2, mn;
-      merge_weights(st.m[g], mo, w1, w2, mn);
-      st.m[g] = mn;
-      st.l[g] = st.l[g] * w1 + lo * w2;
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) {
-        const float ao = __shfl_xor(st.acc[g][e], mask, kWave);
-        st.acc[g][e] = st.acc[g][e] * w1 + ao * w2;
-      }
-    }
-  }
+  if constexpr (kFast) fast_to_generic(st, fs);
+
+  merge_token_groups(st);
 
   // ---- merge the waves through LDS ----
   __shared__ float sm_acc[NW][G][D];
@@ -381,6 +529,238 @@ __device__ __forceinline__ void merge_partitions(const DecodeArgs &a, int r, int
     A += wt * a.ws_acc[(r0 + p) * D + d];
   }
   store_out<QT>(a.out, ((int64_t)q_row * a.num_q_heads + hq) * D + d, A / L);
+}
+
+// ---- balanced split ("stream" decode) ------------------------------------------------
+// All (sequence, kv head, block) tiles of the batch form one list, ordered by
+// sequence, then kv head, then block: sequence s owns blocks [cum[s], cum[s+1]) of
+// the concatenated tables and its kv head h the tiles
+//   [Hkv*cum[s] + h*nblk_s, Hkv*cum[s] + (h+1)*nblk_s).
+// Wave w of the grid takes the tiles [w*tpw, (w+1)*tpw), tpw = max(min_tpw,
+// ceil(T / waves)): every wave streams the same number of K/V bytes whatever the
+// context lengths.  A wave emits one result per (sequence, kv head) segment it
+// touches: the final output when it owns the whole segment, else a partial
+// (m, l, acc) for "piece" w - first_wave(segment), combined by the merge kernel.
+
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m, kWave);
+  return x;
+}
+__device__ __forceinline__ int wave_incl_scan_i(int x, int lane) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y = __shfl_up(x, d, kWave);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// Write this wave's state for (s, kv head h): normalised output when single,
+// else the partial for `piece`.  Lanes of token group 0 hold every column chunk.
+template <int KV, int QT, int D, int G>
+__device__ __forceinline__ void emit_segment(const DecodeArgs &a, DecodeState<KV, QT, D, G> &st,
+                                             int s, int h, bool single, int piece, int lane) {
+  constexpr int EPC = Geom<KV, D>::EPC, LPT = Geom<KV, D>::LPT;
+  merge_token_groups(st);
+  if (lane >= LPT) return;
+  const int c = lane;
+  if (single) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float inv = 1.f / st.l[g];
+      const int64_t o = ((int64_t)s * a.num_q_heads + h * G + g) * D + c * EPC;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) store_out<QT>(a.out, o + e, st.acc[g][e] * inv);
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int64_t r = ((int64_t)s * a.num_q_heads + h * G + g) * a.max_parts + piece;
+      float *dst = a.ws_acc + r * D + c * EPC;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) dst[e] = st.acc[g][e];
+      if (c == 0) {
+        a.ws_m[r] = st.m[g];
+        a.ws_l[r] = st.l[g];
+      }
+    }
+  }
+}
+
+template <int KV, int QT, int D, int G>
+__device__ __forceinline__ void decode_stream(const DecodeArgs &a) {
+  using Gm = Geom<KV, D>;
+  constexpr int NL = Gm::NL, EPC = Gm::EPC, W32 = Gm::W32, LPT = Gm::LPT;
+  constexpr bool kFast = FastGeom<KV, D, G>::kOn;
+  constexpr bool kQuant = (KV == PA_FP8_E4M3 || KV == PA_I8);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = blockIdx.x * kDecodeWaves + threadIdx.x / kWave;
+  const int Hkv = a.num_kv_heads, S = a.num_seqs;
+
+  // ---- total blocks; wave 0 also records every sequence's first block index ----
+  int NB = 0;
+  for (int c0 = 0; c0 < S; c0 += kWave) {
+    const int sq = c0 + lane;
+    const int n = sq < S ? a.ctx[sq] : 0;
+    const int nb = n > 0 ? (n + kBlock - 1) / kBlock : 0;
+    const int incl = wave_incl_scan_i(nb, lane);
+    if (w == 0 && sq < S) a.hdr[1 + sq] = NB + incl - nb;
+    NB += __shfl(incl, kWave - 1, kWave);
+  }
+  const int T = Hkv * NB;
+  const int tpw = max(a.min_tpw, (T + a.num_waves - 1) / a.num_waves);
+  if (w == 0 && lane == 0) a.hdr[0] = tpw;
+  int t = w * tpw;
+  const int tend = min(t + tpw, T);
+  if (t >= tend) return;
+
+  // ---- locate the first tile: sequence s, kv head h, block j ----
+  int s = 0, cum_s = 0, nblk = 0;
+  {
+    int base = 0;
+    for (int c0 = 0; c0 < S; c0 += kWave) {
+      const int sq = c0 + lane;
+      const int n = sq < S ? a.ctx[sq] : 0;
+      const int nb = n > 0 ? (n + kBlock - 1) / kBlock : 0;
+      const int incl = base + wave_incl_scan_i(nb, lane);
+      const int excl = incl - nb;
+      const unsigned long long hit = __ballot(sq < S && Hkv * excl <= t && t < Hkv * incl);
+      if (hit) {
+        const int l = __builtin_ctzll(hit);
+        s = c0 + l;
+        cum_s = __shfl(excl, l, kWave);
+        nblk = __shfl(nb, l, kWave);
+        break;
+      }
+      base = __shfl(incl, kWave - 1, kWave);
+    }
+  }
+  int h = (t - Hkv * cum_s) / nblk;
+  int j = (t - Hkv * cum_s) - h * nblk;
+
+  const int cidx = lane % LPT, tg = lane / LPT;
+  const char *kbase = reinterpret_cast<const char *>(a.k);
+  const char *vbase = reinterpret_cast<const char *>(a.v);
+  const int lane_off = lane * Gm::CB;
+
+  for (;;) {  // one (sequence, kv head) segment per iteration
+    const int n = a.ctx[s];
+    const int last_blk = nblk - 1;
+    const int tail_rows = n - last_blk * kBlock;
+    const int seg0 = Hkv * cum_s + h * nblk;  // first tile of the segment
+    const int wfirst = seg0 / tpw, wlast = (seg0 + nblk - 1) / tpw;
+    const int jend = min(nblk, j + (tend - t));
+    const int32_t *bt = a.bt + (int64_t)s * a.max_blocks_per_seq;
+
+    DecodeState<KV, QT, D, G> st;
+    FastState<KV, D, G> fs;
+    const int64_t qbase = ((int64_t)s * a.num_q_heads + h * G) * D;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      st.q[g].template load<QT>(a.q, qbase + (int64_t)g * D + cidx * EPC);
+      st.m[g] = kNegBig;
+      st.l[g] = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) st.acc[g][e] = 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < FastGeom<KV, D, G>::NVL; ++i) {
+      fs.m[i] = kNegBig;
+      fs.l[i] = 0.f;
+    }
+
+    Chunk<W32> kA[NL], vA[NL], kB[NL], vB[NL];
+    float ksA = 1.f, vsA = 1.f, ksB = 1.f, vsB = 1.f;
+    auto load_tile = [&](int jj, Chunk<W32> *kc, Chunk<W32> *vc, float &ks, float &vs) {
+      const int64_t tile = (int64_t)bt[jj] * Hkv + h;
+      const char *kp = kbase + tile * Gm::TILE_BYTES + lane_off;
+      const char *vp = vbase + tile * Gm::TILE_BYTES + lane_off;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) kc[i] = load_chunk<W32>(kp + i * kWave * Gm::CB);
+#pragma unroll
+      for (int i = 0; i < NL; ++i) vc[i] = load_chunk<W32>(vp + i * kWave * Gm::CB);
+      if constexpr (kQuant) {
+        ks = a.k_scale[tile];
+        vs = a.v_scale[tile];
+      }
+    };
+    auto compute = [&](int jj, const Chunk<W32> *kc, const Chunk<W32> *vc, float ks, float vs) {
+      const float qs = kQuant ? a.qk_scale * ks : a.qk_scale;
+      if constexpr (kFast) {
+        if (jj == last_blk && tail_rows < kBlock)
+          tile_update_fast<KV, QT, D, G, true>(st, fs, kc, vc, qs, vs, tail_rows, tg, cidx);
+        else
+          tile_update_fast<KV, QT, D, G, false>(st, fs, kc, vc, qs, vs, kBlock, tg, cidx);
+      } else {
+        if (jj == last_blk && tail_rows < kBlock)
+          tile_update<KV, QT, D, G, true>(st, kc, vc, qs, vs, tail_rows, tg);
+        else
+          tile_update<KV, QT, D, G, false>(st, kc, vc, qs, vs, kBlock, tg);
+      }
+    };
+
+    int jj = j;
+    load_tile(jj, kA, vA, ksA, vsA);
+    for (;;) {
+      int jn = jj + 1;
+      if (jn < jend) load_tile(jn, kB, vB, ksB, vsB);
+      compute(jj, kA, vA, ksA, vsA);
+      jj = jn;
+      if (jj >= jend) break;
+      jn = jj + 1;
+      if (jn < jend) load_tile(jn, kA, vA, ksA, vsA);
+      compute(jj, kB, vB, ksB, vsB);
+      jj = jn;
+      if (jj >= jend) break;
+    }
+    if constexpr (kFast) fast_to_generic(st, fs);
+    emit_segment<KV, QT, D, G>(a, st, s, h, wfirst == wlast, w - wfirst, lane);
+
+    t += jend - j;
+    if (t >= tend) break;
+    // next segment: the next kv head, else the next sequence with blocks
+    j = 0;
+    if (++h == Hkv) {
+      h = 0;
+      cum_s += nblk;
+      do {
+        ++s;
+        const int nn = a.ctx[s];
+        nblk = nn > 0 ? (nn + kBlock - 1) / kBlock : 0;
+      } while (nblk == 0);
+    }
+  }
+}
+
+// Second pass of the balanced split, one thread per output element d of
+// (sequence s, query head hq): combine the pieces written by the waves that
+// shared the segment (nothing to do when one wave owned it).
+template <int QT, int D>
+__device__ __forceinline__ void merge_stream(const DecodeArgs &a, int s, int hq, int d) {
+  const int n = a.ctx[s];
+  const int64_t o = ((int64_t)s * a.num_q_heads + hq) * D + d;
+  if (n <= 0) {  // undefined input; keep the output finite and defined
+    store_out<QT>(a.out, o, 0.f);
+    return;
+  }
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int h = hq / G;
+  const int nblk = (n + kBlock - 1) / kBlock;
+  const int tpw = a.hdr[0];
+  const int seg0 = a.num_kv_heads * a.hdr[1 + s] + h * nblk;
+  const int pieces = (seg0 + nblk - 1) / tpw - seg0 / tpw + 1;
+  if (pieces <= 1) return;
+  const int64_t r0 = ((int64_t)s * a.num_q_heads + hq) * a.max_parts;
+  float M = kNegBig;
+  for (int p = 0; p < pieces; ++p) M = fmaxf(M, a.ws_m[r0 + p]);
+  float L = 0.f, A = 0.f;
+  for (int p = 0; p < pieces; ++p) {
+    const float wt = fast_exp2(a.ws_m[r0 + p] - M);
+    L += wt * a.ws_l[r0 + p];
+    A += wt * a.ws_acc[(r0 + p) * D + d];
+  }
+  store_out<QT>(a.out, o, A / L);
 }
 
 }  // namespace pa

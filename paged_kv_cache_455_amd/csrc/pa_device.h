@@ -88,6 +88,40 @@ constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within 8
 constexpr int kDppMirror = 0x140;     // lane i <- lane 15-i within 16
+constexpr int kDppRor4 = 0x124;       // lane i <- lane (i-4) mod 16 within 16
+constexpr int kDppRor8 = 0x128;       // lane i <- lane i^8 within 16
+constexpr int kDppRowBcast0 = 0x150;  // + n: every lane of a 16-lane row <- lane n of that row
+
+// Reduce-scatter across one 16-lane row: on entry each lane holds NV partial values
+// x[0..NV); on exit x[0..NV/16) hold full row sums of value indices
+// c*(NV/16) + j, where c is the lane's index within the row.  Each step pairs a lane
+// with a partner holding the complementary half (xor 8 by rotation, bit 2 by the
+// half-row mirror, then xor 2 and xor 1), keeps one half and adds the partner's copy.
+template <int N, int CTRL>
+__device__ __forceinline__ void rs_step(float *x, bool upper) {
+  constexpr int H = N / 2;
+#pragma unroll
+  for (int k = 0; k < H; ++k) {
+    const float keep = upper ? x[k + H] : x[k];
+    const float send = upper ? x[k] : x[k + H];
+    x[k] = keep + dpp_f<CTRL>(send);
+  }
+}
+
+template <int NV>
+__device__ __forceinline__ void row_reduce_scatter(float *x, int c) {
+  static_assert(NV % 16 == 0, "reduce-scatter needs a multiple of 16 values");
+  rs_step<NV, kDppRor8>(x, (c >> 3) & 1);
+  rs_step<NV / 2, kDppHalfMirror>(x, (c >> 2) & 1);
+  rs_step<NV / 4, kDppXor2>(x, (c >> 1) & 1);
+  rs_step<NV / 8, kDppXor1>(x, c & 1);
+}
+
+// Value of x held by lane n of this lane's 16-lane row (n a compile-time constant).
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+  return dpp_f<kDppRowBcast0 + N>(x);
+}
 
 // After the call every lane holds the sum over its aligned group of N lanes.
 // Lanes of one group must hold the same kind of value (a partial dot product).

@@ -22,9 +22,14 @@ struct DecodeArgs {
   int32_t num_kv_heads;
   int32_t num_q_heads;
   int32_t max_blocks_per_seq;
-  int32_t part_blocks;  // blocks per context partition
-  int32_t max_parts;    // partitions of the longest context
+  int32_t part_blocks;  // blocks per context partition (partitioned path)
+  int32_t max_parts;    // partitions (or pieces) of the longest context
   float qk_scale;       // softmax scale * log2(e)
+  // balanced split: waves share the work evenly; see decode_stream
+  int32_t *hdr;         // [1 + num_seqs]: tiles per wave, then each sequence's first block index
+  int32_t num_seqs;
+  int32_t num_waves;    // waves launched
+  int32_t min_tpw;      // lower bound on tiles per wave
 };
 
 struct PrefillArgs {
@@ -58,6 +63,8 @@ struct BlockCopyArgs {
 
 hipError_t launch_decode(const DecodeArgs &a, int kv_dtype, int q_dtype, int head_dim, int group,
                          int num_seqs, hipStream_t st);
+hipError_t launch_decode_stream(const DecodeArgs &a, int kv_dtype, int q_dtype, int head_dim,
+                                int group, int num_seqs, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs &a, int kv_dtype, int q_dtype, int head_dim, int group,
                           int num_rows, hipStream_t st);
 hipError_t launch_cache_write(const CacheWriteArgs &a, hipStream_t st);
