@@ -230,7 +230,7 @@ def main():
     else:
         ws_bytes = pa.pa_prefill_workspace_size(b.num_seqs, b.num_tokens, b.num_q_heads,
                                                 b.num_kv_heads, b.head_dim, b.max_query_len,
-                                                b.max_seq_len)
+                                                b.max_seq_len, pools[0].k.dtype)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 

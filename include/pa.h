@@ -149,10 +149,11 @@ pa_status_t pa_decode(const pa_kv_pool_t *pool, const void *q, int32_t q_dtype, 
                       int32_t max_context_len, float scale, void *workspace,
                       size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace bytes pa_prefill_chunk needs for these sizes. */
+/* Workspace bytes pa_prefill_chunk needs for these sizes and KV storage type
+ * (0 for invalid sizes). */
 size_t pa_prefill_workspace_size(int32_t num_seqs, int32_t num_q_tokens, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim, int32_t max_query_len,
-                                 int32_t max_seq_len);
+                                 int32_t max_seq_len, int32_t kv_dtype);
 
 /*
  * pa_prefill_chunk -- one continuous-batching step ([P1] Continuous

@@ -66,7 +66,7 @@ _SIGS = {
     "pa_decode": (_c.c_int, [_c.POINTER(_Pool), _c.c_void_p, _c.c_int32, _c.c_void_p, _c.c_void_p,
                              _c.c_int32, _c.c_void_p, _c.c_int32, _c.c_int32, _c.c_int32,
                              _c.c_float, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
-    "pa_prefill_workspace_size": (_c.c_size_t, [_c.c_int32] * 7),
+    "pa_prefill_workspace_size": (_c.c_size_t, [_c.c_int32] * 8),
     "pa_prefill_chunk": (_c.c_int, [_c.POINTER(_Pool), _c.c_void_p, _c.c_int32, _c.c_void_p,
                                     _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int32, _c.c_int32,
                                     _c.c_int32, _c.c_int32, _c.c_int32, _c.c_int32, _c.c_float,
@@ -178,10 +178,12 @@ def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_
 
 
 def pa_prefill_workspace_size(num_seqs, num_q_tokens, num_q_heads, num_kv_heads, head_dim,
-                              max_query_len, max_seq_len) -> int:
+                              max_query_len, max_seq_len, kv_dtype=PA_F16) -> int:
+    if not isinstance(kv_dtype, int):
+        kv_dtype = PA_DTYPE[kv_dtype]
     return int(load_library().pa_prefill_workspace_size(num_seqs, num_q_tokens, num_q_heads,
                                                         num_kv_heads, head_dim, max_query_len,
-                                                        max_seq_len))
+                                                        max_seq_len, kv_dtype))
 
 
 def _workspace(nbytes: int, device, workspace):
@@ -216,7 +218,7 @@ def pa_prefill_chunk(pool: KVPool, q, query_start_loc, seq_lens, block_tables, m
     if out is None:
         out = torch.empty_like(q)
     need = pa_prefill_workspace_size(S, T, hq, pool.num_kv_heads, pool.head_dim, max_query_len,
-                                     max_seq_len)
+                                     max_seq_len, pool.k.dtype)
     workspace = _workspace(need, q.device, workspace)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("pa_prefill_chunk", lib.pa_prefill_chunk(

@@ -305,16 +305,55 @@ pa_status_t pa_decode(const pa_kv_pool_t *pool, const void *q, int32_t q_dtype, 
                     "pa_decode launch");
 }
 
+// Workspace of the mixed step.  f16/bf16 KV: a 2-int header, the work lists and
+// per-sequence decode partitions of kMixedPartBlocks blocks.  Other KV types run
+// every query row through the partitioned decode path (per-row partitions).
+constexpr int kMixedPartBlocks = 32;
+constexpr int kMixedTileRows = 64;  // query rows per prefill tile (matches prefill.hip)
+
+struct MixedLayout {
+  size_t hdr_off, p_off, d_off, acc_off, m_off, l_off, total;
+  int p_bound, d_bound, part_blocks, max_parts, qtok;
+};
+
+MixedLayout mixed_layout(int kv_dtype, int64_t S, int64_t T, int Hq, int Hkv, int D,
+                         int max_seq_len) {
+  MixedLayout w{};
+  const int max_blocks = (max_seq_len + kBlockTokens - 1) / kBlockTokens;
+  int64_t rows;
+  if (pa::mixed_uses_tiles(kv_dtype)) {
+    w.qtok = kMixedTileRows / (Hq / Hkv);
+    w.part_blocks = kMixedPartBlocks;
+    w.max_parts = (max_blocks + w.part_blocks - 1) / w.part_blocks;
+    w.p_bound = (int)((T + w.qtok - 1) / w.qtok + S);
+    w.d_bound = (int)(S * w.max_parts);
+    rows = S;
+  } else {
+    w.part_blocks = decode_part_blocks(T, Hkv, max_blocks);
+    w.max_parts = (max_blocks + w.part_blocks - 1) / w.part_blocks;
+    rows = T;
+  }
+  const size_t n_ml = (size_t)rows * Hq * w.max_parts;
+  w.hdr_off = 0;
+  w.p_off = align256(2 * sizeof(int32_t));
+  w.d_off = w.p_off + align256((size_t)w.p_bound * sizeof(int32_t));
+  w.acc_off = w.d_off + align256((size_t)w.d_bound * sizeof(int32_t));
+  w.m_off = w.acc_off + align256(n_ml * D * sizeof(float));
+  w.l_off = w.m_off + align256(n_ml * sizeof(float));
+  w.total = w.l_off + align256(n_ml * sizeof(float));
+  return w;
+}
+
 size_t pa_prefill_workspace_size(int32_t num_seqs, int32_t num_q_tokens, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim, int32_t max_query_len,
-                                 int32_t max_seq_len) {
+                                 int32_t max_seq_len, int32_t kv_dtype) {
   (void)max_query_len;
   if (num_seqs <= 0 || num_q_tokens <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
-      head_dim <= 0 || max_seq_len <= 0)
+      head_dim <= 0 || max_seq_len <= 0 || num_q_heads % num_kv_heads != 0)
     return 0;
-  const int max_blocks = (max_seq_len + kBlockTokens - 1) / kBlockTokens;
-  const int pb = decode_part_blocks(num_q_tokens, num_kv_heads, max_blocks);
-  return ws_layout(num_q_tokens, num_q_heads, head_dim, max_parts_for(max_seq_len, pb)).total;
+  return mixed_layout(kv_dtype, num_seqs, num_q_tokens, num_q_heads, num_kv_heads, head_dim,
+                      max_seq_len)
+      .total;
 }
 
 pa_status_t pa_prefill_chunk(const pa_kv_pool_t *pool, const void *q, int32_t q_dtype,
@@ -328,16 +367,40 @@ pa_status_t pa_prefill_chunk(const pa_kv_pool_t *pool, const void *q, int32_t q_
   if (!query_start_loc) return fail(PA_E_ARG, "query_start_loc is NULL");
   if (max_query_len <= 0 || max_query_len > max_seq_len)
     return fail(PA_E_ARG, "max_query_len %d must be in [1, max_seq_len]", max_query_len);
-  pa::PrefillArgs a;
+  if (num_seqs >= (1 << 19)) return fail(PA_E_UNSUPPORTED, "num_seqs must be < 2^19");
+  pa::MixedArgs m{};
   int group = 0;
   pa_status_t st = fill_decode_args(pool, q, q_dtype, out, block_tables, max_blocks_per_seq,
                                     seq_lens, num_q_tokens, num_q_heads, max_seq_len, scale,
-                                    workspace, workspace_bytes, a.dec, group);
+                                    nullptr, 0, m.dec, group, /*partitioned=*/false);
   if (st != PA_OK) return st;
-  a.qsl = query_start_loc;
-  a.num_seqs = num_seqs;
-  return hip_status(pa::launch_prefill(a, pool->kv_dtype, q_dtype, pool->head_dim, group,
-                                       num_q_tokens, stream),
+  const MixedLayout w = mixed_layout(pool->kv_dtype, num_seqs, num_q_tokens, num_q_heads,
+                                     pool->num_kv_heads, pool->head_dim, max_seq_len);
+  if (pa::mixed_uses_tiles(pool->kv_dtype)) {
+    if (max_query_len > 4096 * w.qtok)
+      return fail(PA_E_UNSUPPORTED, "max_query_len %d too long (limit %d)", max_query_len,
+                  4096 * w.qtok);
+    if (w.max_parts > 4096) return fail(PA_E_UNSUPPORTED, "max_seq_len too long");
+  }
+  if (workspace == nullptr || workspace_bytes < w.total)
+    return fail(PA_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
+                workspace ? workspace_bytes : (size_t)0);
+  char *ws = reinterpret_cast<char *>(workspace);
+  m.dec.ws_acc = reinterpret_cast<float *>(ws + w.acc_off);
+  m.dec.ws_m = reinterpret_cast<float *>(ws + w.m_off);
+  m.dec.ws_l = reinterpret_cast<float *>(ws + w.l_off);
+  m.dec.part_blocks = w.part_blocks;
+  m.dec.max_parts = w.max_parts;
+  m.qsl = query_start_loc;
+  m.hdr = reinterpret_cast<int32_t *>(ws + w.hdr_off);
+  m.p_items = reinterpret_cast<int32_t *>(ws + w.p_off);
+  m.d_items = reinterpret_cast<int32_t *>(ws + w.d_off);
+  m.num_seqs = num_seqs;
+  m.p_bound = w.p_bound;
+  m.d_bound = w.d_bound;
+  m.qtok = w.qtok;
+  return hip_status(pa::launch_mixed(m, pool->kv_dtype, q_dtype, pool->head_dim, group,
+                                     num_q_tokens, stream),
                     "pa_prefill_chunk launch");
 }
 

@@ -7,7 +7,8 @@ namespace pa {
 template <int KV, int QT, int D, int G>
 __global__ __launch_bounds__(kDecodeWaves *kWave) void pa_decode_partition_kernel(DecodeArgs a) {
   const int s = blockIdx.z;
-  decode_partition<KV, QT, D, G>(a, s, blockIdx.y, blockIdx.x, s, a.ctx[s], s);
+  __shared__ float smem[decode_partition_smem_floats<D, G>()];
+  decode_partition<KV, QT, D, G>(a, s, blockIdx.y, blockIdx.x, s, a.ctx[s], s, smem);
 }
 
 template <int KV, int QT, int D, int G>

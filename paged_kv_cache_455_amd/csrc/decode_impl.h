@@ -362,12 +362,18 @@ __device__ __forceinline__ void merge_token_groups(DecodeState<KV, QT, D, G> &st
 
 constexpr int kDecodeWaves = 4;
 
+// LDS floats decode_partition needs for its cross-wave merge.
+template <int D, int G>
+constexpr int decode_partition_smem_floats() {
+  return kDecodeWaves * G * D + 2 * kDecodeWaves * G;
+}
+
 // One workgroup: query row q_row of sequence s (block-table row), kv head h,
 // context partition p, attending to the first n cached tokens.  Partial states
 // go to workspace row ws_row.
 template <int KV, int QT, int D, int G>
 __device__ __forceinline__ void decode_partition(const DecodeArgs &a, int s, int h, int p,
-                                                 int q_row, int n, int ws_row) {
+                                                 int q_row, int n, int ws_row, float *smem) {
   using Gm = Geom<KV, D>;
   constexpr int NL = Gm::NL, EPC = Gm::EPC, W32 = Gm::W32, LPT = Gm::LPT;
   constexpr int NW = kDecodeWaves;
@@ -466,10 +472,10 @@ __device__ __forceinline__ void decode_partition(const DecodeArgs &a, int s, int
 
   merge_token_groups(st);
 
-  // ---- merge the waves through LDS ----
-  __shared__ float sm_acc[NW][G][D];
-  __shared__ float sm_m[NW][G];
-  __shared__ float sm_l[NW][G];
+  // ---- merge the waves through LDS (smem: NW*G*D + 2*NW*G floats) ----
+  float(*sm_acc)[G][D] = reinterpret_cast<float(*)[G][D]>(smem);
+  float(*sm_m)[G] = reinterpret_cast<float(*)[G]>(smem + NW * G * D);
+  float(*sm_l)[G] = reinterpret_cast<float(*)[G]>(smem + NW * G * D + NW * G);
   if (tg == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {

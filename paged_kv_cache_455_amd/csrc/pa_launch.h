@@ -32,10 +32,16 @@ struct DecodeArgs {
   int32_t min_tpw;      // lower bound on tiles per wave
 };
 
-struct PrefillArgs {
-  DecodeArgs dec;        // decode rows (q_len == 1) reuse the decode partition path
-  const int32_t *qsl;    // [num_seqs + 1]
+struct MixedArgs {
+  DecodeArgs dec;       // pools, q/out, tables, seq_lens (as ctx), decode-row workspace
+  const int32_t *qsl;   // [num_seqs + 1]
+  int32_t *hdr;         // [2]: prefill items, decode items (written by the prep kernel)
+  int32_t *p_items;     // [p_bound]
+  int32_t *d_items;     // [d_bound]
   int32_t num_seqs;
+  int32_t p_bound;
+  int32_t d_bound;
+  int32_t qtok;         // query tokens per prefill tile (128 / G)
 };
 
 struct CacheWriteArgs {
@@ -65,8 +71,9 @@ hipError_t launch_decode(const DecodeArgs &a, int kv_dtype, int q_dtype, int hea
                          int num_seqs, hipStream_t st);
 hipError_t launch_decode_stream(const DecodeArgs &a, int kv_dtype, int q_dtype, int head_dim,
                                 int group, int num_seqs, hipStream_t st);
-hipError_t launch_prefill(const PrefillArgs &a, int kv_dtype, int q_dtype, int head_dim, int group,
-                          int num_rows, hipStream_t st);
+bool mixed_uses_tiles(int kv_dtype);
+hipError_t launch_mixed(const MixedArgs &a, int kv_dtype, int q_dtype, int head_dim, int group,
+                        int num_rows, hipStream_t st);
 hipError_t launch_cache_write(const CacheWriteArgs &a, hipStream_t st);
 hipError_t launch_block_copy(const BlockCopyArgs &a, hipStream_t st);
 hipError_t launch_slot_mapping(const int32_t *bt, int32_t mbps, const int32_t *qsl,

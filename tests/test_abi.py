@@ -82,7 +82,9 @@ def test_workspace_sizes(lib):
     b = pa.pa_decode_workspace_size(64, 32, 8, 128, 8192)
     assert 0 < a < b
     assert pa.pa_decode_workspace_size(0, 32, 8, 128, 4096) == 0
-    assert pa.pa_prefill_workspace_size(10, 100, 32, 8, 128, 64, 4096) > 0
+    assert pa.pa_prefill_workspace_size(10, 100, 32, 8, 128, 64, 4096, pa.PA_F16) > 0
+    assert pa.pa_prefill_workspace_size(10, 100, 32, 8, 128, 64, 4096, pa.PA_F32) > 0
+    assert pa.pa_prefill_workspace_size(10, 100, 30, 8, 128, 64, 4096, pa.PA_F16) == 0
 
 
 def test_write_copy_slot_checks(lib):
