@@ -1,5 +1,7 @@
 // Paged decode attention: split-context online softmax + second-pass merge
 // (the device templates and their description are in decode_impl.h).
+#include <stdlib.h>
+
 #include "decode_impl.h"
 
 namespace pa {
@@ -16,9 +18,12 @@ __global__ __launch_bounds__(kDecodeWaves *kWave) void pa_decode_stream_kernel(D
   decode_stream<KV, QT, D, G>(a);
 }
 
+// One wave per (sequence, query head); four per workgroup.
 template <int QT, int D>
-__global__ __launch_bounds__(D) void pa_decode_stream_merge_kernel(DecodeArgs a) {
-  merge_stream<QT, D>(a, blockIdx.y, blockIdx.x, threadIdx.x);
+__global__ __launch_bounds__(4 * kWave) void pa_decode_stream_merge_kernel(DecodeArgs a) {
+  const int row = blockIdx.x * 4 + threadIdx.x / kWave;  // s * num_q_heads + hq
+  if (row >= a.num_seqs * a.num_q_heads) return;
+  merge_stream<QT, D>(a, row / a.num_q_heads, row % a.num_q_heads, threadIdx.x % kWave);
 }
 
 // Second pass: combine a sequence's partitions, one workgroup per (seq, q head).
@@ -80,14 +85,19 @@ static int resident_groups() {
 template <int KV, int QT, int D, int G>
 static hipError_t launch_stream_kg(DecodeArgs a, int num_seqs, hipStream_t st) {
   auto kern = pa_decode_stream_kernel<KV, QT, D, G>;
-  const int groups = resident_groups<KV, QT, D, G>();
+  static const int oversub = [] {
+    const char *v = getenv("PA_STREAM_OVERSUB");
+    const int x = v ? atoi(v) : 0;
+    return x > 0 ? x : 1;
+  }();
+  const int groups = resident_groups<KV, QT, D, G>() * oversub;
   if (groups <= 0) return hipErrorInvalidDeviceFunction;
   a.num_waves = groups * kDecodeWaves;
   hipLaunchKernelGGL(kern, dim3(groups), dim3(kDecodeWaves * kWave), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 mgrid(a.num_q_heads, num_seqs);
-  hipLaunchKernelGGL((pa_decode_stream_merge_kernel<QT, D>), mgrid, dim3(D), 0, st, a);
+  dim3 mgrid((num_seqs * a.num_q_heads + 3) / 4);
+  hipLaunchKernelGGL((pa_decode_stream_merge_kernel<QT, D>), mgrid, dim3(4 * kWave), 0, st, a);
   return hipGetLastError();
 }
 

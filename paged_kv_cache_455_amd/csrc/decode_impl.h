@@ -606,11 +606,16 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a) {
 
   // ---- total blocks; wave 0 also records every sequence's first block index ----
   int NB = 0;
+  int nb0 = 0, incl0 = 0;  // first 64 sequences, kept for the locate pass
   for (int c0 = 0; c0 < S; c0 += kWave) {
     const int sq = c0 + lane;
     const int n = sq < S ? a.ctx[sq] : 0;
     const int nb = n > 0 ? (n + kBlock - 1) / kBlock : 0;
     const int incl = wave_incl_scan_i(nb, lane);
+    if (c0 == 0) {
+      nb0 = nb;
+      incl0 = incl;
+    }
     if (w == 0 && sq < S) a.hdr[1 + sq] = NB + incl - nb;
     NB += __shfl(incl, kWave - 1, kWave);
   }
@@ -627,9 +632,15 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a) {
     int base = 0;
     for (int c0 = 0; c0 < S; c0 += kWave) {
       const int sq = c0 + lane;
-      const int n = sq < S ? a.ctx[sq] : 0;
-      const int nb = n > 0 ? (n + kBlock - 1) / kBlock : 0;
-      const int incl = base + wave_incl_scan_i(nb, lane);
+      int nb, incl;
+      if (c0 == 0) {  // already scanned
+        nb = nb0;
+        incl = incl0;
+      } else {
+        const int n = sq < S ? a.ctx[sq] : 0;
+        nb = n > 0 ? (n + kBlock - 1) / kBlock : 0;
+        incl = base + wave_incl_scan_i(nb, lane);
+      }
       const int excl = incl - nb;
       const unsigned long long hit = __ballot(sq < S && Hkv * excl <= t && t < Hkv * incl);
       if (hit) {
@@ -650,21 +661,28 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a) {
   const char *vbase = reinterpret_cast<const char *>(a.v);
   const int lane_off = lane * Gm::CB;
 
-  for (;;) {  // one (sequence, kv head) segment per iteration
-    const int n = a.ctx[s];
-    const int last_blk = nblk - 1;
-    const int tail_rows = n - last_blk * kBlock;
-    const int seg0 = Hkv * cum_s + h * nblk;  // first tile of the segment
-    const int wfirst = seg0 / tpw, wlast = (seg0 + nblk - 1) / tpw;
-    const int jend = min(nblk, j + (tend - t));
-    const int32_t *bt = a.bt + (int64_t)s * a.max_blocks_per_seq;
+  // The segment being computed (cur) and the load cursor, which runs one tile
+  // ahead and may already stand in the next segment; entering a segment prefetches
+  // its q into qn, so a wave crossing segments keeps its loads in flight.
+  struct Seg {
+    int s, h, nblk, cum, tail;
+  };
+  auto tail_of = [&](int sq, int nb) { return a.ctx[sq] - (nb - 1) * kBlock; };
+  Seg cur{s, h, nblk, cum_s, tail_of(s, nblk)};
+  Seg lseg = cur, pend = cur;
+  int lj = j;
 
-    DecodeState<KV, QT, D, G> st;
-    FastState<KV, D, G> fs;
-    const int64_t qbase = ((int64_t)s * a.num_q_heads + h * G) * D;
+  DecodeState<KV, QT, D, G> st;
+  FastState<KV, D, G> fs;
+  QFrag<KV, EPC> qn[G];
+  auto load_q = [&](QFrag<KV, EPC> *qf, const Seg &sg) {
+    const int64_t qbase = ((int64_t)sg.s * a.num_q_heads + sg.h * G) * D;
+#pragma unroll
+    for (int g = 0; g < G; ++g) qf[g].template load<QT>(a.q, qbase + (int64_t)g * D + cidx * EPC);
+  };
+  auto reset_state = [&]() {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      st.q[g].template load<QT>(a.q, qbase + (int64_t)g * D + cidx * EPC);
       st.m[g] = kNegBig;
       st.l[g] = 0.f;
 #pragma unroll
@@ -675,79 +693,114 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a) {
       fs.m[i] = kNegBig;
       fs.l[i] = 0.f;
     }
+  };
+  load_q(st.q, cur);
+  reset_state();
 
-    Chunk<W32> kA[NL], vA[NL], kB[NL], vB[NL];
-    float ksA = 1.f, vsA = 1.f, ksB = 1.f, vsB = 1.f;
-    auto load_tile = [&](int jj, Chunk<W32> *kc, Chunk<W32> *vc, float &ks, float &vs) {
-      const int64_t tile = (int64_t)bt[jj] * Hkv + h;
-      const char *kp = kbase + tile * Gm::TILE_BYTES + lane_off;
-      const char *vp = vbase + tile * Gm::TILE_BYTES + lane_off;
+  Chunk<W32> kA[NL], vA[NL], kB[NL], vB[NL];
+  float ksA = 1.f, vsA = 1.f, ksB = 1.f, vsB = 1.f;
+  auto load_tile = [&](const Seg &sg, int jj, Chunk<W32> *kc, Chunk<W32> *vc, float &ks,
+                       float &vs) {
+    const int64_t tile = (int64_t)a.bt[(int64_t)sg.s * a.max_blocks_per_seq + jj] * Hkv + sg.h;
+    const char *kp = kbase + tile * Gm::TILE_BYTES + lane_off;
+    const char *vp = vbase + tile * Gm::TILE_BYTES + lane_off;
 #pragma unroll
-      for (int i = 0; i < NL; ++i) kc[i] = load_chunk<W32>(kp + i * kWave * Gm::CB);
+    for (int i = 0; i < NL; ++i) kc[i] = load_chunk<W32>(kp + i * kWave * Gm::CB);
 #pragma unroll
-      for (int i = 0; i < NL; ++i) vc[i] = load_chunk<W32>(vp + i * kWave * Gm::CB);
-      if constexpr (kQuant) {
-        ks = a.k_scale[tile];
-        vs = a.v_scale[tile];
-      }
-    };
-    auto compute = [&](int jj, const Chunk<W32> *kc, const Chunk<W32> *vc, float ks, float vs) {
-      const float qs = kQuant ? a.qk_scale * ks : a.qk_scale;
-      if constexpr (kFast) {
-        if (jj == last_blk && tail_rows < kBlock)
-          tile_update_fast<KV, QT, D, G, true>(st, fs, kc, vc, qs, vs, tail_rows, tg, cidx);
-        else
-          tile_update_fast<KV, QT, D, G, false>(st, fs, kc, vc, qs, vs, kBlock, tg, cidx);
-      } else {
-        if (jj == last_blk && tail_rows < kBlock)
-          tile_update<KV, QT, D, G, true>(st, kc, vc, qs, vs, tail_rows, tg);
-        else
-          tile_update<KV, QT, D, G, false>(st, kc, vc, qs, vs, kBlock, tg);
-      }
-    };
-
-    int jj = j;
-    load_tile(jj, kA, vA, ksA, vsA);
-    for (;;) {
-      int jn = jj + 1;
-      if (jn < jend) load_tile(jn, kB, vB, ksB, vsB);
-      compute(jj, kA, vA, ksA, vsA);
-      jj = jn;
-      if (jj >= jend) break;
-      jn = jj + 1;
-      if (jn < jend) load_tile(jn, kA, vA, ksA, vsA);
-      compute(jj, kB, vB, ksB, vsB);
-      jj = jn;
-      if (jj >= jend) break;
+    for (int i = 0; i < NL; ++i) vc[i] = load_chunk<W32>(vp + i * kWave * Gm::CB);
+    if constexpr (kQuant) {
+      ks = a.k_scale[tile];
+      vs = a.v_scale[tile];
     }
-    if constexpr (kFast) fast_to_generic(st, fs);
-    emit_segment<KV, QT, D, G>(a, st, s, h, wfirst == wlast, w - wfirst, lane);
-
-    t += jend - j;
-    if (t >= tend) break;
-    // next segment: the next kv head, else the next sequence with blocks
-    j = 0;
-    if (++h == Hkv) {
-      h = 0;
-      cum_s += nblk;
+  };
+  // Move the load cursor to the next tile of the wave's range (one exists).
+  auto advance = [&]() {
+    if (++lj < lseg.nblk) return;
+    lj = 0;
+    if (++lseg.h == Hkv) {
+      lseg.h = 0;
+      lseg.cum += lseg.nblk;
+      int nb;
       do {
-        ++s;
-        const int nn = a.ctx[s];
-        nblk = nn > 0 ? (nn + kBlock - 1) / kBlock : 0;
-      } while (nblk == 0);
+        ++lseg.s;
+        const int nn = a.ctx[lseg.s];
+        nb = nn > 0 ? (nn + kBlock - 1) / kBlock : 0;
+      } while (nb == 0);
+      lseg.nblk = nb;
     }
+    lseg.tail = tail_of(lseg.s, lseg.nblk);
+    load_q(qn, lseg);
+    pend = lseg;
+  };
+  auto compute = [&](int jj, const Chunk<W32> *kc, const Chunk<W32> *vc, float ks, float vs) {
+    const float qs = kQuant ? a.qk_scale * ks : a.qk_scale;
+    const bool masked = jj == cur.nblk - 1 && cur.tail < kBlock;
+    if constexpr (kFast) {
+      if (masked)
+        tile_update_fast<KV, QT, D, G, true>(st, fs, kc, vc, qs, vs, cur.tail, tg, cidx);
+      else
+        tile_update_fast<KV, QT, D, G, false>(st, fs, kc, vc, qs, vs, kBlock, tg, cidx);
+    } else {
+      if (masked)
+        tile_update<KV, QT, D, G, true>(st, kc, vc, qs, vs, cur.tail, tg);
+      else
+        tile_update<KV, QT, D, G, false>(st, kc, vc, qs, vs, kBlock, tg);
+    }
+  };
+  // After a tile: emit the segment if it ended (or the range did), then switch.
+  auto after = [&](int jj, bool has_next) {
+    if (jj != cur.nblk - 1 && has_next) return;
+    if constexpr (kFast) fast_to_generic(st, fs);
+    const int seg0 = Hkv * cur.cum + cur.h * cur.nblk;  // first tile of the segment
+    const int wfirst = seg0 / tpw, wlast = (seg0 + cur.nblk - 1) / tpw;
+    emit_segment<KV, QT, D, G>(a, st, cur.s, cur.h, wfirst == wlast, w - wfirst, lane);
+    if (!has_next) return;
+    cur = pend;
+#pragma unroll
+    for (int g = 0; g < G; ++g) st.q[g] = qn[g];
+    reset_state();
+  };
+
+  const int ntiles = tend - t;
+  int jA = lj, jB = 0;
+  load_tile(lseg, lj, kA, vA, ksA, vsA);
+  for (int k = 0;;) {
+    bool more = k + 1 < ntiles;
+    if (more) {
+      advance();
+      jB = lj;
+      load_tile(lseg, lj, kB, vB, ksB, vsB);
+    }
+    compute(jA, kA, vA, ksA, vsA);
+    after(jA, more);
+    if (!more) break;
+    ++k;
+    more = k + 1 < ntiles;
+    if (more) {
+      advance();
+      jA = lj;
+      load_tile(lseg, lj, kA, vA, ksA, vsA);
+    }
+    compute(jB, kB, vB, ksB, vsB);
+    after(jB, more);
+    if (!more) break;
+    ++k;
   }
 }
 
-// Second pass of the balanced split, one thread per output element d of
-// (sequence s, query head hq): combine the pieces written by the waves that
-// shared the segment (nothing to do when one wave owned it).
+
+// Second pass of the balanced split.  One wave per (sequence s, query head hq):
+// lane p reads piece p's (m, l) (all pieces in flight at once), wave reductions
+// give M = max_p m_p and L = sum_p 2^(m_p - M) l_p, then every lane combines its
+// output elements d, issuing the pieces' acc loads eight at a time:
+//   out[d] = sum_p 2^(m_p - M) acc_p[d] / L.
+// Nothing to do where one wave owned the whole segment (pieces == 1).
 template <int QT, int D>
-__device__ __forceinline__ void merge_stream(const DecodeArgs &a, int s, int hq, int d) {
+__device__ __forceinline__ void merge_stream(const DecodeArgs &a, int s, int hq, int lane) {
   const int n = a.ctx[s];
-  const int64_t o = ((int64_t)s * a.num_q_heads + hq) * D + d;
+  const int64_t o = ((int64_t)s * a.num_q_heads + hq) * D;
   if (n <= 0) {  // undefined input; keep the output finite and defined
-    store_out<QT>(a.out, o, 0.f);
+    for (int d = lane; d < D; d += kWave) store_out<QT>(a.out, o + d, 0.f);
     return;
   }
   const int G = a.num_q_heads / a.num_kv_heads;
@@ -758,15 +811,60 @@ __device__ __forceinline__ void merge_stream(const DecodeArgs &a, int s, int hq,
   const int pieces = (seg0 + nblk - 1) / tpw - seg0 / tpw + 1;
   if (pieces <= 1) return;
   const int64_t r0 = ((int64_t)s * a.num_q_heads + hq) * a.max_parts;
-  float M = kNegBig;
-  for (int p = 0; p < pieces; ++p) M = fmaxf(M, a.ws_m[r0 + p]);
-  float L = 0.f, A = 0.f;
-  for (int p = 0; p < pieces; ++p) {
-    const float wt = fast_exp2(a.ws_m[r0 + p] - M);
-    L += wt * a.ws_l[r0 + p];
-    A += wt * a.ws_acc[(r0 + p) * D + d];
+  constexpr int PER = (D + kWave - 1) / kWave;  // output elements per lane
+  constexpr int PB = 8;                         // pieces whose acc loads are in flight together
+  // Round 1 of loads: (m, l) of every piece (lane p) and the acc of the first PB pieces
+  // (the acc loads do not wait for the weights).
+  float mp = kNegBig, lp = 0.f;
+  if (lane < pieces) {
+    mp = a.ws_m[r0 + lane];
+    lp = a.ws_l[r0 + lane];
   }
-  store_out<QT>(a.out, o, A / L);
+  float v[PB][PER];
+#pragma unroll
+  for (int j = 0; j < PB; ++j)
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int d = lane + i * kWave;
+      v[j][i] = (j < pieces && d < D) ? a.ws_acc[(r0 + j) * D + d] : 0.f;
+    }
+  float M = mp;
+  for (int p = lane + kWave; p < pieces; p += kWave) M = fmaxf(M, a.ws_m[r0 + p]);
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) M = fmaxf(M, __shfl_xor(M, m, kWave));
+  float L = lane < pieces ? fast_exp2(mp - M) * lp : 0.f;
+  for (int p = lane + kWave; p < pieces; p += kWave) L += fast_exp2(a.ws_m[r0 + p] - M) * a.ws_l[r0 + p];
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) L += __shfl_xor(L, m, kWave);
+  const float invL = 1.f / L;
+  float acc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  for (int p0 = 0; p0 < pieces; p0 += PB) {
+    if (p0 > 0) {
+#pragma unroll
+      for (int j = 0; j < PB; ++j)
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          const int d = lane + i * kWave;
+          v[j][i] = (p0 + j < pieces && d < D) ? a.ws_acc[(r0 + p0 + j) * D + d] : 0.f;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < PB; ++j) {
+      // weight of piece p0 + j: lane (p0 + j) % 64 holds its m when p0 + j < 64
+      const int p = p0 + j;
+      const float mpj = p < kWave ? __shfl(mp, p, kWave) : (p < pieces ? a.ws_m[r0 + p] : kNegBig);
+      const float wt = p < pieces ? fast_exp2(mpj - M) : 0.f;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[i] += wt * v[j][i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int d = lane + i * kWave;
+    if (d < D) store_out<QT>(a.out, o + d, acc[i] * invL);
+  }
 }
 
 }  // namespace pa
