@@ -594,15 +594,171 @@ __device__ __forceinline__ void emit_segment(const DecodeArgs &a, DecodeState<KV
   }
 }
 
+// ---- 1-byte KV with a GQA group of 8: q.k on MFMA --------------------------------
+// A (block, kv head) tile of 16 keys x 128 dims against the group's 8 query heads
+// is a dense [16 x 128] . [128 x 8] product: it goes to v_mfma_f32_16x16x32 (bf16,
+// or f16 for f16 queries) with the codes converted exactly, heads padded to 16.
+// Lane (c16, g16) supplies key row c16 and dims {16*g16 + 8*kk} (kk = 0, 1) and
+// {64 + 16*g16 + 8*(kk-2)} (kk = 2, 3) -- two coalesced 16-byte loads per lane --
+// and receives the scores of keys 4*g16 .. +3 for head c16.  Each head's running
+// max is shared by the whole wave; the probabilities reach the P.V lanes (the
+// coalesced V layout of the VALU path) through a small wave-private LDS area.
+typedef _Float16 h8v_t __attribute__((ext_vector_type(8)));
+typedef __bf16 b8v_t __attribute__((ext_vector_type(8)));
+typedef float f4v_t __attribute__((ext_vector_type(4)));
+
+template <int KV, int D, int G>
+struct Q8Geom {
+  static constexpr bool kOn = (KV == PA_FP8_E4M3 || KV == PA_I8) && G == 8 && D == 128;
+  static constexpr int kLdsFloats = 16 * 8 + 8;  // P[16 keys][8 heads] + alpha[8]
+};
+
+struct Q8State {
+  u32x4 qb[4];  // B operand per k-step: q[head c16][8 dims]
+  float m, l;   // running max (shared by the head's lanes) and this lane's partial sum
+};
+
+// 8 codes (two words) -> 8 MFMA inputs (bf16 or f16, exact) packed in 4 words.
+template <int KV, int QT>
+__device__ __forceinline__ void codes_to_mfma(uint32_t w0, uint32_t w1, uint32_t *out) {
+  float f[8];
+  if constexpr (KV == PA_FP8_E4M3) {
+    fp8x4_to_f32(w0, f);
+    fp8x4_to_f32(w1, f + 4);
+  } else {
+    i8x4_to_f32(w0, f);
+    i8x4_to_f32(w1, f + 4);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (QT == PA_F16) {
+      out[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[2 * i], f[2 * i + 1]));
+    } else {
+      out[i] = (__builtin_bit_cast(uint32_t, f[2 * i]) >> 16) |
+               (__builtin_bit_cast(uint32_t, f[2 * i + 1]) & 0xffff0000u);
+    }
+  }
+}
+
+template <int QT>
+__device__ __forceinline__ f4v_t mfma_q(const u32x4 &a, const u32x4 &b, const f4v_t &c) {
+  if constexpr (QT == PA_F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8v_t, a),
+                                                  __builtin_bit_cast(h8v_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8v_t, a),
+                                                   __builtin_bit_cast(b8v_t, b), c, 0, 0, 0);
+}
+
+// dims of k-step kk held by lane group g16 (the same map for K and q)
+__device__ __forceinline__ int q8_dim0(int kk, int g16) {
+  return (kk < 2 ? 0 : 64) + 16 * g16 + 8 * (kk & 1);
+}
+
+// One tile for the MFMA q.k path (see above).  kc holds this lane's 32 K codes
+// (key c16); vc the coalesced V chunks of rows 4i + r (r = tg).
+template <int KV, int QT, int D, int G>
+__device__ __forceinline__ void tile_update_q8(DecodeState<KV, QT, D, G> &st, Q8State &q8,
+                                               float *lds, const Chunk<2> *kc, const Chunk<2> *vc,
+                                               float qk_scale, float v_scale, int valid_rows,
+                                               int r, int g16, int c16) {
+  constexpr int EPC = 8, NL = 4;
+  f4v_t sacc = f4v_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    u32x4 ka;
+    uint32_t t4[4];
+    codes_to_mfma<KV, QT>(kc[kk].w[0], kc[kk].w[1], t4);
+    ka[0] = t4[0]; ka[1] = t4[1]; ka[2] = t4[2]; ka[3] = t4[3];
+    sacc = mfma_q<QT>(ka, q8.qb[kk], sacc);
+  }
+  // scores of keys 4*g16 + i for head c16
+  float sv[4];
+  float mx = kNegBig;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool ok = 4 * g16 + i < valid_rows;
+    sv[i] = ok ? sacc[i] * qk_scale : kNegBig;
+    mx = fmaxf(mx, sv[i]);
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+  const float mn = fmaxf(q8.m, mx);
+  const bool changed = mn > q8.m;
+  const float alpha = fast_exp2(q8.m - mn);
+  float psum = 0.f;
+  float pv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float p = 4 * g16 + i < valid_rows ? fast_exp2(sv[i] - mn) : 0.f;
+    psum += p;
+    pv[i] = p * v_scale;
+  }
+  q8.l = q8.l * alpha + psum;
+  q8.m = mn;
+  if (c16 < G) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds[(4 * g16 + i) * 8 + c16] = pv[i];
+    if (g16 == 0) lds[128 + c16] = alpha;
+  }
+  if (__any(changed)) {  // the heads' rescale factors
+    const f4v_t alo = *reinterpret_cast<const f4v_t *>(lds + 128);
+    const f4v_t ahi = *reinterpret_cast<const f4v_t *>(lds + 132);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float ag = g < 4 ? alo[g] : ahi[g - 4];
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) st.acc[g][e] *= ag;
+    }
+  }
+  // P.V one V row (token 4i + r) at a time: its 8 probabilities and 8 values
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const f4v_t plo = *reinterpret_cast<const f4v_t *>(lds + (4 * i + r) * 8);
+    const f4v_t phi = *reinterpret_cast<const f4v_t *>(lds + (4 * i + r) * 8 + 4);
+    Chunk<2> cv = vc[i];
+    const bool ok = 4 * i + r < valid_rows;
+    cv.w[0] = ok ? cv.w[0] : 0u;
+    cv.w[1] = ok ? cv.w[1] : 0u;
+    float vf[EPC];
+    chunk_to_f32<KV, 2>(cv, vf);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float pg = g < 4 ? plo[g] : phi[g - 4];
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) st.acc[g][e] = __builtin_fmaf(pg, vf[e], st.acc[g][e]);
+    }
+  }
+}
+
+// The MFMA path's state as the generic per-lane (m[G], l[G]): the maxima are shared
+// by the wave; the whole l goes to token group 0 (its merge sums the groups).
+template <int KV, int QT, int D, int G>
+__device__ __forceinline__ void q8_to_generic(DecodeState<KV, QT, D, G> &st, Q8State &q8, int r) {
+  float lt = q8.l;
+  lt += __shfl_xor(lt, 16, kWave);
+  lt += __shfl_xor(lt, 32, kWave);
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    st.m[g] = __shfl(q8.m, g, kWave);
+    const float lg = __shfl(lt, g, kWave);
+    st.l[g] = r == 0 ? lg : 0.f;
+  }
+}
+
 template <int KV, int QT, int D, int G>
 __device__ __forceinline__ void decode_stream(const DecodeArgs &a) {
   using Gm = Geom<KV, D>;
   constexpr int NL = Gm::NL, EPC = Gm::EPC, W32 = Gm::W32, LPT = Gm::LPT;
   constexpr bool kFast = FastGeom<KV, D, G>::kOn;
   constexpr bool kQuant = (KV == PA_FP8_E4M3 || KV == PA_I8);
+  constexpr bool kQ8 = Q8Geom<KV, D, G>::kOn;
   const int lane = threadIdx.x & (kWave - 1);
   const int w = blockIdx.x * kDecodeWaves + threadIdx.x / kWave;
   const int Hkv = a.num_kv_heads, S = a.num_seqs;
+  __shared__ float q8_lds[kQ8 ? kDecodeWaves * Q8Geom<KV, D, G>::kLdsFloats : 1];
+  float *q8l = q8_lds + (kQ8 ? (threadIdx.x / kWave) * Q8Geom<KV, D, G>::kLdsFloats : 0);
+  const int g16 = lane >> 4, c16 = lane & 15;
 
   // ---- total blocks; wave 0 also records every sequence's first block index ----
   int NB = 0;
@@ -674,11 +830,26 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a) {
 
   DecodeState<KV, QT, D, G> st;
   FastState<KV, D, G> fs;
-  QFrag<KV, EPC> qn[G];
-  auto load_q = [&](QFrag<KV, EPC> *qf, const Seg &sg) {
+  QFrag<KV, EPC> qn[kQ8 ? 1 : G];
+  Q8State q8, q8n;  // q8n: unused by the MFMA path (it loads q at a segment switch)
+  auto load_q = [&](QFrag<KV, EPC> *qf, Q8State &q8s, const Seg &sg) {
     const int64_t qbase = ((int64_t)sg.s * a.num_q_heads + sg.h * G) * D;
+    if constexpr (kQ8) {
+      (void)qf;
 #pragma unroll
-    for (int g = 0; g < G; ++g) qf[g].template load<QT>(a.q, qbase + (int64_t)g * D + cidx * EPC);
+      for (int kk = 0; kk < 4; ++kk) q8s.qb[kk] = u32x4{0, 0, 0, 0};
+      if (c16 < G) {
+        const char *qp = reinterpret_cast<const char *>(a.q) + (qbase + (int64_t)c16 * D) * 2;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          q8s.qb[kk] = *reinterpret_cast<const u32x4 *>(qp + q8_dim0(kk, g16) * 2);
+      }
+    } else {
+      (void)q8s;
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        qf[g].template load<QT>(a.q, qbase + (int64_t)g * D + cidx * EPC);
+    }
   };
   auto reset_state = [&]() {
 #pragma unroll
@@ -693,8 +864,10 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a) {
       fs.m[i] = kNegBig;
       fs.l[i] = 0.f;
     }
+    q8.m = kNegBig;
+    q8.l = 0.f;
   };
-  load_q(st.q, cur);
+  load_q(st.q, q8, cur);
   reset_state();
 
   Chunk<W32> kA[NL], vA[NL], kB[NL], vB[NL];
@@ -702,10 +875,20 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a) {
   auto load_tile = [&](const Seg &sg, int jj, Chunk<W32> *kc, Chunk<W32> *vc, float &ks,
                        float &vs) {
     const int64_t tile = (int64_t)a.bt[(int64_t)sg.s * a.max_blocks_per_seq + jj] * Hkv + sg.h;
-    const char *kp = kbase + tile * Gm::TILE_BYTES + lane_off;
     const char *vp = vbase + tile * Gm::TILE_BYTES + lane_off;
+    if constexpr (kQ8) {
+      // K as the MFMA A operand: key row c16, bytes [16*g16, +16) and [64 + 16*g16, +16)
+      static_assert(NL * W32 == 8, "q8 K staging uses the 8 words of kc");
+      const char *kp = kbase + tile * Gm::TILE_BYTES + c16 * D + 16 * g16;
+      const u32x4 k0 = *reinterpret_cast<const u32x4 *>(kp);
+      const u32x4 k1 = *reinterpret_cast<const u32x4 *>(kp + 64);
+      kc[0].w[0] = k0[0]; kc[0].w[1] = k0[1]; kc[1].w[0] = k0[2]; kc[1].w[1] = k0[3];
+      kc[2].w[0] = k1[0]; kc[2].w[1] = k1[1]; kc[3].w[0] = k1[2]; kc[3].w[1] = k1[3];
+    } else {
+      const char *kp = kbase + tile * Gm::TILE_BYTES + lane_off;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) kc[i] = load_chunk<W32>(kp + i * kWave * Gm::CB);
+      for (int i = 0; i < NL; ++i) kc[i] = load_chunk<W32>(kp + i * kWave * Gm::CB);
+    }
 #pragma unroll
     for (int i = 0; i < NL; ++i) vc[i] = load_chunk<W32>(vp + i * kWave * Gm::CB);
     if constexpr (kQuant) {
@@ -729,13 +912,16 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a) {
       lseg.nblk = nb;
     }
     lseg.tail = tail_of(lseg.s, lseg.nblk);
-    load_q(qn, lseg);
+    if constexpr (!kQ8) load_q(qn, q8n, lseg);  // the MFMA path loads q at the switch
     pend = lseg;
   };
   auto compute = [&](int jj, const Chunk<W32> *kc, const Chunk<W32> *vc, float ks, float vs) {
     const float qs = kQuant ? a.qk_scale * ks : a.qk_scale;
     const bool masked = jj == cur.nblk - 1 && cur.tail < kBlock;
-    if constexpr (kFast) {
+    if constexpr (kQ8) {
+      tile_update_q8<KV, QT, D, G>(st, q8, q8l, kc, vc, qs, vs, masked ? cur.tail : kBlock, tg,
+                                   g16, c16);
+    } else if constexpr (kFast) {
       if (masked)
         tile_update_fast<KV, QT, D, G, true>(st, fs, kc, vc, qs, vs, cur.tail, tg, cidx);
       else
@@ -750,14 +936,19 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a) {
   // After a tile: emit the segment if it ended (or the range did), then switch.
   auto after = [&](int jj, bool has_next) {
     if (jj != cur.nblk - 1 && has_next) return;
-    if constexpr (kFast) fast_to_generic(st, fs);
+    if constexpr (kQ8) q8_to_generic<KV, QT, D, G>(st, q8, tg);
+    else if constexpr (kFast) fast_to_generic(st, fs);
     const int seg0 = Hkv * cur.cum + cur.h * cur.nblk;  // first tile of the segment
     const int wfirst = seg0 / tpw, wlast = (seg0 + cur.nblk - 1) / tpw;
     emit_segment<KV, QT, D, G>(a, st, cur.s, cur.h, wfirst == wlast, w - wfirst, lane);
     if (!has_next) return;
     cur = pend;
+    if constexpr (kQ8) {
+      load_q(qn, q8, cur);
+    } else {
 #pragma unroll
-    for (int g = 0; g < G; ++g) st.q[g] = qn[g];
+      for (int g = 0; g < G; ++g) st.q[g] = qn[g];
+    }
     reset_state();
   };
 

@@ -128,8 +128,8 @@ def test_decode_tiny_fp32_poisoned():
     ("f32", "f32", 4, 2, 64), ("f32", "f32", 8, 1, 128),
     ("f16", "f16", 32, 8, 128), ("f16", "f16", 8, 8, 64), ("f16", "f16", 16, 2, 128),
     ("bf16", "bf16", 32, 8, 128), ("bf16", "bf16", 4, 4, 128),
-    ("fp8", "bf16", 64, 8, 128), ("fp8", "f16", 8, 4, 64),
-    ("i8", "bf16", 64, 8, 128), ("i8", "f16", 16, 16, 128),
+    ("fp8", "bf16", 64, 8, 128), ("fp8", "f16", 8, 4, 64), ("fp8", "f16", 64, 8, 128),
+    ("i8", "bf16", 64, 8, 128), ("i8", "f16", 16, 16, 128), ("i8", "f16", 32, 4, 128),
 ])
 def test_decode_shapes_ragged(kv, qd, hq, hkv, hd):
     # contexts around block and partition edges (partitions are 8-32 blocks); data scaled
