@@ -302,7 +302,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(attn_gbps, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": profiled_traffic(args.workload),
-                     "kernel": "pa_decode (partition + merge launches)" if b.kind == "decode"
+                     "kernel": "pa_decode (balanced-split kernel + piece merge)" if b.kind == "decode"
                      else "pa_prefill_chunk"},
     }
     if b.kind != "decode":
