@@ -336,28 +336,36 @@ __device__ __forceinline__ void merge_weights(float m1, float m2, float &w1, flo
   w2 = fast_exp2(m2 - mn);
 }
 
-// Merge the token groups of one wave (lanes that differ above the LPT lanes of a
-// row) so that every lane ends with the wave's (m, l, acc) for its column chunk.
-template <int KV, int QT, int D, int G>
-__device__ __forceinline__ void merge_token_groups(DecodeState<KV, QT, D, G> &st) {
-  constexpr int LPT = Geom<KV, D>::LPT, EPC = Geom<KV, D>::EPC;
-#pragma unroll
-  for (int mask = LPT; mask < kWave; mask <<= 1) {
+// One step of the token-group merge: combine with the lanes MASK apart, then the
+// next higher lane bit, up to 32 (cross-lane moves without LDS).
+template <int MASK, int KV, int QT, int D, int G>
+__device__ __forceinline__ void merge_token_step(DecodeState<KV, QT, D, G> &st) {
+  if constexpr (MASK < kWave) {
+    constexpr int EPC = Geom<KV, D>::EPC;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float mo = __shfl_xor(st.m[g], mask, kWave);
-      const float lo = __shfl_xor(st.l[g], mask, kWave);
+      const float mo = xor_lanes<MASK>(st.m[g]);
+      const float lo = xor_lanes<MASK>(st.l[g]);
       float w1, w2, mn;
       merge_weights(st.m[g], mo, w1, w2, mn);
       st.m[g] = mn;
       st.l[g] = st.l[g] * w1 + lo * w2;
 #pragma unroll
       for (int e = 0; e < EPC; ++e) {
-        const float ao = __shfl_xor(st.acc[g][e], mask, kWave);
+        const float ao = xor_lanes<MASK>(st.acc[g][e]);
         st.acc[g][e] = st.acc[g][e] * w1 + ao * w2;
       }
     }
+    merge_token_step<MASK * 2>(st);
   }
+}
+
+// Merge the token groups of one wave (lanes that differ above the LPT lanes of a
+// row) so that every lane ends with the wave's (m, l, acc) for its column chunk.
+template <int KV, int QT, int D, int G>
+__device__ __forceinline__ void merge_token_groups(DecodeState<KV, QT, D, G> &st) {
+  constexpr int LPT = Geom<KV, D>::LPT, EPC = Geom<KV, D>::EPC;
+  merge_token_step<LPT>(st);
 }
 
 constexpr int kDecodeWaves = 4;
@@ -736,8 +744,8 @@ __device__ __forceinline__ void tile_update_q8(DecodeState<KV, QT, D, G> &st, Q8
 template <int KV, int QT, int D, int G>
 __device__ __forceinline__ void q8_to_generic(DecodeState<KV, QT, D, G> &st, Q8State &q8, int r) {
   float lt = q8.l;
-  lt += __shfl_xor(lt, 16, kWave);
-  lt += __shfl_xor(lt, 32, kWave);
+  lt += xor_lanes<16>(lt);
+  lt += xor_lanes<32>(lt);
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     st.m[g] = __shfl(q8.m, g, kWave);
@@ -1021,12 +1029,15 @@ __device__ __forceinline__ void merge_stream(const DecodeArgs &a, int s, int hq,
     }
   float M = mp;
   for (int p = lane + kWave; p < pieces; p += kWave) M = fmaxf(M, a.ws_m[r0 + p]);
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) M = fmaxf(M, __shfl_xor(M, m, kWave));
+  M = fmaxf(M, xor_lanes<1>(M));
+  M = fmaxf(M, xor_lanes<2>(M));
+  M = fmaxf(M, dpp_f<kDppHalfMirror>(M));  // quads already agree: pairs quad 0 with quad 1
+  M = fmaxf(M, xor_lanes<8>(M));
+  M = fmaxf(M, xor_lanes<16>(M));
+  M = fmaxf(M, xor_lanes<32>(M));
   float L = lane < pieces ? fast_exp2(mp - M) * lp : 0.f;
   for (int p = lane + kWave; p < pieces; p += kWave) L += fast_exp2(a.ws_m[r0 + p] - M) * a.ws_l[r0 + p];
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) L += __shfl_xor(L, m, kWave);
+  L = group_sum<64>(L);
   const float invL = 1.f / L;
   float acc[PER];
 #pragma unroll

@@ -123,6 +123,36 @@ __device__ __forceinline__ float row_bcast(float x) {
   return dpp_f<kDppRowBcast0 + N>(x);
 }
 
+// Value held by lane (lane ^ MASK), for MASK in {1, 2, 8, 16, 32} without LDS:
+// DPP inside a 16-lane row, v_permlane{16,32}_swap across rows (each returns the
+// pair (x[lane & ~MASK], x[lane | MASK]); the partner is the one that differs).
+template <int MASK>
+__device__ __forceinline__ float xor_lanes(float x) {
+  if constexpr (MASK == 1) {
+    return dpp_f<kDppXor1>(x);
+  } else if constexpr (MASK == 2) {
+    return dpp_f<kDppXor2>(x);
+  } else if constexpr (MASK == 8) {
+    return dpp_f<kDppRor8>(x);
+  } else if constexpr (MASK == 16 || MASK == 32) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    unsigned lo, hi;
+    if constexpr (MASK == 16) {
+      auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+      lo = r[0];
+      hi = r[1];
+    } else {
+      auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+      lo = r[0];
+      hi = r[1];
+    }
+    const bool upper = (__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) & MASK) != 0;
+    return __builtin_bit_cast(float, upper ? lo : hi);
+  } else {
+    return __shfl_xor(x, MASK, 64);
+  }
+}
+
 // After the call every lane holds the sum over its aligned group of N lanes.
 // Lanes of one group must hold the same kind of value (a partial dot product).
 template <int N>
@@ -132,8 +162,8 @@ __device__ __forceinline__ float group_sum(float x) {
   if constexpr (N >= 4) x += dpp_f<kDppXor2>(x);
   if constexpr (N >= 8) x += dpp_f<kDppHalfMirror>(x);
   if constexpr (N >= 16) x += dpp_f<kDppMirror>(x);
-  if constexpr (N >= 32) x += __shfl_xor(x, 16, 64);
-  if constexpr (N >= 64) x += __shfl_xor(x, 32, 64);
+  if constexpr (N >= 32) x += xor_lanes<16>(x);
+  if constexpr (N >= 64) x += xor_lanes<32>(x);
   return x;
 }
 

@@ -224,8 +224,8 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
       float mx = sc[0];
 #pragma unroll
       for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sc[j]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      mx = fmaxf(mx, xor_lanes<16>(mx));
+      mx = fmaxf(mx, xor_lanes<32>(mx));
       const float mn = fmaxf(m[rb], mx);
       rescale |= mn > m[rb];
       alpha[rb] = fast_exp2(m[rb] - mn);
@@ -278,8 +278,8 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     float tot = l[rb];
-    tot += __shfl_xor(tot, 16, kWave);
-    tot += __shfl_xor(tot, 32, kWave);
+    tot += xor_lanes<16>(tot);
+    tot += xor_lanes<32>(tot);
     if (!row_ok[rb]) continue;
     const float inv = 1.f / tot;
 #pragma unroll
