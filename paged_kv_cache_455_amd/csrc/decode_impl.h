@@ -364,7 +364,7 @@ __device__ __forceinline__ void merge_token_step(DecodeState<KV, QT, D, G> &st) 
 // row) so that every lane ends with the wave's (m, l, acc) for its column chunk.
 template <int KV, int QT, int D, int G>
 __device__ __forceinline__ void merge_token_groups(DecodeState<KV, QT, D, G> &st) {
-  constexpr int LPT = Geom<KV, D>::LPT, EPC = Geom<KV, D>::EPC;
+  constexpr int LPT = Geom<KV, D>::LPT;
   merge_token_step<LPT>(st);
 }
 
@@ -602,173 +602,28 @@ __device__ __forceinline__ void emit_segment(const DecodeArgs &a, DecodeState<KV
   }
 }
 
-// ---- 1-byte KV with a GQA group of 8: q.k on MFMA --------------------------------
-// A (block, kv head) tile of 16 keys x 128 dims against the group's 8 query heads
-// is a dense [16 x 128] . [128 x 8] product: it goes to v_mfma_f32_16x16x32 (bf16,
-// or f16 for f16 queries) with the codes converted exactly, heads padded to 16.
-// Lane (c16, g16) supplies key row c16 and dims {16*g16 + 8*kk} (kk = 0, 1) and
-// {64 + 16*g16 + 8*(kk-2)} (kk = 2, 3) -- two coalesced 16-byte loads per lane --
-// and receives the scores of keys 4*g16 .. +3 for head c16.  Each head's running
-// max is shared by the whole wave; the probabilities reach the P.V lanes (the
-// coalesced V layout of the VALU path) through a small wave-private LDS area.
-typedef _Float16 h8v_t __attribute__((ext_vector_type(8)));
-typedef __bf16 b8v_t __attribute__((ext_vector_type(8)));
-typedef float f4v_t __attribute__((ext_vector_type(4)));
-
-template <int KV, int D, int G>
-struct Q8Geom {
-  static constexpr bool kOn = (KV == PA_FP8_E4M3 || KV == PA_I8) && G == 8 && D == 128;
-  static constexpr int kLdsFloats = 16 * 8 + 8;  // P[16 keys][8 heads] + alpha[8]
+// ---- balanced split: the wave's range of tiles ---------------------------------------
+struct StreamSeg {
+  int s, h;   // sequence, kv head
+  int nblk;   // blocks of the sequence
+  int cum;    // blocks of the sequences before it
+  int tail;   // valid rows of its last block
 };
 
-struct Q8State {
-  u32x4 qb[4];  // B operand per k-step: q[head c16][8 dims]
-  float m, l;   // running max (shared by the head's lanes) and this lane's partial sum
+struct StreamRange {
+  int t, tend, tpw;  // the wave's tiles [t, tend); tiles per wave
+  int j;             // block of tile t inside its segment
+  StreamSeg seg;     // tile t's segment
 };
 
-// 8 codes (two words) -> 8 MFMA inputs (bf16 or f16, exact) packed in 4 words.
-template <int KV, int QT>
-__device__ __forceinline__ void codes_to_mfma(uint32_t w0, uint32_t w1, uint32_t *out) {
-  float f[8];
-  if constexpr (KV == PA_FP8_E4M3) {
-    fp8x4_to_f32(w0, f);
-    fp8x4_to_f32(w1, f + 4);
-  } else {
-    i8x4_to_f32(w0, f);
-    i8x4_to_f32(w1, f + 4);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if constexpr (QT == PA_F16) {
-      out[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[2 * i], f[2 * i + 1]));
-    } else {
-      out[i] = (__builtin_bit_cast(uint32_t, f[2 * i]) >> 16) |
-               (__builtin_bit_cast(uint32_t, f[2 * i + 1]) & 0xffff0000u);
-    }
-  }
+__device__ __forceinline__ int stream_tail(const DecodeArgs &a, int s, int nblk) {
+  return a.ctx[s] - (nblk - 1) * kBlock;
 }
 
-template <int QT>
-__device__ __forceinline__ f4v_t mfma_q(const u32x4 &a, const u32x4 &b, const f4v_t &c) {
-  if constexpr (QT == PA_F16)
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8v_t, a),
-                                                  __builtin_bit_cast(h8v_t, b), c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8v_t, a),
-                                                   __builtin_bit_cast(b8v_t, b), c, 0, 0, 0);
-}
-
-// dims of k-step kk held by lane group g16 (the same map for K and q)
-__device__ __forceinline__ int q8_dim0(int kk, int g16) {
-  return (kk < 2 ? 0 : 64) + 16 * g16 + 8 * (kk & 1);
-}
-
-// One tile for the MFMA q.k path (see above).  kc holds this lane's 32 K codes
-// (key c16); vc the coalesced V chunks of rows 4i + r (r = tg).
-template <int KV, int QT, int D, int G>
-__device__ __forceinline__ void tile_update_q8(DecodeState<KV, QT, D, G> &st, Q8State &q8,
-                                               float *lds, const Chunk<2> *kc, const Chunk<2> *vc,
-                                               float qk_scale, float v_scale, int valid_rows,
-                                               int r, int g16, int c16) {
-  constexpr int EPC = 8, NL = 4;
-  f4v_t sacc = f4v_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    u32x4 ka;
-    uint32_t t4[4];
-    codes_to_mfma<KV, QT>(kc[kk].w[0], kc[kk].w[1], t4);
-    ka[0] = t4[0]; ka[1] = t4[1]; ka[2] = t4[2]; ka[3] = t4[3];
-    sacc = mfma_q<QT>(ka, q8.qb[kk], sacc);
-  }
-  // scores of keys 4*g16 + i for head c16
-  float sv[4];
-  float mx = kNegBig;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bool ok = 4 * g16 + i < valid_rows;
-    sv[i] = ok ? sacc[i] * qk_scale : kNegBig;
-    mx = fmaxf(mx, sv[i]);
-  }
-  mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-  const float mn = fmaxf(q8.m, mx);
-  const bool changed = mn > q8.m;
-  const float alpha = fast_exp2(q8.m - mn);
-  float psum = 0.f;
-  float pv[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float p = 4 * g16 + i < valid_rows ? fast_exp2(sv[i] - mn) : 0.f;
-    psum += p;
-    pv[i] = p * v_scale;
-  }
-  q8.l = q8.l * alpha + psum;
-  q8.m = mn;
-  if (c16 < G) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lds[(4 * g16 + i) * 8 + c16] = pv[i];
-    if (g16 == 0) lds[128 + c16] = alpha;
-  }
-  if (__any(changed)) {  // the heads' rescale factors
-    const f4v_t alo = *reinterpret_cast<const f4v_t *>(lds + 128);
-    const f4v_t ahi = *reinterpret_cast<const f4v_t *>(lds + 132);
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float ag = g < 4 ? alo[g] : ahi[g - 4];
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) st.acc[g][e] *= ag;
-    }
-  }
-  // P.V one V row (token 4i + r) at a time: its 8 probabilities and 8 values
-#pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    const f4v_t plo = *reinterpret_cast<const f4v_t *>(lds + (4 * i + r) * 8);
-    const f4v_t phi = *reinterpret_cast<const f4v_t *>(lds + (4 * i + r) * 8 + 4);
-    Chunk<2> cv = vc[i];
-    const bool ok = 4 * i + r < valid_rows;
-    cv.w[0] = ok ? cv.w[0] : 0u;
-    cv.w[1] = ok ? cv.w[1] : 0u;
-    float vf[EPC];
-    chunk_to_f32<KV, 2>(cv, vf);
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float pg = g < 4 ? plo[g] : phi[g - 4];
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) st.acc[g][e] = __builtin_fmaf(pg, vf[e], st.acc[g][e]);
-    }
-  }
-}
-
-// The MFMA path's state as the generic per-lane (m[G], l[G]): the maxima are shared
-// by the wave; the whole l goes to token group 0 (its merge sums the groups).
-template <int KV, int QT, int D, int G>
-__device__ __forceinline__ void q8_to_generic(DecodeState<KV, QT, D, G> &st, Q8State &q8, int r) {
-  float lt = q8.l;
-  lt += xor_lanes<16>(lt);
-  lt += xor_lanes<32>(lt);
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    st.m[g] = __shfl(q8.m, g, kWave);
-    const float lg = __shfl(lt, g, kWave);
-    st.l[g] = r == 0 ? lg : 0.f;
-  }
-}
-
-template <int KV, int QT, int D, int G>
-__device__ __forceinline__ void decode_stream(const DecodeArgs &a) {
-  using Gm = Geom<KV, D>;
-  constexpr int NL = Gm::NL, EPC = Gm::EPC, W32 = Gm::W32, LPT = Gm::LPT;
-  constexpr bool kFast = FastGeom<KV, D, G>::kOn;
-  constexpr bool kQuant = (KV == PA_FP8_E4M3 || KV == PA_I8);
-  constexpr bool kQ8 = Q8Geom<KV, D, G>::kOn;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int w = blockIdx.x * kDecodeWaves + threadIdx.x / kWave;
+// Count the batch's tiles, record tpw and every sequence's first block index (wave
+// 0 does), and find wave w's first tile.  False when the wave has no tiles.
+__device__ __forceinline__ bool stream_range(const DecodeArgs &a, int w, int lane, StreamRange &r) {
   const int Hkv = a.num_kv_heads, S = a.num_seqs;
-  __shared__ float q8_lds[kQ8 ? kDecodeWaves * Q8Geom<KV, D, G>::kLdsFloats : 1];
-  float *q8l = q8_lds + (kQ8 ? (threadIdx.x / kWave) * Q8Geom<KV, D, G>::kLdsFloats : 0);
-  const int g16 = lane >> 4, c16 = lane & 15;
-
-  // ---- total blocks; wave 0 also records every sequence's first block index ----
   int NB = 0;
   int nb0 = 0, incl0 = 0;  // first 64 sequences, kept for the locate pass
   for (int c0 = 0; c0 < S; c0 += kWave) {
@@ -784,80 +639,96 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a) {
     NB += __shfl(incl, kWave - 1, kWave);
   }
   const int T = Hkv * NB;
-  const int tpw = max(a.min_tpw, (T + a.num_waves - 1) / a.num_waves);
-  if (w == 0 && lane == 0) a.hdr[0] = tpw;
-  int t = w * tpw;
-  const int tend = min(t + tpw, T);
-  if (t >= tend) return;
+  r.tpw = max(a.min_tpw, (T + a.num_waves - 1) / a.num_waves);
+  if (w == 0 && lane == 0) a.hdr[0] = r.tpw;
+  r.t = w * r.tpw;
+  r.tend = min(r.t + r.tpw, T);
+  if (r.t >= r.tend) return false;
 
-  // ---- locate the first tile: sequence s, kv head h, block j ----
-  int s = 0, cum_s = 0, nblk = 0;
-  {
-    int base = 0;
-    for (int c0 = 0; c0 < S; c0 += kWave) {
-      const int sq = c0 + lane;
-      int nb, incl;
-      if (c0 == 0) {  // already scanned
-        nb = nb0;
-        incl = incl0;
-      } else {
-        const int n = sq < S ? a.ctx[sq] : 0;
-        nb = n > 0 ? (n + kBlock - 1) / kBlock : 0;
-        incl = base + wave_incl_scan_i(nb, lane);
-      }
-      const int excl = incl - nb;
-      const unsigned long long hit = __ballot(sq < S && Hkv * excl <= t && t < Hkv * incl);
-      if (hit) {
-        const int l = __builtin_ctzll(hit);
-        s = c0 + l;
-        cum_s = __shfl(excl, l, kWave);
-        nblk = __shfl(nb, l, kWave);
-        break;
-      }
-      base = __shfl(incl, kWave - 1, kWave);
+  int s = 0, cum_s = 0, nblk = 1;
+  int base = 0;
+  for (int c0 = 0; c0 < S; c0 += kWave) {
+    const int sq = c0 + lane;
+    int nb, incl;
+    if (c0 == 0) {  // already scanned
+      nb = nb0;
+      incl = incl0;
+    } else {
+      const int n = sq < S ? a.ctx[sq] : 0;
+      nb = n > 0 ? (n + kBlock - 1) / kBlock : 0;
+      incl = base + wave_incl_scan_i(nb, lane);
     }
+    const int excl = incl - nb;
+    const unsigned long long hit = __ballot(sq < S && Hkv * excl <= r.t && r.t < Hkv * incl);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      s = c0 + l;
+      cum_s = __shfl(excl, l, kWave);
+      nblk = __shfl(nb, l, kWave);
+      break;
+    }
+    base = __shfl(incl, kWave - 1, kWave);
   }
-  int h = (t - Hkv * cum_s) / nblk;
-  int j = (t - Hkv * cum_s) - h * nblk;
+  const int h = (r.t - Hkv * cum_s) / nblk;
+  r.j = (r.t - Hkv * cum_s) - h * nblk;
+  r.seg = StreamSeg{s, h, nblk, cum_s, stream_tail(a, s, nblk)};
+  return true;
+}
+
+// Step sg to the next (sequence, kv head) segment of the tile order (one exists).
+__device__ __forceinline__ void stream_next_seg(const DecodeArgs &a, StreamSeg &sg) {
+  if (++sg.h == a.num_kv_heads) {
+    sg.h = 0;
+    sg.cum += sg.nblk;
+    int nb;
+    do {
+      ++sg.s;
+      const int n = a.ctx[sg.s];
+      nb = n > 0 ? (n + kBlock - 1) / kBlock : 0;
+    } while (nb == 0);
+    sg.nblk = nb;
+  }
+  sg.tail = stream_tail(a, sg.s, sg.nblk);
+}
+
+// True when one wave owns all of sg's tiles; piece = this wave's index among them.
+__device__ __forceinline__ bool stream_single(const StreamSeg &sg, int Hkv, int tpw, int w,
+                                              int &piece) {
+  const int seg0 = Hkv * sg.cum + sg.h * sg.nblk;  // first tile of the segment
+  const int wfirst = seg0 / tpw, wlast = (seg0 + sg.nblk - 1) / tpw;
+  piece = w - wfirst;
+  return wfirst == wlast;
+}
+
+template <int KV, int QT, int D, int G>
+__device__ __forceinline__ void decode_stream(const DecodeArgs &a) {
+  using Gm = Geom<KV, D>;
+  constexpr int NL = Gm::NL, EPC = Gm::EPC, W32 = Gm::W32, LPT = Gm::LPT;
+  constexpr bool kFast = FastGeom<KV, D, G>::kOn;
+  constexpr bool kQuant = (KV == PA_FP8_E4M3 || KV == PA_I8);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = blockIdx.x * kDecodeWaves + threadIdx.x / kWave;
+  const int Hkv = a.num_kv_heads;
+  StreamRange rg;
+  if (!stream_range(a, w, lane, rg)) return;
 
   const int cidx = lane % LPT, tg = lane / LPT;
-  const char *kbase = reinterpret_cast<const char *>(a.k);
-  const char *vbase = reinterpret_cast<const char *>(a.v);
-  const int lane_off = lane * Gm::CB;
+  const char *kbase = reinterpret_cast<const char *>(a.k) + lane * Gm::CB;
+  const char *vbase = reinterpret_cast<const char *>(a.v) + lane * Gm::CB;
 
   // The segment being computed (cur) and the load cursor, which runs one tile
   // ahead and may already stand in the next segment; entering a segment prefetches
   // its q into qn, so a wave crossing segments keeps its loads in flight.
-  struct Seg {
-    int s, h, nblk, cum, tail;
-  };
-  auto tail_of = [&](int sq, int nb) { return a.ctx[sq] - (nb - 1) * kBlock; };
-  Seg cur{s, h, nblk, cum_s, tail_of(s, nblk)};
-  Seg lseg = cur, pend = cur;
-  int lj = j;
+  StreamSeg cur = rg.seg, lseg = cur, pend = cur;
+  int lj = rg.j;
 
   DecodeState<KV, QT, D, G> st;
   FastState<KV, D, G> fs;
-  QFrag<KV, EPC> qn[kQ8 ? 1 : G];
-  Q8State q8, q8n;  // q8n: unused by the MFMA path (it loads q at a segment switch)
-  auto load_q = [&](QFrag<KV, EPC> *qf, Q8State &q8s, const Seg &sg) {
+  QFrag<KV, EPC> qn[G];
+  auto load_q = [&](QFrag<KV, EPC> *qf, const StreamSeg &sg) {
     const int64_t qbase = ((int64_t)sg.s * a.num_q_heads + sg.h * G) * D;
-    if constexpr (kQ8) {
-      (void)qf;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) q8s.qb[kk] = u32x4{0, 0, 0, 0};
-      if (c16 < G) {
-        const char *qp = reinterpret_cast<const char *>(a.q) + (qbase + (int64_t)c16 * D) * 2;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          q8s.qb[kk] = *reinterpret_cast<const u32x4 *>(qp + q8_dim0(kk, g16) * 2);
-      }
-    } else {
-      (void)q8s;
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-        qf[g].template load<QT>(a.q, qbase + (int64_t)g * D + cidx * EPC);
-    }
+    for (int g = 0; g < G; ++g) qf[g].template load<QT>(a.q, qbase + (int64_t)g * D + cidx * EPC);
   };
   auto reset_state = [&]() {
 #pragma unroll
@@ -872,31 +743,19 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a) {
       fs.m[i] = kNegBig;
       fs.l[i] = 0.f;
     }
-    q8.m = kNegBig;
-    q8.l = 0.f;
   };
-  load_q(st.q, q8, cur);
+  load_q(st.q, cur);
   reset_state();
 
   Chunk<W32> kA[NL], vA[NL], kB[NL], vB[NL];
   float ksA = 1.f, vsA = 1.f, ksB = 1.f, vsB = 1.f;
-  auto load_tile = [&](const Seg &sg, int jj, Chunk<W32> *kc, Chunk<W32> *vc, float &ks,
+  auto load_tile = [&](const StreamSeg &sg, int jj, Chunk<W32> *kc, Chunk<W32> *vc, float &ks,
                        float &vs) {
     const int64_t tile = (int64_t)a.bt[(int64_t)sg.s * a.max_blocks_per_seq + jj] * Hkv + sg.h;
-    const char *vp = vbase + tile * Gm::TILE_BYTES + lane_off;
-    if constexpr (kQ8) {
-      // K as the MFMA A operand: key row c16, bytes [16*g16, +16) and [64 + 16*g16, +16)
-      static_assert(NL * W32 == 8, "q8 K staging uses the 8 words of kc");
-      const char *kp = kbase + tile * Gm::TILE_BYTES + c16 * D + 16 * g16;
-      const u32x4 k0 = *reinterpret_cast<const u32x4 *>(kp);
-      const u32x4 k1 = *reinterpret_cast<const u32x4 *>(kp + 64);
-      kc[0].w[0] = k0[0]; kc[0].w[1] = k0[1]; kc[1].w[0] = k0[2]; kc[1].w[1] = k0[3];
-      kc[2].w[0] = k1[0]; kc[2].w[1] = k1[1]; kc[3].w[0] = k1[2]; kc[3].w[1] = k1[3];
-    } else {
-      const char *kp = kbase + tile * Gm::TILE_BYTES + lane_off;
+    const char *kp = kbase + tile * Gm::TILE_BYTES;
+    const char *vp = vbase + tile * Gm::TILE_BYTES;
 #pragma unroll
-      for (int i = 0; i < NL; ++i) kc[i] = load_chunk<W32>(kp + i * kWave * Gm::CB);
-    }
+    for (int i = 0; i < NL; ++i) kc[i] = load_chunk<W32>(kp + i * kWave * Gm::CB);
 #pragma unroll
     for (int i = 0; i < NL; ++i) vc[i] = load_chunk<W32>(vp + i * kWave * Gm::CB);
     if constexpr (kQuant) {
@@ -908,28 +767,14 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a) {
   auto advance = [&]() {
     if (++lj < lseg.nblk) return;
     lj = 0;
-    if (++lseg.h == Hkv) {
-      lseg.h = 0;
-      lseg.cum += lseg.nblk;
-      int nb;
-      do {
-        ++lseg.s;
-        const int nn = a.ctx[lseg.s];
-        nb = nn > 0 ? (nn + kBlock - 1) / kBlock : 0;
-      } while (nb == 0);
-      lseg.nblk = nb;
-    }
-    lseg.tail = tail_of(lseg.s, lseg.nblk);
-    if constexpr (!kQ8) load_q(qn, q8n, lseg);  // the MFMA path loads q at the switch
+    stream_next_seg(a, lseg);
+    load_q(qn, lseg);
     pend = lseg;
   };
   auto compute = [&](int jj, const Chunk<W32> *kc, const Chunk<W32> *vc, float ks, float vs) {
     const float qs = kQuant ? a.qk_scale * ks : a.qk_scale;
     const bool masked = jj == cur.nblk - 1 && cur.tail < kBlock;
-    if constexpr (kQ8) {
-      tile_update_q8<KV, QT, D, G>(st, q8, q8l, kc, vc, qs, vs, masked ? cur.tail : kBlock, tg,
-                                   g16, c16);
-    } else if constexpr (kFast) {
+    if constexpr (kFast) {
       if (masked)
         tile_update_fast<KV, QT, D, G, true>(st, fs, kc, vc, qs, vs, cur.tail, tg, cidx);
       else
@@ -944,23 +789,18 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a) {
   // After a tile: emit the segment if it ended (or the range did), then switch.
   auto after = [&](int jj, bool has_next) {
     if (jj != cur.nblk - 1 && has_next) return;
-    if constexpr (kQ8) q8_to_generic<KV, QT, D, G>(st, q8, tg);
-    else if constexpr (kFast) fast_to_generic(st, fs);
-    const int seg0 = Hkv * cur.cum + cur.h * cur.nblk;  // first tile of the segment
-    const int wfirst = seg0 / tpw, wlast = (seg0 + cur.nblk - 1) / tpw;
-    emit_segment<KV, QT, D, G>(a, st, cur.s, cur.h, wfirst == wlast, w - wfirst, lane);
+    if constexpr (kFast) fast_to_generic(st, fs);
+    int piece;
+    const bool single = stream_single(cur, Hkv, rg.tpw, w, piece);
+    emit_segment<KV, QT, D, G>(a, st, cur.s, cur.h, single, piece, lane);
     if (!has_next) return;
     cur = pend;
-    if constexpr (kQ8) {
-      load_q(qn, q8, cur);
-    } else {
 #pragma unroll
-      for (int g = 0; g < G; ++g) st.q[g] = qn[g];
-    }
+    for (int g = 0; g < G; ++g) st.q[g] = qn[g];
     reset_state();
   };
 
-  const int ntiles = tend - t;
+  const int ntiles = rg.tend - rg.t;
   int jA = lj, jB = 0;
   load_tile(lseg, lj, kA, vA, ksA, vsA);
   for (int k = 0;;) {
@@ -981,6 +821,320 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a) {
       load_tile(lseg, lj, kA, vA, ksA, vsA);
     }
     compute(jB, kB, vB, ksB, vsB);
+    after(jB, more);
+    if (!more) break;
+    ++k;
+  }
+}
+
+// ---- 1-byte KV, GQA group 8, head_dim 128: both products on MFMA ----------------------
+// Against the group's 8 query heads, one (block, kv head) tile of 16 keys x 128 dims
+// gives two small dense products, run on matrix cores with the heads padded to 16:
+//  * scores S^T[key][head] = K . Q^T on v_mfma_f32_16x16x32 (bf16, or f16 for f16
+//    queries; the codes convert exactly).  Lane (c16, g16) supplies key row c16,
+//    dims q8_dim0(kk, g16) .. +7 of k-step kk (two coalesced 16-byte loads per lane)
+//    and receives the scores of keys 4*g16 .. +3 for head c16;
+//  * that is already the A-operand layout of O[head][dim] += P[head][key] . V[key][dim]
+//    on v_mfma_f32_16x16x16 bf16 (row c16, keys 4*g16 .. +3): the probabilities
+//    never leave the lane.  They enter with the tile's value scale folded in, split
+//    as bf16 hi + lo (hi + lo matches p to about 2^-17 relative);
+//  * the B operand (keys 4*g16 .. +3 of one dim) comes from four 8-byte loads of
+//    value rows 4*g16 + i, dims 8*c16 .. +7, transposed inside the lane by byte
+//    permutes and converted exactly to bf16; product e covers dims 8*c16 + e;
+//  * lane (c16, g16) accumulates O rows 4*g16 + i (heads; rows 8..15 are padding)
+//    at dims 8*c16 + e.  Head c16's running max is the same in its four lanes; its
+//    running sum is kept per lane over that lane's keys and summed at the end.
+typedef _Float16 h8v_t __attribute__((ext_vector_type(8)));
+typedef __bf16 b8v_t __attribute__((ext_vector_type(8)));
+typedef short s4v_t __attribute__((ext_vector_type(4)));
+typedef float f4v_t __attribute__((ext_vector_type(4)));
+
+template <int KV, int D, int G>
+struct Q8Geom {
+  static constexpr bool kOn = (KV == PA_FP8_E4M3 || KV == PA_I8) && G == 8 && D == 128;
+};
+
+// Codes 2*HI and 2*HI + 1 of word w as two exact 16-bit values (T16 = PA_BF16 or
+// PA_F16) packed in one word, the lower code in the low half.
+template <int KV, int T16, bool HI>
+__device__ __forceinline__ uint32_t codes2_to_16(uint32_t w) {
+  if constexpr (KV == PA_FP8_E4M3) {
+    if constexpr (T16 == PA_F16)
+      return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, HI));
+    else
+      return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, HI));
+  } else {
+    const float f0 = (float)(int8_t)(w >> (HI ? 16 : 0));
+    const float f1 = (float)(int8_t)(w >> (HI ? 24 : 8));
+    if constexpr (T16 == PA_F16)
+      return __builtin_bit_cast(uint32_t, h2_t{(_Float16)f0, (_Float16)f1});
+    else
+      return __builtin_bit_cast(uint32_t, bf2_t{(__bf16)f0, (__bf16)f1});
+  }
+}
+
+// Two floats as a bf16 pair, each rounded to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
+  return __builtin_bit_cast(uint32_t, bf2_t{(__bf16)x, (__bf16)y});
+}
+
+template <int QT>
+__device__ __forceinline__ f4v_t mfma_qk(const u32x4 &a, const u32x4 &b, const f4v_t &c) {
+  if constexpr (QT == PA_F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8v_t, a),
+                                                  __builtin_bit_cast(h8v_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8v_t, a),
+                                                   __builtin_bit_cast(b8v_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f4v_t mfma_pv(const u32x2 &p, const u32x2 &v, const f4v_t &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4v_t, p),
+                                                   __builtin_bit_cast(s4v_t, v), c, 0, 0, 0);
+}
+
+// First of the 8 dims that lane group g16 supplies at k-step kk (same map for K and q).
+__device__ __forceinline__ int q8_dim0(int kk, int g16) {
+  return (kk < 2 ? 0 : 64) + 16 * g16 + 8 * (kk & 1);
+}
+
+struct Q8Tile {
+  u32x4 k0, k1;  // key row c16: dims [16*g16, +16) and [64 + 16*g16, +16)
+  u32x2 v[4];    // value row 4*g16 + i: dims [8*c16, +8)
+  float ks, vs;  // the tile's K and V scales
+};
+
+struct Q8Acc {
+  f4v_t o[8];  // o[e][i] = O[head 4*g16 + i][dim 8*c16 + e]
+  float m, l;  // head c16: running max (log2 units), this lane's running sum
+};
+
+template <int KV, int QT, bool MASK>
+__device__ __forceinline__ void q8_tile(Q8Acc &st, const u32x4 *qb, const Q8Tile &t,
+                                        float qk_scale, int valid_rows, int g16) {
+  constexpr int T16 = QT == PA_F16 ? PA_F16 : PA_BF16;
+  f4v_t sacc = f4v_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const u32x4 &kw = kk < 2 ? t.k0 : t.k1;
+    const uint32_t w0 = kw[2 * (kk & 1)], w1 = kw[2 * (kk & 1) + 1];
+    u32x4 ka;
+    ka[0] = codes2_to_16<KV, T16, false>(w0);
+    ka[1] = codes2_to_16<KV, T16, true>(w0);
+    ka[2] = codes2_to_16<KV, T16, false>(w1);
+    ka[3] = codes2_to_16<KV, T16, true>(w1);
+    sacc = mfma_qk<QT>(ka, qb[kk], sacc);
+  }
+  const float qs = qk_scale * t.ks;
+  bool ok[4];
+  float sv[4];
+  float mx = kNegBig;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ok[i] = !MASK || 4 * g16 + i < valid_rows;
+    sv[i] = ok[i] ? sacc[i] * qs : kNegBig;
+    mx = fmaxf(mx, sv[i]);
+  }
+  mx = fmaxf(mx, xor_lanes<16>(mx));
+  mx = fmaxf(mx, xor_lanes<32>(mx));
+  const float mn = fmaxf(st.m, mx);
+  if (__any(mn > st.m)) {
+    const float alpha = fast_exp2(st.m - mn);
+    st.l *= alpha;
+    float ar[4];  // factors of this lane's O rows: heads 4*g16 + i live in lanes 4*g16 + i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * g16 + i, kWave);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.o[e][i] *= ar[i];
+  }
+  st.m = mn;
+  float pv[4];
+  float psum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float p = fast_exp2(sv[i] - mn);
+    if constexpr (MASK) p = ok[i] ? p : 0.f;
+    psum += p;
+    pv[i] = p * t.vs;
+  }
+  st.l += psum;
+  u32x2 ph, pl;
+  ph[0] = pack_bf16(pv[0], pv[1]);
+  ph[1] = pack_bf16(pv[2], pv[3]);
+  pl[0] = pack_bf16(pv[0] - bf16_lo(ph[0]), pv[1] - bf16_hi(ph[0]));
+  pl[1] = pack_bf16(pv[2] - bf16_lo(ph[1]), pv[3] - bf16_hi(ph[1]));
+
+  // value rows past the context may hold anything (NaN included): zero their bits
+  uint32_t vr[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    vr[i][0] = ok[i] ? t.v[i][0] : 0u;
+    vr[i][1] = ok[i] ? t.v[i][1] : 0u;
+  }
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    // bytes (r0.b, r1.b, ...) interleaved, then one word per dim: keys 0..3 of dim 4c + m
+    const uint32_t t01l = __builtin_amdgcn_perm(vr[1][c], vr[0][c], 0x05010400u);
+    const uint32_t t01h = __builtin_amdgcn_perm(vr[1][c], vr[0][c], 0x07030602u);
+    const uint32_t t23l = __builtin_amdgcn_perm(vr[3][c], vr[2][c], 0x05010400u);
+    const uint32_t t23h = __builtin_amdgcn_perm(vr[3][c], vr[2][c], 0x07030602u);
+    uint32_t col[4];
+    col[0] = __builtin_amdgcn_perm(t23l, t01l, 0x05040100u);
+    col[1] = __builtin_amdgcn_perm(t23l, t01l, 0x07060302u);
+    col[2] = __builtin_amdgcn_perm(t23h, t01h, 0x05040100u);
+    col[3] = __builtin_amdgcn_perm(t23h, t01h, 0x07060302u);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      u32x2 vb;
+      vb[0] = codes2_to_16<KV, PA_BF16, false>(col[m]);
+      vb[1] = codes2_to_16<KV, PA_BF16, true>(col[m]);
+      st.o[4 * c + m] = mfma_pv(ph, vb, st.o[4 * c + m]);
+      st.o[4 * c + m] = mfma_pv(pl, vb, st.o[4 * c + m]);
+    }
+  }
+}
+
+// Write the wave's result for (s, kv head h): the normalised output when single,
+// else the partial (m, l, acc) of `piece`.
+template <int QT>
+__device__ __forceinline__ void q8_emit(const DecodeArgs &a, const Q8Acc &st, int s, int h,
+                                        bool single, int piece, int lane) {
+  constexpr int D = 128, G = 8;
+  const int g16 = lane >> 4, c16 = lane & 15;
+  float L = st.l;
+  L += xor_lanes<16>(L);
+  L += xor_lanes<32>(L);
+  float mh[4], Lh[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    mh[i] = __shfl(st.m, 4 * g16 + i, kWave);
+    Lh[i] = __shfl(L, 4 * g16 + i, kWave);
+  }
+  if (g16 >= 2) return;  // padding heads
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = (int64_t)s * a.num_q_heads + h * G + 4 * g16 + i;
+    if (single) {
+      const float inv = 1.f / Lh[i];
+      u32x4 pk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = st.o[2 * e][i] * inv, y = st.o[2 * e + 1][i] * inv;
+        if constexpr (QT == PA_F16)
+          pk[e] = __builtin_bit_cast(uint32_t, h2_t{(_Float16)x, (_Float16)y});
+        else
+          pk[e] = pack_bf16(x, y);
+      }
+      *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(a.out) + (row * D + 8 * c16) * 2) = pk;
+    } else {
+      const int64_t r = row * a.max_parts + piece;
+      float *dst = a.ws_acc + r * D + 8 * c16;
+      *reinterpret_cast<f4v_t *>(dst) = f4v_t{st.o[0][i], st.o[1][i], st.o[2][i], st.o[3][i]};
+      *reinterpret_cast<f4v_t *>(dst + 4) = f4v_t{st.o[4][i], st.o[5][i], st.o[6][i], st.o[7][i]};
+      if (c16 == 0) {
+        a.ws_m[r] = mh[i];
+        a.ws_l[r] = Lh[i];
+      }
+    }
+  }
+}
+
+template <int KV, int QT>
+__device__ __forceinline__ void decode_stream_q8(const DecodeArgs &a) {
+  constexpr int D = 128, G = 8, kTileBytes = kBlock * D;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = blockIdx.x * kDecodeWaves + threadIdx.x / kWave;
+  const int Hkv = a.num_kv_heads;
+  StreamRange rg;
+  if (!stream_range(a, w, lane, rg)) return;
+  const int g16 = lane >> 4, c16 = lane & 15;
+  const char *kbase = reinterpret_cast<const char *>(a.k) + c16 * D + 16 * g16;
+  const char *vbase = reinterpret_cast<const char *>(a.v) + 4 * g16 * D + 8 * c16;
+
+  StreamSeg cur = rg.seg, lseg = cur, pend = cur;
+  int lj = rg.j;
+  u32x4 qb[4], qn[4];  // B operand per k-step: q[head c16][8 dims]; qn: next segment's
+  auto load_q = [&](u32x4 *qf, const StreamSeg &sg) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qf[kk] = u32x4{0, 0, 0, 0};
+    if (c16 < G) {
+      const char *qp = reinterpret_cast<const char *>(a.q) +
+                       (((int64_t)sg.s * a.num_q_heads + sg.h * G + c16) * D) * 2;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        qf[kk] = *reinterpret_cast<const u32x4 *>(qp + q8_dim0(kk, g16) * 2);
+    }
+  };
+  Q8Acc st;
+  auto reset_state = [&]() {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.o[e] = f4v_t{0.f, 0.f, 0.f, 0.f};
+    st.m = kNegBig;
+    st.l = 0.f;
+  };
+  load_q(qb, cur);
+  reset_state();
+
+  auto load_tile = [&](const StreamSeg &sg, int jj, Q8Tile &tt) {
+    const int64_t tile = (int64_t)a.bt[(int64_t)sg.s * a.max_blocks_per_seq + jj] * Hkv + sg.h;
+    const char *kp = kbase + tile * kTileBytes;
+    tt.k0 = *reinterpret_cast<const u32x4 *>(kp);
+    tt.k1 = *reinterpret_cast<const u32x4 *>(kp + 64);
+    const char *vp = vbase + tile * kTileBytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tt.v[i] = *reinterpret_cast<const u32x2 *>(vp + i * D);
+    tt.ks = a.k_scale[tile];
+    tt.vs = a.v_scale[tile];
+  };
+  auto advance = [&]() {
+    if (++lj < lseg.nblk) return;
+    lj = 0;
+    stream_next_seg(a, lseg);
+    load_q(qn, lseg);
+    pend = lseg;
+  };
+  auto compute = [&](int jj, const Q8Tile &tt) {
+    if (jj == cur.nblk - 1 && cur.tail < kBlock)
+      q8_tile<KV, QT, true>(st, qb, tt, a.qk_scale, cur.tail, g16);
+    else
+      q8_tile<KV, QT, false>(st, qb, tt, a.qk_scale, kBlock, g16);
+  };
+  auto after = [&](int jj, bool has_next) {
+    if (jj != cur.nblk - 1 && has_next) return;
+    int piece;
+    const bool single = stream_single(cur, Hkv, rg.tpw, w, piece);
+    q8_emit<QT>(a, st, cur.s, cur.h, single, piece, lane);
+    if (!has_next) return;
+    cur = pend;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qb[kk] = qn[kk];
+    reset_state();
+  };
+
+  const int ntiles = rg.tend - rg.t;
+  Q8Tile tA, tB;
+  int jA = lj, jB = 0;
+  load_tile(lseg, lj, tA);
+  for (int k = 0;;) {
+    bool more = k + 1 < ntiles;
+    if (more) {
+      advance();
+      jB = lj;
+      load_tile(lseg, lj, tB);
+    }
+    compute(jA, tA);
+    after(jA, more);
+    if (!more) break;
+    ++k;
+    more = k + 1 < ntiles;
+    if (more) {
+      advance();
+      jA = lj;
+      load_tile(lseg, lj, tA);
+    }
+    compute(jB, tB);
     after(jB, more);
     if (!more) break;
     ++k;

@@ -67,8 +67,6 @@ struct BlockCopyArgs {
   int32_t tile_bytes;  // 16 * head_dim * element bytes
 };
 
-hipError_t launch_decode(const DecodeArgs &a, int kv_dtype, int q_dtype, int head_dim, int group,
-                         int num_seqs, hipStream_t st);
 hipError_t launch_decode_stream(const DecodeArgs &a, int kv_dtype, int q_dtype, int head_dim,
                                 int group, int num_seqs, hipStream_t st);
 bool mixed_uses_tiles(int kv_dtype);
