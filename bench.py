@@ -213,6 +213,7 @@ def main():
     q, bt, lens, qsl = to(b.q), to(b.block_tables), to(b.seq_lens), to(b.query_start_loc)
     k_new, v_new, pairs = to(b.k_new), to(b.v_new), to(b.copy_pairs)
     R = max(1, args.rotate)
+    shared = b.shares_blocks
     pools = []
     k0, v0 = to(b.k_pool), to(b.v_pool)
     ks0, vs0 = to(b.k_scale), to(b.v_scale)
@@ -221,7 +222,7 @@ def main():
         v = v0 if r == 0 else v0.clone()
         ks = ks0 if (r == 0 or ks0 is None) else ks0.clone()
         vs = vs0 if (r == 0 or vs0 is None) else vs0.clone()
-        pools.append(pa.KVPool(k, v, ks, vs))
+        pools.append(pa.KVPool(k, v, ks, vs, shared_blocks=shared))
     out = torch.empty_like(q)
     slots = torch.empty(b.num_tokens, dtype=torch.int64, device=dev)
     if b.kind == "decode":

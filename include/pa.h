@@ -12,6 +12,8 @@
  *
  * Conventions shared by every call
  *  - Every pointer is a DEVICE pointer unless its comment says "host".
+ *  - The pools (k, v) and the q, out and workspace arrays of the attention calls
+ *    must be 16-byte aligned (PA_E_ARG otherwise); kernels move 16 bytes per lane.
  *  - Calls validate their scalar arguments on the host, then only enqueue
  *    work on `stream`; they never allocate, free or synchronise.  A non-OK
  *    status means nothing was enqueued (PA_E_HIP: a launch was attempted and
@@ -58,6 +60,14 @@ typedef enum pa_status {
 } pa_status_t;
 
 /* Host struct describing caller-owned device memory. */
+/* pa_kv_pool_t.flags */
+#define PA_POOL_SHARED_BLOCKS 1 /* some physical blocks appear in several sequences'
+                                   tables (prefix sharing, [P1] Prefix Sharing): pa_decode
+                                   then reads K/V tiles with ordinary cached loads so that
+                                   repeated reads of a shared tile can hit in cache.
+                                   Without it every tile is read once per call and is
+                                   streamed with a nontemporal hint. */
+
 typedef struct pa_kv_pool {
   void *k;          /* [num_blocks][num_kv_heads][16][head_dim] */
   void *v;          /* same shape */
@@ -68,6 +78,7 @@ typedef struct pa_kv_pool {
   int32_t block_size; /* must be 16 ([P2] 3.2, [P3] 3.2) */
   int32_t head_dim;   /* 64 or 128 */
   int32_t kv_dtype;   /* pa_dtype_t */
+  int32_t flags;      /* PA_POOL_* bits; 0 for none */
 } pa_kv_pool_t;
 
 /* Version string of the library (static storage). */

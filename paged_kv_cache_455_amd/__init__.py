@@ -18,7 +18,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "KVPool", "PagedAttentionError", "library_path", "load_library",
+    "KVPool", "PA_POOL_SHARED_BLOCKS", "PagedAttentionError", "library_path", "load_library",
     "pa_slot_mapping", "kv_cache_write", "kv_block_copy", "pa_decode", "pa_prefill_chunk",
     "pa_decode_workspace_size", "pa_prefill_workspace_size", "PA_DTYPE",
 ]
@@ -49,6 +49,7 @@ class _Pool(ctypes.Structure):
         ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
         ("num_blocks", ctypes.c_int64), ("num_kv_heads", ctypes.c_int32),
         ("block_size", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
     ]
 
 
@@ -125,16 +126,26 @@ def _dt(t: torch.Tensor) -> int:
         raise ValueError(f"unsupported dtype {t.dtype}") from None
 
 
+PA_POOL_SHARED_BLOCKS = 1
+
+
 class KVPool:
-    """Device K/V pools ``[num_blocks][num_kv_heads][16][head_dim]`` (+ scales)."""
+    """Device K/V pools ``[num_blocks][num_kv_heads][16][head_dim]`` (+ scales).
+
+    ``shared_blocks=True`` declares that some physical blocks appear in several
+    sequences' block tables (prefix sharing); decode then reads tiles with cached
+    loads instead of streaming them (``PA_POOL_SHARED_BLOCKS``).
+    """
 
     def __init__(self, k: torch.Tensor, v: torch.Tensor, k_scale: Optional[torch.Tensor] = None,
-                 v_scale: Optional[torch.Tensor] = None):
+                 v_scale: Optional[torch.Tensor] = None, shared_blocks: bool = False):
         if k.shape != v.shape or k.dim() != 4 or k.dtype != v.dtype:
             raise ValueError("k and v pools must share one 4-d shape and dtype")
         self.k, self.v, self.k_scale, self.v_scale = k, v, k_scale, v_scale
         nb, hkv, bs, d = k.shape
-        self._s = _Pool(_ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale), nb, hkv, bs, d, _dt(k))
+        flags = PA_POOL_SHARED_BLOCKS if shared_blocks else 0
+        self._s = _Pool(_ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale), nb, hkv, bs, d, _dt(k),
+                        flags)
 
     @property
     def num_kv_heads(self) -> int:

@@ -55,6 +55,9 @@ pa_status_t check_pool(const pa_kv_pool_t *pool, bool need_scales_if_quantised) 
     return fail(PA_E_ARG, "1-byte kv_dtype needs k_scale and v_scale");
   if (!is_quantised(pool->kv_dtype) && (pool->k_scale != nullptr || pool->v_scale != nullptr))
     return fail(PA_E_ARG, "scales are only meaningful for 1-byte kv_dtype");
+  if (((uintptr_t)pool->k | (uintptr_t)pool->v) & 15)
+    return fail(PA_E_ARG, "pool k/v must be 16-byte aligned");
+  if (pool->flags & ~PA_POOL_SHARED_BLOCKS) return fail(PA_E_ARG, "unknown pool flags 0x%x", pool->flags);
   return PA_OK;
 }
 
@@ -240,6 +243,8 @@ static pa_status_t fill_decode_args(const pa_kv_pool_t *pool, const void *q, int
   if ((st = check_q_dtype(pool->kv_dtype, q_dtype)) != PA_OK) return st;
   if ((st = check_heads(num_q_heads, pool->num_kv_heads, &group)) != PA_OK) return st;
   if (!q || !out || !block_tables || !lens) return fail(PA_E_ARG, "NULL array argument");
+  if (((uintptr_t)q | (uintptr_t)out | (uintptr_t)workspace) & 15)
+    return fail(PA_E_ARG, "q, out and workspace must be 16-byte aligned");
   if (max_blocks_per_seq <= 0) return fail(PA_E_ARG, "max_blocks_per_seq must be > 0");
   if (max_len <= 0) return fail(PA_E_ARG, "max length must be > 0");
   if ((int64_t)max_len > (int64_t)max_blocks_per_seq * kBlockTokens)
@@ -300,8 +305,9 @@ pa_status_t pa_decode(const pa_kv_pool_t *pool, const void *q, int32_t q_dtype, 
   a.max_parts = stream_pieces(max_context_len);
   a.num_seqs = num_seqs;
   a.min_tpw = kMinTilesPerWave;
+  const bool stream_loads = (pool->flags & PA_POOL_SHARED_BLOCKS) == 0;
   return hip_status(pa::launch_decode_stream(a, pool->kv_dtype, q_dtype, pool->head_dim, group,
-                                             num_seqs, stream),
+                                             num_seqs, stream_loads, stream),
                     "pa_decode launch");
 }
 

@@ -67,8 +67,19 @@ struct BlockCopyArgs {
   int32_t tile_bytes;  // 16 * head_dim * element bytes
 };
 
+// stream_loads: read K/V tiles with the nontemporal hint (off when blocks are shared)
 hipError_t launch_decode_stream(const DecodeArgs &a, int kv_dtype, int q_dtype, int head_dim,
-                                int group, int num_seqs, hipStream_t st);
+                                int group, int num_seqs, bool stream_loads, hipStream_t st);
+hipError_t launch_decode_f32(const DecodeArgs &a, int q_dtype, int D, int G, int num_seqs,
+                             bool stream_loads, hipStream_t st);
+hipError_t launch_decode_f16(const DecodeArgs &a, int q_dtype, int D, int G, int num_seqs,
+                             bool stream_loads, hipStream_t st);
+hipError_t launch_decode_bf16(const DecodeArgs &a, int q_dtype, int D, int G, int num_seqs,
+                              bool stream_loads, hipStream_t st);
+hipError_t launch_decode_fp8(const DecodeArgs &a, int q_dtype, int D, int G, int num_seqs,
+                             bool stream_loads, hipStream_t st);
+hipError_t launch_decode_i8(const DecodeArgs &a, int q_dtype, int D, int G, int num_seqs,
+                            bool stream_loads, hipStream_t st);
 bool mixed_uses_tiles(int kv_dtype);
 hipError_t launch_mixed(const MixedArgs &a, int kv_dtype, int q_dtype, int head_dim, int group,
                         int num_rows, hipStream_t st);

@@ -88,6 +88,17 @@ class PagedBatch:
         return int(self.seq_lens.max())
 
     @property
+    def shares_blocks(self) -> bool:
+        """True when a physical block appears in more than one sequence's used table
+        entries (prefix sharing): the pool is then declared with shared blocks."""
+        used = []
+        for s in range(self.num_seqs):
+            nb = (int(self.seq_lens[s]) + 15) // 16
+            used.append(self.block_tables[s, :nb])
+        ids = torch.cat(used) if used else torch.empty(0, dtype=torch.int32)
+        return int(torch.unique(ids).numel()) < int(ids.numel())
+
+    @property
     def max_query_len(self) -> int:
         qsl = self.query_start_loc
         return int((qsl[1:] - qsl[:-1]).max())

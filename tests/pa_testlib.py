@@ -86,7 +86,7 @@ def oracle_mixed(b: W.PagedBatch, seqs=None):
 class Dev:
     """A batch's arrays on the GPU plus a KVPool over them."""
 
-    def __init__(self, b: W.PagedBatch, device="cuda"):
+    def __init__(self, b: W.PagedBatch, device="cuda", shared_blocks=None):
         import paged_kv_cache_455_amd as pa
         to = lambda t: None if t is None else t.to(device).contiguous()
         self.b = b
@@ -101,7 +101,9 @@ class Dev:
         self.k_new = to(b.k_new)
         self.v_new = to(b.v_new)
         self.pairs = to(b.copy_pairs)
-        self.pool = pa.KVPool(self.k, self.v, self.ks, self.vs)
+        if shared_blocks is None:
+            shared_blocks = b.shares_blocks
+        self.pool = pa.KVPool(self.k, self.v, self.ks, self.vs, shared_blocks=shared_blocks)
 
 
 def max_err(gpu: torch.Tensor, ref: np.ndarray) -> float:

@@ -43,14 +43,14 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, n), f"{n} declared in pa.h but not exported"
 
 
-def pool(kv=pa.PA_F16, head_dim=128, block=16, hkv=8, nb=100, scales=False):
-    return pa._Pool(FAKE, FAKE, FAKE if scales else None, FAKE if scales else None, nb, hkv,
-                    block, head_dim, kv)
+def pool(kv=pa.PA_F16, head_dim=128, block=16, hkv=8, nb=100, scales=False, flags=0, k=FAKE):
+    return pa._Pool(k, FAKE, FAKE if scales else None, FAKE if scales else None, nb, hkv,
+                    block, head_dim, kv, flags)
 
 
 def decode(lib, p, q_dtype=pa.PA_F16, hq=32, S=4, max_ctx=100, mbps=10, ws=None, wsb=0,
-           scale=0.1):
-    return lib.pa_decode(ctypes.byref(p), FAKE, q_dtype, FAKE, FAKE, mbps, FAKE, S, hq, max_ctx,
+           scale=0.1, q=FAKE):
+    return lib.pa_decode(ctypes.byref(p), q, q_dtype, FAKE, FAKE, mbps, FAKE, S, hq, max_ctx,
                          scale, ws, wsb, None)
 
 
@@ -70,6 +70,15 @@ def test_decode_argument_checks(lib):
     assert need > 0
     assert decode(lib, pool(), max_ctx=4096, mbps=256) == PA_E_WORKSPACE
     assert decode(lib, pool(), max_ctx=4096, mbps=256, ws=FAKE, wsb=need - 1) == PA_E_WORKSPACE
+    # pool flags: the shared-blocks bit is accepted (the call gets as far as the
+    # workspace check), unknown bits are not
+    assert decode(lib, pool(flags=pa.PA_POOL_SHARED_BLOCKS), max_ctx=4096, mbps=256) == PA_E_WORKSPACE
+    assert decode(lib, pool(flags=2)) == PA_E_ARG
+    assert b"flags" in lib.pa_last_error()
+    # 16-byte alignment of the pools and of q/out/workspace
+    assert decode(lib, pool(k=FAKE + 8)) == PA_E_ARG
+    assert decode(lib, pool(), q=FAKE + 4) == PA_E_ARG
+    assert b"aligned" in lib.pa_last_error()
     # empty batch: nothing to do
     assert decode(lib, pool(), S=0) == PA_OK
     assert lib.pa_status_string(PA_E_WORKSPACE) == b"workspace too small"

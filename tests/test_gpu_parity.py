@@ -201,6 +201,22 @@ def test_decode_deterministic_and_block_permutation_invariant():
     assert torch.equal(o1, o3)
 
 
+@pytest.mark.parametrize("kv,qd,hq,hkv", [("f16", "f16", 32, 8), ("bf16", "bf16", 16, 8),
+                                           ("fp8", "bf16", 64, 8), ("i8", "f16", 32, 8)])
+def test_decode_cached_and_streamed_loads_agree(kv, qd, hq, hkv):
+    # the pool's shared-blocks flag only changes the cache hint of the K/V loads:
+    # both kernels give the same bits, and both match the oracle
+    b = W.decode_batch(31, [1, 17, 300, 1024, 2100], hq, hkv, 128, kv, qd, poison=True,
+                       div=128 ** 0.5, name=f"hint-{kv}-{qd}")
+    b = poison_tails(b)
+    streamed = run_decode(Dev(b, shared_blocks=False)).clone()
+    cached = run_decode(Dev(b, shared_blocks=True)).clone()
+    assert torch.equal(streamed, cached)
+    err = max_err(streamed, oracle_decode_rows(b))
+    say(b.name, "max_err", err)
+    assert err <= TOL[kv]
+
+
 def test_decode_shared_prefix_equals_private_copies():
     b = W.prefix_cow(n_req=12, n_forks=0, suffix_hi=400)
     d = Dev(b)
