@@ -311,39 +311,35 @@ pa_status_t pa_decode(const pa_kv_pool_t *pool, const void *q, int32_t q_dtype, 
                     "pa_decode launch");
 }
 
-// Workspace of the mixed step.  f16/bf16 KV: a 2-int header, the work lists and
-// per-sequence decode partitions of kMixedPartBlocks blocks.  Other KV types run
-// every query row through the partitioned decode path (per-row partitions).
-constexpr int kMixedPartBlocks = 32;
-constexpr int kMixedTileRows = 64;  // query rows per prefill tile (matches prefill.hip)
-
+// Workspace of the mixed step.  f16/bf16 KV: a header int, the prefill tile list,
+// then the balanced-split decode workspace of the one-token rows (pieces for every
+// sequence, as pa_decode lays them out).  Other KV types run every query row
+// through the partitioned decode path (per-row partitions).
 struct MixedLayout {
-  size_t hdr_off, p_off, d_off, acc_off, m_off, l_off, total;
-  int p_bound, d_bound, part_blocks, max_parts, qtok;
+  size_t hdr_off, p_off, acc_off, m_off, l_off, stream_off, total;
+  WsLayout stream;  // offsets relative to stream_off
+  int p_bound, part_blocks, max_parts, qtok;
 };
 
 MixedLayout mixed_layout(int kv_dtype, int64_t S, int64_t T, int Hq, int Hkv, int D,
                          int max_seq_len) {
   MixedLayout w{};
   const int max_blocks = (max_seq_len + kBlockTokens - 1) / kBlockTokens;
-  int64_t rows;
   if (pa::mixed_uses_tiles(kv_dtype)) {
-    w.qtok = kMixedTileRows / (Hq / Hkv);
-    w.part_blocks = kMixedPartBlocks;
-    w.max_parts = (max_blocks + w.part_blocks - 1) / w.part_blocks;
+    w.qtok = pa::mixed_tile_rows() / (Hq / Hkv);
     w.p_bound = (int)((T + w.qtok - 1) / w.qtok + S);
-    w.d_bound = (int)(S * w.max_parts);
-    rows = S;
-  } else {
-    w.part_blocks = decode_part_blocks(T, Hkv, max_blocks);
-    w.max_parts = (max_blocks + w.part_blocks - 1) / w.part_blocks;
-    rows = T;
+    w.max_parts = stream_pieces(max_seq_len);
+    w.stream = stream_layout(S, Hq, D, max_seq_len);
+    w.hdr_off = 0;
+    w.p_off = align256(sizeof(int32_t));
+    w.stream_off = w.p_off + align256((size_t)w.p_bound * sizeof(int32_t));
+    w.total = w.stream_off + w.stream.total;
+    return w;
   }
-  const size_t n_ml = (size_t)rows * Hq * w.max_parts;
-  w.hdr_off = 0;
-  w.p_off = align256(2 * sizeof(int32_t));
-  w.d_off = w.p_off + align256((size_t)w.p_bound * sizeof(int32_t));
-  w.acc_off = w.d_off + align256((size_t)w.d_bound * sizeof(int32_t));
+  w.part_blocks = decode_part_blocks(T, Hkv, max_blocks);
+  w.max_parts = (max_blocks + w.part_blocks - 1) / w.part_blocks;
+  const size_t n_ml = (size_t)T * Hq * w.max_parts;
+  w.acc_off = 0;
   w.m_off = w.acc_off + align256(n_ml * D * sizeof(float));
   w.l_off = w.m_off + align256(n_ml * sizeof(float));
   w.total = w.l_off + align256(n_ml * sizeof(float));
@@ -382,31 +378,40 @@ pa_status_t pa_prefill_chunk(const pa_kv_pool_t *pool, const void *q, int32_t q_
   if (st != PA_OK) return st;
   const MixedLayout w = mixed_layout(pool->kv_dtype, num_seqs, num_q_tokens, num_q_heads,
                                      pool->num_kv_heads, pool->head_dim, max_seq_len);
-  if (pa::mixed_uses_tiles(pool->kv_dtype)) {
-    if (max_query_len > 4096 * w.qtok)
-      return fail(PA_E_UNSUPPORTED, "max_query_len %d too long (limit %d)", max_query_len,
-                  4096 * w.qtok);
-    if (w.max_parts > 4096) return fail(PA_E_UNSUPPORTED, "max_seq_len too long");
-  }
+  const bool tiles = pa::mixed_uses_tiles(pool->kv_dtype);
+  if (tiles && max_query_len > 4096 * w.qtok)
+    return fail(PA_E_UNSUPPORTED, "max_query_len %d too long (limit %d)", max_query_len,
+                4096 * w.qtok);
   if (workspace == nullptr || workspace_bytes < w.total)
     return fail(PA_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
                 workspace ? workspace_bytes : (size_t)0);
   char *ws = reinterpret_cast<char *>(workspace);
-  m.dec.ws_acc = reinterpret_cast<float *>(ws + w.acc_off);
-  m.dec.ws_m = reinterpret_cast<float *>(ws + w.m_off);
-  m.dec.ws_l = reinterpret_cast<float *>(ws + w.l_off);
-  m.dec.part_blocks = w.part_blocks;
-  m.dec.max_parts = w.max_parts;
   m.qsl = query_start_loc;
-  m.hdr = reinterpret_cast<int32_t *>(ws + w.hdr_off);
-  m.p_items = reinterpret_cast<int32_t *>(ws + w.p_off);
-  m.d_items = reinterpret_cast<int32_t *>(ws + w.d_off);
   m.num_seqs = num_seqs;
-  m.p_bound = w.p_bound;
-  m.d_bound = w.d_bound;
-  m.qtok = w.qtok;
+  if (tiles) {
+    char *sw = ws + w.stream_off;
+    m.hdr = reinterpret_cast<int32_t *>(ws + w.hdr_off);
+    m.p_items = reinterpret_cast<int32_t *>(ws + w.p_off);
+    m.p_bound = w.p_bound;
+    m.qtok = w.qtok;
+    m.dec.ws_acc = reinterpret_cast<float *>(sw + w.stream.acc_off);
+    m.dec.ws_m = reinterpret_cast<float *>(sw + w.stream.m_off);
+    m.dec.ws_l = reinterpret_cast<float *>(sw + w.stream.l_off);
+    m.dec.hdr = reinterpret_cast<int32_t *>(sw + w.stream.hdr_off);
+    m.dec.max_parts = w.max_parts;
+    m.dec.num_seqs = num_seqs;
+    m.dec.min_tpw = kMinTilesPerWave;
+    m.dec.qsl = query_start_loc;
+  } else {
+    m.dec.ws_acc = reinterpret_cast<float *>(ws + w.acc_off);
+    m.dec.ws_m = reinterpret_cast<float *>(ws + w.m_off);
+    m.dec.ws_l = reinterpret_cast<float *>(ws + w.l_off);
+    m.dec.part_blocks = w.part_blocks;
+    m.dec.max_parts = w.max_parts;
+  }
+  const bool stream_loads = (pool->flags & PA_POOL_SHARED_BLOCKS) == 0;
   return hip_status(pa::launch_mixed(m, pool->kv_dtype, q_dtype, pool->head_dim, group,
-                                     num_q_tokens, stream),
+                                     num_q_tokens, stream_loads, stream),
                     "pa_prefill_chunk launch");
 }
 

@@ -583,11 +583,23 @@ __device__ __forceinline__ int wave_incl_scan_i(int x, int lane) {
   return x;
 }
 
+// Decode rows of a mixed step: with a.qsl set, sequence s's query row is qsl[s] and
+// only sequences with one new token (q_len == 1) take part; without it sequence s
+// is row s.
+__device__ __forceinline__ int decode_len(const DecodeArgs &a, int s) {
+  if (a.qsl != nullptr && a.qsl[s + 1] - a.qsl[s] != 1) return 0;
+  return a.ctx[s];
+}
+__device__ __forceinline__ int64_t decode_row(const DecodeArgs &a, int s) {
+  return a.qsl != nullptr ? a.qsl[s] : s;
+}
+
 // Write this wave's state for (s, kv head h): normalised output when single,
 // else the partial for `piece`.  Lanes of token group 0 hold every column chunk.
 template <int KV, int QT, int D, int G>
 __device__ __forceinline__ void emit_segment(const DecodeArgs &a, DecodeState<KV, QT, D, G> &st,
                                              int s, int h, bool single, int piece, int lane) {
+  const int64_t row = decode_row(a, s);
   constexpr int EPC = Geom<KV, D>::EPC, LPT = Geom<KV, D>::LPT;
   merge_token_groups(st);
   if (lane >= LPT) return;
@@ -596,7 +608,7 @@ __device__ __forceinline__ void emit_segment(const DecodeArgs &a, DecodeState<KV
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float inv = 1.f / st.l[g];
-      const int64_t o = ((int64_t)s * a.num_q_heads + h * G + g) * D + c * EPC;
+      const int64_t o = (row * a.num_q_heads + h * G + g) * D + c * EPC;
 #pragma unroll
       for (int e = 0; e < EPC; ++e) store_out<QT>(a.out, o + e, st.acc[g][e] * inv);
     }
@@ -645,7 +657,7 @@ __device__ __forceinline__ bool stream_range(const DecodeArgs &a, int w, int lan
   int nb0 = 0, incl0 = 0;  // first 64 sequences, kept for the locate pass
   for (int c0 = 0; c0 < S; c0 += kWave) {
     const int sq = c0 + lane;
-    const int n = sq < S ? a.ctx[sq] : 0;
+    const int n = sq < S ? decode_len(a, sq) : 0;
     const int nb = n > 0 ? (n + kBlock - 1) / kBlock : 0;
     const int incl = wave_incl_scan_i(nb, lane);
     if (c0 == 0) {
@@ -671,7 +683,7 @@ __device__ __forceinline__ bool stream_range(const DecodeArgs &a, int w, int lan
       nb = nb0;
       incl = incl0;
     } else {
-      const int n = sq < S ? a.ctx[sq] : 0;
+      const int n = sq < S ? decode_len(a, sq) : 0;
       nb = n > 0 ? (n + kBlock - 1) / kBlock : 0;
       incl = base + wave_incl_scan_i(nb, lane);
     }
@@ -699,7 +711,7 @@ struct SeqWindow {
   int s0, ctx_l;
   __device__ __forceinline__ void load(const DecodeArgs &a, int first, int lane) {
     s0 = first;
-    ctx_l = first + lane < a.num_seqs ? a.ctx[first + lane] : 0;
+    ctx_l = first + lane < a.num_seqs ? decode_len(a, first + lane) : 0;
   }
   __device__ __forceinline__ int ctx(const DecodeArgs &a, int s, int lane) {
     if (s - s0 >= kWave) load(a, s, lane);
@@ -848,7 +860,7 @@ struct GenericPath {
     }
   }
   __device__ __forceinline__ void prefetch_q(const StreamSeg &sg) {
-    const int64_t qbase = ((int64_t)sg.s * a.num_q_heads + sg.h * G) * D;
+    const int64_t qbase = (decode_row(a, sg.s) * a.num_q_heads + sg.h * G) * D;
 #pragma unroll
     for (int g = 0; g < G; ++g) qn[g].template load<QT>(a.q, qbase + (int64_t)g * D + cidx * EPC);
   }
@@ -1081,9 +1093,11 @@ __device__ __forceinline__ void q8_emit(const DecodeArgs &a, const Q8Acc &st, in
     Lh[i] = __shfl(L, 4 * g16 + i, kWave);
   }
   if (g16 >= 2) return;  // padding heads
+  const int64_t qrow = decode_row(a, s);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t row = (int64_t)s * a.num_q_heads + h * G + 4 * g16 + i;
+    const int64_t row = (int64_t)s * a.num_q_heads + h * G + 4 * g16 + i;      // workspace
+    const int64_t orow = qrow * a.num_q_heads + h * G + 4 * g16 + i;          // output
     if (single) {
       const float inv = 1.f / Lh[i];
       u32x4 pk;
@@ -1095,7 +1109,7 @@ __device__ __forceinline__ void q8_emit(const DecodeArgs &a, const Q8Acc &st, in
         else
           pk[e] = pack_bf16(x, y);
       }
-      *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(a.out) + (row * D + 8 * c16) * 2) = pk;
+      *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(a.out) + (orow * D + 8 * c16) * 2) = pk;
     } else {
       const int64_t r = row * a.max_parts + piece;
       float *dst = a.ws_acc + r * D + 8 * c16;
@@ -1139,7 +1153,7 @@ struct Q8Path {
     for (int kk = 0; kk < 4; ++kk) qn[kk] = u32x4{0, 0, 0, 0};
     if (c16 < G) {
       const char *qp = reinterpret_cast<const char *>(a.q) +
-                       (((int64_t)sg.s * a.num_q_heads + sg.h * G + c16) * D) * 2;
+                       ((decode_row(a, sg.s) * a.num_q_heads + sg.h * G + c16) * D) * 2;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
         qn[kk] = *reinterpret_cast<const u32x4 *>(qp + q8_dim0(kk, g16) * 2);
@@ -1181,8 +1195,9 @@ __device__ __forceinline__ void decode_stream_q8(const DecodeArgs &a) {
 // Nothing to do where one wave owned the whole segment (pieces == 1).
 template <int QT, int D>
 __device__ __forceinline__ void merge_stream(const DecodeArgs &a, int s, int hq, int lane) {
+  if (a.qsl != nullptr && a.qsl[s + 1] - a.qsl[s] != 1) return;  // not a decode row
   const int n = a.ctx[s];
-  const int64_t o = ((int64_t)s * a.num_q_heads + hq) * D;
+  const int64_t o = (decode_row(a, s) * a.num_q_heads + hq) * D;
   if (n <= 0) {  // undefined input; keep the output finite and defined
     for (int d = lane; d < D; d += kWave) store_out<QT>(a.out, o + d, 0.f);
     return;

@@ -30,18 +30,20 @@ struct DecodeArgs {
   int32_t num_seqs;
   int32_t num_waves;    // waves launched
   int32_t min_tpw;      // lower bound on tiles per wave
+  // mixed step: [num_seqs + 1] query starts; only q_len == 1 sequences are decoded,
+  // sequence s's query/output row being qsl[s] (nullptr: every sequence, row s)
+  const int32_t *qsl;
 };
 
 struct MixedArgs {
-  DecodeArgs dec;       // pools, q/out, tables, seq_lens (as ctx), decode-row workspace
+  DecodeArgs dec;       // pools, q/out, tables, seq_lens (as ctx); for f16/bf16 KV also the
+                        // balanced-split decode of the one-token rows (dec.qsl set)
   const int32_t *qsl;   // [num_seqs + 1]
-  int32_t *hdr;         // [2]: prefill items, decode items (written by the prep kernel)
+  int32_t *hdr;         // [1]: prefill tiles listed (written by the prep kernel)
   int32_t *p_items;     // [p_bound]
-  int32_t *d_items;     // [d_bound]
   int32_t num_seqs;
   int32_t p_bound;
-  int32_t d_bound;
-  int32_t qtok;         // query tokens per prefill tile (128 / G)
+  int32_t qtok;         // query tokens per prefill tile (tile rows / G)
 };
 
 struct CacheWriteArgs {
@@ -81,8 +83,9 @@ hipError_t launch_decode_fp8(const DecodeArgs &a, int q_dtype, int D, int G, int
 hipError_t launch_decode_i8(const DecodeArgs &a, int q_dtype, int D, int G, int num_seqs,
                             bool stream_loads, hipStream_t st);
 bool mixed_uses_tiles(int kv_dtype);
+int mixed_tile_rows();  // query rows (token, head) per prefill tile of the mixed kernel
 hipError_t launch_mixed(const MixedArgs &a, int kv_dtype, int q_dtype, int head_dim, int group,
-                        int num_rows, hipStream_t st);
+                        int num_rows, bool stream_loads, hipStream_t st);
 hipError_t launch_cache_write(const CacheWriteArgs &a, hipStream_t st);
 hipError_t launch_block_copy(const BlockCopyArgs &a, hipStream_t st);
 hipError_t launch_slot_mapping(const int32_t *bt, int32_t mbps, const int32_t *qsl,

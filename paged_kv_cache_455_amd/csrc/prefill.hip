@@ -6,10 +6,11 @@
 // sequence to seq_len tokens sits at position seq_len - q_len + i and attends to
 // keys 0 .. that position.
 //
-// One launch runs two kinds of workgroups, from a work list built on the device:
-//  * prefill tiles (f16 / bf16 KV): 128 query rows -- (token, head) pairs of one
-//    kv head's GQA group -- against 32-key steps of the chunk's context, with the
-//    dense products on MFMA (v_mfma_f32_16x16x32_{f16,bf16}):
+// For f16 / bf16 KV the step is two launches (after a small one that lists the
+// prefill tiles on the device):
+//  * prefill tiles: 64 * RB query rows -- (token, head) pairs of one kv head's GQA
+//    group -- against 32-key steps of the chunk's context, with the dense products
+//    on MFMA (v_mfma_f32_16x16x32_{f16,bf16}):
 //      S^T = K . Q^T   (A = 16 keys x 32 dims from LDS, B = q rows in registers)
 //      O^T += V^T . P^T (A = 16 dims x 32 keys of the transposed V tile in LDS,
 //                        B = the probabilities straight from S^T's registers)
@@ -17,8 +18,9 @@
 //    (first: keys 8(r/4) + r%4, second: the same + 4) so that each lane's 8 scores
 //    are the 8 consecutive keys its P^T operand needs; computing O^T rather than O
 //    keeps each query row's running max, sum and rescale inside one lane.
-//  * decode rows (q_len == 1): the partitioned VALU decode path of decode_impl.h.
-// Decode rows split over several partitions are combined by a second launch.
+//  * decode rows (q_len == 1): the balanced-split decode of decode_impl.h over
+//    the batch's one-token sequences (query row qsl[s]), with its piece merge.
+// Other KV types run every query row through the partitioned decode path.
 #include "decode_impl.h"
 
 namespace pa {
@@ -27,21 +29,28 @@ typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kRowBlocks = 1;   // 16-row MFMA blocks per wave
+#ifndef PA_PREFILL_RB
+#define PA_PREFILL_RB 2
+#endif
+constexpr int kRowBlocks = PA_PREFILL_RB;       // 16-row MFMA blocks per wave
 constexpr int kTileRows = 4 * 16 * kRowBlocks;  // query rows (token, head) per prefill workgroup
 constexpr int kKeyStep = 32;    // keys per step (two blocks)
 constexpr int kVtStride = 40;   // halves per transposed-V row: 32 keys + 8 pad (80 bytes)
-constexpr int kBtCache = 512;   // block-table entries of a tile kept in LDS (8192 keys)
 constexpr int kItemBits = 12;   // item = (sequence << 12) | tile or partition index
+#ifndef PA_PREFILL_STAGES
+#define PA_PREFILL_STAGES 3
+#endif
+constexpr int kStages = PA_PREFILL_STAGES;  // key steps whose K/V loads are in flight in registers
+constexpr float kLazy = 8.f;    // running-max slack before a rescale (log2 units)
 
+int mixed_tile_rows() { return kTileRows; }
 
 template <int D>
 struct PrefillLds {
   static constexpr int kKHalves = kKeyStep * D;     // K: [32 keys][D], chunks swizzled
   static constexpr int kVtHalves = D * kVtStride;   // V^T: [D][32 keys + pad], groups swizzled
   static constexpr int kBufHalves = kKHalves + kVtHalves;
-  static constexpr int kBtOffset = 2 * kBufHalves * 2;        // bytes: two K/V buffers first
-  static constexpr int kBytes = kBtOffset + kBtCache * 4;     // then the block-table cache
+  static constexpr int kBytes = 2 * kBufHalves * 2;  // two K/V buffers
 };
 
 template <int KV>
@@ -75,9 +84,12 @@ __device__ __forceinline__ u32x4 pack8(const float *p) {
 
 // One prefill tile: query tokens [qt*QTOK, ...) of sequence s, kv head h.
 // Rows: wave w, row block rb, lane column c16 -> row (w*RB + rb)*16 + c16 = token*G + head.
-// Pipeline: the block-table entries of the tile sit in LDS; K/V of step n+2 are
-// loaded into registers while step n is computed from LDS and step n+1 is written
-// to the other LDS buffer.
+// Pipeline, per 32-key step n (NS = kStages): the two block-table entries of step
+// n+NS+1 are read, K/V of step n+NS are loaded into registers, step n is computed
+// from LDS and step n+1 is written to the other LDS buffer.  Every load is issued unconditionally
+// (indices clamped to the tile's last block, keys past its reach zeroed when they
+// reach LDS) so that the compiler's waits count loads instead of draining them.
+// Each K or V operand read from LDS serves all RB row blocks of the wave.
 template <int KV, int D, int G>
 __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, int qt,
                                              char *smem) {
@@ -86,10 +98,11 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
   constexpr int NKK = D / 32;        // QK MFMAs along head_dim
   constexpr int NSL = D / 16;        // 16-dim output slices
   constexpr int CPR = D / 8;         // 16-byte chunks per key row
-  constexpr int NCH = kKeyStep * CPR / 256;  // K (and V) chunks per thread per step
+  constexpr int NCH = kKeyStep * CPR / 256;  // K chunks per thread per step
+  constexpr int NVB = (kKeyStep / 4) * (D / 4);  // V blocks of 4 keys x 4 dims per step
+  static_assert(NVB <= 256, "one V block per thread");
   using L = PrefillLds<D>;
   _Float16 *lds = reinterpret_cast<_Float16 *>(smem);
-  int32_t *bt_lds = reinterpret_cast<int32_t *>(smem + L::kBtOffset);
   const DecodeArgs &d = a.dec;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g16 = lane >> 4, c16 = lane & 15;
@@ -98,13 +111,14 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
   const int t0 = qt * QTOK;
   const int t_end = min(t0 + QTOK, q_len);
   const int nkeys = first_pos + t_end;  // keys any row of the tile can see
-  const int min_pos = first_pos + t0;
   const int32_t *bt = d.bt + (int64_t)s * d.max_blocks_per_seq;
   const int Hq = d.num_q_heads, Hkv = d.num_kv_heads;
+  // the wave's rows: tokens t0 + (wave*RB*16) / G ... ; positions bound its keys
+  const int wave_tok0 = t0 + (wave * RB * 16) / G;
+  const int wave_min_pos = first_pos + wave_tok0;
+  const int wave_max_pos = first_pos + min(t0 + ((wave + 1) * RB * 16 - 1) / G, q_len - 1);
 
-  // block-table entries of the tile's keys -> LDS (beyond the cache: read directly)
   const int nblk = (nkeys + kBlock - 1) / kBlock;
-  for (int i = tid; i < nblk && i < kBtCache; i += 256) bt_lds[i] = bt[i];
 
   // query operands: lane (row c16 of row block rb) holds dims 32*kk + 8*g16 .. +8
   u32x4 qop[RB][NKK];
@@ -137,48 +151,80 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
 #pragma unroll
     for (int sl = 0; sl < NSL; ++sl) o[rb][sl] = f4_t{0.f, 0.f, 0.f, 0.f};
   }
-  __syncthreads();  // block-table cache ready
 
   // ---- global -> registers -> LDS staging of one 32-key step ----
   const char *kpool = reinterpret_cast<const char *>(d.k);
   const char *vpool = reinterpret_cast<const char *>(d.v);
-  struct Stage {
-    u32x4 k[NCH], v[NCH];
+  // block-table entries of step n's two blocks (clamped to the last block)
+  struct StepBt {
+    int b0, b1;
   };
-  auto gload = [&](int kb, Stage &st) {
+  auto bt_load = [&](int n) {
+    StepBt r;
+    r.b0 = bt[min(2 * n, nblk - 1)];
+    r.b1 = bt[min(2 * n + 1, nblk - 1)];
+    return r;
+  };
+  // byte offset of key row `key` (0..31 within the step) in its (block, h) tile
+  auto row_off = [&](const StepBt &b, int key) {
+    const int64_t tile = (int64_t)(key < kBlock ? b.b0 : b.b1) * Hkv + h;
+    return (tile * kBlock + (key % kBlock)) * D * 2;
+  };
+  // K: chunk q of the step = key q / CPR, 16-byte column q % CPR.
+  // V: thread tid < NVB owns dims 4*(tid % (D/4)) .. +3 of keys 4*(tid / (D/4)) .. +3
+  // (a wave's loads of one key row are contiguous).
+  struct Stage {
+    u32x4 k[NCH];
+    u32x2 v[4];
+  };
+  const int vdg = tid % (D / 4), vkg = tid / (D / 4);
+  auto gload = [&](const StepBt &b, Stage &st) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int q = tid + 256 * c;
-      const int key = q / CPR, cc = q % CPR;
-      const int kabs = kb + key;
-      if (kabs < nkeys) {  // keys past the tile's reach are never read (zeros instead)
-        const int bi = kabs / kBlock;
-        const int64_t tile = (int64_t)(bi < kBtCache ? bt_lds[bi] : bt[bi]) * Hkv + h;
-        const int64_t off = (tile * kBlock + (kabs % kBlock)) * D * 2 + cc * 16;
-        st.k[c] = *reinterpret_cast<const u32x4 *>(kpool + off);
-        st.v[c] = *reinterpret_cast<const u32x4 *>(vpool + off);
-      } else {
-        st.k[c] = u32x4{0, 0, 0, 0};
-        st.v[c] = u32x4{0, 0, 0, 0};
-      }
+      st.k[c] = *reinterpret_cast<const u32x4 *>(kpool + row_off(b, q / CPR) + (q % CPR) * 16);
     }
+    // (threads past NVB, for head_dim 64, load rows of the step's second block too;
+    // lstore ignores them)
+    const int64_t vb = row_off(b, (4 * vkg) % kKeyStep) + vdg * 8;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) st.v[r] = *reinterpret_cast<const u32x2 *>(vpool + vb + r * D * 2);
   };
   // V^T rows hold the 32 keys in 4 groups of 8; group gk of dim row d sits at
-  // position gk ^ ((d / 8) & 3) so that a wave's 2-byte stores spread over banks.
-  auto lstore = [&](int buf, const Stage &st) {
+  // position gk ^ ((d / 8) & 3) so that the operand reads spread over banks.  A
+  // thread's 4 x 4 block is transposed in registers (16-bit halves picked by byte
+  // permutes) and written as four 8-byte rows.
+  // Keys at or past nkeys (the tile's reach; they may hold anything, NaN included)
+  // are zeroed on the way in.
+  auto lstore = [&](int buf, int kb, const Stage &st) {
     _Float16 *K = lds + buf * L::kBufHalves;
-    uint16_t *Vt = reinterpret_cast<uint16_t *>(K + L::kKHalves);
+    _Float16 *Vt = K + L::kKHalves;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int q = tid + 256 * c;
       const int key = q / CPR, cc = q % CPR;
       const int pc = cc ^ (key & (CPR - 1));  // swizzle: rows hit different banks
-      *reinterpret_cast<u32x4 *>(K + key * D + pc * 8) = st.k[c];
-      const int col = ((key >> 3) ^ (cc & 3)) * 8 + (key & 7);
+      const bool ok = kb + key < nkeys;
+      *reinterpret_cast<u32x4 *>(K + key * D + pc * 8) = ok ? st.k[c] : u32x4{0, 0, 0, 0};
+    }
+    if (tid < NVB) {
+      uint32_t v[4][2];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        Vt[(cc * 8 + 2 * w) * kVtStride + col] = (uint16_t)(st.v[c][w] & 0xffffu);
-        Vt[(cc * 8 + 2 * w + 1) * kVtStride + col] = (uint16_t)(st.v[c][w] >> 16);
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = kb + 4 * vkg + r < nkeys;
+        v[r][0] = ok ? st.v[r][0] : 0u;
+        v[r][1] = ok ? st.v[r][1] : 0u;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const int w = e >> 1;
+        u32x2 col;
+        col[0] = __builtin_amdgcn_perm(v[1][w], v[0][w], sel);  // keys 0, 1
+        col[1] = __builtin_amdgcn_perm(v[3][w], v[2][w], sel);  // keys 2, 3
+        const int dim = 4 * vdg + e;
+        const int pos = (((vkg >> 1) ^ ((dim >> 3) & 3)) * 8) + (vkg & 1) * 4;
+        *reinterpret_cast<u32x2 *>(Vt + dim * kVtStride + pos) = col;
       }
     }
   };
@@ -186,6 +232,7 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
   const int key1 = 8 * (c16 >> 2) + (c16 & 3);  // key row of this lane in QK product 1
   const int key2 = key1 + 4;                      // ... in product 2
   auto compute = [&](int buf, int kb) {
+    if (kb > wave_max_pos) return;  // every key of the step is in the future of every row
     const _Float16 *K = lds + buf * L::kBufHalves;
     const _Float16 *Vt = K + L::kKHalves;
     f4_t s1[RB], s2[RB];
@@ -205,7 +252,8 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
         s2[rb] = mfma32<KV>(a2, qop[rb][kk], s2[rb]);
       }
     }
-    const bool need_mask = kb + kKeyStep - 1 > min_pos;
+    const bool need_mask = kb + kKeyStep - 1 > wave_min_pos;
+    const float c = d.qk_scale;  // softmax scale * log2(e); m is kept in these units
     u32x4 pk[RB];
     bool rescale = false;
     float alpha[RB];
@@ -214,26 +262,32 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
       float sc[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sc[i] = s1[rb][i] * d.qk_scale;
-        sc[4 + i] = s2[rb][i] * d.qk_scale;
+        sc[i] = s1[rb][i];
+        sc[4 + i] = s2[rb][i];
       }
       if (need_mask) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sc[j] = (kb + 8 * g16 + j <= row_pos[rb]) ? sc[j] : kNegBig;
+        for (int j = 0; j < 8; ++j) sc[j] = (kb + 8 * g16 + j <= row_pos[rb]) ? sc[j] : -INFINITY;
       }
       float mx = sc[0];
 #pragma unroll
       for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sc[j]);
       mx = fmaxf(mx, xor_lanes<16>(mx));
       mx = fmaxf(mx, xor_lanes<32>(mx));
-      const float mn = fmaxf(m[rb], mx);
-      rescale |= mn > m[rb];
+      // Lazy rescale: the running max moves only when a score exceeds it by more
+      // than kLazy (log2 units), so p = 2^(s*c - m) stays below 2^kLazy, well inside
+      // the range of the 16-bit P operand and of the fp32 sums; the result does not
+      // depend on m (numerator and denominator carry the same factor).
+      const float mt = mx * c;
+      const bool grow = mt > m[rb] + kLazy;
+      const float mn = grow ? mt : m[rb];
+      rescale |= grow;
       alpha[rb] = fast_exp2(m[rb] - mn);
       m[rb] = mn;
       float p[8], ps = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        p[j] = fast_exp2(sc[j] - mn);
+        p[j] = fast_exp2(__builtin_fmaf(sc[j], c, -mn));
         ps += p[j];
       }
       l[rb] = l[rb] * alpha[rb] + ps;
@@ -255,23 +309,31 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
     }
   };
 
+  constexpr int NS = kStages;
+  constexpr int U = NS % 2 ? 2 * NS : NS;  // unroll: stage ring and LDS buffer parity
   const int nsteps = (nkeys + kKeyStep - 1) / kKeyStep;
-  Stage sa, sb;
-  gload(0, sa);
-  if (nsteps > 1) gload(kKeyStep, sb);
-  lstore(0, sa);
+  Stage st[NS];
+  StepBt bnext = bt_load(NS);  // clamped when the tile has fewer steps
+#pragma unroll
+  for (int i = 0; i < NS; ++i) gload(bt_load(i), st[i]);
+  lstore(0, 0, st[0]);
   __syncthreads();
-  // iteration n: load step n+2 into the stage step n used, compute step n from LDS,
-  // then move step n+1 (already in registers) into the other LDS buffer.
-  auto iter = [&](int n, Stage &mine, Stage &next) {
-    if (n + 2 < nsteps) gload((n + 2) * kKeyStep, mine);
+  // iteration n: read step n+NS+1's block-table entries, load step n+NS into the
+  // stage step n used, compute step n from LDS, then move step n+1 (already in
+  // registers) into the other LDS buffer.  Past the last step the loads repeat
+  // the last block.
+  auto iter = [&](int n, Stage &mine, const Stage &next) {
+    const StepBt bn = bt_load(n + NS + 1);
+    gload(bnext, mine);
+    bnext = bn;
     compute(n & 1, n * kKeyStep);
-    if (n + 1 < nsteps) lstore((n + 1) & 1, next);
+    if (n + 1 < nsteps) lstore((n + 1) & 1, (n + 1) * kKeyStep, next);
     __syncthreads();
   };
-  for (int n = 0; n < nsteps; n += 2) {
-    iter(n, sa, sb);
-    if (n + 1 < nsteps) iter(n + 1, sb, sa);
+  for (int n0 = 0; n0 < nsteps; n0 += U) {
+#pragma unroll
+    for (int i = 0; i < U; ++i)
+      if (n0 + i < nsteps) iter(n0 + i, st[i % NS], st[(i + 1) % NS]);
   }
 
   // ---- normalise and store: lane holds dims sl*16 + 4*g16 + i of query row c16 ----
@@ -290,81 +352,46 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
   }
 }
 
-template <int D, int G>
-constexpr int mixed_lds_bytes() {
-  constexpr int a = PrefillLds<D>::kBytes;
-  constexpr int b = decode_partition_smem_floats<D, G>() * 4;
-  return a > b ? a : b;
-}
-
-// Work list: prefill tiles (heaviest tile of each chunk first), then decode
-// partitions.  One workgroup of 256 threads scans the sequences in rounds of 256.
+// Work list of prefill tiles (heaviest tile of each chunk first).  One workgroup of
+// 256 threads scans the sequences in rounds of 256.
 __global__ __launch_bounds__(256) void pa_mixed_prep_kernel(MixedArgs a) {
-  __shared__ int sp[256], sd[256];
+  __shared__ int sp[256];
   const int tid = threadIdx.x;
-  const int part_tokens = a.dec.part_blocks * kBlock;
-  int base_p = 0, base_d = 0;
+  int base_p = 0;
   for (int c0 = 0; c0 < a.num_seqs; c0 += 256) {
     const int s = c0 + tid;
-    int np = 0, nd = 0;
+    int np = 0;
     if (s < a.num_seqs) {
       const int ql = a.qsl[s + 1] - a.qsl[s];
-      if (ql > 1) {
-        np = min((ql + a.qtok - 1) / a.qtok, (1 << kItemBits));
-      } else {
-        const int n = a.dec.ctx[s];
-        nd = n > 0 ? min((n + part_tokens - 1) / part_tokens, a.dec.max_parts) : 1;
-      }
+      if (ql > 1) np = min((ql + a.qtok - 1) / a.qtok, (1 << kItemBits));
     }
     sp[tid] = np;
-    sd[tid] = nd;
     __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {  // inclusive scans
+    for (int off = 1; off < 256; off <<= 1) {  // inclusive scan
       const int vp = tid >= off ? sp[tid - off] : 0;
-      const int vd = tid >= off ? sd[tid - off] : 0;
       __syncthreads();
       sp[tid] += vp;
-      sd[tid] += vd;
       __syncthreads();
     }
-    const int ep = base_p + sp[tid] - np, ed = base_d + sd[tid] - nd;
+    const int ep = base_p + sp[tid] - np;
     for (int k = 0; k < np && ep + k < a.p_bound; ++k)
       a.p_items[ep + k] = (s << kItemBits) | (np - 1 - k);
-    for (int k = 0; k < nd && ed + k < a.d_bound; ++k) a.d_items[ed + k] = (s << kItemBits) | k;
     base_p += sp[255];
-    base_d += sd[255];
     __syncthreads();
   }
-  if (tid == 0) {
-    a.hdr[0] = min(base_p, a.p_bound);
-    a.hdr[1] = min(base_d, a.d_bound);
-  }
+  if (tid == 0) a.hdr[0] = min(base_p, a.p_bound);
 }
 
-template <int KV, int QT, int D, int G>
-__global__ __launch_bounds__(256) void pa_mixed_kernel(MixedArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[mixed_lds_bytes<D, G>()];
-  const int x = blockIdx.x, h = blockIdx.y;
-  if (x < a.p_bound) {
-    if (x >= a.hdr[0]) return;
-    const int item = a.p_items[x];
-    prefill_tile<KV, D, G>(a, item >> kItemBits, h, item & ((1 << kItemBits) - 1), smem);
-    return;
-  }
-  const int y = x - a.p_bound;
-  if (y >= a.hdr[1]) return;
-  const int item = a.d_items[y];
-  const int s = item >> kItemBits, p = item & ((1 << kItemBits) - 1);
-  decode_partition<KV, QT, D, G>(a.dec, s, h, p, a.qsl[s], a.dec.ctx[s], s,
-                                 reinterpret_cast<float *>(smem));
-}
-
-// Decode rows split over several partitions: combine them (one group per row, head).
-template <int QT, int D>
-__global__ __launch_bounds__(D) void pa_mixed_decode_merge_kernel(MixedArgs a) {
-  const int s = blockIdx.y;
-  if (a.qsl[s + 1] - a.qsl[s] != 1) return;
-  merge_partitions<QT, D>(a.dec, s, blockIdx.x, threadIdx.x, a.dec.ctx[s], a.qsl[s]);
+// Grid (Hkv, items): the kv head is the fastest index, so with workgroups handed to
+// the 8 XCDs in turn, all tiles of one (sequence, kv head) run on one XCD (for
+// 8 kv heads; on 8 / Hkv of them otherwise) and share its L2 copy of their K/V.
+template <int KV, int D, int G>
+__global__ __launch_bounds__(256) void pa_prefill_tiles_kernel(MixedArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[PrefillLds<D>::kBytes];
+  const int x = blockIdx.y, h = blockIdx.x;
+  if (x >= a.hdr[0]) return;
+  const int item = a.p_items[x];
+  prefill_tile<KV, D, G>(a, item >> kItemBits, h, item & ((1 << kItemBits) - 1), smem);
 }
 
 // ---- fallback for KV types without an MFMA tile path (fp32, fp8, int8): every
@@ -402,17 +429,13 @@ __global__ __launch_bounds__(D) void pa_mixed_rows_merge_kernel(MixedArgs a) {
 // host-side dispatch
 // ---------------------------------------------------------------------------------------
 template <int KV, int QT, int D, int G>
-static hipError_t launch_tiles(const MixedArgs &a, hipStream_t st) {
+static hipError_t launch_tiles(const MixedArgs &a, bool stream_loads, hipStream_t st) {
   hipLaunchKernelGGL(pa_mixed_prep_kernel, dim3(1), dim3(256), 0, st, a);
-  dim3 grid(a.p_bound + a.d_bound, a.dec.num_kv_heads);
-  hipLaunchKernelGGL((pa_mixed_kernel<KV, QT, D, G>), grid, dim3(256), 0, st, a);
+  dim3 grid(a.dec.num_kv_heads, a.p_bound);
+  hipLaunchKernelGGL((pa_prefill_tiles_kernel<KV, D, G>), grid, dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.dec.max_parts > 1) {
-    dim3 mg(a.dec.num_q_heads, a.num_seqs);
-    hipLaunchKernelGGL((pa_mixed_decode_merge_kernel<QT, D>), mg, dim3(D), 0, st, a);
-  }
-  return hipGetLastError();
+  return launch_decode_stream(a.dec, KV, QT, D, G, a.num_seqs, stream_loads, st);
 }
 
 template <int KV, int QT, int D, int G>
@@ -428,12 +451,13 @@ static hipError_t launch_rows(const MixedArgs &a, int num_rows, hipStream_t st) 
 }
 
 template <int KV, int QT, int D>
-static hipError_t launch_g(const MixedArgs &a, int G, int num_rows, bool tiles, hipStream_t st) {
+static hipError_t launch_g(const MixedArgs &a, int G, int num_rows, bool tiles, bool stream_loads,
+                           hipStream_t st) {
   constexpr bool kMfma = (KV == PA_F16 || KV == PA_BF16);
 #define PA_CASE(g)                                                              \
   case g:                                                                       \
     if constexpr (kMfma) {                                                      \
-      if (tiles) return launch_tiles<KV, QT, D, g>(a, st);                      \
+      if (tiles) return launch_tiles<KV, QT, D, g>(a, stream_loads, st);        \
     }                                                                           \
     return launch_rows<KV, QT, D, g>(a, num_rows, st);
   switch (G) {
@@ -448,28 +472,28 @@ static hipError_t launch_g(const MixedArgs &a, int G, int num_rows, bool tiles, 
 
 template <int KV, int QT>
 static hipError_t launch_d(const MixedArgs &a, int D, int G, int num_rows, bool tiles,
-                           hipStream_t st) {
-  if (D == 64) return launch_g<KV, QT, 64>(a, G, num_rows, tiles, st);
-  if (D == 128) return launch_g<KV, QT, 128>(a, G, num_rows, tiles, st);
+                           bool stream_loads, hipStream_t st) {
+  if (D == 64) return launch_g<KV, QT, 64>(a, G, num_rows, tiles, stream_loads, st);
+  if (D == 128) return launch_g<KV, QT, 128>(a, G, num_rows, tiles, stream_loads, st);
   return hipErrorInvalidValue;
 }
 
 bool mixed_uses_tiles(int kv_dtype) { return kv_dtype == PA_F16 || kv_dtype == PA_BF16; }
 
 hipError_t launch_mixed(const MixedArgs &a, int kv_dtype, int q_dtype, int head_dim, int group,
-                        int num_rows, hipStream_t st) {
+                        int num_rows, bool stream_loads, hipStream_t st) {
   const bool tiles = mixed_uses_tiles(kv_dtype);
   switch (kv_dtype) {
-    case PA_F32: return launch_d<PA_F32, PA_F32>(a, head_dim, group, num_rows, tiles, st);
-    case PA_F16: return launch_d<PA_F16, PA_F16>(a, head_dim, group, num_rows, tiles, st);
-    case PA_BF16: return launch_d<PA_BF16, PA_BF16>(a, head_dim, group, num_rows, tiles, st);
+    case PA_F32: return launch_d<PA_F32, PA_F32>(a, head_dim, group, num_rows, tiles, stream_loads, st);
+    case PA_F16: return launch_d<PA_F16, PA_F16>(a, head_dim, group, num_rows, tiles, stream_loads, st);
+    case PA_BF16: return launch_d<PA_BF16, PA_BF16>(a, head_dim, group, num_rows, tiles, stream_loads, st);
     case PA_FP8_E4M3:
       return q_dtype == PA_F16
-                 ? launch_d<PA_FP8_E4M3, PA_F16>(a, head_dim, group, num_rows, tiles, st)
-                 : launch_d<PA_FP8_E4M3, PA_BF16>(a, head_dim, group, num_rows, tiles, st);
+                 ? launch_d<PA_FP8_E4M3, PA_F16>(a, head_dim, group, num_rows, tiles, stream_loads, st)
+                 : launch_d<PA_FP8_E4M3, PA_BF16>(a, head_dim, group, num_rows, tiles, stream_loads, st);
     case PA_I8:
-      return q_dtype == PA_F16 ? launch_d<PA_I8, PA_F16>(a, head_dim, group, num_rows, tiles, st)
-                               : launch_d<PA_I8, PA_BF16>(a, head_dim, group, num_rows, tiles, st);
+      return q_dtype == PA_F16 ? launch_d<PA_I8, PA_F16>(a, head_dim, group, num_rows, tiles, stream_loads, st)
+                               : launch_d<PA_I8, PA_BF16>(a, head_dim, group, num_rows, tiles, stream_loads, st);
   }
   return hipErrorInvalidValue;
 }
