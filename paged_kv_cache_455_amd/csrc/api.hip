@@ -127,6 +127,15 @@ WsLayout ws_layout(int64_t rows, int num_q_heads, int head_dim, int max_parts) {
 // Balanced-split decode: every wave streams at least this many tiles, which bounds
 // how many waves (pieces) can share one (sequence, kv head) segment.
 constexpr int kMinTilesPerWave = 8;
+// Cost, in tiles, of starting a (sequence, kv head) segment in the balanced split
+// (emitting its result, switching q); PA_SEG_COST overrides it for tuning.
+static int seg_cost() {
+  static const int c = [] {
+    const char *v = getenv("PA_SEG_COST");
+    return v ? atoi(v) : 4;
+  }();
+  return c;
+}
 
 int stream_pieces(int max_ctx) {
   const int max_blocks = (max_ctx + kBlockTokens - 1) / kBlockTokens;
@@ -305,6 +314,7 @@ pa_status_t pa_decode(const pa_kv_pool_t *pool, const void *q, int32_t q_dtype, 
   a.max_parts = stream_pieces(max_context_len);
   a.num_seqs = num_seqs;
   a.min_tpw = kMinTilesPerWave;
+  a.seg_cost = seg_cost();
   const bool stream_loads = (pool->flags & PA_POOL_SHARED_BLOCKS) == 0;
   return hip_status(pa::launch_decode_stream(a, pool->kv_dtype, q_dtype, pool->head_dim, group,
                                              num_seqs, stream_loads, stream),
@@ -401,6 +411,7 @@ pa_status_t pa_prefill_chunk(const pa_kv_pool_t *pool, const void *q, int32_t q_
     m.dec.max_parts = w.max_parts;
     m.dec.num_seqs = num_seqs;
     m.dec.min_tpw = kMinTilesPerWave;
+    m.dec.seg_cost = seg_cost();
     m.dec.qsl = query_start_loc;
   } else {
     m.dec.ws_acc = reinterpret_cast<float *>(ws + w.acc_off);

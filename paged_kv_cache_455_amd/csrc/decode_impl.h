@@ -631,77 +631,19 @@ __device__ __forceinline__ void emit_segment(const DecodeArgs &a, DecodeState<KV
 struct StreamSeg {
   int s, h;   // sequence, kv head
   int nblk;   // blocks of the sequence
-  int cum;    // blocks of the sequences before it
+  int cum;    // cost units of the sequences before it
   int tail;   // valid rows of its last block
 };
 
 struct StreamRange {
-  int t, tend, tpw;  // the wave's tiles [t, tend); tiles per wave
-  int j;             // block of tile t inside its segment
-  StreamSeg seg;     // tile t's segment
+  int tpw;        // cost units per wave
+  int n;          // tiles of the wave
+  int j;          // block of the wave's first tile inside its segment
+  StreamSeg seg;  // the first tile's segment
 };
 
 __device__ __forceinline__ int stream_tail(const DecodeArgs &a, int s, int nblk) {
   return a.ctx[s] - (nblk - 1) * kBlock;
-}
-
-// Count the batch's tiles, record tpw and every sequence's first block index (wave
-// 0 does), and find wave w's first tile.  False when the wave has no tiles.
-// Everything it returns is wave-uniform and taken from lanes by readlane, so the
-// compiler keeps the tile cursor in scalar registers: block-table entries, context
-// lengths and scales are then scalar loads, which do not wait behind the vector
-// K/V loads in flight.
-__device__ __forceinline__ bool stream_range(const DecodeArgs &a, int w, int lane, StreamRange &r) {
-  const int Hkv = a.num_kv_heads, S = a.num_seqs;
-  int NB = 0;
-  int nb0 = 0, incl0 = 0;  // first 64 sequences, kept for the locate pass
-  for (int c0 = 0; c0 < S; c0 += kWave) {
-    const int sq = c0 + lane;
-    const int n = sq < S ? decode_len(a, sq) : 0;
-    const int nb = n > 0 ? (n + kBlock - 1) / kBlock : 0;
-    const int incl = wave_incl_scan_i(nb, lane);
-    if (c0 == 0) {
-      nb0 = nb;
-      incl0 = incl;
-    }
-    if (w == 0 && sq < S) a.hdr[1 + sq] = NB + incl - nb;
-    NB += __builtin_amdgcn_readlane(incl, kWave - 1);
-  }
-  const int T = Hkv * NB;
-  r.tpw = max(a.min_tpw, (T + a.num_waves - 1) / a.num_waves);
-  if (w == 0 && lane == 0) a.hdr[0] = r.tpw;
-  r.t = w * r.tpw;
-  r.tend = min(r.t + r.tpw, T);
-  if (r.t >= r.tend) return false;
-
-  int s = 0, cum_s = 0, nblk = 1;
-  int base = 0;
-  for (int c0 = 0; c0 < S; c0 += kWave) {
-    const int sq = c0 + lane;
-    int nb, incl;
-    if (c0 == 0) {  // already scanned
-      nb = nb0;
-      incl = incl0;
-    } else {
-      const int n = sq < S ? decode_len(a, sq) : 0;
-      nb = n > 0 ? (n + kBlock - 1) / kBlock : 0;
-      incl = base + wave_incl_scan_i(nb, lane);
-    }
-    const int excl = incl - nb;
-    const unsigned long long hit = __ballot(sq < S && Hkv * excl <= r.t && r.t < Hkv * incl);
-    if (hit) {
-      const int l = __builtin_ctzll(hit);
-      s = c0 + l;
-      cum_s = __builtin_amdgcn_readlane(excl, l);
-      nblk = __builtin_amdgcn_readlane(nb, l);
-      break;
-    }
-    base = __builtin_amdgcn_readlane(incl, kWave - 1);
-  }
-  const int h = (r.t - Hkv * cum_s) / nblk;
-  r.j = (r.t - Hkv * cum_s) - h * nblk;
-  r.seg = StreamSeg{s, h, nblk, cum_s, stream_tail(a, s, nblk)};
-  return true;
 }
 
 // Context lengths of the sequences [s0, s0 + 64), one per lane (0 past the batch),
@@ -719,29 +661,122 @@ struct SeqWindow {
   }
 };
 
+// Move sg to the first segment of the next sequence that has blocks (one exists).
+__device__ __forceinline__ void next_sequence(const DecodeArgs &a, SeqWindow &win, StreamSeg &sg,
+                                              int lane) {
+  sg.h = 0;
+  sg.cum += a.num_kv_heads * (sg.nblk + a.seg_cost);
+  int n, nb;
+  do {  // bounded by the batch: callers only step to a sequence that exists
+    ++sg.s;
+    n = win.ctx(a, sg.s, lane);
+    nb = n > 0 ? (n + kBlock - 1) / kBlock : 0;
+  } while (nb == 0 && sg.s < a.num_seqs - 1);
+  sg.nblk = max(nb, 1);
+  sg.tail = n - (sg.nblk - 1) * kBlock;
+}
+
+// Cost of the work: each (sequence, kv head) segment counts seg_cost units for its
+// start (the result it emits, the switch of q) plus one per tile, and waves take
+// equal ranges of cost units.  Segment (s, h) covers units
+// [cum_s + h*L_s, cum_s + (h+1)*L_s), L_s = nblk_s + seg_cost, its tile j sitting
+// at cum_s + h*L_s + seg_cost + j; a wave owns the tiles whose units fall in its
+// range.
+//
+// stream_range counts the batch's cost, records tpw and every sequence's first
+// cost unit (wave 0 does), finds wave w's first tile and counts its tiles.  False
+// when the wave has no tiles.  Everything it returns is wave-uniform and taken
+// from lanes by readlane, so the compiler keeps the tile cursor in scalar
+// registers: block-table entries, context lengths and scales are then scalar loads,
+// which do not wait behind the vector K/V loads in flight.
+__device__ __forceinline__ bool stream_range(const DecodeArgs &a, int w, int lane, StreamRange &r) {
+  const int Hkv = a.num_kv_heads, S = a.num_seqs, c = a.seg_cost;
+  auto seq_cost = [&](int nb) { return nb > 0 ? Hkv * (nb + c) : 0; };
+  int TC = 0;
+  int nb0 = 0, incl0 = 0;  // first 64 sequences, kept for the locate pass
+  for (int c0 = 0; c0 < S; c0 += kWave) {
+    const int sq = c0 + lane;
+    const int n = sq < S ? decode_len(a, sq) : 0;
+    const int nb = n > 0 ? (n + kBlock - 1) / kBlock : 0;
+    const int incl = wave_incl_scan_i(seq_cost(nb), lane);
+    if (c0 == 0) {
+      nb0 = nb;
+      incl0 = incl;
+    }
+    if (w == 0 && sq < S) a.hdr[1 + sq] = TC + incl - seq_cost(nb);
+    TC += __builtin_amdgcn_readlane(incl, kWave - 1);
+  }
+  r.tpw = max(a.min_tpw, (TC + a.num_waves - 1) / a.num_waves);
+  if (w == 0 && lane == 0) a.hdr[0] = r.tpw;
+  const int t = w * r.tpw;
+  const int tend = min(t + r.tpw, TC);
+  if (t >= tend) return false;
+
+  int s = 0, cum_s = 0, nblk = 1;
+  int base = 0;
+  for (int c0 = 0; c0 < S; c0 += kWave) {
+    const int sq = c0 + lane;
+    int nb, incl;
+    if (c0 == 0) {  // already scanned
+      nb = nb0;
+      incl = incl0;
+    } else {
+      const int n = sq < S ? decode_len(a, sq) : 0;
+      nb = n > 0 ? (n + kBlock - 1) / kBlock : 0;
+      incl = base + wave_incl_scan_i(seq_cost(nb), lane);
+    }
+    const int excl = incl - seq_cost(nb);
+    const unsigned long long hit = __ballot(sq < S && nb > 0 && excl <= t && t < incl);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      s = c0 + l;
+      cum_s = __builtin_amdgcn_readlane(excl, l);
+      nblk = __builtin_amdgcn_readlane(nb, l);
+      break;
+    }
+    base = __builtin_amdgcn_readlane(incl, kWave - 1);
+  }
+  const int L = nblk + c;
+  const int h = (t - cum_s) / L;
+  const int u = (t - cum_s) - h * L;
+  r.j = u < c ? 0 : u - c;
+  r.seg = StreamSeg{s, h, nblk, cum_s, stream_tail(a, s, nblk)};
+
+  // count the wave's tiles: walk the segments its range touches
+  SeqWindow win;
+  win.load(a, s, lane);
+  StreamSeg sg = r.seg;
+  int first = sg.cum + sg.h * (sg.nblk + c) + c + r.j;  // unit of the next tile
+  int n = 0;
+  for (;;) {
+    const int seg_end = sg.cum + (sg.h + 1) * (sg.nblk + c);
+    n += max(0, min(seg_end, tend) - first);
+    if (seg_end >= tend || (sg.s >= S - 1 && sg.h == Hkv - 1)) break;
+    if (++sg.h == Hkv) {
+      sg.h = Hkv - 1;
+      next_sequence(a, win, sg, lane);
+    }
+    first = sg.cum + sg.h * (sg.nblk + c) + c;
+  }
+  r.n = n;
+  return n > 0;
+}
+
 // Step (sg, j) to the next tile of the tile order (one exists).
 __device__ __forceinline__ void stream_step(const DecodeArgs &a, SeqWindow &win, StreamSeg &sg,
                                             int &j, int lane) {
   if (++j < sg.nblk) return;
   j = 0;
   if (++sg.h < a.num_kv_heads) return;
-  sg.h = 0;
-  sg.cum += sg.nblk;
-  int n, nb;
-  do {
-    ++sg.s;
-    n = win.ctx(a, sg.s, lane);
-    nb = n > 0 ? (n + kBlock - 1) / kBlock : 0;
-  } while (nb == 0);
-  sg.nblk = nb;
-  sg.tail = n - (nb - 1) * kBlock;
+  sg.h = a.num_kv_heads - 1;
+  next_sequence(a, win, sg, lane);
 }
 
 // True when one wave owns all of sg's tiles; piece = this wave's index among them.
-__device__ __forceinline__ bool stream_single(const StreamSeg &sg, int Hkv, int tpw, int w,
-                                              int &piece) {
-  const int seg0 = Hkv * sg.cum + sg.h * sg.nblk;  // first tile of the segment
-  const int wfirst = seg0 / tpw, wlast = (seg0 + sg.nblk - 1) / tpw;
+__device__ __forceinline__ bool stream_single(const DecodeArgs &a, const StreamSeg &sg, int tpw,
+                                              int w, int &piece) {
+  const int first = sg.cum + sg.h * (sg.nblk + a.seg_cost) + a.seg_cost;  // first tile's unit
+  const int wfirst = first / tpw, wlast = (first + sg.nblk - 1) / tpw;
   piece = w - wfirst;
   return wfirst == wlast;
 }
@@ -760,7 +795,7 @@ template <class P>
 __device__ __forceinline__ void stream_run(const DecodeArgs &a, P &path, int w, int lane) {
   StreamRange rg;
   if (!stream_range(a, w, lane, rg)) return;
-  const int Hkv = a.num_kv_heads, n = rg.tend - rg.t;
+  const int Hkv = a.num_kv_heads, n = rg.n;
   SeqWindow win;
   win.load(a, rg.seg.s, lane);
   auto bt_of = [&](const StreamSeg &sg, int j) {
@@ -787,7 +822,7 @@ __device__ __forceinline__ void stream_run(const DecodeArgs &a, P &path, int w, 
     path.compute(cur, masked ? sg0.tail : kBlock, masked);
     if (j0 == sg0.nblk - 1 || !has_next) {
       int piece;
-      const bool single = stream_single(sg0, Hkv, rg.tpw, w, piece);
+      const bool single = stream_single(a, sg0, rg.tpw, w, piece);
       path.emit(sg0, single, piece);
       if (has_next) path.begin_segment();
     }
@@ -1205,8 +1240,8 @@ __device__ __forceinline__ void merge_stream(const DecodeArgs &a, int s, int hq,
   const int G = a.num_q_heads / a.num_kv_heads;
   const int h = hq / G;
   const int nblk = (n + kBlock - 1) / kBlock;
-  const int tpw = a.hdr[0];
-  const int seg0 = a.num_kv_heads * a.hdr[1 + s] + h * nblk;
+  const int tpw = a.hdr[0];  // cost units per wave; the split is described at stream_range
+  const int seg0 = a.hdr[1 + s] + h * (nblk + a.seg_cost) + a.seg_cost;
   const int pieces = (seg0 + nblk - 1) / tpw - seg0 / tpw + 1;
   if (pieces <= 1) return;
   const int64_t r0 = ((int64_t)s * a.num_q_heads + hq) * a.max_parts;

@@ -29,7 +29,8 @@ struct DecodeArgs {
   int32_t *hdr;         // [1 + num_seqs]: tiles per wave, then each sequence's first block index
   int32_t num_seqs;
   int32_t num_waves;    // waves launched
-  int32_t min_tpw;      // lower bound on tiles per wave
+  int32_t min_tpw;      // lower bound on cost units per wave
+  int32_t seg_cost;     // cost units charged for each (sequence, kv head) segment start
   // mixed step: [num_seqs + 1] query starts; only q_len == 1 sequences are decoded,
   // sequence s's query/output row being qsl[s] (nullptr: every sequence, row s)
   const int32_t *qsl;
