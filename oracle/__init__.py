@@ -22,6 +22,7 @@ from .paged_attention import (  # noqa: F401
     decode,
     prefill_chunk,
     cache_write,
+    quantised_cache_write,
     block_copy,
 )
 from .codec import (  # noqa: F401

@@ -32,7 +32,7 @@ business; the tests convert.
 """
 import numpy as np
 
-from .codec import e4m3fn_decode, int8_decode
+from .codec import e4m3fn_decode, e4m3fn_encode, int8_decode, int8_encode
 
 BLOCK_SIZE = 16
 
@@ -170,6 +170,64 @@ def cache_write(k_pool, v_pool, k_new, v_new, slot_mapping):
         k_out[b, :, o, :] = k_new[t]
         v_out[b, :, o, :] = v_new[t]
     return k_out, v_out
+
+
+def quantised_cache_write(codes, scales, x_new, slot_mapping, kind):
+    """Write new tokens' K (or V) into a 1-byte pool, keeping one scale per
+    (block, kv head) ("从KV Cache到vLLM" §2.2-2.3 store the cache as INT8 or FP8,
+    one byte per element).  Returns new (codes, scales).
+
+    The pages fix no scale policy for a block that fills up over several steps;
+    the reading here (all arithmetic in float32, rounding to nearest even):
+
+    * the rows one call writes into a block are the block's next rows in order;
+      rows below the first of them already hold data (none when it is row 0);
+    * the tile's scale never shrinks: s_new = max(s_old, amax_new / qmax), with
+      s_old = 0 for a tile with no earlier rows, amax_new the largest magnitude
+      among the new rows (every dim) and qmax 448 (FP8 E4M3FN) or 127 (INT8);
+    * when the scale grows, each earlier code c is encoded again as
+      encode(value(c) * (s_old / s_new));
+    * a new value x is stored as encode(x / s_new), or code 0 while s_new is 0;
+    * encode clamps to [-qmax, qmax] and rounds to nearest even (E4M3FN by the
+      code grid, INT8 by rint).
+
+    codes  [NB][H][16][D] uint8 (fp8) or int8;  scales float32 [NB][H]
+    x_new  [T][H][D] float values (float32 or narrower; read as float32)
+    """
+    codes = np.array(codes, copy=True)
+    scales = np.array(scales, dtype=np.float32, copy=True)
+    x_new = np.asarray(x_new, dtype=np.float32)
+    qmax = np.float32(448.0 if kind == "fp8" else 127.0)
+    encode = e4m3fn_encode if kind == "fp8" else int8_encode
+    values = e4m3fn_decode if kind == "fp8" else int8_decode
+    slots = np.asarray(slot_mapping)
+    # group the call's tokens by block, in token order
+    runs = {}
+    for t, slot in enumerate(slots):
+        if slot < 0:
+            continue
+        runs.setdefault(int(slot) // BLOCK_SIZE, []).append((int(slot) % BLOCK_SIZE, t))
+    for b, rows in runs.items():
+        offs = [o for o, _ in rows]
+        off0 = min(offs)
+        for h in range(codes.shape[1]):
+            s_old = scales[b, h] if off0 > 0 else np.float32(0.0)
+            xs = np.stack([x_new[t, h] for _, t in rows])
+            amax = np.float32(np.max(np.abs(xs)))
+            s_new = np.maximum(s_old, np.float32(amax / qmax))
+            if s_new > s_old and off0 > 0:
+                ratio = np.float32(s_old / s_new)
+                old = values(codes[b, h, :off0]).astype(np.float32)
+                y = np.clip((old * ratio).astype(np.float32), -qmax, qmax)
+                codes[b, h, :off0] = encode(y)
+            for o, t in rows:
+                if s_new > 0:
+                    y = np.clip((x_new[t, h] / s_new).astype(np.float32), -qmax, qmax)
+                    codes[b, h, o] = encode(y)
+                else:
+                    codes[b, h, o] = 0
+            scales[b, h] = s_new
+    return codes, scales
 
 
 def block_copy(k_pool, v_pool, pairs, k_scale=None, v_scale=None):

@@ -111,3 +111,72 @@ def test_fp8_wrong_bias_is_caught(monkeypatch):
     monkeypatch.setattr(codec, "_E4M3_TABLE", _E4M3_WRONG_BIAS)
     with pytest.raises(AssertionError):
         pins.test_e4m3fn_decode_all_codes_match_torch()
+
+
+# ---- quantise-on-write: plausible mistakes, each must fail a pin in test_oracle_quant ----
+from tests import test_oracle_quant as qpins  # noqa: E402
+
+
+def _qcw_variant(no_reencode=False, scale_from_new_only=False, trunc_int8=False,
+                 reencode_short=False):
+    def f(codes, scales, x_new, slot_mapping, kind):
+        codes = np.array(codes, copy=True)
+        scales = np.array(scales, dtype=np.float32, copy=True)
+        x_new = np.asarray(x_new, dtype=np.float32)
+        qmax = np.float32(448.0 if kind == "fp8" else 127.0)
+        if kind == "fp8":
+            encode, values = codec.e4m3fn_encode, codec.e4m3fn_decode
+        else:
+            rnd = np.trunc if trunc_int8 else np.rint
+            encode = lambda y: np.clip(rnd(np.asarray(y, np.float64)), -127, 127).astype(np.int8)
+            values = codec.int8_decode
+        runs = {}
+        for t, slot in enumerate(np.asarray(slot_mapping)):
+            if slot >= 0:
+                runs.setdefault(int(slot) // 16, []).append((int(slot) % 16, t))
+        for b, rows in runs.items():
+            off0 = min(o for o, _ in rows)
+            for h in range(codes.shape[1]):
+                s_old = scales[b, h] if off0 > 0 else np.float32(0.0)
+                amax = np.float32(np.max(np.abs(np.stack([x_new[t, h] for _, t in rows]))))
+                s_new = np.float32(amax / qmax) if scale_from_new_only else np.maximum(s_old, np.float32(amax / qmax))
+                n_old = max(off0 - 1, 0) if reencode_short else off0
+                if s_new != s_old and off0 > 0 and not no_reencode:
+                    ratio = np.float32(s_old / s_new)
+                    old = values(codes[b, h, :n_old]).astype(np.float32)
+                    codes[b, h, :n_old] = encode(np.clip((old * ratio).astype(np.float32), -qmax, qmax))
+                for o, t in rows:
+                    y = np.clip((x_new[t, h] / s_new).astype(np.float32), -qmax, qmax) if s_new > 0 else 0 * x_new[t, h]
+                    codes[b, h, o] = encode(y)
+                scales[b, h] = s_new
+        return codes, scales
+    return f
+
+
+QUANT_MUTATIONS = {
+    "no_reencode_on_growth": (_qcw_variant(no_reencode=True),
+                              [lambda: qpins.test_dequantised_values_within_rounding_bound("fp8")]),
+    "scale_from_new_rows_only": (_qcw_variant(scale_from_new_only=True),
+                                 [lambda: qpins.test_scale_is_running_amax_over_valid_rows("i8")]),
+    "int8_truncates": (_qcw_variant(trunc_int8=True),
+                       [lambda: qpins.test_stored_codes_are_the_nearest_codes("i8")]),
+    "reencode_misses_a_row": (_qcw_variant(reencode_short=True),
+                              [lambda: qpins.test_dequantised_values_within_rounding_bound("i8")]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(QUANT_MUTATIONS))
+def test_quant_write_mutation_is_caught(name, monkeypatch):
+    fn, checks = QUANT_MUTATIONS[name]
+    monkeypatch.setattr(oracle, "quantised_cache_write", fn)
+    for check in checks:
+        with pytest.raises(AssertionError):
+            check()
+
+
+def test_quant_write_variant_without_mutation_passes(monkeypatch):
+    # the variant machinery itself, unmutated, agrees with the oracle's pins
+    monkeypatch.setattr(oracle, "quantised_cache_write", _qcw_variant())
+    qpins.test_dequantised_values_within_rounding_bound("fp8")
+    qpins.test_scale_is_running_amax_over_valid_rows("i8")
+    qpins.test_stored_codes_are_the_nearest_codes("i8")
