@@ -90,8 +90,8 @@ def side_bytes(b):
     """Cache write (read new K/V, write pool rows), slots, and CoW copies (read + write)."""
     e = ELEM[b.kv_dtype]
     tot = b.num_tokens * 8
-    if b.k_new is not None:
-        tot += 2 * 2 * b.num_tokens * b.num_kv_heads * b.head_dim * e
+    if b.k_new is not None:  # read the new rows (their own dtype), write them in the pool's
+        tot += 2 * b.num_tokens * b.num_kv_heads * b.head_dim * (b.k_new.element_size() + e)
     if b.copy_pairs is not None:
         tot += 2 * 2 * int(b.copy_pairs.shape[0]) * b.num_kv_heads * 16 * b.head_dim * e
     return tot
@@ -234,6 +234,7 @@ def main():
                                                 b.max_seq_len, pools[0].k.dtype)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
+    quantised = b.k_scale is not None
 
     def step(i, ev=None):
         pool = pools[i % R]
@@ -241,7 +242,10 @@ def main():
             pa.kv_block_copy(pool, pairs)
         pa.pa_slot_mapping(bt, qsl, lens, b.num_tokens, out=slots)
         if k_new is not None:
-            pa.kv_cache_write(pool, k_new, v_new, slots)
+            if quantised:  # 1-byte pool: quantise this step's K/V on the way in
+                pa.kv_cache_write_quant(pool, k_new, v_new, slots)
+            else:
+                pa.kv_cache_write(pool, k_new, v_new, slots)
         if ev is not None:
             ev[0].record(stream)
         if b.kind == "decode":

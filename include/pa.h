@@ -116,12 +116,36 @@ pa_status_t pa_slot_mapping(const int32_t *block_tables, int32_t max_blocks_per_
  *   k_new, v_new  [num_tokens][num_kv_heads][head_dim], dtype = pool kv_dtype
  *   slot_mapping  int64 [num_tokens]; slot = block * 16 + offset; slot < 0
  *                 means "no token" and is skipped.
- * A pure bit copy.  Pools with 1-byte codes return PA_E_UNSUPPORTED (codes
- * and their per-block scales are produced outside this library).
+ * A pure bit copy.  Pools with 1-byte codes return PA_E_UNSUPPORTED: they are
+ * written by kv_cache_write_quant.
  */
 pa_status_t kv_cache_write(const pa_kv_pool_t *pool, const void *k_new, const void *v_new,
                            const int64_t *slot_mapping, int32_t num_tokens,
                            hipStream_t stream);
+
+/*
+ * kv_cache_write_quant -- write new tokens' K and V into a pool of 1-byte codes
+ * (fp8 E4M3FN or int8), keeping one scale per (block, kv head) ([P3] 2.2-2.3:
+ * the cache may be stored as INT8 or FP8, one byte per element).
+ *   k_new, v_new  [num_tokens][num_kv_heads][head_dim] values of src_dtype
+ *                 (PA_F32, PA_F16 or PA_BF16)
+ *   slot_mapping  int64 [num_tokens]; slot < 0 means "no token" and is skipped.
+ * The rows one call writes into a block must be that block's next rows, in
+ * order and contiguous in token order (pa_slot_mapping of one step gives
+ * exactly that); rows below them already hold data.  The pages fix no scale
+ * policy for a block that fills over several steps; this one, per (block, kv
+ * head), in fp32 with round-to-nearest-even:
+ *   s_new = max(s_old, amax / qmax)   amax over the new rows, qmax 448 or 127,
+ *                                     s_old = 0 when the new rows start at row 0
+ *   if s_new > s_old, each earlier code c becomes encode(value(c) * (s_old / s_new))
+ *   each new value x becomes encode(x / s_new)   (code 0 while s_new is 0)
+ *   encode = clamp to [-qmax, qmax], then nearest code, ties to even.
+ * A tile whose rows are all zero has scale 0.  PA_E_UNSUPPORTED for pools of
+ * other types (see kv_cache_write).
+ */
+pa_status_t kv_cache_write_quant(const pa_kv_pool_t *pool, const void *k_new, const void *v_new,
+                                 int32_t src_dtype, const int64_t *slot_mapping,
+                                 int32_t num_tokens, hipStream_t stream);
 
 /*
  * kv_block_copy -- copy-on-write duplication of physical blocks ([P1]

@@ -6,7 +6,7 @@ the HIP kernels; PyTorch only provides device memory and the current stream.
 There is no CPU fallback: without the built library every call raises.
 
 Entry points (same names as the C ABI): ``pa_slot_mapping``,
-``kv_cache_write``, ``kv_block_copy``, ``pa_decode``, ``pa_prefill_chunk``,
+``kv_cache_write``, ``kv_cache_write_quant``, ``kv_block_copy``, ``pa_decode``, ``pa_prefill_chunk``,
 ``pa_decode_workspace_size``, ``pa_prefill_workspace_size``.
 """
 from __future__ import annotations
@@ -19,7 +19,8 @@ import torch
 
 __all__ = [
     "KVPool", "PA_POOL_SHARED_BLOCKS", "PagedAttentionError", "library_path", "load_library",
-    "pa_slot_mapping", "kv_cache_write", "kv_block_copy", "pa_decode", "pa_prefill_chunk",
+    "pa_slot_mapping", "kv_cache_write", "kv_cache_write_quant", "kv_block_copy", "pa_decode",
+    "pa_prefill_chunk",
     "pa_decode_workspace_size", "pa_prefill_workspace_size", "PA_DTYPE",
 ]
 
@@ -63,6 +64,8 @@ _SIGS = {
     "kv_cache_write": (_c.c_int, [_c.POINTER(_Pool), _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                   _c.c_int32, _c.c_void_p]),
     "kv_block_copy": (_c.c_int, [_c.POINTER(_Pool), _c.c_void_p, _c.c_int32, _c.c_void_p]),
+    "kv_cache_write_quant": (_c.c_int, [_c.POINTER(_Pool), _c.c_void_p, _c.c_void_p, _c.c_int32,
+                                        _c.c_void_p, _c.c_int32, _c.c_void_p]),
     "pa_decode_workspace_size": (_c.c_size_t, [_c.c_int32] * 5),
     "pa_decode": (_c.c_int, [_c.POINTER(_Pool), _c.c_void_p, _c.c_int32, _c.c_void_p, _c.c_void_p,
                              _c.c_int32, _c.c_void_p, _c.c_int32, _c.c_int32, _c.c_int32,
@@ -175,6 +178,16 @@ def kv_cache_write(pool: KVPool, k_new, v_new, slot_mapping, stream=None):
     _check("kv_cache_write", lib.kv_cache_write(
         pool.ref(), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), int(slot_mapping.shape[0]),
         _stream(pool.k, stream)))
+
+
+def kv_cache_write_quant(pool: KVPool, k_new, v_new, slot_mapping, stream=None):
+    """Quantise new K/V rows (f32/f16/bf16) into a 1-byte pool, keeping its scales."""
+    lib = load_library()
+    if k_new.dtype != v_new.dtype:
+        raise ValueError("k_new and v_new must share a dtype")
+    _check("kv_cache_write_quant", lib.kv_cache_write_quant(
+        pool.ref(), _ptr(k_new), _ptr(v_new), _dt(k_new), _ptr(slot_mapping),
+        int(slot_mapping.shape[0]), _stream(pool.k, stream)))
 
 
 def kv_block_copy(pool: KVPool, src_dst, stream=None):

@@ -197,7 +197,7 @@ pa_status_t kv_cache_write(const pa_kv_pool_t *pool, const void *k_new, const vo
   pa_status_t st = check_pool(pool, false);
   if (st != PA_OK) return st;
   if (is_quantised(pool->kv_dtype))
-    return fail(PA_E_UNSUPPORTED, "kv_cache_write into 1-byte pools is not implemented");
+    return fail(PA_E_UNSUPPORTED, "1-byte pools are written by kv_cache_write_quant");
   if (num_tokens < 0) return fail(PA_E_ARG, "num_tokens must be >= 0");
   if (num_tokens == 0) return PA_OK;
   if (!k_new || !v_new || !slot_mapping) return fail(PA_E_ARG, "NULL array argument");
@@ -212,6 +212,37 @@ pa_status_t kv_cache_write(const pa_kv_pool_t *pool, const void *k_new, const vo
   a.num_kv_heads = pool->num_kv_heads;
   a.row_bytes = pool->head_dim * elem_bytes(pool->kv_dtype);
   return hip_status(pa::launch_cache_write(a, stream), "kv_cache_write launch");
+}
+
+pa_status_t kv_cache_write_quant(const pa_kv_pool_t *pool, const void *k_new, const void *v_new,
+                                 int32_t src_dtype, const int64_t *slot_mapping,
+                                 int32_t num_tokens, hipStream_t stream) {
+  pa_status_t st = check_pool(pool, true);
+  if (st != PA_OK) return st;
+  if (!is_quantised(pool->kv_dtype))
+    return fail(PA_E_UNSUPPORTED, "kv_cache_write_quant needs a 1-byte pool (use kv_cache_write)");
+  if (src_dtype != PA_F32 && src_dtype != PA_F16 && src_dtype != PA_BF16)
+    return fail(PA_E_UNSUPPORTED, "src_dtype %d: f32, f16 or bf16 values only", src_dtype);
+  if (num_tokens < 0) return fail(PA_E_ARG, "num_tokens must be >= 0");
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping) return fail(PA_E_ARG, "NULL array argument");
+  if (pool->num_kv_heads > 65535)  // grid y limit
+    return fail(PA_E_UNSUPPORTED, "too many kv heads for one launch");
+  pa::CacheWriteArgs a{};
+  a.k = pool->k;
+  a.v = pool->v;
+  a.k_scale = pool->k_scale;
+  a.v_scale = pool->v_scale;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.slots = slot_mapping;
+  a.num_blocks = pool->num_blocks;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.row_bytes = pool->head_dim;
+  return hip_status(pa::launch_cache_write_quant(a, pool->kv_dtype, src_dtype, pool->head_dim,
+                                                 stream),
+                    "kv_cache_write_quant launch");
 }
 
 pa_status_t kv_block_copy(const pa_kv_pool_t *pool, const int32_t *src_dst, int32_t num_pairs,

@@ -54,6 +54,100 @@ __global__ __launch_bounds__(256) void kv_cache_write_kernel(CacheWriteArgs a, i
   }
 }
 
+// ---- quantise-on-write into a 1-byte pool ----------------------------------------
+// "从KV Cache到vLLM" §2.2-2.3 store the cache as INT8 or FP8 codes; one fp32 scale
+// per (block, kv head) maps codes to values.  The rows one call writes into a
+// block are that block's next rows, contiguous in token order (a "run").  One
+// wave per (run, kv head, K or V):
+//   amax   = largest |x| over the run's rows (every dim)
+//   s_new  = max(s_old, amax / qmax)      s_old = 0 when the run starts at row 0
+//   if s_new > s_old: earlier rows c -> encode(value(c) * (s_old / s_new))
+//   new rows x -> encode(x / s_new)       (code 0 while s_new is 0)
+// All arithmetic is fp32, rounded to nearest even; encode clamps to +-qmax and
+// rounds to nearest even (E4M3FN by the hardware convert, int8 by v_rndne).
+template <int ST>
+__device__ __forceinline__ float src_value(const void *p, int64_t i) {
+  if constexpr (ST == PA_F32) return reinterpret_cast<const float *>(p)[i];
+  else if constexpr (ST == PA_F16) return (float)reinterpret_cast<const _Float16 *>(p)[i];
+  else return __builtin_bit_cast(float, (uint32_t)reinterpret_cast<const uint16_t *>(p)[i] << 16);
+}
+
+template <int KV>
+__device__ __forceinline__ uint8_t encode_code(float y) {
+  constexpr float qmax = KV == PA_FP8_E4M3 ? 448.f : 127.f;
+  y = fminf(fmaxf(y, -qmax), qmax);
+  if constexpr (KV == PA_FP8_E4M3) {
+    return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(y, y, 0, false) & 0xff);
+  } else {
+    return (uint8_t)(int8_t)(int)__builtin_rintf(y);
+  }
+}
+
+template <int KV>
+__device__ __forceinline__ float code_value(uint8_t c) {
+  if constexpr (KV == PA_FP8_E4M3) {
+    float f[4];
+    fp8x4_to_f32((uint32_t)c, f);
+    return f[0];
+  } else {
+    return (float)(int8_t)c;
+  }
+}
+
+template <int KV, int ST, int D>
+__global__ __launch_bounds__(64) void kv_cache_write_quant_kernel(CacheWriteArgs a) {
+  constexpr float qmax = KV == PA_FP8_E4M3 ? 448.f : 127.f;
+  constexpr int EPL = D / 64;  // dims per lane
+  const int t = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const bool is_v = blockIdx.z != 0;
+  const int64_t slot = a.slots[t];
+  if (slot < 0) return;
+  const int64_t blk = slot / kBlock;
+  const int off = (int)(slot % kBlock);
+  if (t > 0) {  // not the first row of its run: the run's first row does the work
+    const int64_t prev = a.slots[t - 1];
+    if (prev >= 0 && prev / kBlock == blk) return;
+  }
+  int len = 1;
+  while (len < kBlock - off && t + len < a.num_tokens && a.slots[t + len] >= 0 &&
+         a.slots[t + len] / kBlock == blk)
+    ++len;
+
+  const void *src = is_v ? a.v_new : a.k_new;
+  uint8_t *tile = reinterpret_cast<uint8_t *>(is_v ? a.v : a.k) +
+                  (blk * a.num_kv_heads + h) * (int64_t)(kBlock * D);
+  float *scale = (is_v ? a.v_scale : a.k_scale) + blk * a.num_kv_heads + h;
+  const int d0 = lane * EPL;
+
+  auto src_at = [&](int i, int e) {
+    return src_value<ST>(src, ((int64_t)(t + i) * a.num_kv_heads + h) * D + d0 + e);
+  };
+  float amax = 0.f;
+  for (int i = 0; i < len; ++i)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(src_at(i, e)));
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kWave));
+  const float s_old = off > 0 ? *scale : 0.f;
+  const float s_new = fmaxf(s_old, amax / qmax);
+  if (off > 0 && s_new > s_old) {
+    const float ratio = s_old / s_new;
+    for (int r = 0; r < off; ++r) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        uint8_t *c = tile + r * D + d0 + e;
+        *c = encode_code<KV>(code_value<KV>(*c) * ratio);
+      }
+    }
+  }
+  for (int i = 0; i < len; ++i) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+      tile[(off + i) * D + d0 + e] = s_new > 0.f ? encode_code<KV>(src_at(i, e) / s_new) : (uint8_t)0;
+  }
+  if (lane == 0) *scale = s_new;
+}
+
 // One thread per 16-byte chunk of a block's K or V (all kv heads), plus the
 // per-(block, kv head) scales of 1-byte pools.
 __global__ __launch_bounds__(256) void kv_block_copy_kernel(BlockCopyArgs a, int64_t total) {
@@ -94,6 +188,30 @@ hipError_t launch_cache_write(const CacheWriteArgs &a, hipStream_t st) {
   const int64_t total = 2 * (int64_t)a.num_tokens * a.num_kv_heads * (a.row_bytes / 16);
   hipLaunchKernelGGL(kv_cache_write_kernel, dim3(grid_for(total)), dim3(256), 0, st, a, total);
   return hipGetLastError();
+}
+
+template <int KV, int ST>
+static hipError_t launch_quant_d(const CacheWriteArgs &a, int D, hipStream_t st) {
+  dim3 grid(a.num_tokens, a.num_kv_heads, 2);
+  if (D == 64) hipLaunchKernelGGL((kv_cache_write_quant_kernel<KV, ST, 64>), grid, dim3(64), 0, st, a);
+  else hipLaunchKernelGGL((kv_cache_write_quant_kernel<KV, ST, 128>), grid, dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int KV>
+static hipError_t launch_quant_s(const CacheWriteArgs &a, int src_dtype, int D, hipStream_t st) {
+  switch (src_dtype) {
+    case PA_F32: return launch_quant_d<KV, PA_F32>(a, D, st);
+    case PA_F16: return launch_quant_d<KV, PA_F16>(a, D, st);
+    case PA_BF16: return launch_quant_d<KV, PA_BF16>(a, D, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_cache_write_quant(const CacheWriteArgs &a, int kv_dtype, int src_dtype,
+                                    int head_dim, hipStream_t st) {
+  return kv_dtype == PA_FP8_E4M3 ? launch_quant_s<PA_FP8_E4M3>(a, src_dtype, head_dim, st)
+                                 : launch_quant_s<PA_I8>(a, src_dtype, head_dim, st);
 }
 
 hipError_t launch_block_copy(const BlockCopyArgs &a, hipStream_t st) {

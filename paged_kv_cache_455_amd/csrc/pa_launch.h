@@ -50,6 +50,8 @@ struct MixedArgs {
 struct CacheWriteArgs {
   void *k;
   void *v;
+  float *k_scale;     // 1-byte pools (quantise-on-write)
+  float *v_scale;
   const void *k_new;
   const void *v_new;
   const int64_t *slots;
@@ -88,6 +90,8 @@ int mixed_tile_rows();  // query rows (token, head) per prefill tile of the mixe
 hipError_t launch_mixed(const MixedArgs &a, int kv_dtype, int q_dtype, int head_dim, int group,
                         int num_rows, bool stream_loads, hipStream_t st);
 hipError_t launch_cache_write(const CacheWriteArgs &a, hipStream_t st);
+hipError_t launch_cache_write_quant(const CacheWriteArgs &a, int kv_dtype, int src_dtype,
+                                    int head_dim, hipStream_t st);
 hipError_t launch_block_copy(const BlockCopyArgs &a, hipStream_t st);
 hipError_t launch_slot_mapping(const int32_t *bt, int32_t mbps, const int32_t *qsl,
                                const int32_t *seq_lens, int32_t num_seqs, int64_t *slots,

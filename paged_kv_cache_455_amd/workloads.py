@@ -214,7 +214,11 @@ def decode_batch(seed: int, ctx, hq: int, hkv: int, d: int, kv: str, qd: str, *,
         # same seed quantise the same N(0,1) data
         k_pool, k_scale = _quantised_pool(rng, nb, hkv, d, div, kv)
         v_pool, v_scale = _quantised_pool(rng, nb, hkv, d, div, kv)
-        k_new = v_new = None
+        if with_new:  # this step's K/V in the model's dtype, quantised on write
+            k_new = _cast(_normal(rng, (S, hkv, d), div), qd)
+            v_new = _cast(_normal(rng, (S, hkv, d), div), qd)
+        else:
+            k_new = v_new = None
     else:
         k_pool = _float_pool(rng, nb, hkv, d, div, kv)
         v_pool = _float_pool(rng, nb, hkv, d, div, kv)
@@ -391,7 +395,7 @@ def long_quantised(kv: str = "fp8", batch: int = 16, ctx: int = 32768, seed: int
     The int8 batch quantises the same N(0,1) draws as the fp8 batch.
     """
     return decode_batch(seed, [ctx] * batch, 64, 8, 128, kv, "bf16", poison=poison,
-                        name=f"long-{kv}-b{batch}x{ctx}", with_new=False)
+                        name=f"long-{kv}-b{batch}x{ctx}")
 
 
 WORKLOADS = {

@@ -32,7 +32,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("pa_decode", "pa_prefill_chunk", "kv_cache_write", "kv_block_copy",
+    for n in ("pa_decode", "pa_prefill_chunk", "kv_cache_write", "kv_cache_write_quant",
+              "kv_block_copy",
               "pa_slot_mapping", "pa_decode_workspace_size", "pa_prefill_workspace_size",
               "pa_status_string", "pa_last_error", "pa_version"):
         assert n in names, n
@@ -108,6 +109,14 @@ def test_write_copy_slot_checks(lib):
     assert lib.kv_block_copy(ctypes.byref(p), FAKE, 0, None) == PA_OK
     assert lib.kv_block_copy(ctypes.byref(pool(kv=pa.PA_FP8_E4M3)), FAKE, 2, None) == PA_E_ARG
     assert lib.pa_slot_mapping(None, 4, FAKE, FAKE, 3, 3, FAKE, None) == PA_E_ARG
+    # quantise-on-write: 1-byte pools only, float sources only, scales required
+    qw = lambda pl, sd=pa.PA_BF16, n=4: lib.kv_cache_write_quant(ctypes.byref(pl), FAKE, FAKE, sd,
+                                                                 FAKE, n, None)
+    assert qw(pool()) == PA_E_UNSUPPORTED                                    # f16 pool
+    assert qw(pool(kv=pa.PA_FP8_E4M3)) == PA_E_ARG                            # no scales
+    assert qw(pool(kv=pa.PA_FP8_E4M3, scales=True), sd=pa.PA_I8) == PA_E_UNSUPPORTED
+    assert qw(pool(kv=pa.PA_I8, scales=True), n=-1) == PA_E_ARG
+    assert qw(pool(kv=pa.PA_I8, scales=True), n=0) == PA_OK
     assert lib.pa_slot_mapping(FAKE, 4, FAKE, FAKE, 0, 0, FAKE, None) == PA_OK
 
 

@@ -350,3 +350,100 @@ def test_fp8_hardware_decode_matches_ocp_table():
         want_bf16 = torch.from_numpy(want).to(torch.bfloat16).float().numpy()
         for h in range(hq):
             assert np.array_equal(out[s, h], want_bf16)
+
+
+# ---------------------------------------------------------------------------------------
+# quantise-on-write into 1-byte pools: codes and scales bit-exact against the oracle
+# ---------------------------------------------------------------------------------------
+def _quant_schedule(rng, nb):
+    """Calls of (slot list) that append rows to blocks in order, as steps would:
+    single-token decode appends, a chunk that crosses blocks, padding slots."""
+    fill = {}
+    free = list(rng.permutation(nb))
+    seqs = [[free.pop()] for _ in range(6)]   # each sequence: its blocks
+    fill = {s: int(rng.integers(0, 15)) for s in range(6)}  # rows already written
+    calls = []
+
+    def take(s, k):
+        out = []
+        for _ in range(k):
+            if fill[s] == 16 * len(seqs[s]):
+                seqs[s].append(free.pop())
+            pos = fill[s]
+            out.append(seqs[s][pos // 16] * 16 + pos % 16)
+            fill[s] += 1
+        return out
+
+    for step in range(5):  # decode steps: one token per sequence, one padding row
+        slots = []
+        for s in range(6):
+            slots += take(s, 1)
+        slots.insert(3, -1)
+        calls.append(slots)
+    calls.append(take(0, 37) + [-1, -1] + take(4, 3))  # chunks crossing blocks
+    calls.append(take(2, 16))
+    return calls, seqs, fill
+
+
+@pytest.mark.parametrize("kind,src,hd", [("fp8", torch.bfloat16, 128), ("fp8", torch.float16, 128),
+                                         ("i8", torch.bfloat16, 128), ("i8", torch.float32, 64),
+                                         ("fp8", torch.float32, 64)])
+def test_quantised_cache_write_bit_exact(kind, src, hd):
+    rng = np.random.default_rng(11)
+    nb, hkv = 40, 4
+    say("quant-write", kind, src, hd)
+    cdt = torch.uint8 if kind == "fp8" else torch.int8
+    # start from a valid pool state: codes and scales of earlier writes
+    codes0 = torch.from_numpy(rng.integers(-100, 100, (nb, hkv, 16, hd)).astype(np.int8)).view(cdt)
+    if kind == "fp8":
+        codes0 = codes0 & 0x7E | (codes0 & 0x80)   # no NaN patterns
+    scales0 = torch.from_numpy(rng.uniform(0.001, 0.01, (nb, hkv)).astype(np.float32))
+    kc, vc = codes0.clone().cuda(), codes0.clone().cuda()
+    ks, vs = scales0.clone().cuda(), scales0.clone().cuda()
+    pool = pa.KVPool(kc, vc, ks, vs)
+    ok, ovc = codes0.numpy().copy(), codes0.numpy().copy()
+    oks, ovs = scales0.numpy().copy(), scales0.numpy().copy()
+    calls, _, _ = _quant_schedule(rng, nb)
+    for i, slots in enumerate(calls):
+        n = len(slots)
+        mag = rng.uniform(0.2, 8.0, (n, 1, 1)) * (0.004 if i % 2 else 0.02)
+        kx = torch.from_numpy((rng.standard_normal((n, hkv, hd)) * mag).astype(np.float32)).to(src)
+        vx = torch.from_numpy((rng.standard_normal((n, hkv, hd)) * mag).astype(np.float32)).to(src)
+        sl = torch.tensor(slots, dtype=torch.int64)
+        pa.kv_cache_write_quant(pool, kx.cuda(), vx.cuda(), sl.cuda())
+        torch.cuda.synchronize()
+        kf, vf = kx.float().numpy(), vx.float().numpy()
+        ok, oks = oracle.quantised_cache_write(ok, oks, kf, sl.numpy(), kind)
+        ovc, ovs = oracle.quantised_cache_write(ovc, ovs, vf, sl.numpy(), kind)
+        gk, gv = kc.cpu().numpy(), vc.cpu().numpy()
+        assert np.array_equal(ks.cpu().numpy().view(np.uint32), oks.view(np.uint32)), ("k scale", i)
+        assert np.array_equal(vs.cpu().numpy().view(np.uint32), ovs.view(np.uint32)), ("v scale", i)
+        bad = np.argwhere(gk != ok)
+        assert len(bad) == 0, ("k codes", i, bad[:5], gk[tuple(bad[0])] if len(bad) else None,
+                               ok[tuple(bad[0])] if len(bad) else None)
+        assert np.array_equal(gv, ovc), ("v codes", i)
+
+
+def test_quantised_write_then_decode():
+    # a decode step on a 1-byte pool: write this step's K/V rows, then attend
+    b = W.long_quantised("fp8", batch=3, ctx=700)
+    rng = np.random.default_rng(12)
+    d = Dev(b)
+    S, hkv, hd = b.num_seqs, b.num_kv_heads, b.head_dim
+    kx = torch.from_numpy(rng.standard_normal((S, hkv, hd)).astype(np.float32)).to(torch.bfloat16)
+    vx = torch.from_numpy(rng.standard_normal((S, hkv, hd)).astype(np.float32)).to(torch.bfloat16)
+    qsl = torch.arange(S + 1, dtype=torch.int32)
+    slots = pa.pa_slot_mapping(d.bt, qsl.cuda(), d.lens, S)
+    pa.kv_cache_write_quant(d.pool, kx.cuda(), vx.cuda(), slots)
+    out = run_decode(d)
+    torch.cuda.synchronize()
+    ok, oks = oracle.quantised_cache_write(b.k_pool.numpy(), b.k_scale.numpy(), kx.float().numpy(),
+                                           slots.cpu().numpy(), "fp8")
+    ovc, ovs = oracle.quantised_cache_write(b.v_pool.numpy(), b.v_scale.numpy(), vx.float().numpy(),
+                                            slots.cpu().numpy(), "fp8")
+    assert np.array_equal(d.k.cpu().numpy(), ok) and np.array_equal(d.v.cpu().numpy(), ovc)
+    b2 = W.PagedBatch(**{**b.__dict__, "k_pool": torch.from_numpy(ok), "v_pool": torch.from_numpy(ovc),
+                         "k_scale": torch.from_numpy(oks), "v_scale": torch.from_numpy(ovs)})
+    err = max_err(out, oracle_decode_rows(b2))
+    say("write-then-decode fp8 max_err", err)
+    assert err <= TOL["fp8"]
