@@ -56,7 +56,8 @@ typedef enum pa_status {
   PA_E_ARG = 1,         /* a null pointer or an out-of-range scalar */
   PA_E_UNSUPPORTED = 2, /* a valid but unimplemented shape or dtype combination */
   PA_E_WORKSPACE = 3,   /* workspace missing or smaller than *_workspace_size */
-  PA_E_HIP = 4          /* a HIP launch failed */
+  PA_E_HIP = 4,         /* a HIP launch failed */
+  PA_E_NO_BLOCKS = 5    /* block manager: the free list cannot cover the request */
 } pa_status_t;
 
 /* Host struct describing caller-owned device memory. */
@@ -208,6 +209,72 @@ pa_status_t pa_prefill_chunk(const pa_kv_pool_t *pool, const void *q, int32_t q_
                              int32_t num_seqs, int32_t num_q_tokens, int32_t num_q_heads,
                              int32_t max_query_len, int32_t max_seq_len, float scale,
                              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * ---- Host block manager ([P1] PagedAttention, Prefix Sharing, Continuous
+ * Batching; [P2] 3.2) -- host memory only, no device calls. ----
+ * A request's cache is a list of 16-token physical blocks taken from a free list
+ * of num_blocks (the device pool's blocks) as it grows: a token goes at the end of
+ * the last block, a full block is followed by a fresh one.  Blocks are reference
+ * counted: pa_bm_fork shares every block of a request with a new one (parallel
+ * sampling), and a request that appends into a shared, partly filled last block
+ * first moves to a copy of it (copy-on-write).  Full blocks enter a prefix cache
+ * under a hash of the tokens up to their end; pa_bm_add reuses cached blocks for
+ * a new prompt's leading full blocks (a hit is checked token by token and block
+ * by block, so a hash collision cannot share wrong rows).  A block returns to the
+ * free list, and leaves the prefix cache, with its last reference.
+ *
+ * Step protocol.  After adds, appends, forks and releases, pa_bm_step hands out
+ * one step's host arrays; the caller then runs, in this order on one stream:
+ * kv_block_copy over the pairs, the K/V writes of the query tokens (slot mapping
+ * from the arrays), attention.  A request's query rows in a step are all its
+ * tokens not yet written (the cached prefix of a prompt excluded); a block
+ * enters the prefix cache in the step that writes its last token.  With that
+ * order the pairs' destinations are unique and disjoint from their sources, and
+ * no slot is written twice in a step.  Not thread safe: one manager per thread.
+ */
+typedef struct pa_block_manager pa_block_manager_t;
+
+/* A manager over blocks 0 .. num_blocks-1, all free.  NULL for num_blocks <= 0
+ * or out of host memory. */
+pa_block_manager_t *pa_bm_create(int32_t num_blocks);
+void pa_bm_destroy(pa_block_manager_t *bm);
+/* Free blocks (-1 for a NULL manager).  A copy source whose last reference went
+ * in this step counts as free only after the next pa_bm_step. */
+int32_t pa_bm_num_free(const pa_block_manager_t *bm);
+/* References to a block (-1 out of range); for tests and diagnostics. */
+int32_t pa_bm_refcount(const pa_block_manager_t *bm, int32_t block);
+
+/* New request `req` with its n >= 1 prompt tokens (host array).  *cached (may
+ * be NULL) receives how many leading prompt tokens already sit in shared cached
+ * blocks -- a multiple of 16, at most n - 1 -- which the next step does not
+ * compute.  PA_E_NO_BLOCKS (nothing changed) when the free list is short;
+ * PA_E_ARG for a used id. */
+pa_status_t pa_bm_add(pa_block_manager_t *bm, int64_t req, const int32_t *tokens, int32_t n,
+                      int32_t *cached);
+/* New request `child` sharing every block of `parent` (reference counts + 1).
+ * PA_E_ARG if the parent has tokens no step has handed out yet. */
+pa_status_t pa_bm_fork(pa_block_manager_t *bm, int64_t parent, int64_t child);
+/* Append n tokens to `req` (one per decode step, or a prompt chunk); may queue
+ * a copy-on-write pair.  PA_E_NO_BLOCKS (nothing changed) when the free list is
+ * short. */
+pa_status_t pa_bm_append(pa_block_manager_t *bm, int64_t req, const int32_t *tokens, int32_t n);
+/* Drop `req`: its blocks lose a reference each. */
+pa_status_t pa_bm_release(pa_block_manager_t *bm, int64_t req);
+/* The host arrays of one step over the n distinct requests `reqs`, each with at
+ * least one token not yet written; those tokens are its query rows:
+ *   block_tables    int32 [n][max_blocks_per_seq], -1 past each request's blocks
+ *   seq_lens        int32 [n]: each request's length (its tokens so far)
+ *   query_start_loc int32 [n + 1]: prefix sums of the query row counts
+ *   copy_pairs      int32 [max_pairs][2]: every copy-on-write pair queued since
+ *                   the last step, then *num_pairs = their count (may be NULL
+ *                   when none are queued).  The queue is emptied.
+ * PA_E_ARG (nothing changed) for an unknown or repeated request, one with no new
+ * token or more than max_blocks_per_seq blocks, or too little pair room. */
+pa_status_t pa_bm_step(pa_block_manager_t *bm, const int64_t *reqs, int32_t n,
+                       int32_t max_blocks_per_seq, int32_t *block_tables, int32_t *seq_lens,
+                       int32_t *query_start_loc, int32_t *copy_pairs, int32_t max_pairs,
+                       int32_t *num_pairs);
 
 #ifdef __cplusplus
 }

@@ -18,7 +18,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "KVPool", "PA_POOL_SHARED_BLOCKS", "PagedAttentionError", "library_path", "load_library",
+    "KVPool", "PA_POOL_SHARED_BLOCKS", "PagedAttentionError", "BlockManager", "library_path", "load_library",
     "pa_slot_mapping", "kv_cache_write", "kv_cache_write_quant", "kv_block_copy", "pa_decode",
     "pa_prefill_chunk",
     "pa_decode_workspace_size", "pa_prefill_workspace_size", "PA_DTYPE",
@@ -35,7 +35,8 @@ PA_DTYPE = {
     torch.float8_e4m3fn: PA_FP8_E4M3,
     torch.int8: PA_I8,
 }
-_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP error"}
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP error",
+           5: "no free block"}
 
 
 class PagedAttentionError(RuntimeError):
@@ -71,6 +72,16 @@ _SIGS = {
                              _c.c_int32, _c.c_void_p, _c.c_int32, _c.c_int32, _c.c_int32,
                              _c.c_float, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "pa_prefill_workspace_size": (_c.c_size_t, [_c.c_int32] * 8),
+    "pa_bm_create": (_c.c_void_p, [_c.c_int32]),
+    "pa_bm_destroy": (None, [_c.c_void_p]),
+    "pa_bm_num_free": (_c.c_int32, [_c.c_void_p]),
+    "pa_bm_refcount": (_c.c_int32, [_c.c_void_p, _c.c_int32]),
+    "pa_bm_add": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_void_p, _c.c_int32, _c.c_void_p]),
+    "pa_bm_fork": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int64]),
+    "pa_bm_append": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_void_p, _c.c_int32]),
+    "pa_bm_release": (_c.c_int, [_c.c_void_p, _c.c_int64]),
+    "pa_bm_step": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_int32, _c.c_int32, _c.c_void_p,
+                              _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int32, _c.c_void_p]),
     "pa_prefill_chunk": (_c.c_int, [_c.POINTER(_Pool), _c.c_void_p, _c.c_int32, _c.c_void_p,
                                     _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int32, _c.c_int32,
                                     _c.c_int32, _c.c_int32, _c.c_int32, _c.c_int32, _c.c_float,
@@ -250,3 +261,72 @@ def pa_prefill_chunk(pool: KVPool, q, query_start_loc, seq_lens, block_tables, m
         _ptr(block_tables), int(block_tables.shape[1]), S, int(T), int(hq), int(max_query_len),
         int(max_seq_len), float(scale), _ptr(workspace), wbytes, _stream(q, stream)))
     return out
+
+
+class BlockManager:
+    """Host block manager of the C ABI (``pa_bm_*``): allocation, prefix cache,
+    reference counts, copy-on-write and the per-step host arrays.  Marshalling
+    only; the bookkeeping runs in the library."""
+
+    def __init__(self, num_blocks: int):
+        lib = load_library()
+        self._lib = lib
+        self._h = lib.pa_bm_create(int(num_blocks))
+        if not self._h:
+            raise PagedAttentionError("pa_bm_create", 1, "bad num_blocks or out of memory")
+        self.num_blocks = int(num_blocks)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            self._lib.pa_bm_destroy(h)
+            self._h = None
+
+    @staticmethod
+    def _ints(xs):
+        import numpy as np
+        a = np.ascontiguousarray(np.asarray(xs, dtype=np.int32))
+        return a, a.ctypes.data_as(ctypes.c_void_p)
+
+    def num_free(self) -> int:
+        return int(self._lib.pa_bm_num_free(self._h))
+
+    def refcount(self, block: int) -> int:
+        return int(self._lib.pa_bm_refcount(self._h, int(block)))
+
+    def add(self, req: int, tokens) -> int:
+        """Register a request's prompt; returns the number of leading prompt tokens
+        already held by shared cached blocks."""
+        a, p = self._ints(tokens)
+        cached = ctypes.c_int32(0)
+        _check("pa_bm_add", self._lib.pa_bm_add(self._h, int(req), p, int(a.size),
+                                                ctypes.byref(cached)))
+        return int(cached.value)
+
+    def fork(self, parent: int, child: int):
+        _check("pa_bm_fork", self._lib.pa_bm_fork(self._h, int(parent), int(child)))
+
+    def append(self, req: int, tokens):
+        a, p = self._ints(tokens)
+        _check("pa_bm_append", self._lib.pa_bm_append(self._h, int(req), p, int(a.size)))
+
+    def release(self, req: int):
+        _check("pa_bm_release", self._lib.pa_bm_release(self._h, int(req)))
+
+    def step(self, reqs, max_blocks_per_seq: int, max_pairs: int = 1024):
+        """Host arrays of one step; each request's query rows are its tokens not
+        yet written.  Returns (block_tables [n][mb], seq_lens [n],
+        query_start_loc [n+1], copy_pairs [P][2]) as numpy int32 arrays."""
+        import numpy as np
+        n = len(reqs)
+        r = np.ascontiguousarray(np.asarray(reqs, dtype=np.int64))
+        bt = np.zeros((n, max_blocks_per_seq), dtype=np.int32)
+        lens = np.zeros(n, dtype=np.int32)
+        qsl = np.zeros(n + 1, dtype=np.int32)
+        pairs = np.zeros((max(max_pairs, 1), 2), dtype=np.int32)
+        npairs = ctypes.c_int32(0)
+        vp = lambda x: x.ctypes.data_as(ctypes.c_void_p)
+        _check("pa_bm_step", self._lib.pa_bm_step(
+            self._h, vp(r), n, int(max_blocks_per_seq), vp(bt), vp(lens), vp(qsl), vp(pairs),
+            int(max_pairs), ctypes.byref(npairs)))
+        return bt, lens, qsl, pairs[:npairs.value].copy()

@@ -1,6 +1,7 @@
 """Build the HIP library ``libpa.so`` in-tree for gfx950 with hipcc.
 
-Every translation unit under ``csrc/`` is compiled to an object (in parallel)
+Every translation unit under ``csrc/`` (``.hip`` kernels, ``.cpp`` host code) is
+compiled to an object (in parallel)
 and linked into ``paged_kv_cache_455_amd/libpa.so``.  Run as
 ``python -m paged_kv_cache_455_amd._build``.
 """
@@ -37,7 +38,7 @@ def hipcc() -> str:
 
 
 def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
 def _compile(src: str) -> str:

@@ -161,6 +161,17 @@ int max_parts_for(int max_ctx, int part_blocks) {
 
 }  // namespace
 
+namespace pa {
+// Record a failure for pa_last_error() (used by the host-side modules).
+pa_status_t set_error(pa_status_t st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+}  // namespace pa
+
 extern "C" {
 
 const char *pa_version(void) { return "paged_kv_cache_455_amd 0.1 (gfx950)"; }
@@ -172,6 +183,7 @@ const char *pa_status_string(pa_status_t s) {
     case PA_E_UNSUPPORTED: return "unsupported shape or dtype";
     case PA_E_WORKSPACE: return "workspace too small";
     case PA_E_HIP: return "HIP error";
+    case PA_E_NO_BLOCKS: return "no free block";
   }
   return "unknown status";
 }

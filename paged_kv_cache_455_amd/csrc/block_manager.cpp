@@ -1,0 +1,303 @@
+// Host-side block manager: the bookkeeping that feeds the device calls.
+//
+// uml.org.cn "PagedAttention": a request's KV cache is a list of fixed-size
+// physical blocks, taken from a free pool as the request grows, and found through
+// its block table.  5688vip chapter 3, section 3.2: a new token goes at the end of
+// the request's last block; a full block is followed by a fresh one.
+// uml.org.cn "Prefix Sharing": requests with the same prompt prefix map it to the
+// same physical blocks (reference counted); a request that writes into a shared
+// block first gets its own copy of it (copy-on-write).  uml.org.cn "Continuous
+// Batching": each step runs whatever requests are active, so the step's block
+// tables, lengths and query ranges are rebuilt every step.
+//
+// The device work of one step runs in this order on one stream: the step's
+// copy-on-write pairs (kv_block_copy), the K/V writes of its query tokens, then
+// attention.  The manager keeps every hand-out consistent with that order:
+//  * a request's query rows in a step are exactly its tokens not yet written, so
+//    every token is written once, by the request that holds it;
+//  * a block enters the prefix cache only in the step that writes its last token,
+//    so a request that hits it in a later step reads written rows;
+//  * a request is forked only when all its tokens are written, so two requests
+//    never write the same slot in one step;
+//  * a step's pairs have unique destinations disjoint from their sources: a
+//    destination is a fresh block of a request with unwritten tokens, so it is
+//    neither forked nor a cache hit (nor a source) before the step; a source whose
+//    last reference goes waits for the step before it is free again; a
+//    destination whose last reference goes takes its pair with it.
+#include <stdint.h>
+#include <stdlib.h>
+
+#include <algorithm>
+#include <new>
+#include <unordered_map>
+#include <unordered_set>
+#include <vector>
+
+#include "../../include/pa.h"
+#include "pa_launch.h"
+
+namespace {
+
+constexpr int kBlockSize = 16;
+
+uint64_t mix(uint64_t h, uint64_t x) {  // splitmix64 step over the running hash
+  h ^= x + 0x9e3779b97f4a7c15ull + (h << 6) + (h >> 2);
+  h ^= h >> 30;
+  h *= 0xbf58476d1ce4e5b9ull;
+  h ^= h >> 27;
+  h *= 0x94d049bb133111ebull;
+  h ^= h >> 31;
+  return h;
+}
+
+// prefix hash through one more full block of 16 tokens (0 is kept for "none")
+uint64_t chain(uint64_t prev, const int32_t *tokens16) {
+  uint64_t h = prev;
+  for (int k = 0; k < kBlockSize; ++k) h = mix(h, (uint32_t)tokens16[k]);
+  return h == 0 ? 1 : h;
+}
+
+constexpr uint64_t kSeed = 0x6a09e667f3bcc909ull;
+
+struct Request {
+  std::vector<int32_t> blocks;  // physical block ids, logical order
+  std::vector<int32_t> tokens;  // every token so far
+  int32_t written = 0;          // leading tokens whose K/V a handed-out step writes
+  int32_t published = 0;        // leading full blocks already offered to the cache
+  uint64_t hash = kSeed;        // prefix hash through block `published - 1`
+};
+
+struct Pair {
+  int32_t src, dst;
+};
+
+}  // namespace
+
+struct pa_block_manager {
+  int32_t num_blocks = 0;
+  std::vector<int32_t> free_list;       // stack of free block ids
+  std::vector<int32_t> refs;            // references per block
+  std::vector<uint64_t> cached_hash;    // prefix-cache key of a block, 0 if not cached
+  std::vector<int32_t> cached_parent;   // block before it in the request that cached it
+  std::vector<std::vector<int32_t>> cached_tokens;  // the 16 tokens a cached block holds
+  std::unordered_map<uint64_t, int32_t> cache;      // hash -> block
+  std::unordered_map<int64_t, Request> reqs;
+  std::vector<Pair> pending;            // copy-on-write pairs for the next step
+  std::vector<int32_t> held;            // freed pending sources, free after the step
+
+  int32_t take() {
+    const int32_t b = free_list.back();
+    free_list.pop_back();
+    refs[b] = 1;
+    return b;
+  }
+  void drop(int32_t b) {
+    if (--refs[b] > 0) return;
+    if (cached_hash[b] != 0) {
+      auto it = cache.find(cached_hash[b]);
+      if (it != cache.end() && it->second == b) cache.erase(it);
+      cached_hash[b] = 0;
+    }
+    for (const Pair &p : pending)
+      if (p.src == b) {  // its step-start rows are still to be copied
+        held.push_back(b);
+        return;
+      }
+    pending.erase(std::remove_if(pending.begin(), pending.end(),
+                                 [b](const Pair &p) { return p.dst == b; }),
+                  pending.end());
+    free_list.push_back(b);
+  }
+  // offer request r's full blocks to the prefix cache (first holder of a hash wins)
+  void publish(Request &r) {
+    const int32_t full = r.written / kBlockSize;
+    for (; r.published < full; ++r.published) {
+      const int32_t i = r.published;
+      r.hash = chain(r.hash, r.tokens.data() + (size_t)i * kBlockSize);
+      const int32_t b = r.blocks[i];
+      if (cache.count(r.hash) != 0 || cached_hash[b] != 0) continue;
+      cache.emplace(r.hash, b);
+      cached_hash[b] = r.hash;
+      cached_parent[b] = i == 0 ? -1 : r.blocks[i - 1];
+      cached_tokens[b].assign(r.tokens.begin() + (size_t)i * kBlockSize,
+                              r.tokens.begin() + (size_t)(i + 1) * kBlockSize);
+    }
+  }
+  // Append tokens to r: fresh blocks at block boundaries, a private copy of a
+  // shared last block before writing into it.  Fails (changing nothing) when the
+  // free list cannot cover it.
+  pa_status_t append(Request &r, const int32_t *tokens, int32_t n) {
+    if (n == 0) return PA_OK;
+    const int32_t len = (int32_t)r.tokens.size();
+    const int32_t have = (int32_t)r.blocks.size();
+    int32_t needed = (len + n + kBlockSize - 1) / kBlockSize - have;
+    const bool cow = len % kBlockSize != 0 && refs[r.blocks.back()] > 1;
+    if (cow) ++needed;
+    if (needed > (int32_t)free_list.size())
+      return pa::set_error(PA_E_NO_BLOCKS, "no free block for the request's new tokens");
+    if (cow) {
+      const int32_t src = r.blocks.back();
+      const int32_t dst = take();
+      pending.push_back({src, dst});
+      r.blocks.back() = dst;
+      drop(src);  // still referenced by the other holders
+    }
+    for (int32_t i = 0; i < n; ++i) {
+      if ((int32_t)r.tokens.size() == (int32_t)r.blocks.size() * kBlockSize)
+        r.blocks.push_back(take());
+      r.tokens.push_back(tokens[i]);
+    }
+    return PA_OK;
+  }
+};
+
+extern "C" {
+
+pa_block_manager_t *pa_bm_create(int32_t num_blocks) {
+  if (num_blocks <= 0) return nullptr;
+  pa_block_manager *bm = new (std::nothrow) pa_block_manager();
+  if (bm == nullptr) return nullptr;
+  try {
+    bm->num_blocks = num_blocks;
+    bm->free_list.resize(num_blocks);
+    for (int32_t i = 0; i < num_blocks; ++i) bm->free_list[i] = num_blocks - 1 - i;  // 0 first
+    bm->refs.assign(num_blocks, 0);
+    bm->cached_hash.assign(num_blocks, 0);
+    bm->cached_parent.assign(num_blocks, -1);
+    bm->cached_tokens.resize(num_blocks);
+  } catch (const std::bad_alloc &) {
+    delete bm;
+    return nullptr;
+  }
+  return bm;
+}
+
+void pa_bm_destroy(pa_block_manager_t *bm) { delete bm; }
+
+int32_t pa_bm_num_free(const pa_block_manager_t *bm) {
+  return bm ? (int32_t)bm->free_list.size() : -1;
+}
+
+int32_t pa_bm_refcount(const pa_block_manager_t *bm, int32_t block) {
+  if (!bm || block < 0 || block >= bm->num_blocks) return -1;
+  return bm->refs[block];
+}
+
+pa_status_t pa_bm_add(pa_block_manager_t *bm, int64_t req, const int32_t *tokens, int32_t n,
+                      int32_t *cached) {
+  if (!bm || !tokens || n < 1) return pa::set_error(PA_E_ARG, "pa_bm_add: bad argument");
+  if (bm->reqs.count(req)) return pa::set_error(PA_E_ARG, "pa_bm_add: request id already in use");
+  // leading full blocks found in the prefix cache; a hit must hold the same 16
+  // tokens and follow the block matched before it, so the whole prefix is equal.
+  // The last prompt token is always computed: at most (n - 1) / 16 blocks reused.
+  const int32_t max_hit = (n - 1) / kBlockSize;
+  std::vector<int32_t> shared;
+  uint64_t h = kSeed;
+  for (int32_t i = 0; i < max_hit; ++i) {
+    const uint64_t key = chain(h, tokens + (size_t)i * kBlockSize);
+    auto it = bm->cache.find(key);
+    if (it == bm->cache.end()) break;
+    const int32_t b = it->second;
+    if (bm->cached_parent[b] != (i == 0 ? -1 : shared.back())) break;
+    if (!std::equal(bm->cached_tokens[b].begin(), bm->cached_tokens[b].end(),
+                    tokens + (size_t)i * kBlockSize))
+      break;
+    shared.push_back(b);
+    h = key;
+  }
+  const int32_t hit = (int32_t)shared.size();
+  const int32_t fresh = (n + kBlockSize - 1) / kBlockSize - hit;
+  if (fresh > (int32_t)bm->free_list.size())
+    return pa::set_error(PA_E_NO_BLOCKS, "pa_bm_add: not enough free blocks for the prompt");
+  for (int32_t b : shared) ++bm->refs[b];
+  Request r;
+  r.blocks = shared;
+  r.tokens.assign(tokens, tokens + (size_t)hit * kBlockSize);
+  r.written = hit * kBlockSize;
+  r.published = hit;
+  r.hash = h;
+  Request &rr = bm->reqs.emplace(req, std::move(r)).first->second;
+  bm->append(rr, tokens + (size_t)hit * kBlockSize, n - hit * kBlockSize);  // fits: checked
+  if (cached) *cached = hit * kBlockSize;
+  return PA_OK;
+}
+
+pa_status_t pa_bm_fork(pa_block_manager_t *bm, int64_t parent, int64_t child) {
+  if (!bm) return pa::set_error(PA_E_ARG, "pa_bm_fork: NULL manager");
+  auto it = bm->reqs.find(parent);
+  if (it == bm->reqs.end()) return pa::set_error(PA_E_ARG, "pa_bm_fork: unknown parent");
+  if (bm->reqs.count(child)) return pa::set_error(PA_E_ARG, "pa_bm_fork: child id in use");
+  if (it->second.written != (int32_t)it->second.tokens.size())
+    return pa::set_error(PA_E_ARG, "pa_bm_fork: the parent has tokens no step has written yet");
+  Request c = it->second;
+  for (int32_t b : c.blocks) ++bm->refs[b];
+  bm->reqs.emplace(child, std::move(c));
+  return PA_OK;
+}
+
+pa_status_t pa_bm_append(pa_block_manager_t *bm, int64_t req, const int32_t *tokens, int32_t n) {
+  if (!bm || n < 0 || (!tokens && n > 0)) return pa::set_error(PA_E_ARG, "pa_bm_append: bad argument");
+  auto it = bm->reqs.find(req);
+  if (it == bm->reqs.end()) return pa::set_error(PA_E_ARG, "pa_bm_append: unknown request");
+  return bm->append(it->second, tokens, n);
+}
+
+pa_status_t pa_bm_release(pa_block_manager_t *bm, int64_t req) {
+  if (!bm) return pa::set_error(PA_E_ARG, "pa_bm_release: NULL manager");
+  auto it = bm->reqs.find(req);
+  if (it == bm->reqs.end()) return pa::set_error(PA_E_ARG, "pa_bm_release: unknown request");
+  for (int32_t b : it->second.blocks) bm->drop(b);
+  bm->reqs.erase(it);
+  return PA_OK;
+}
+
+pa_status_t pa_bm_step(pa_block_manager_t *bm, const int64_t *reqs, int32_t n,
+                       int32_t max_blocks_per_seq, int32_t *block_tables, int32_t *seq_lens,
+                       int32_t *query_start_loc, int32_t *copy_pairs, int32_t max_pairs,
+                       int32_t *num_pairs) {
+  if (!bm || n < 0 || max_blocks_per_seq <= 0 || max_pairs < 0 || !num_pairs ||
+      !query_start_loc || (n > 0 && (!reqs || !block_tables || !seq_lens)))
+    return pa::set_error(PA_E_ARG, "pa_bm_step: bad argument");
+  const int32_t pairs = (int32_t)bm->pending.size();
+  if (pairs > max_pairs || (pairs > 0 && !copy_pairs))
+    return pa::set_error(PA_E_ARG, "pa_bm_step: %d copy pairs pending, room for %d", pairs,
+                         max_pairs);
+  std::unordered_set<int64_t> seen;
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->reqs.find(reqs[i]);
+    if (it == bm->reqs.end()) return pa::set_error(PA_E_ARG, "pa_bm_step: unknown request");
+    if (!seen.insert(reqs[i]).second)
+      return pa::set_error(PA_E_ARG, "pa_bm_step: request listed twice");
+    const Request &r = it->second;
+    if ((int32_t)r.blocks.size() > max_blocks_per_seq)
+      return pa::set_error(PA_E_ARG, "pa_bm_step: request needs %d blocks > %d",
+                           (int32_t)r.blocks.size(), max_blocks_per_seq);
+    if (r.written == (int32_t)r.tokens.size())
+      return pa::set_error(PA_E_ARG, "pa_bm_step: request has no new token");
+  }
+  int32_t q = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    Request &r = bm->reqs.find(reqs[i])->second;
+    int32_t *row = block_tables + (int64_t)i * max_blocks_per_seq;
+    for (int32_t j = 0; j < max_blocks_per_seq; ++j)
+      row[j] = j < (int32_t)r.blocks.size() ? r.blocks[j] : -1;
+    const int32_t len = (int32_t)r.tokens.size();
+    seq_lens[i] = len;
+    query_start_loc[i] = q;
+    q += len - r.written;
+    r.written = len;
+    bm->publish(r);
+  }
+  query_start_loc[n] = q;
+  for (int32_t i = 0; i < pairs; ++i) {
+    copy_pairs[2 * i] = bm->pending[i].src;
+    copy_pairs[2 * i + 1] = bm->pending[i].dst;
+  }
+  *num_pairs = pairs;
+  bm->pending.clear();
+  for (int32_t b : bm->held) bm->free_list.push_back(b);
+  bm->held.clear();
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/pa.h"
+
 namespace pa {
 
 struct DecodeArgs {
@@ -96,5 +98,8 @@ hipError_t launch_block_copy(const BlockCopyArgs &a, hipStream_t st);
 hipError_t launch_slot_mapping(const int32_t *bt, int32_t mbps, const int32_t *qsl,
                                const int32_t *seq_lens, int32_t num_seqs, int64_t *slots,
                                hipStream_t st);
+
+// Record a failure for pa_last_error(); returns st.
+pa_status_t set_error(pa_status_t st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 
 }  // namespace pa

@@ -35,7 +35,9 @@ def test_header_declares_the_entry_points():
     for n in ("pa_decode", "pa_prefill_chunk", "kv_cache_write", "kv_cache_write_quant",
               "kv_block_copy",
               "pa_slot_mapping", "pa_decode_workspace_size", "pa_prefill_workspace_size",
-              "pa_status_string", "pa_last_error", "pa_version"):
+              "pa_status_string", "pa_last_error", "pa_version",
+              "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free", "pa_bm_refcount", "pa_bm_add",
+              "pa_bm_fork", "pa_bm_append", "pa_bm_release", "pa_bm_step"):
         assert n in names, n
 
 
