@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 256 MiB device copy three times (byte-counter calibration)")
+    ap.add_argument("--swap", action="store_true",
+                    help="measure kv_swap (device pool <-> pinned host pool) instead of the step")
     return ap.parse_args()
 
 
@@ -137,6 +139,81 @@ def calibrate_copy():
     print(json.dumps({"calibration": "device copy", "bytes_each_way": n, "copies": 3}))
 
 
+PCIE_PEAK_GBPS = 64.0  # PCIe 5.0 x16, per direction
+
+
+def swap_bench(args):
+    """kv_swap at the decode layer's block geometry (8 kv heads x 16 x 128, fp16:
+    64 KiB of K+V per block): 4096 scattered blocks (256 MiB) out of a 1 GiB
+    device pool into a pinned host pool and back in to other device blocks, one
+    launch per direction.  Beside it, one contiguous DMA copy of the same bytes
+    each way (torch copy_ into / out of pinned memory), and the same kernel
+    between two device pools."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_455_amd as pa
+    nb, nh, n, hkv, d = 16384, 8192, 4096, 8, 128
+    rng = np.random.default_rng(0)
+    shape = lambda m: (m, hkv, 16, d)
+    dk = torch.randn(shape(nb), dtype=torch.float16, device="cuda")
+    dv = torch.randn(shape(nb), dtype=torch.float16, device="cuda")
+    hk = torch.empty(shape(nh), dtype=torch.float16, pin_memory=True)
+    hv = torch.empty(shape(nh), dtype=torch.float16, pin_memory=True)
+    dev, host = pa.KVPool(dk, dv), pa.KVPool(hk, hv)
+    dk2, dv2 = torch.empty_like(dk), torch.empty_like(dv)
+    dev2 = pa.KVPool(dk2, dv2)
+    blocks = rng.choice(nb, 2 * n, replace=False)   # swap-ins land on other blocks
+    src, dst = blocks[:n], blocks[n:]
+    slots = rng.choice(nh, n, replace=False)
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    out_pairs = to_dev(np.stack([src, slots], 1))
+    in_pairs = to_dev(np.stack([slots, dst], 1))
+    dd_pairs = to_dev(np.stack([src, dst], 1))
+    nbytes = n * 2 * hkv * 16 * d * 2
+    flat_d = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    flat_h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    stream = torch.cuda.current_stream()
+    reps = max(1, args.steps)
+
+    def timed(fn):
+        for _ in range(max(1, args.warmup)):
+            fn()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(reps):
+            fn()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / reps
+        return {"us": round(ms * 1e3, 1), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 2)}
+
+    r_out = timed(lambda: pa.kv_swap(host, dev, out_pairs, stream=stream))
+    r_in = timed(lambda: pa.kv_swap(dev, host, in_pairs, stream=stream))
+    r_dd = timed(lambda: pa.kv_swap(dev2, dev, dd_pairs, stream=stream))
+    r_d2h = timed(lambda: flat_h.copy_(flat_d, non_blocking=True))
+    r_h2d = timed(lambda: flat_d.copy_(flat_h, non_blocking=True))
+    # the round trip lands the same rows in the destination blocks
+    torch.cuda.synchronize()
+    ok = bool(torch.equal(dk[torch.from_numpy(src).cuda()], dk[torch.from_numpy(dst).cuda()]))
+    print(json.dumps({
+        "metric": "kv_swap GB/s, device pool <-> pinned host pool over PCIe",
+        "value": round(min(r_out["GBps"], r_in["GBps"]), 2), "unit": "GB/s",
+        "higher_is_better": True, "n_gpus": 1, "steps": reps, "warmup": args.warmup,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "kv swap, 4096 scattered blocks of 8x16x128 fp16 K+V (256 MiB)",
+                   "device_blocks": nb, "host_blocks": nh},
+        "swap_out": r_out, "swap_in": r_in, "device_to_device_same_kernel": r_dd,
+        "dma_contiguous_d2h": r_d2h, "dma_contiguous_h2d": r_h2d,
+        "roofline": {"bound": "pcie", "achieved": round(min(r_out["GBps"], r_in["GBps"]), 2),
+                     "peak": PCIE_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(min(r_out["GBps"], r_in["GBps"]) / PCIE_PEAK_GBPS, 4),
+                     "traffic": None, "kernel": "kv_block_copy_kernel (kv_swap)"},
+        "round_trip_rows_equal": ok,
+    }), flush=True)
+
+
 def cpu_baseline(b, budget_s):
     """The oracle as it stands, timed on this host over a bounded sample of the batch."""
     import numpy as np
@@ -205,6 +282,9 @@ def main():
         sys.exit(1)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.swap:
+        swap_bench(args)
         return
     pa.load_library()
     dev = torch.device("cuda:0")

@@ -159,6 +159,22 @@ pa_status_t kv_cache_write_quant(const pa_kv_pool_t *pool, const void *k_new, co
 pa_status_t kv_block_copy(const pa_kv_pool_t *pool, const int32_t *src_dst, int32_t num_pairs,
                           hipStream_t stream);
 
+/*
+ * kv_swap -- move blocks between two pools of the same kv_dtype, num_kv_heads
+ * and head_dim, typically the device pool and a host pool in pinned memory
+ * ([P1] PagedAttention: under memory pressure pages go out to CPU memory and come
+ * back when the request runs again).
+ *   src_dst int32 [num_pairs][2] (device or pinned host memory): every kv head's
+ *           K and V tile (and both scales, for 1-byte pools) of block src of
+ *           `src` is copied to block dst of `dst`.
+ * Each pool's k, v and scales must be device memory or pinned host memory
+ * (hipHostMalloc, torch pin_memory); pageable memory gives PA_E_ARG.  One kernel
+ * moves every pair: the copies to or from host memory cross PCIe.  Destinations
+ * must be unique; when src and dst are one pool, also disjoint from the sources.
+ */
+pa_status_t kv_swap(const pa_kv_pool_t *dst, const pa_kv_pool_t *src, const int32_t *src_dst,
+                    int32_t num_pairs, hipStream_t stream);
+
 /* Workspace bytes pa_decode needs for these sizes (0 is a valid answer). */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t max_context_len);
@@ -235,13 +251,17 @@ pa_status_t pa_prefill_chunk(const pa_kv_pool_t *pool, const void *q, int32_t q_
  */
 typedef struct pa_block_manager pa_block_manager_t;
 
-/* A manager over blocks 0 .. num_blocks-1, all free.  NULL for num_blocks <= 0
- * or out of host memory. */
-pa_block_manager_t *pa_bm_create(int32_t num_blocks);
+/* A manager over device blocks 0 .. num_blocks-1 and host slots 0 ..
+ * num_host_blocks-1 (a host pool for swapping; 0 for none), all free.  NULL for
+ * num_blocks <= 0, num_host_blocks < 0 or out of host memory. */
+pa_block_manager_t *pa_bm_create(int32_t num_blocks, int32_t num_host_blocks);
 void pa_bm_destroy(pa_block_manager_t *bm);
-/* Free blocks (-1 for a NULL manager).  A copy source whose last reference went
- * in this step counts as free only after the next pa_bm_step. */
+/* Free device blocks (-1 for a NULL manager).  A copy source whose last
+ * reference went in this step counts as free only after the next pa_bm_step. */
 int32_t pa_bm_num_free(const pa_block_manager_t *bm);
+/* Free host slots (-1 for a NULL manager); a slot a pending swap-in reads is
+ * free again after the next pa_bm_step. */
+int32_t pa_bm_num_free_host(const pa_block_manager_t *bm);
 /* References to a block (-1 out of range); for tests and diagnostics. */
 int32_t pa_bm_refcount(const pa_block_manager_t *bm, int32_t block);
 
@@ -259,8 +279,38 @@ pa_status_t pa_bm_fork(pa_block_manager_t *bm, int64_t parent, int64_t child);
  * a copy-on-write pair.  PA_E_NO_BLOCKS (nothing changed) when the free list is
  * short. */
 pa_status_t pa_bm_append(pa_block_manager_t *bm, int64_t req, const int32_t *tokens, int32_t n);
-/* Drop `req`: its blocks lose a reference each. */
+/* Drop `req`: its device blocks lose a reference each, its host slots are freed. */
 pa_status_t pa_bm_release(pa_block_manager_t *bm, int64_t req);
+
+/* ---- Swapping ([P1] PagedAttention: under memory pressure a request's pages
+ * go out to CPU memory and come back when it runs again). ----
+ * pa_bm_swap_out moves every block `req` holds alone to a host slot (queued as
+ * a (device block, host slot) pair) and frees those device blocks; blocks it
+ * shares with other requests stay on the device.  *moved (may be NULL) gets the
+ * number of blocks moved.  The request must have all its tokens written; until
+ * pa_bm_swap_in it cannot be appended, forked or stepped.  pa_bm_swap_in takes
+ * fresh device blocks for its host slots (queued as (host slot, device block)
+ * pairs).  A request moves at most once between two steps (PA_E_ARG otherwise);
+ * PA_E_NO_BLOCKS (nothing changed) when slots or blocks are short.
+ * Before pa_bm_step, pa_bm_swaps hands out the queued pairs (pa_bm_step refuses
+ * while any are queued); the step's device work is then: kv_swap(host pool <-
+ * device pool, out pairs), kv_swap(device pool <- host pool, in pairs),
+ * kv_block_copy, the K/V writes, attention. */
+pa_status_t pa_bm_swap_out(pa_block_manager_t *bm, int64_t req, int32_t *moved);
+pa_status_t pa_bm_swap_in(pa_block_manager_t *bm, int64_t req);
+/* *req = the resident request that the fewest recent steps listed (least
+ * recently used; ties to the smaller id) among those with all tokens written
+ * and not moved since the last step.  PA_E_NO_BLOCKS if there is none. */
+pa_status_t pa_bm_lru(const pa_block_manager_t *bm, int64_t *req);
+/* Where `req`'s logical blocks are: device_blocks[i] (-1 if in a host slot) and
+ * host_slots[i] (-1 if on the device), *num_blocks entries. */
+pa_status_t pa_bm_blocks(const pa_block_manager_t *bm, int64_t req, int32_t *device_blocks,
+                         int32_t *host_slots, int32_t max_blocks, int32_t *num_blocks);
+/* Hand out (and clear) the queued swap pairs: out_pairs [max_out][2] (device
+ * block, host slot), in_pairs [max_in][2] (host slot, device block).  PA_E_ARG
+ * (nothing changed) if either has too little room. */
+pa_status_t pa_bm_swaps(pa_block_manager_t *bm, int32_t *out_pairs, int32_t max_out,
+                        int32_t *num_out, int32_t *in_pairs, int32_t max_in, int32_t *num_in);
 /* The host arrays of one step over the n distinct requests `reqs`, each with at
  * least one token not yet written; those tokens are its query rows:
  *   block_tables    int32 [n][max_blocks_per_seq], -1 past each request's blocks
@@ -269,8 +319,9 @@ pa_status_t pa_bm_release(pa_block_manager_t *bm, int64_t req);
  *   copy_pairs      int32 [max_pairs][2]: every copy-on-write pair queued since
  *                   the last step, then *num_pairs = their count (may be NULL
  *                   when none are queued).  The queue is emptied.
- * PA_E_ARG (nothing changed) for an unknown or repeated request, one with no new
- * token or more than max_blocks_per_seq blocks, or too little pair room. */
+ * PA_E_ARG (nothing changed) for an unknown, repeated or swapped-out request,
+ * one with no new token or more than max_blocks_per_seq blocks, too little pair
+ * room, or swap pairs not yet handed out by pa_bm_swaps. */
 pa_status_t pa_bm_step(pa_block_manager_t *bm, const int64_t *reqs, int32_t n,
                        int32_t max_blocks_per_seq, int32_t *block_tables, int32_t *seq_lens,
                        int32_t *query_start_loc, int32_t *copy_pairs, int32_t max_pairs,

@@ -24,6 +24,7 @@ from .paged_attention import (  # noqa: F401
     cache_write,
     quantised_cache_write,
     block_copy,
+    swap_blocks,
 )
 from .codec import (  # noqa: F401
     e4m3fn_decode,

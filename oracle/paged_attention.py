@@ -249,3 +249,26 @@ def block_copy(k_pool, v_pool, pairs, k_scale=None, v_scale=None):
         new[dsts] = src_data
         outs.append(new)
     return tuple(outs)
+
+
+def swap_blocks(dst, src, pairs):
+    """Move blocks between two pools of one geometry (uml.org.cn "PagedAttention":
+    under memory pressure a request's pages go out to CPU memory and come back
+    when it runs again).
+
+    ``dst`` and ``src`` are ``(k, v, k_scale, v_scale)`` tuples (scales None for
+    pools without them).  For each ``(s, d)`` pair, every kv head's K and V tile
+    of block ``s`` of ``src``, and its scales, becomes block ``d`` of ``dst``.
+    Returns the new ``dst`` tuple; ``src`` is left as it is.
+    """
+    pairs = np.asarray(pairs).reshape(-1, 2)
+    out = []
+    for a_dst, a_src in zip(dst, src):
+        if a_dst is None:
+            out.append(None)
+            continue
+        new = np.array(a_dst, copy=True)
+        for s, d in pairs:
+            new[int(d)] = a_src[int(s)]
+        out.append(new)
+    return tuple(out)

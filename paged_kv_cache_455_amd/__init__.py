@@ -18,7 +18,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "KVPool", "PA_POOL_SHARED_BLOCKS", "PagedAttentionError", "BlockManager", "library_path", "load_library",
+    "KVPool", "PA_POOL_SHARED_BLOCKS", "PagedAttentionError", "BlockManager", "kv_swap", "library_path", "load_library",
     "pa_slot_mapping", "kv_cache_write", "kv_cache_write_quant", "kv_block_copy", "pa_decode",
     "pa_prefill_chunk",
     "pa_decode_workspace_size", "pa_prefill_workspace_size", "PA_DTYPE",
@@ -72,7 +72,17 @@ _SIGS = {
                              _c.c_int32, _c.c_void_p, _c.c_int32, _c.c_int32, _c.c_int32,
                              _c.c_float, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "pa_prefill_workspace_size": (_c.c_size_t, [_c.c_int32] * 8),
-    "pa_bm_create": (_c.c_void_p, [_c.c_int32]),
+    "pa_bm_create": (_c.c_void_p, [_c.c_int32, _c.c_int32]),
+    "pa_bm_num_free_host": (_c.c_int32, [_c.c_void_p]),
+    "pa_bm_swap_out": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_void_p]),
+    "pa_bm_swap_in": (_c.c_int, [_c.c_void_p, _c.c_int64]),
+    "pa_bm_lru": (_c.c_int, [_c.c_void_p, _c.c_void_p]),
+    "pa_bm_blocks": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_void_p, _c.c_void_p, _c.c_int32,
+                                _c.c_void_p]),
+    "pa_bm_swaps": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_int32, _c.c_void_p, _c.c_void_p,
+                               _c.c_int32, _c.c_void_p]),
+    "kv_swap": (_c.c_int, [_c.POINTER(_Pool), _c.POINTER(_Pool), _c.c_void_p, _c.c_int32,
+                           _c.c_void_p]),
     "pa_bm_destroy": (None, [_c.c_void_p]),
     "pa_bm_num_free": (_c.c_int32, [_c.c_void_p]),
     "pa_bm_refcount": (_c.c_int32, [_c.c_void_p, _c.c_int32]),
@@ -207,6 +217,15 @@ def kv_block_copy(pool: KVPool, src_dst, stream=None):
         pool.ref(), _ptr(src_dst), int(src_dst.shape[0]), _stream(pool.k, stream)))
 
 
+def kv_swap(dst: KVPool, src: KVPool, src_dst, stream=None):
+    """Copy blocks src -> dst between two pools of one geometry; either pool may
+    live in pinned host memory (``pin_memory=True``), src_dst too."""
+    lib = load_library()
+    dev = dst.k if dst.k.is_cuda else src.k
+    _check("kv_swap", lib.kv_swap(dst.ref(), src.ref(), _ptr(src_dst), int(src_dst.shape[0]),
+                                  _stream(dev, stream)))
+
+
 def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len) -> int:
     return int(load_library().pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads,
                                                        head_dim, max_context_len))
@@ -268,13 +287,14 @@ class BlockManager:
     reference counts, copy-on-write and the per-step host arrays.  Marshalling
     only; the bookkeeping runs in the library."""
 
-    def __init__(self, num_blocks: int):
+    def __init__(self, num_blocks: int, num_host_blocks: int = 0):
         lib = load_library()
         self._lib = lib
-        self._h = lib.pa_bm_create(int(num_blocks))
+        self._h = lib.pa_bm_create(int(num_blocks), int(num_host_blocks))
         if not self._h:
-            raise PagedAttentionError("pa_bm_create", 1, "bad num_blocks or out of memory")
+            raise PagedAttentionError("pa_bm_create", 1, "bad block counts or out of memory")
         self.num_blocks = int(num_blocks)
+        self.num_host_blocks = int(num_host_blocks)
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -290,6 +310,47 @@ class BlockManager:
 
     def num_free(self) -> int:
         return int(self._lib.pa_bm_num_free(self._h))
+
+    def num_free_host(self) -> int:
+        return int(self._lib.pa_bm_num_free_host(self._h))
+
+    def swap_out(self, req: int) -> int:
+        """Move the blocks ``req`` holds alone to host slots; returns how many."""
+        moved = ctypes.c_int32(0)
+        _check("pa_bm_swap_out", self._lib.pa_bm_swap_out(self._h, int(req), ctypes.byref(moved)))
+        return int(moved.value)
+
+    def swap_in(self, req: int):
+        _check("pa_bm_swap_in", self._lib.pa_bm_swap_in(self._h, int(req)))
+
+    def lru(self) -> int:
+        r = ctypes.c_int64(0)
+        _check("pa_bm_lru", self._lib.pa_bm_lru(self._h, ctypes.byref(r)))
+        return int(r.value)
+
+    def blocks(self, req: int, max_blocks: int = 4096):
+        """(device_blocks, host_slots) of ``req``'s logical blocks, -1 where absent."""
+        import numpy as np
+        dev = np.zeros(max_blocks, dtype=np.int32)
+        host = np.zeros(max_blocks, dtype=np.int32)
+        n = ctypes.c_int32(0)
+        vp = lambda x: x.ctypes.data_as(ctypes.c_void_p)
+        _check("pa_bm_blocks", self._lib.pa_bm_blocks(self._h, int(req), vp(dev), vp(host),
+                                                      int(max_blocks), ctypes.byref(n)))
+        return dev[:n.value].copy(), host[:n.value].copy()
+
+    def swaps(self, max_pairs: int = 4096):
+        """Queued (out_pairs, in_pairs): out (device block, host slot), in (host
+        slot, device block); to run before the next step's copies."""
+        import numpy as np
+        out = np.zeros((max(max_pairs, 1), 2), dtype=np.int32)
+        inn = np.zeros((max(max_pairs, 1), 2), dtype=np.int32)
+        no, ni = ctypes.c_int32(0), ctypes.c_int32(0)
+        vp = lambda x: x.ctypes.data_as(ctypes.c_void_p)
+        _check("pa_bm_swaps", self._lib.pa_bm_swaps(self._h, vp(out), int(max_pairs),
+                                                    ctypes.byref(no), vp(inn), int(max_pairs),
+                                                    ctypes.byref(ni)))
+        return out[:no.value].copy(), inn[:ni.value].copy()
 
     def refcount(self, block: int) -> int:
         return int(self._lib.pa_bm_refcount(self._h, int(block)))

@@ -265,15 +265,71 @@ pa_status_t kv_block_copy(const pa_kv_pool_t *pool, const int32_t *src_dst, int3
   if (num_pairs == 0) return PA_OK;
   if (!src_dst) return fail(PA_E_ARG, "src_dst is NULL");
   pa::BlockCopyArgs a{};
-  a.k = pool->k;
-  a.v = pool->v;
-  a.k_scale = pool->k_scale;
-  a.v_scale = pool->v_scale;
+  a.src_k = a.dst_k = pool->k;
+  a.src_v = a.dst_v = pool->v;
+  a.src_ks = a.dst_ks = pool->k_scale;
+  a.src_vs = a.dst_vs = pool->v_scale;
   a.pairs = src_dst;
   a.num_pairs = num_pairs;
   a.num_kv_heads = pool->num_kv_heads;
   a.tile_bytes = kBlockTokens * pool->head_dim * elem_bytes(pool->kv_dtype);
   return hip_status(pa::launch_block_copy(a, stream), "kv_block_copy launch");
+}
+
+// The address a kernel uses for p: p itself for device (or managed) memory, the
+// mapped device address for pinned host memory; pageable host memory is refused.
+static pa_status_t device_address(const void *p, const char *what, void **out) {
+  *out = nullptr;
+  if (p == nullptr) return PA_OK;
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PA_E_ARG, "%s is neither device memory nor pinned host memory", what);
+  }
+  if (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged) {
+    *out = const_cast<void *>(p);
+  } else if (at.type == hipMemoryTypeHost && at.devicePointer != nullptr) {
+    *out = at.devicePointer;
+  } else {
+    return fail(PA_E_ARG, "%s is neither device memory nor pinned host memory", what);
+  }
+  return PA_OK;
+}
+
+pa_status_t kv_swap(const pa_kv_pool_t *dst, const pa_kv_pool_t *src, const int32_t *src_dst,
+                    int32_t num_pairs, hipStream_t stream) {
+  pa_status_t st = check_pool(dst, true);
+  if (st != PA_OK) return st;
+  if ((st = check_pool(src, true)) != PA_OK) return st;
+  if (dst->kv_dtype != src->kv_dtype || dst->num_kv_heads != src->num_kv_heads ||
+      dst->head_dim != src->head_dim)
+    return fail(PA_E_ARG, "kv_swap pools differ in kv_dtype, num_kv_heads or head_dim");
+  if (num_pairs < 0) return fail(PA_E_ARG, "num_pairs must be >= 0");
+  if (num_pairs == 0) return PA_OK;
+  if (!src_dst) return fail(PA_E_ARG, "src_dst is NULL");
+  void *p[8];
+  const void *in[8] = {src->k, src->v, src->k_scale, src->v_scale,
+                       dst->k, dst->v, dst->k_scale, dst->v_scale};
+  static const char *names[8] = {"src k", "src v", "src k_scale", "src v_scale",
+                                 "dst k", "dst v", "dst k_scale", "dst v_scale"};
+  for (int i = 0; i < 8; ++i)
+    if ((st = device_address(in[i], names[i], &p[i])) != PA_OK) return st;
+  void *pairs_dev;
+  if ((st = device_address(src_dst, "src_dst", &pairs_dev)) != PA_OK) return st;
+  pa::BlockCopyArgs a{};
+  a.src_k = p[0];
+  a.src_v = p[1];
+  a.src_ks = static_cast<const float *>(p[2]);
+  a.src_vs = static_cast<const float *>(p[3]);
+  a.dst_k = p[4];
+  a.dst_v = p[5];
+  a.dst_ks = static_cast<float *>(p[6]);
+  a.dst_vs = static_cast<float *>(p[7]);
+  a.pairs = static_cast<const int32_t *>(pairs_dev);
+  a.num_pairs = num_pairs;
+  a.num_kv_heads = src->num_kv_heads;
+  a.tile_bytes = kBlockTokens * src->head_dim * elem_bytes(src->kv_dtype);
+  return hip_status(pa::launch_block_copy(a, stream), "kv_swap launch");
 }
 
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,

@@ -24,6 +24,17 @@
 //    neither forked nor a cache hit (nor a source) before the step; a source whose
 //    last reference goes waits for the step before it is free again; a
 //    destination whose last reference goes takes its pair with it.
+//
+// Swapping (uml.org.cn "PagedAttention": under memory pressure a request's pages
+// go out to CPU memory and come back when it runs again) moves the blocks a
+// request holds alone to slots of a host pool, and back into fresh device blocks.
+// Blocks it shares stay on the device, held by it as before.  A step's device
+// work then starts with the swap-outs and the swap-ins (pa_bm_swaps hands them
+// out), in that order, before the copy-on-write pairs: a swap-out source freed in
+// the phase may be taken again by a swap-in, a copy or a write, all of which run
+// after it; a host slot a swap-in reads stays off the host free list until the
+// step; a request moves at most once between two steps.  The least recently
+// stepped resident request is offered as the victim (pa_bm_lru).
 #include <stdint.h>
 #include <stdlib.h>
 
@@ -60,11 +71,15 @@ uint64_t chain(uint64_t prev, const int32_t *tokens16) {
 constexpr uint64_t kSeed = 0x6a09e667f3bcc909ull;
 
 struct Request {
-  std::vector<int32_t> blocks;  // physical block ids, logical order
+  std::vector<int32_t> blocks;  // device block ids, logical order (-1: in a host slot)
+  std::vector<int32_t> host;    // host slot of each logical block (-1: on the device)
   std::vector<int32_t> tokens;  // every token so far
   int32_t written = 0;          // leading tokens whose K/V a handed-out step writes
   int32_t published = 0;        // leading full blocks already offered to the cache
   uint64_t hash = kSeed;        // prefix hash through block `published - 1`
+  bool swapped = false;         // swapped out: not runnable until swapped in
+  bool moved = false;           // swapped out or in since the last step
+  int64_t stamp = 0;            // the last step that listed it (LRU order)
 };
 
 struct Pair {
@@ -84,6 +99,13 @@ struct pa_block_manager {
   std::unordered_map<int64_t, Request> reqs;
   std::vector<Pair> pending;            // copy-on-write pairs for the next step
   std::vector<int32_t> held;            // freed pending sources, free after the step
+  int32_t num_host = 0;
+  std::vector<int32_t> host_free;       // stack of free host slots
+  std::vector<int32_t> host_held;       // host slots read by pending swap-ins
+  std::vector<Pair> swap_out;           // (device block, host slot) for the next step
+  std::vector<Pair> swap_in;            // (host slot, device block) for the next step
+  std::vector<int64_t> moved_reqs;      // requests with `moved` set
+  int64_t steps = 0;
 
   int32_t take() {
     const int32_t b = free_list.back();
@@ -103,10 +125,14 @@ struct pa_block_manager {
         held.push_back(b);
         return;
       }
-    pending.erase(std::remove_if(pending.begin(), pending.end(),
-                                 [b](const Pair &p) { return p.dst == b; }),
-                  pending.end());
+    const auto to_b = [b](const Pair &p) { return p.dst == b; };
+    pending.erase(std::remove_if(pending.begin(), pending.end(), to_b), pending.end());
+    swap_in.erase(std::remove_if(swap_in.begin(), swap_in.end(), to_b), swap_in.end());
     free_list.push_back(b);
+  }
+  void mark_moved(int64_t id, Request &r) {
+    r.moved = true;
+    moved_reqs.push_back(id);
   }
   // offer request r's full blocks to the prefix cache (first holder of a hash wins)
   void publish(Request &r) {
@@ -143,8 +169,10 @@ struct pa_block_manager {
       drop(src);  // still referenced by the other holders
     }
     for (int32_t i = 0; i < n; ++i) {
-      if ((int32_t)r.tokens.size() == (int32_t)r.blocks.size() * kBlockSize)
+      if ((int32_t)r.tokens.size() == (int32_t)r.blocks.size() * kBlockSize) {
         r.blocks.push_back(take());
+        r.host.push_back(-1);
+      }
       r.tokens.push_back(tokens[i]);
     }
     return PA_OK;
@@ -153,8 +181,8 @@ struct pa_block_manager {
 
 extern "C" {
 
-pa_block_manager_t *pa_bm_create(int32_t num_blocks) {
-  if (num_blocks <= 0) return nullptr;
+pa_block_manager_t *pa_bm_create(int32_t num_blocks, int32_t num_host_blocks) {
+  if (num_blocks <= 0 || num_host_blocks < 0) return nullptr;
   pa_block_manager *bm = new (std::nothrow) pa_block_manager();
   if (bm == nullptr) return nullptr;
   try {
@@ -165,6 +193,9 @@ pa_block_manager_t *pa_bm_create(int32_t num_blocks) {
     bm->cached_hash.assign(num_blocks, 0);
     bm->cached_parent.assign(num_blocks, -1);
     bm->cached_tokens.resize(num_blocks);
+    bm->num_host = num_host_blocks;
+    bm->host_free.resize(num_host_blocks);
+    for (int32_t i = 0; i < num_host_blocks; ++i) bm->host_free[i] = num_host_blocks - 1 - i;
   } catch (const std::bad_alloc &) {
     delete bm;
     return nullptr;
@@ -176,6 +207,10 @@ void pa_bm_destroy(pa_block_manager_t *bm) { delete bm; }
 
 int32_t pa_bm_num_free(const pa_block_manager_t *bm) {
   return bm ? (int32_t)bm->free_list.size() : -1;
+}
+
+int32_t pa_bm_num_free_host(const pa_block_manager_t *bm) {
+  return bm ? (int32_t)bm->host_free.size() : -1;
 }
 
 int32_t pa_bm_refcount(const pa_block_manager_t *bm, int32_t block) {
@@ -212,6 +247,8 @@ pa_status_t pa_bm_add(pa_block_manager_t *bm, int64_t req, const int32_t *tokens
   for (int32_t b : shared) ++bm->refs[b];
   Request r;
   r.blocks = shared;
+  r.host.assign(shared.size(), -1);
+  r.stamp = bm->steps;
   r.tokens.assign(tokens, tokens + (size_t)hit * kBlockSize);
   r.written = hit * kBlockSize;
   r.published = hit;
@@ -227,9 +264,11 @@ pa_status_t pa_bm_fork(pa_block_manager_t *bm, int64_t parent, int64_t child) {
   auto it = bm->reqs.find(parent);
   if (it == bm->reqs.end()) return pa::set_error(PA_E_ARG, "pa_bm_fork: unknown parent");
   if (bm->reqs.count(child)) return pa::set_error(PA_E_ARG, "pa_bm_fork: child id in use");
+  if (it->second.swapped) return pa::set_error(PA_E_ARG, "pa_bm_fork: the parent is swapped out");
   if (it->second.written != (int32_t)it->second.tokens.size())
     return pa::set_error(PA_E_ARG, "pa_bm_fork: the parent has tokens no step has written yet");
   Request c = it->second;
+  c.moved = false;
   for (int32_t b : c.blocks) ++bm->refs[b];
   bm->reqs.emplace(child, std::move(c));
   return PA_OK;
@@ -239,6 +278,7 @@ pa_status_t pa_bm_append(pa_block_manager_t *bm, int64_t req, const int32_t *tok
   if (!bm || n < 0 || (!tokens && n > 0)) return pa::set_error(PA_E_ARG, "pa_bm_append: bad argument");
   auto it = bm->reqs.find(req);
   if (it == bm->reqs.end()) return pa::set_error(PA_E_ARG, "pa_bm_append: unknown request");
+  if (it->second.swapped) return pa::set_error(PA_E_ARG, "pa_bm_append: request is swapped out");
   return bm->append(it->second, tokens, n);
 }
 
@@ -246,8 +286,133 @@ pa_status_t pa_bm_release(pa_block_manager_t *bm, int64_t req) {
   if (!bm) return pa::set_error(PA_E_ARG, "pa_bm_release: NULL manager");
   auto it = bm->reqs.find(req);
   if (it == bm->reqs.end()) return pa::set_error(PA_E_ARG, "pa_bm_release: unknown request");
-  for (int32_t b : it->second.blocks) bm->drop(b);
+  const Request &r = it->second;
+  for (size_t i = 0; i < r.blocks.size(); ++i) {
+    if (r.host[i] < 0) {
+      bm->drop(r.blocks[i]);
+      continue;
+    }
+    const int32_t h = r.host[i];  // its swap-out, if still pending, is not needed now
+    bm->swap_out.erase(std::remove_if(bm->swap_out.begin(), bm->swap_out.end(),
+                                      [h](const Pair &p) { return p.dst == h; }),
+                       bm->swap_out.end());
+    bm->host_free.push_back(h);
+  }
   bm->reqs.erase(it);
+  return PA_OK;
+}
+
+pa_status_t pa_bm_swap_out(pa_block_manager_t *bm, int64_t req, int32_t *moved) {
+  if (!bm) return pa::set_error(PA_E_ARG, "pa_bm_swap_out: NULL manager");
+  auto it = bm->reqs.find(req);
+  if (it == bm->reqs.end()) return pa::set_error(PA_E_ARG, "pa_bm_swap_out: unknown request");
+  Request &r = it->second;
+  if (r.swapped) return pa::set_error(PA_E_ARG, "pa_bm_swap_out: already swapped out");
+  if (r.moved) return pa::set_error(PA_E_ARG, "pa_bm_swap_out: request moved since the last step");
+  if (r.written != (int32_t)r.tokens.size())
+    return pa::set_error(PA_E_ARG, "pa_bm_swap_out: the request has tokens no step has written yet");
+  int32_t alone = 0;
+  for (int32_t b : r.blocks) alone += bm->refs[b] == 1;
+  if (alone > (int32_t)bm->host_free.size())
+    return pa::set_error(PA_E_NO_BLOCKS, "pa_bm_swap_out: %d host slots needed, %d free", alone,
+                         (int32_t)bm->host_free.size());
+  for (size_t i = 0; i < r.blocks.size(); ++i) {
+    const int32_t b = r.blocks[i];
+    if (bm->refs[b] != 1) continue;  // shared: stays on the device
+    const int32_t h = bm->host_free.back();
+    bm->host_free.pop_back();
+    bm->swap_out.push_back({b, h});
+    r.host[i] = h;
+    r.blocks[i] = -1;
+    bm->drop(b);
+  }
+  r.swapped = true;
+  bm->mark_moved(req, r);
+  if (moved) *moved = alone;
+  return PA_OK;
+}
+
+pa_status_t pa_bm_swap_in(pa_block_manager_t *bm, int64_t req) {
+  if (!bm) return pa::set_error(PA_E_ARG, "pa_bm_swap_in: NULL manager");
+  auto it = bm->reqs.find(req);
+  if (it == bm->reqs.end()) return pa::set_error(PA_E_ARG, "pa_bm_swap_in: unknown request");
+  Request &r = it->second;
+  if (!r.swapped) return pa::set_error(PA_E_ARG, "pa_bm_swap_in: not swapped out");
+  if (r.moved) return pa::set_error(PA_E_ARG, "pa_bm_swap_in: request moved since the last step");
+  int32_t out = 0;
+  for (int32_t h : r.host) out += h >= 0;
+  if (out > (int32_t)bm->free_list.size())
+    return pa::set_error(PA_E_NO_BLOCKS, "pa_bm_swap_in: %d device blocks needed, %d free", out,
+                         (int32_t)bm->free_list.size());
+  for (size_t i = 0; i < r.blocks.size(); ++i) {
+    const int32_t h = r.host[i];
+    if (h < 0) continue;
+    const int32_t d = bm->take();
+    bm->swap_in.push_back({h, d});
+    bm->host_held.push_back(h);
+    r.blocks[i] = d;
+    r.host[i] = -1;
+  }
+  r.swapped = false;
+  bm->mark_moved(req, r);
+  return PA_OK;
+}
+
+pa_status_t pa_bm_lru(const pa_block_manager_t *bm, int64_t *req) {
+  if (!bm || !req) return pa::set_error(PA_E_ARG, "pa_bm_lru: bad argument");
+  bool found = false;
+  int64_t best = 0, best_stamp = 0;
+  for (const auto &kv : bm->reqs) {
+    const Request &r = kv.second;
+    if (r.swapped || r.moved || r.written != (int32_t)r.tokens.size()) continue;
+    if (!found || r.stamp < best_stamp || (r.stamp == best_stamp && kv.first < best)) {
+      found = true;
+      best = kv.first;
+      best_stamp = r.stamp;
+    }
+  }
+  if (!found) return pa::set_error(PA_E_NO_BLOCKS, "pa_bm_lru: no resident request to swap out");
+  *req = best;
+  return PA_OK;
+}
+
+pa_status_t pa_bm_blocks(const pa_block_manager_t *bm, int64_t req, int32_t *device_blocks,
+                         int32_t *host_slots, int32_t max_blocks, int32_t *num_blocks) {
+  if (!bm || !num_blocks || max_blocks < 0) return pa::set_error(PA_E_ARG, "pa_bm_blocks: bad argument");
+  auto it = bm->reqs.find(req);
+  if (it == bm->reqs.end()) return pa::set_error(PA_E_ARG, "pa_bm_blocks: unknown request");
+  const Request &r = it->second;
+  const int32_t n = (int32_t)r.blocks.size();
+  if (n > max_blocks || (n > 0 && (!device_blocks || !host_slots)))
+    return pa::set_error(PA_E_ARG, "pa_bm_blocks: %d blocks, room for %d", n, max_blocks);
+  for (int32_t i = 0; i < n; ++i) {
+    device_blocks[i] = r.blocks[i];
+    host_slots[i] = r.host[i];
+  }
+  *num_blocks = n;
+  return PA_OK;
+}
+
+pa_status_t pa_bm_swaps(pa_block_manager_t *bm, int32_t *out_pairs, int32_t max_out,
+                        int32_t *num_out, int32_t *in_pairs, int32_t max_in, int32_t *num_in) {
+  if (!bm || !num_out || !num_in || max_out < 0 || max_in < 0)
+    return pa::set_error(PA_E_ARG, "pa_bm_swaps: bad argument");
+  const int32_t no = (int32_t)bm->swap_out.size(), ni = (int32_t)bm->swap_in.size();
+  if (no > max_out || ni > max_in || (no > 0 && !out_pairs) || (ni > 0 && !in_pairs))
+    return pa::set_error(PA_E_ARG, "pa_bm_swaps: %d out / %d in pairs pending, room for %d / %d",
+                         no, ni, max_out, max_in);
+  for (int32_t i = 0; i < no; ++i) {
+    out_pairs[2 * i] = bm->swap_out[i].src;
+    out_pairs[2 * i + 1] = bm->swap_out[i].dst;
+  }
+  for (int32_t i = 0; i < ni; ++i) {
+    in_pairs[2 * i] = bm->swap_in[i].src;
+    in_pairs[2 * i + 1] = bm->swap_in[i].dst;
+  }
+  *num_out = no;
+  *num_in = ni;
+  bm->swap_out.clear();
+  bm->swap_in.clear();
   return PA_OK;
 }
 
@@ -258,6 +423,8 @@ pa_status_t pa_bm_step(pa_block_manager_t *bm, const int64_t *reqs, int32_t n,
   if (!bm || n < 0 || max_blocks_per_seq <= 0 || max_pairs < 0 || !num_pairs ||
       !query_start_loc || (n > 0 && (!reqs || !block_tables || !seq_lens)))
     return pa::set_error(PA_E_ARG, "pa_bm_step: bad argument");
+  if (!bm->swap_out.empty() || !bm->swap_in.empty())
+    return pa::set_error(PA_E_ARG, "pa_bm_step: swap pairs pending; pa_bm_swaps hands them out first");
   const int32_t pairs = (int32_t)bm->pending.size();
   if (pairs > max_pairs || (pairs > 0 && !copy_pairs))
     return pa::set_error(PA_E_ARG, "pa_bm_step: %d copy pairs pending, room for %d", pairs,
@@ -269,6 +436,7 @@ pa_status_t pa_bm_step(pa_block_manager_t *bm, const int64_t *reqs, int32_t n,
     if (!seen.insert(reqs[i]).second)
       return pa::set_error(PA_E_ARG, "pa_bm_step: request listed twice");
     const Request &r = it->second;
+    if (r.swapped) return pa::set_error(PA_E_ARG, "pa_bm_step: request is swapped out");
     if ((int32_t)r.blocks.size() > max_blocks_per_seq)
       return pa::set_error(PA_E_ARG, "pa_bm_step: request needs %d blocks > %d",
                            (int32_t)r.blocks.size(), max_blocks_per_seq);
@@ -276,8 +444,10 @@ pa_status_t pa_bm_step(pa_block_manager_t *bm, const int64_t *reqs, int32_t n,
       return pa::set_error(PA_E_ARG, "pa_bm_step: request has no new token");
   }
   int32_t q = 0;
+  ++bm->steps;
   for (int32_t i = 0; i < n; ++i) {
     Request &r = bm->reqs.find(reqs[i])->second;
+    r.stamp = bm->steps;
     int32_t *row = block_tables + (int64_t)i * max_blocks_per_seq;
     for (int32_t j = 0; j < max_blocks_per_seq; ++j)
       row[j] = j < (int32_t)r.blocks.size() ? r.blocks[j] : -1;
@@ -297,6 +467,13 @@ pa_status_t pa_bm_step(pa_block_manager_t *bm, const int64_t *reqs, int32_t n,
   bm->pending.clear();
   for (int32_t b : bm->held) bm->free_list.push_back(b);
   bm->held.clear();
+  for (int32_t h : bm->host_held) bm->host_free.push_back(h);
+  bm->host_held.clear();
+  for (int64_t id : bm->moved_reqs) {
+    auto it = bm->reqs.find(id);
+    if (it != bm->reqs.end()) it->second.moved = false;
+  }
+  bm->moved_reqs.clear();
   return PA_OK;
 }
 

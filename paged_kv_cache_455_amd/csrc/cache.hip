@@ -161,13 +161,15 @@ __global__ __launch_bounds__(256) void kv_block_copy_kernel(BlockCopyArgs a, int
     const int64_t c = r % per_blk;
     const int64_t src_b = a.pairs[2 * pair];
     const int64_t dst_b = a.pairs[2 * pair + 1];
-    char *base = reinterpret_cast<char *>(is_v ? a.v : a.k);
+    const char *src = reinterpret_cast<const char *>(is_v ? a.src_v : a.src_k);
+    char *dst = reinterpret_cast<char *>(is_v ? a.dst_v : a.dst_k);
     const int64_t blk_bytes = per_blk * 16;
-    *reinterpret_cast<u32x4 *>(base + dst_b * blk_bytes + c * 16) =
-        *reinterpret_cast<const u32x4 *>(base + src_b * blk_bytes + c * 16);
-    float *sc = is_v ? a.v_scale : a.k_scale;
-    if (sc != nullptr && c < a.num_kv_heads)
-      sc[dst_b * a.num_kv_heads + c] = sc[src_b * a.num_kv_heads + c];
+    *reinterpret_cast<u32x4 *>(dst + dst_b * blk_bytes + c * 16) =
+        *reinterpret_cast<const u32x4 *>(src + src_b * blk_bytes + c * 16);
+    const float *ss = is_v ? a.src_vs : a.src_ks;
+    float *ds = is_v ? a.dst_vs : a.dst_ks;
+    if (ds != nullptr && c < a.num_kv_heads)
+      ds[dst_b * a.num_kv_heads + c] = ss[src_b * a.num_kv_heads + c];
   }
 }
 

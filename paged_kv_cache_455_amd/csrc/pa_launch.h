@@ -63,11 +63,18 @@ struct CacheWriteArgs {
   int32_t row_bytes;  // head_dim * element bytes
 };
 
+// Block tiles (and scales) copied from one pool to another of the same geometry;
+// the same pool on both sides is the copy-on-write case.  Any of the pointers may
+// be device addresses of pinned host memory.
 struct BlockCopyArgs {
-  void *k;
-  void *v;
-  float *k_scale;
-  float *v_scale;
+  const void *src_k;
+  const void *src_v;
+  const float *src_ks;
+  const float *src_vs;
+  void *dst_k;
+  void *dst_v;
+  float *dst_ks;
+  float *dst_vs;
   const int32_t *pairs;
   int32_t num_pairs;
   int32_t num_kv_heads;

@@ -37,7 +37,9 @@ def test_header_declares_the_entry_points():
               "pa_slot_mapping", "pa_decode_workspace_size", "pa_prefill_workspace_size",
               "pa_status_string", "pa_last_error", "pa_version",
               "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free", "pa_bm_refcount", "pa_bm_add",
-              "pa_bm_fork", "pa_bm_append", "pa_bm_release", "pa_bm_step"):
+              "pa_bm_fork", "pa_bm_append", "pa_bm_release", "pa_bm_step", "pa_bm_num_free_host",
+              "pa_bm_swap_out", "pa_bm_swap_in", "pa_bm_lru", "pa_bm_blocks", "pa_bm_swaps",
+              "kv_swap"):
         assert n in names, n
 
 

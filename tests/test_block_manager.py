@@ -33,14 +33,36 @@ def lib():
 
 
 class DevicePoolModel:
-    """The device side of the step protocol on a pool of prefix ids."""
+    """The device side of the step protocol on pools of prefix ids."""
 
-    def __init__(self, num_blocks):
+    def __init__(self, num_blocks, num_host=0):
         self.cells = [[None] * BS for _ in range(num_blocks)]
+        self.host = [[None] * BS for _ in range(num_host)]
         self.prefix_ids = {}
 
     def pid(self, prefix):
         return self.prefix_ids.setdefault(tuple(prefix), len(self.prefix_ids))
+
+    def swap(self, out_pairs, in_pairs):
+        """Swap-outs (device -> host), then swap-ins (host -> device)."""
+        assert len({int(p[1]) for p in out_pairs}) == len(out_pairs), "host slot written twice"
+        for b, h in out_pairs:
+            self.host[h] = list(self.cells[b])
+        assert len({int(p[1]) for p in in_pairs}) == len(in_pairs), "device block written twice"
+        assert not {int(p[0]) for p in in_pairs} & {int(p[1]) for p in out_pairs}, \
+            "a swap-in reads a host slot this step's swap-outs write"
+        for h, b in in_pairs:
+            self.cells[b] = list(self.host[h])
+
+    def read_back(self, bm, r, toks):
+        """Every written row of request r, found on the device or in a host slot."""
+        dev, host = bm.blocks(r)
+        assert len(dev) == -(-len(toks) // BS)
+        for pos in range(len(toks)):
+            i = pos // BS
+            cell = self.cells[dev[i]] if dev[i] >= 0 else self.host[host[i]]
+            assert (dev[i] >= 0) != (host[i] >= 0)
+            assert cell[pos % BS] == self.pid(toks[:pos + 1]), (r, pos, dev[i], host[i])
 
     def run_step(self, reqs, history, bt, lens, qsl, pairs):
         srcs, dsts = [int(p[0]) for p in pairs], [int(p[1]) for p in pairs]
@@ -344,3 +366,206 @@ def test_accounting_after_every_step():
             tables[r] = list(bt[0][bt[0] >= 0])
         if not full:
             check_accounting(bm, tables)
+
+
+def _write_prompt(bm, model, hist, reqs):
+    out, inn = bm.swaps()
+    model.swap(out, inn)
+    bt, lens, qsl, pairs = bm.step(reqs, 64)
+    model.run_step(reqs, hist, bt, lens, qsl, pairs)
+
+
+def test_swap_out_moves_only_blocks_held_alone():
+    bm = pa.BlockManager(10, 6)
+    model = DevicePoolModel(10, 6)
+    hist = {1: list(range(40))}                    # blocks A, B full, C with 8 rows
+    bm.add(1, hist[1])
+    _write_prompt(bm, model, hist, [1])
+    bm.fork(1, 2)
+    hist[2] = list(hist[1])
+    assert bm.swap_out(2) == 0                     # every block shared: nothing moves
+    _write_prompt(bm, model, hist, [])
+    bm.swap_in(2)
+    bm.append(1, [5])                              # 1 moves to a copy C' of C
+    hist[1] += [5]
+    _write_prompt(bm, model, hist, [1])
+    a, b, c1 = bm.blocks(1)[0]
+    assert bm.swap_out(1) == 1 and bm.num_free_host() == 5
+    dev, host = bm.blocks(1)
+    assert list(dev) == [a, b, -1] and list(host[:2]) == [-1, -1] and host[2] >= 0
+    out, inn = bm.swaps()
+    assert [list(p) for p in out] == [[c1, host[2]]] and len(inn) == 0
+    model.swap(out, inn)
+    model.read_back(bm, 1, hist[1])
+    model.read_back(bm, 2, hist[2])
+    bm.step([], 64)
+    assert bm.refcount(a) == 2 and bm.refcount(c1) == 0
+
+
+def test_swap_round_trip_keeps_the_rows():
+    bm = pa.BlockManager(12, 8)
+    model = DevicePoolModel(12, 8)
+    hist = {1: list(range(50)), 2: list(range(100, 120))}
+    bm.add(1, hist[1])
+    bm.add(2, hist[2])
+    _write_prompt(bm, model, hist, [1, 2])
+    before = list(bm.blocks(1)[0])
+    assert bm.swap_out(1) == 4 and bm.num_free() == 12 - 2
+    out, inn = bm.swaps()
+    model.swap(out, inn)
+    bm.step([], 64)
+    model.read_back(bm, 1, hist[1])
+    # other requests may now reuse the freed device blocks
+    hist[3] = list(range(200, 264))
+    bm.add(3, hist[3])
+    _write_prompt(bm, model, hist, [3])
+    assert set(bm.blocks(3)[0]) & set(before)
+    bm.release(3)
+    bm.swap_in(1)
+    bm.append(1, [9])
+    hist[1] += [9]
+    _write_prompt(bm, model, hist, [1])
+    model.read_back(bm, 1, hist[1])
+    assert bm.num_free_host() == 8
+
+
+def test_swap_rules():
+    bm = pa.BlockManager(10, 2)
+    bm.add(1, list(range(20)))
+    with pytest.raises(pa.PagedAttentionError):
+        bm.swap_out(1)                             # rows not written yet
+    bm.step([1], 64)
+    bm.add(2, list(range(100, 140)))
+    bm.step([2], 64)
+    with pytest.raises(pa.PagedAttentionError) as e:
+        bm.swap_out(2)                             # 3 blocks, 2 host slots
+    assert e.value.status == 5 and bm.num_free_host() == 2
+    bm.swap_out(1)
+    for call in (lambda: bm.swap_in(1),            # moved since the last step
+                 lambda: bm.swap_out(1),           # already out
+                 lambda: bm.append(1, [3]),
+                 lambda: bm.fork(1, 7),
+                 lambda: bm.step([2], 64)):        # swap pairs not handed out
+        with pytest.raises(pa.PagedAttentionError):
+            call()
+    out, inn = bm.swaps()
+    assert len(out) == 2 and len(inn) == 0
+    bm.append(2, [1])
+    with pytest.raises(pa.PagedAttentionError):
+        bm.step([1, 2], 64)                        # 1 is swapped out
+    bm.step([2], 64)
+    bm.swap_in(1)
+    with pytest.raises(pa.PagedAttentionError):
+        bm.swap_out(1)                             # moved since the last step
+    assert bm.num_free_host() == 0                 # read by the pending swap-in
+    bm.swaps()
+    bm.step([], 64)
+    assert bm.num_free_host() == 2
+
+
+def test_release_of_a_swapped_request_cancels_its_swap_out():
+    bm = pa.BlockManager(10, 4)
+    bm.add(1, list(range(30)))
+    bm.step([1], 64)
+    bm.swap_out(1)
+    bm.release(1)
+    out, inn = bm.swaps()
+    assert len(out) == 0 and len(inn) == 0 and bm.num_free_host() == 4 and bm.num_free() == 10
+
+
+def test_lru_picks_the_least_recently_stepped():
+    bm = pa.BlockManager(40, 40)
+    for r in (1, 2, 3):
+        bm.add(r, list(range(10 * r)))
+    bm.step([1, 2, 3], 64)
+    bm.append(2, [1])
+    bm.append(3, [1])
+    bm.step([2, 3], 64)
+    bm.append(3, [1])
+    bm.step([3], 64)
+    assert bm.lru() == 1
+    bm.swap_out(1)
+    assert bm.lru() == 2
+    bm.append(2, [5])                              # unwritten rows: not a victim
+    assert bm.lru() == 3
+    bm.swap_out(3)
+    with pytest.raises(pa.PagedAttentionError) as e:
+        bm.lru()
+    assert e.value.status == 5
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_random_workload_with_swaps_against_the_model(seed):
+    rng = np.random.default_rng(100 + seed)
+    NB, NH = 64, 48
+    bm = pa.BlockManager(NB, NH)
+    model = DevicePoolModel(NB, NH)
+    hist, unwritten, swapped, next_id = {}, set(), set(), 1
+    moved = set()
+    prompts = [list(rng.integers(0, 30, int(rng.integers(1, 60)))) for _ in range(4)]
+    steps = swaps = 0
+    for it in range(600):
+        op = int(rng.integers(0, 8))
+        live = sorted(hist)
+        resident = [r for r in live if r not in swapped]
+        try:
+            if op == 0 or not live:
+                p = prompts[int(rng.integers(0, 4))]
+                p = p[:int(rng.integers(1, len(p) + 1))] + list(rng.integers(0, 30, int(rng.integers(0, 3))))
+                bm.add(next_id, p)
+                hist[next_id] = list(p)
+                unwritten.add(next_id)
+                next_id += 1
+            elif op == 1 and resident:
+                r = resident[int(rng.integers(0, len(resident)))]
+                new = list(rng.integers(0, 30, int(rng.integers(1, 18))))
+                bm.append(r, new)
+                hist[r] += new
+                unwritten.add(r)
+            elif op == 2 and resident:
+                r = resident[int(rng.integers(0, len(resident)))]
+                if r in unwritten:
+                    continue
+                bm.fork(r, next_id)
+                hist[next_id] = list(hist[r])
+                next_id += 1
+            elif op == 3:
+                r = live[int(rng.integers(0, len(live)))]
+                bm.release(r)
+                del hist[r]
+                unwritten.discard(r)
+                swapped.discard(r)
+            elif op == 4:
+                try:
+                    r = bm.lru()
+                except pa.PagedAttentionError as e:
+                    assert e.status == 5
+                    continue
+                assert r not in swapped and r not in unwritten and r not in moved
+                bm.swap_out(r)
+                swapped.add(r)
+                moved.add(r)
+                swaps += 1
+            elif op == 5 and swapped:
+                cand = sorted(swapped - moved)
+                if not cand:
+                    continue
+                r = cand[int(rng.integers(0, len(cand)))]
+                bm.swap_in(r)
+                swapped.discard(r)
+                moved.add(r)
+            else:
+                out, inn = bm.swaps()
+                model.swap(out, inn)
+                reqs = sorted(r for r in unwritten if rng.random() < 0.8 and r not in swapped)
+                bt, lens, qsl, pairs = bm.step(reqs, 64)
+                model.run_step(reqs, hist, bt, lens, qsl, pairs)
+                unwritten -= set(reqs)
+                moved.clear()
+                steps += 1
+                for r in hist:                     # every written row, wherever it is
+                    if r not in unwritten:
+                        model.read_back(bm, r, hist[r])
+        except pa.PagedAttentionError as e:
+            assert e.status == 5, e                # only "out of blocks / slots"
+    assert steps > 50 and swaps > 20

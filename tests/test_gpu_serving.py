@@ -1,16 +1,18 @@
 """A short serving loop: the host block manager drives the device calls.
 
 Each step follows the protocol the manager's arrays are made for (uml.org.cn
-"Prefix Sharing" and "Continuous Batching"; 5688vip chapter 3, section 3.2):
-kv_block_copy over the step's copy-on-write pairs, pa_slot_mapping, the K/V
-writes of the query tokens, then pa_decode (all rows decodes) or
-pa_prefill_chunk (a mixed step).  Requests are added with shared prompts (prefix
-cache hits), forked (parallel sampling, copy-on-write), grown and released.
+"PagedAttention", "Prefix Sharing" and "Continuous Batching"; 5688vip chapter 3,
+section 3.2): kv_swap of the step's swap-outs (device -> pinned host pool) and
+swap-ins (host -> device), kv_block_copy over its copy-on-write pairs,
+pa_slot_mapping, the K/V writes of the query tokens, then pa_decode (all rows
+decodes) or pa_prefill_chunk (a mixed step).  Requests are added with shared
+prompts (prefix cache hits), forked (parallel sampling, copy-on-write), grown,
+swapped out (their device blocks reused meanwhile), swapped back in and released.
 
 Checked every step:
 * the device slot mapping equals the oracle's slot of every query position;
-* the device pools (and scales) equal, bit for bit, an oracle mirror that
-  applies the same copies and writes;
+* the device and host pools (and scales) equal, bit for bit, an oracle mirror
+  that applies the same swaps, copies and writes;
 * the attention outputs match the oracle on the mirror, and for 16-bit pools
   also a paging-free recompute: softmax attention over each request's history,
   whose row at position p is a fixed function of the tokens 0..p.  The rows are
@@ -29,7 +31,7 @@ from .pa_testlib import err_over_bar, max_err, np_of
 
 pytestmark = pytest.mark.gpu
 
-BS, NB, MB = 16, 64, 16
+BS, NB, NH, MB = 16, 64, 24, 16
 HQ, HKV, D = 16, 2, 128
 SCALE = 1.0 / np.sqrt(D)
 TORCH = {"f16": torch.float16, "bf16": torch.bfloat16}
@@ -72,31 +74,48 @@ def scenario():
         dict(add={6: Q}, append={r: [tok()] for r in (1, 3, 4, 5)}),
         dict(add={7: P + [1] * 30}, fork=[(3, 8)], append={r: [tok()] for r in (1, 3, 4, 6, 8)}),
         dict(release=[5], append={r: [tok()] for r in (1, 3, 4, 6, 7, 8)}),
+        dict(swap_out=[4, 6], append={r: [tok()] for r in (1, 3, 7, 8)}),
+        dict(add={9: Q[:5] + [3] * 60}, append={r: [tok()] for r in (1, 3, 7, 8)}),
+        dict(swap_in=[4, 6], append={r: [tok()] for r in (1, 3, 4, 6, 7, 8, 9)}),
     ]
-    for _ in range(6):
-        steps.append(dict(append={r: [tok()] for r in (1, 3, 4, 6, 7, 8)}))
+    for _ in range(3):
+        steps.append(dict(append={r: [tok()] for r in (1, 3, 4, 6, 7, 8, 9)}))
     steps.append(dict(append={1: [tok() for _ in range(21)], 8: [tok()]}))  # a chunk
     return steps
 
 
-def _pool(kv):
+def _pool(kv, n=NB, device="cuda"):
+    pin = device == "cpu"
     if kv in TORCH:
-        z = lambda: torch.zeros((NB, HKV, BS, D), dtype=TORCH[kv], device="cuda")
+        z = lambda: torch.zeros((n, HKV, BS, D), dtype=TORCH[kv], device=device, pin_memory=pin)
         return pa.KVPool(z(), z(), shared_blocks=True), None
-    z = lambda: torch.zeros((NB, HKV, BS, D), dtype=torch.uint8, device="cuda")
-    s = lambda: torch.zeros((NB, HKV), dtype=torch.float32, device="cuda")
+    z = lambda: torch.zeros((n, HKV, BS, D), dtype=torch.uint8, device=device, pin_memory=pin)
+    s = lambda: torch.zeros((n, HKV), dtype=torch.float32, device=device, pin_memory=pin)
     return pa.KVPool(z(), z(), s(), s(), shared_blocks=True), "e4m3fn"
+
+
+def _mirror(codec, n):
+    mk = np.zeros((n, HKV, BS, D), dtype=np.uint8 if codec else np.float32)
+    return dict(k=mk.copy(), v=mk.copy(), ks=np.zeros((n, HKV), np.float32),
+                vs=np.zeros((n, HKV), np.float32))
+
+
+def _tup(m):
+    return (m["k"], m["v"], m["ks"], m["vs"])
+
+
+def _untup(t):
+    return dict(k=t[0], v=t[1], ks=t[2], vs=t[3])
 
 
 @pytest.mark.parametrize("kv", ["f16", "bf16", "fp8"])
 def test_block_manager_drives_the_device_path(kv):
     say(f"[serving] kv={kv}")
     pool, codec = _pool(kv)
+    hpool, _ = _pool(kv, NH, "cpu")
     qdt = TORCH.get(kv, torch.float16)
-    mk = np.zeros((NB, HKV, BS, D), dtype=np.uint8 if codec else np.float32)
-    mirror = dict(k=mk.copy(), v=mk.copy(), ks=np.zeros((NB, HKV), np.float32),
-                  vs=np.zeros((NB, HKV), np.float32))
-    bm = pa.BlockManager(NB)
+    mirror, hmirror = _mirror(codec, NB), _mirror(codec, NH)
+    bm = pa.BlockManager(NB, NH)
     hist, live, unwritten = History(), {}, set()
     rng = np.random.default_rng(11)
     ws = None
@@ -108,6 +127,10 @@ def test_block_manager_drives_the_device_path(kv):
         for p, c in ev.get("fork", []):
             bm.fork(p, c)
             live[c] = list(live[p])
+        for r in ev.get("swap_out", []):
+            say(f"  step {si}: swap out {r} ({bm.swap_out(r)} blocks)")
+        for r in ev.get("swap_in", []):
+            bm.swap_in(r)
         for r, toks in ev.get("add", {}).items():
             cached = bm.add(r, toks)
             live[r] = list(toks)
@@ -117,17 +140,23 @@ def test_block_manager_drives_the_device_path(kv):
             bm.append(r, toks)
             live[r] += toks
             unwritten.add(r)
+        out_np, in_np = bm.swaps()
         reqs = sorted(unwritten)
         bt_np, lens_np, qsl_np, pairs_np = bm.step(reqs, MB)
         unwritten.clear()
         T = int(qsl_np[-1])
         q_lens = np.diff(qsl_np)
-        say(f"  step {si}: {len(reqs)} requests, {T} query rows, {len(pairs_np)} copies")
+        say(f"  step {si}: {len(reqs)} requests, {T} query rows, {len(pairs_np)} copies, "
+            f"{len(out_np)} out / {len(in_np)} in")
 
-        # device: copies, slot mapping, writes, attention
+        # device: swaps, copies, slot mapping, writes, attention
         bt = torch.from_numpy(bt_np).cuda()
         lens = torch.from_numpy(lens_np).cuda()
         qsl = torch.from_numpy(qsl_np).cuda()
+        if len(out_np):
+            pa.kv_swap(hpool, pool, torch.from_numpy(out_np.copy()).cuda())
+        if len(in_np):
+            pa.kv_swap(pool, hpool, torch.from_numpy(in_np.copy()).cuda())
         if len(pairs_np):
             pa.kv_block_copy(pool, torch.from_numpy(pairs_np.copy()).cuda())
         slots = pa.pa_slot_mapping(bt, qsl, lens, T)
@@ -155,6 +184,10 @@ def test_block_manager_drives_the_device_path(kv):
         # oracle: slots, mirror pools, attention
         want_slots = [oracle.slot_for_position(bt_np[i], p) for i, _, p in pos]
         assert slots.cpu().tolist() == want_slots
+        if len(out_np):
+            hmirror = _untup(oracle.swap_blocks(_tup(hmirror), _tup(mirror), out_np))
+        if len(in_np):
+            mirror = _untup(oracle.swap_blocks(_tup(mirror), _tup(hmirror), in_np))
         if len(pairs_np):
             k2, v2, ks2, vs2 = oracle.block_copy(mirror["k"], mirror["v"], pairs_np,
                                                  mirror["ks"], mirror["vs"])
@@ -172,6 +205,10 @@ def test_block_manager_drives_the_device_path(kv):
                                                           np.array(want_slots))
         assert np.array_equal(np_of(pool.k.cpu()), mirror["k"]), f"step {si}: K pool"
         assert np.array_equal(np_of(pool.v.cpu()), mirror["v"]), f"step {si}: V pool"
+        assert np.array_equal(np_of(hpool.k), hmirror["k"]), f"step {si}: host K pool"
+        assert np.array_equal(np_of(hpool.v), hmirror["v"]), f"step {si}: host V pool"
+        if codec:
+            assert np.array_equal(hpool.k_scale.numpy(), hmirror["ks"])
         kw = {}
         if codec:
             kw = dict(k_scale=mirror["ks"].astype(np.float64), v_scale=mirror["vs"].astype(np.float64),

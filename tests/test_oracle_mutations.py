@@ -180,3 +180,50 @@ def test_quant_write_variant_without_mutation_passes(monkeypatch):
     qpins.test_dequantised_values_within_rounding_bound("fp8")
     qpins.test_scale_is_running_amax_over_valid_rows("i8")
     qpins.test_stored_codes_are_the_nearest_codes("i8")
+
+
+def _swap_kv_crossed(dst, src, pairs):
+    out = pa.__dict__["_orig_swap_blocks"](dst, src, pairs)
+    return (out[1], out[0], out[2], out[3])
+
+
+def _swap_without_scales(dst, src, pairs):
+    out = pa.__dict__["_orig_swap_blocks"](dst, src, pairs)
+    return (out[0], out[1], dst[2], dst[3])
+
+
+def _swap_reversed_pairs(dst, src, pairs):
+    p = np.asarray(pairs).reshape(-1, 2)[:, ::-1]
+    n = min(len(dst[0]), len(src[0]))
+    p = np.where(p < n, p, 0)
+    return pa.__dict__["_orig_swap_blocks"](dst, src, p)
+
+
+def _swap_next_block(dst, src, pairs):
+    p = np.asarray(pairs).reshape(-1, 2).copy()
+    p[:, 0] = (p[:, 0] + 1) % len(src[0])
+    return pa.__dict__["_orig_swap_blocks"](dst, src, p)
+
+
+SWAP_MUTATIONS = {
+    "k_v_crossed": _swap_kv_crossed,
+    "scales_left_behind": _swap_without_scales,
+    "pairs_reversed": _swap_reversed_pairs,
+    "source_off_by_one": _swap_next_block,
+}
+
+
+@pytest.mark.parametrize("name", sorted(SWAP_MUTATIONS))
+def test_swap_mutation_is_caught(name, monkeypatch):
+    from tests import test_oracle_swap as swap_pins
+    monkeypatch.setitem(pa.__dict__, "_orig_swap_blocks", pa.swap_blocks)
+    monkeypatch.setattr(oracle, "swap_blocks", SWAP_MUTATIONS[name])
+    caught = False
+    for test in (swap_pins.test_request_reads_the_same_through_its_host_table,
+                 swap_pins.test_out_and_back_in_is_the_identity_on_the_rows):
+        for quant in (False, True):
+            try:
+                test(quant)
+            except (AssertionError, IndexError, ValueError):
+                caught = True
+    assert caught, name
