@@ -43,16 +43,20 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 256 MiB device copy three times (byte-counter calibration)")
+    ap.add_argument("--block-size", type=int, default=16, choices=[16, 32],
+                    help="tokens per KV block (the pages allow 16 or 32)")
     ap.add_argument("--swap", action="store_true",
                     help="measure kv_swap (device pool <-> pinned host pool) instead of the step")
     return ap.parse_args()
 
 
-def make_batch(name):
+def make_batch(name, block_size=16):
     from paged_kv_cache_455_amd import workloads as W
-    return {"llama3-decode": W.llama3_8b_decode, "tiny": W.tiny_fp32, "prefix-cow": W.prefix_cow,
-            "mixed": W.mixed_step, "long-fp8": lambda: W.long_quantised("fp8"),
-            "long-i8": lambda: W.long_quantised("i8")}[name]()
+    kw = dict(block_size=block_size)
+    return {"llama3-decode": lambda: W.llama3_8b_decode(**kw),
+            "tiny": lambda: W.tiny_fp32(**kw), "prefix-cow": lambda: W.prefix_cow(**kw),
+            "mixed": lambda: W.mixed_step(**kw), "long-fp8": lambda: W.long_quantised("fp8", **kw),
+            "long-i8": lambda: W.long_quantised("i8", **kw)}[name]()
 
 
 # ---------------------------------------------------------------------------------------
@@ -69,7 +73,7 @@ def attention_bytes(b, seqs=None):
     for s in seqs:
         n = lens[s]
         q_len = qsl[s + 1] - qsl[s]
-        nblk = -(-n // 16)
+        nblk = -(-n // b.block_size)
         tot += 2 * n * b.num_kv_heads * b.head_dim * e
         if b.kv_dtype in ("fp8", "i8"):
             tot += 2 * nblk * b.num_kv_heads * 4
@@ -95,7 +99,7 @@ def side_bytes(b):
     if b.k_new is not None:  # read the new rows (their own dtype), write them in the pool's
         tot += 2 * b.num_tokens * b.num_kv_heads * b.head_dim * (b.k_new.element_size() + e)
     if b.copy_pairs is not None:
-        tot += 2 * 2 * int(b.copy_pairs.shape[0]) * b.num_kv_heads * 16 * b.head_dim * e
+        tot += 2 * 2 * int(b.copy_pairs.shape[0]) * b.num_kv_heads * b.block_size * b.head_dim * e
     return tot
 
 
@@ -288,7 +292,7 @@ def main():
         return
     pa.load_library()
     dev = torch.device("cuda:0")
-    b = make_batch(args.workload)
+    b = make_batch(args.workload, args.block_size)
     to = lambda t: None if t is None else t.to(dev).contiguous()
     q, bt, lens, qsl = to(b.q), to(b.block_tables), to(b.seq_lens), to(b.query_start_loc)
     k_new, v_new, pairs = to(b.k_new), to(b.v_new), to(b.copy_pairs)
@@ -320,7 +324,7 @@ def main():
         pool = pools[i % R]
         if pairs is not None:
             pa.kv_block_copy(pool, pairs)
-        pa.pa_slot_mapping(bt, qsl, lens, b.num_tokens, out=slots)
+        pa.pa_slot_mapping(bt, qsl, lens, b.num_tokens, out=slots, block_size=b.block_size)
         if k_new is not None:
             if quantised:  # 1-byte pool: quantise this step's K/V on the way in
                 pa.kv_cache_write_quant(pool, k_new, v_new, slots)
@@ -374,7 +378,7 @@ def main():
         "config": {
             "workload": b.name, "num_seqs": b.num_seqs, "num_q_tokens": b.num_tokens,
             "q_heads": b.num_q_heads, "kv_heads": b.num_kv_heads, "head_dim": b.head_dim,
-            "block_size": 16, "kv_dtype": b.kv_dtype, "q_dtype": b.q_dtype, "accumulate": "f32",
+            "block_size": b.block_size, "kv_dtype": b.kv_dtype, "q_dtype": b.q_dtype, "accumulate": "f32",
             "max_context": b.max_seq_len, "pool_copies_rotated": R,
         },
         "tokens_per_s": round(tokens / (ms_per_step * 1e-3), 1),
@@ -386,7 +390,7 @@ def main():
         "algorithmic": {"attention_bytes": a_bytes, "side_bytes": s_bytes, "attention_flops": flops},
         "roofline": {"bound": "hbm", "achieved": round(attn_gbps, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": profiled_traffic(args.workload),
+                     "traffic": profiled_traffic(args.workload) if b.block_size == 16 else None,
                      "kernel": "pa_decode (balanced-split kernel + piece merge)" if b.kind == "decode"
                      else "pa_prefill_chunk"},
     }

@@ -25,10 +25,12 @@
  *    duplicate write slots or overlapping copy pairs are undefined behaviour.
  *
  * KV pool layout (the pages fix the paging, not the memory layout):
- *    k, v : [num_blocks][num_kv_heads][block_size = 16][head_dim], kv_dtype
+ *    k, v : [num_blocks][num_kv_heads][block_size][head_dim], kv_dtype
  *    k_scale, v_scale : float32 [num_blocks][num_kv_heads] for 1-byte codes
- *  so one (block, kv head) tile of 16 token rows is contiguous: 4 KiB for
- *  fp16/bf16 at head_dim 128, 2 KiB for fp8/int8.
+ *  with block_size 16 or 32 tokens ([P2] 3.2), so one (block, kv head) tile of
+ *  block_size token rows is contiguous: 4 KiB for fp16/bf16 at head_dim 128 and
+ *  16 tokens, 2 KiB for fp8/int8; a 32-token block holds two such 16-row
+ *  halves per kv head, under one scale.
  *
  * GQA ([P3] 2.2): query head h reads kv head h / (num_q_heads / num_kv_heads).
  */
@@ -70,13 +72,13 @@ typedef enum pa_status {
                                    streamed with a nontemporal hint. */
 
 typedef struct pa_kv_pool {
-  void *k;          /* [num_blocks][num_kv_heads][16][head_dim] */
+  void *k;          /* [num_blocks][num_kv_heads][block_size][head_dim] */
   void *v;          /* same shape */
   float *k_scale;   /* [num_blocks][num_kv_heads]; NULL unless kv_dtype is 1 byte */
   float *v_scale;
   int64_t num_blocks;
   int32_t num_kv_heads;
-  int32_t block_size; /* must be 16 ([P2] 3.2, [P3] 3.2) */
+  int32_t block_size; /* 16 or 32 tokens ([P2] 3.2; [P3] 3.2 names 16) */
   int32_t head_dim;   /* 64 or 128 */
   int32_t kv_dtype;   /* pa_dtype_t */
   int32_t flags;      /* PA_POOL_* bits; 0 for none */
@@ -99,7 +101,8 @@ const char *pa_last_error(void);
  * For sequence s, query rows t in [query_start_loc[s], query_start_loc[s+1])
  * are the q_len newest tokens; row t sits at logical position
  *     p = seq_lens[s] - q_len + (t - query_start_loc[s])
- * and its slot is   block_tables[s][p / 16] * 16 + p % 16.
+ * and its slot is   block_tables[s][p / bs] * bs + p % bs,  bs = block_size
+ * (16 or 32; PA_E_UNSUPPORTED otherwise).
  *   block_tables    int32 [num_seqs][max_blocks_per_seq]
  *   query_start_loc int32 [num_seqs + 1], non-decreasing, [0] = 0,
  *                   [num_seqs] = num_tokens
@@ -107,7 +110,8 @@ const char *pa_last_error(void);
  *   slot_mapping    int64 [num_tokens] (output)
  */
 pa_status_t pa_slot_mapping(const int32_t *block_tables, int32_t max_blocks_per_seq,
-                            const int32_t *query_start_loc, const int32_t *seq_lens,
+                            int32_t block_size, const int32_t *query_start_loc,
+                            const int32_t *seq_lens,
                             int32_t num_seqs, int32_t num_tokens, int64_t *slot_mapping,
                             hipStream_t stream);
 
@@ -115,7 +119,7 @@ pa_status_t pa_slot_mapping(const int32_t *block_tables, int32_t max_blocks_per_
  * kv_cache_write -- scatter new tokens' K and V into the pools by slot
  * ([P2] 3.2 prefill writes every prompt token, decode appends one token).
  *   k_new, v_new  [num_tokens][num_kv_heads][head_dim], dtype = pool kv_dtype
- *   slot_mapping  int64 [num_tokens]; slot = block * 16 + offset; slot < 0
+ *   slot_mapping  int64 [num_tokens]; slot = block * block_size + offset; slot < 0
  *                 means "no token" and is skipped.
  * A pure bit copy.  Pools with 1-byte codes return PA_E_UNSUPPORTED: they are
  * written by kv_cache_write_quant.
@@ -229,7 +233,8 @@ pa_status_t pa_prefill_chunk(const pa_kv_pool_t *pool, const void *q, int32_t q_
 /*
  * ---- Host block manager ([P1] PagedAttention, Prefix Sharing, Continuous
  * Batching; [P2] 3.2) -- host memory only, no device calls. ----
- * A request's cache is a list of 16-token physical blocks taken from a free list
+ * A request's cache is a list of physical blocks of block_size (16 or 32)
+ * tokens, the device pool's, taken from a free list
  * of num_blocks (the device pool's blocks) as it grows: a token goes at the end of
  * the last block, a full block is followed by a fresh one.  Blocks are reference
  * counted: pa_bm_fork shares every block of a request with a new one (parallel
@@ -251,10 +256,11 @@ pa_status_t pa_prefill_chunk(const pa_kv_pool_t *pool, const void *q, int32_t q_
  */
 typedef struct pa_block_manager pa_block_manager_t;
 
-/* A manager over device blocks 0 .. num_blocks-1 and host slots 0 ..
- * num_host_blocks-1 (a host pool for swapping; 0 for none), all free.  NULL for
- * num_blocks <= 0, num_host_blocks < 0 or out of host memory. */
-pa_block_manager_t *pa_bm_create(int32_t num_blocks, int32_t num_host_blocks);
+/* A manager over device blocks 0 .. num_blocks-1 of block_size tokens (16 or
+ * 32, the pool's) and host slots 0 .. num_host_blocks-1 (a host pool for
+ * swapping; 0 for none), all free.  NULL for num_blocks <= 0, num_host_blocks
+ * < 0, another block_size or out of host memory. */
+pa_block_manager_t *pa_bm_create(int32_t num_blocks, int32_t num_host_blocks, int32_t block_size);
 void pa_bm_destroy(pa_block_manager_t *bm);
 /* Free device blocks (-1 for a NULL manager).  A copy source whose last
  * reference went in this step counts as free only after the next pa_bm_step. */
@@ -267,7 +273,7 @@ int32_t pa_bm_refcount(const pa_block_manager_t *bm, int32_t block);
 
 /* New request `req` with its n >= 1 prompt tokens (host array).  *cached (may
  * be NULL) receives how many leading prompt tokens already sit in shared cached
- * blocks -- a multiple of 16, at most n - 1 -- which the next step does not
+ * blocks -- a multiple of block_size, at most n - 1 -- which the next step does not
  * compute.  PA_E_NO_BLOCKS (nothing changed) when the free list is short;
  * PA_E_ARG for a used id. */
 pa_status_t pa_bm_add(pa_block_manager_t *bm, int64_t req, const int32_t *tokens, int32_t n,

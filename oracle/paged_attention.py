@@ -70,19 +70,21 @@ def _decode_values(x, codec):
 def gather_sequence(pool, block_table_row, n, scales=None, codec=None):
     """K (or V) of one request as a contiguous float64 array ``[n][H][D]``.
 
-    Concatenates physical blocks ``block_table_row[0 .. ceil(n/16)-1]`` along
-    the token axis and keeps the first ``n`` tokens.  For 1-byte pools the
+    The block size ``bs`` is the pool's third axis (16 or 32 tokens, 5688vip
+    §3.2).  Concatenates physical blocks ``block_table_row[0 .. ceil(n/bs)-1]``
+    along the token axis and keeps the first ``n`` tokens.  For 1-byte pools the
     codes are decoded and multiplied by that block's per-(block, kv_head)
     scale, ``scales[b][h]``.
     """
-    n_blocks = -(-n // BLOCK_SIZE)
+    bs = pool.shape[2]
+    n_blocks = -(-n // bs)
     pieces = []
     for j in range(n_blocks):
         b = int(block_table_row[j])
-        tile = _decode_values(pool[b], codec)  # [H][16][D]
+        tile = _decode_values(pool[b], codec)  # [H][bs][D]
         if scales is not None:
             tile = tile * np.asarray(scales[b], dtype=np.float64)[:, None, None]
-        pieces.append(np.transpose(tile, (1, 0, 2)))  # [16][H][D]
+        pieces.append(np.transpose(tile, (1, 0, 2)))  # [bs][H][D]
     return np.concatenate(pieces, axis=0)[:n]
 
 
@@ -157,7 +159,8 @@ def prefill_chunk(q, k_pool, v_pool, query_start_loc, seq_lens, block_tables, sc
 def cache_write(k_pool, v_pool, k_new, v_new, slot_mapping):
     """Scatter new tokens' K/V into the pools by slot; returns new pools.
 
-    Token ``t`` goes to block ``slot // 16``, offset ``slot % 16``; a negative
+    Token ``t`` goes to block ``slot // bs``, offset ``slot % bs`` (``bs`` the
+    pools' third axis, 16 or 32); a negative
     slot means "no token" and is skipped.  Values are stored as given (the pool's
     own element type), so the result is an exact bit copy.
     """
@@ -166,7 +169,7 @@ def cache_write(k_pool, v_pool, k_new, v_new, slot_mapping):
     for t, slot in enumerate(np.asarray(slot_mapping)):
         if slot < 0:
             continue
-        b, o = int(slot) // BLOCK_SIZE, int(slot) % BLOCK_SIZE
+        b, o = int(slot) // k_pool.shape[2], int(slot) % k_pool.shape[2]
         k_out[b, :, o, :] = k_new[t]
         v_out[b, :, o, :] = v_new[t]
     return k_out, v_out
@@ -191,7 +194,8 @@ def quantised_cache_write(codes, scales, x_new, slot_mapping, kind):
     * encode clamps to [-qmax, qmax] and rounds to nearest even (E4M3FN by the
       code grid, INT8 by rint).
 
-    codes  [NB][H][16][D] uint8 (fp8) or int8;  scales float32 [NB][H]
+    codes  [NB][H][bs][D] uint8 (fp8) or int8 (bs = 16 or 32 tokens per block);
+           scales float32 [NB][H]
     x_new  [T][H][D] float values (float32 or narrower; read as float32)
     """
     codes = np.array(codes, copy=True)
@@ -206,7 +210,7 @@ def quantised_cache_write(codes, scales, x_new, slot_mapping, kind):
     for t, slot in enumerate(slots):
         if slot < 0:
             continue
-        runs.setdefault(int(slot) // BLOCK_SIZE, []).append((int(slot) % BLOCK_SIZE, t))
+        runs.setdefault(int(slot) // codes.shape[2], []).append((int(slot) % codes.shape[2], t))
     for b, rows in runs.items():
         offs = [o for o, _ in rows]
         off0 = min(offs)

@@ -60,8 +60,8 @@ _SIGS = {
     "pa_version": (_c.c_char_p, []),
     "pa_status_string": (_c.c_char_p, [_c.c_int]),
     "pa_last_error": (_c.c_char_p, []),
-    "pa_slot_mapping": (_c.c_int, [_c.c_void_p, _c.c_int32, _c.c_void_p, _c.c_void_p, _c.c_int32,
-                                   _c.c_int32, _c.c_void_p, _c.c_void_p]),
+    "pa_slot_mapping": (_c.c_int, [_c.c_void_p, _c.c_int32, _c.c_int32, _c.c_void_p, _c.c_void_p,
+                                   _c.c_int32, _c.c_int32, _c.c_void_p, _c.c_void_p]),
     "kv_cache_write": (_c.c_int, [_c.POINTER(_Pool), _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                   _c.c_int32, _c.c_void_p]),
     "kv_block_copy": (_c.c_int, [_c.POINTER(_Pool), _c.c_void_p, _c.c_int32, _c.c_void_p]),
@@ -72,7 +72,7 @@ _SIGS = {
                              _c.c_int32, _c.c_void_p, _c.c_int32, _c.c_int32, _c.c_int32,
                              _c.c_float, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "pa_prefill_workspace_size": (_c.c_size_t, [_c.c_int32] * 8),
-    "pa_bm_create": (_c.c_void_p, [_c.c_int32, _c.c_int32]),
+    "pa_bm_create": (_c.c_void_p, [_c.c_int32, _c.c_int32, _c.c_int32]),
     "pa_bm_num_free_host": (_c.c_int32, [_c.c_void_p]),
     "pa_bm_swap_out": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_void_p]),
     "pa_bm_swap_in": (_c.c_int, [_c.c_void_p, _c.c_int64]),
@@ -183,14 +183,15 @@ class KVPool:
         return ctypes.byref(self._s)
 
 
-def pa_slot_mapping(block_tables, query_start_loc, seq_lens, num_tokens: int, out=None, stream=None):
+def pa_slot_mapping(block_tables, query_start_loc, seq_lens, num_tokens: int, out=None, stream=None,
+                    block_size: int = 16):
     lib = load_library()
     if out is None:
         out = torch.empty(num_tokens, dtype=torch.int64, device=block_tables.device)
     S = int(seq_lens.shape[0])
     _check("pa_slot_mapping", lib.pa_slot_mapping(
-        _ptr(block_tables), int(block_tables.shape[1]), _ptr(query_start_loc), _ptr(seq_lens), S,
-        int(num_tokens), _ptr(out), _stream(block_tables, stream)))
+        _ptr(block_tables), int(block_tables.shape[1]), int(block_size), _ptr(query_start_loc),
+        _ptr(seq_lens), S, int(num_tokens), _ptr(out), _stream(block_tables, stream)))
     return out
 
 
@@ -287,14 +288,15 @@ class BlockManager:
     reference counts, copy-on-write and the per-step host arrays.  Marshalling
     only; the bookkeeping runs in the library."""
 
-    def __init__(self, num_blocks: int, num_host_blocks: int = 0):
+    def __init__(self, num_blocks: int, num_host_blocks: int = 0, block_size: int = 16):
         lib = load_library()
         self._lib = lib
-        self._h = lib.pa_bm_create(int(num_blocks), int(num_host_blocks))
+        self._h = lib.pa_bm_create(int(num_blocks), int(num_host_blocks), int(block_size))
         if not self._h:
             raise PagedAttentionError("pa_bm_create", 1, "bad block counts or out of memory")
         self.num_blocks = int(num_blocks)
         self.num_host_blocks = int(num_host_blocks)
+        self.block_size = int(block_size)
 
     def __del__(self):
         h = getattr(self, "_h", None)

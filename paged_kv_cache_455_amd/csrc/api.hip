@@ -27,7 +27,7 @@ pa_status_t hip_status(hipError_t e, const char *what) {
   return fail(PA_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-constexpr int kBlockTokens = 16;
+constexpr int kTileRows = 16;  // rows per tile; the splits and workspaces count tiles
 
 int elem_bytes(int dt) {
   switch (dt) {
@@ -45,8 +45,8 @@ pa_status_t check_pool(const pa_kv_pool_t *pool, bool need_scales_if_quantised) 
   if (pool->k == nullptr || pool->v == nullptr) return fail(PA_E_ARG, "pool k/v pointer is NULL");
   if (pool->num_blocks <= 0) return fail(PA_E_ARG, "num_blocks must be > 0");
   if (pool->num_kv_heads <= 0) return fail(PA_E_ARG, "num_kv_heads must be > 0");
-  if (pool->block_size != kBlockTokens)
-    return fail(PA_E_UNSUPPORTED, "block_size %d unsupported (must be 16)", pool->block_size);
+  if (pool->block_size != 16 && pool->block_size != 32)
+    return fail(PA_E_UNSUPPORTED, "block_size %d unsupported (16 or 32)", pool->block_size);
   if (pool->head_dim != 64 && pool->head_dim != 128)
     return fail(PA_E_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", pool->head_dim);
   if (elem_bytes(pool->kv_dtype) == 0) return fail(PA_E_ARG, "unknown kv_dtype %d", pool->kv_dtype);
@@ -138,7 +138,7 @@ static int seg_cost() {
 }
 
 int stream_pieces(int max_ctx) {
-  const int max_blocks = (max_ctx + kBlockTokens - 1) / kBlockTokens;
+  const int max_blocks = (max_ctx + kTileRows - 1) / kTileRows;
   return (max_blocks + kMinTilesPerWave - 1) / kMinTilesPerWave + 1;
 }
 
@@ -155,7 +155,7 @@ WsLayout stream_layout(int64_t num_seqs, int num_q_heads, int head_dim, int max_
 }
 
 int max_parts_for(int max_ctx, int part_blocks) {
-  const int max_blocks = (max_ctx + kBlockTokens - 1) / kBlockTokens;
+  const int max_blocks = (max_ctx + kTileRows - 1) / kTileRows;
   return (max_blocks + part_blocks - 1) / part_blocks;
 }
 
@@ -191,7 +191,7 @@ const char *pa_status_string(pa_status_t s) {
 const char *pa_last_error(void) { return g_last_error; }
 
 pa_status_t pa_slot_mapping(const int32_t *block_tables, int32_t max_blocks_per_seq,
-                            const int32_t *query_start_loc, const int32_t *seq_lens,
+                            int32_t block_size, const int32_t *query_start_loc, const int32_t *seq_lens,
                             int32_t num_seqs, int32_t num_tokens, int64_t *slot_mapping,
                             hipStream_t stream) {
   if (num_seqs < 0 || num_tokens < 0) return fail(PA_E_ARG, "negative num_seqs/num_tokens");
@@ -199,7 +199,10 @@ pa_status_t pa_slot_mapping(const int32_t *block_tables, int32_t max_blocks_per_
   if (!block_tables || !query_start_loc || !seq_lens || !slot_mapping)
     return fail(PA_E_ARG, "NULL array argument");
   if (max_blocks_per_seq <= 0) return fail(PA_E_ARG, "max_blocks_per_seq must be > 0");
-  return hip_status(pa::launch_slot_mapping(block_tables, max_blocks_per_seq, query_start_loc,
+  if (block_size != 16 && block_size != 32)
+    return fail(PA_E_UNSUPPORTED, "block_size %d unsupported (16 or 32)", block_size);
+  return hip_status(pa::launch_slot_mapping(block_tables, max_blocks_per_seq, block_size,
+                                            query_start_loc,
                                             seq_lens, num_seqs, slot_mapping, stream),
                     "pa_slot_mapping launch");
 }
@@ -223,6 +226,7 @@ pa_status_t kv_cache_write(const pa_kv_pool_t *pool, const void *k_new, const vo
   a.num_tokens = num_tokens;
   a.num_kv_heads = pool->num_kv_heads;
   a.row_bytes = pool->head_dim * elem_bytes(pool->kv_dtype);
+  a.block_size = pool->block_size;
   return hip_status(pa::launch_cache_write(a, stream), "kv_cache_write launch");
 }
 
@@ -252,6 +256,7 @@ pa_status_t kv_cache_write_quant(const pa_kv_pool_t *pool, const void *k_new, co
   a.num_tokens = num_tokens;
   a.num_kv_heads = pool->num_kv_heads;
   a.row_bytes = pool->head_dim;
+  a.block_size = pool->block_size;
   return hip_status(pa::launch_cache_write_quant(a, pool->kv_dtype, src_dtype, pool->head_dim,
                                                  stream),
                     "kv_cache_write_quant launch");
@@ -272,7 +277,7 @@ pa_status_t kv_block_copy(const pa_kv_pool_t *pool, const int32_t *src_dst, int3
   a.pairs = src_dst;
   a.num_pairs = num_pairs;
   a.num_kv_heads = pool->num_kv_heads;
-  a.tile_bytes = kBlockTokens * pool->head_dim * elem_bytes(pool->kv_dtype);
+  a.tile_bytes = pool->block_size * pool->head_dim * elem_bytes(pool->kv_dtype);
   return hip_status(pa::launch_block_copy(a, stream), "kv_block_copy launch");
 }
 
@@ -302,8 +307,8 @@ pa_status_t kv_swap(const pa_kv_pool_t *dst, const pa_kv_pool_t *src, const int3
   if (st != PA_OK) return st;
   if ((st = check_pool(src, true)) != PA_OK) return st;
   if (dst->kv_dtype != src->kv_dtype || dst->num_kv_heads != src->num_kv_heads ||
-      dst->head_dim != src->head_dim)
-    return fail(PA_E_ARG, "kv_swap pools differ in kv_dtype, num_kv_heads or head_dim");
+      dst->head_dim != src->head_dim || dst->block_size != src->block_size)
+    return fail(PA_E_ARG, "kv_swap pools differ in kv_dtype, num_kv_heads, head_dim or block_size");
   if (num_pairs < 0) return fail(PA_E_ARG, "num_pairs must be >= 0");
   if (num_pairs == 0) return PA_OK;
   if (!src_dst) return fail(PA_E_ARG, "src_dst is NULL");
@@ -328,7 +333,7 @@ pa_status_t kv_swap(const pa_kv_pool_t *dst, const pa_kv_pool_t *src, const int3
   a.pairs = static_cast<const int32_t *>(pairs_dev);
   a.num_pairs = num_pairs;
   a.num_kv_heads = src->num_kv_heads;
-  a.tile_bytes = kBlockTokens * src->head_dim * elem_bytes(src->kv_dtype);
+  a.tile_bytes = src->block_size * src->head_dim * elem_bytes(src->kv_dtype);
   return hip_status(pa::launch_block_copy(a, stream), "kv_swap launch");
 }
 
@@ -355,10 +360,10 @@ static pa_status_t fill_decode_args(const pa_kv_pool_t *pool, const void *q, int
     return fail(PA_E_ARG, "q, out and workspace must be 16-byte aligned");
   if (max_blocks_per_seq <= 0) return fail(PA_E_ARG, "max_blocks_per_seq must be > 0");
   if (max_len <= 0) return fail(PA_E_ARG, "max length must be > 0");
-  if ((int64_t)max_len > (int64_t)max_blocks_per_seq * kBlockTokens)
-    return fail(PA_E_ARG, "max length %d exceeds max_blocks_per_seq * 16", max_len);
+  if ((int64_t)max_len > (int64_t)max_blocks_per_seq * pool->block_size)
+    return fail(PA_E_ARG, "max length %d exceeds max_blocks_per_seq * block_size", max_len);
   if (!(scale == scale)) return fail(PA_E_ARG, "scale is NaN");
-  const int max_blocks = (max_len + kBlockTokens - 1) / kBlockTokens;
+  const int max_blocks = (max_len + kTileRows - 1) / kTileRows;
   const int pb = decode_part_blocks(rows, pool->num_kv_heads, max_blocks);
   const int parts = max_parts_for(max_len, pb);
   const WsLayout w =
@@ -385,6 +390,7 @@ static pa_status_t fill_decode_args(const pa_kv_pool_t *pool, const void *q, int
   a.part_blocks = pb;
   a.max_parts = parts;
   a.qk_scale = scale * 1.4426950408889634f;
+  a.bs_shift = pool->block_size == 32 ? 1 : 0;
   return PA_OK;
 }
 
@@ -433,7 +439,7 @@ struct MixedLayout {
 MixedLayout mixed_layout(int kv_dtype, int64_t S, int64_t T, int Hq, int Hkv, int D,
                          int max_seq_len) {
   MixedLayout w{};
-  const int max_blocks = (max_seq_len + kBlockTokens - 1) / kBlockTokens;
+  const int max_blocks = (max_seq_len + kTileRows - 1) / kTileRows;
   if (pa::mixed_uses_tiles(kv_dtype)) {
     w.qtok = pa::mixed_tile_rows() / (Hq / Hkv);
     w.p_bound = (int)((T + w.qtok - 1) / w.qtok + S);

@@ -49,8 +49,6 @@
 
 namespace {
 
-constexpr int kBlockSize = 16;
-
 uint64_t mix(uint64_t h, uint64_t x) {  // splitmix64 step over the running hash
   h ^= x + 0x9e3779b97f4a7c15ull + (h << 6) + (h >> 2);
   h ^= h >> 30;
@@ -61,10 +59,10 @@ uint64_t mix(uint64_t h, uint64_t x) {  // splitmix64 step over the running hash
   return h;
 }
 
-// prefix hash through one more full block of 16 tokens (0 is kept for "none")
-uint64_t chain(uint64_t prev, const int32_t *tokens16) {
+// prefix hash through one more full block of bs tokens (0 is kept for "none")
+uint64_t chain(uint64_t prev, const int32_t *tokens, int bs) {
   uint64_t h = prev;
-  for (int k = 0; k < kBlockSize; ++k) h = mix(h, (uint32_t)tokens16[k]);
+  for (int k = 0; k < bs; ++k) h = mix(h, (uint32_t)tokens[k]);
   return h == 0 ? 1 : h;
 }
 
@@ -90,11 +88,12 @@ struct Pair {
 
 struct pa_block_manager {
   int32_t num_blocks = 0;
+  int32_t bs = 16;                      // tokens per block (16 or 32)
   std::vector<int32_t> free_list;       // stack of free block ids
   std::vector<int32_t> refs;            // references per block
   std::vector<uint64_t> cached_hash;    // prefix-cache key of a block, 0 if not cached
   std::vector<int32_t> cached_parent;   // block before it in the request that cached it
-  std::vector<std::vector<int32_t>> cached_tokens;  // the 16 tokens a cached block holds
+  std::vector<std::vector<int32_t>> cached_tokens;  // the bs tokens a cached block holds
   std::unordered_map<uint64_t, int32_t> cache;      // hash -> block
   std::unordered_map<int64_t, Request> reqs;
   std::vector<Pair> pending;            // copy-on-write pairs for the next step
@@ -136,17 +135,17 @@ struct pa_block_manager {
   }
   // offer request r's full blocks to the prefix cache (first holder of a hash wins)
   void publish(Request &r) {
-    const int32_t full = r.written / kBlockSize;
+    const int32_t full = r.written / bs;
     for (; r.published < full; ++r.published) {
       const int32_t i = r.published;
-      r.hash = chain(r.hash, r.tokens.data() + (size_t)i * kBlockSize);
+      r.hash = chain(r.hash, r.tokens.data() + (size_t)i * bs, bs);
       const int32_t b = r.blocks[i];
       if (cache.count(r.hash) != 0 || cached_hash[b] != 0) continue;
       cache.emplace(r.hash, b);
       cached_hash[b] = r.hash;
       cached_parent[b] = i == 0 ? -1 : r.blocks[i - 1];
-      cached_tokens[b].assign(r.tokens.begin() + (size_t)i * kBlockSize,
-                              r.tokens.begin() + (size_t)(i + 1) * kBlockSize);
+      cached_tokens[b].assign(r.tokens.begin() + (size_t)i * bs,
+                              r.tokens.begin() + (size_t)(i + 1) * bs);
     }
   }
   // Append tokens to r: fresh blocks at block boundaries, a private copy of a
@@ -156,8 +155,8 @@ struct pa_block_manager {
     if (n == 0) return PA_OK;
     const int32_t len = (int32_t)r.tokens.size();
     const int32_t have = (int32_t)r.blocks.size();
-    int32_t needed = (len + n + kBlockSize - 1) / kBlockSize - have;
-    const bool cow = len % kBlockSize != 0 && refs[r.blocks.back()] > 1;
+    int32_t needed = (len + n + bs - 1) / bs - have;
+    const bool cow = len % bs != 0 && refs[r.blocks.back()] > 1;
     if (cow) ++needed;
     if (needed > (int32_t)free_list.size())
       return pa::set_error(PA_E_NO_BLOCKS, "no free block for the request's new tokens");
@@ -169,7 +168,7 @@ struct pa_block_manager {
       drop(src);  // still referenced by the other holders
     }
     for (int32_t i = 0; i < n; ++i) {
-      if ((int32_t)r.tokens.size() == (int32_t)r.blocks.size() * kBlockSize) {
+      if ((int32_t)r.tokens.size() == (int32_t)r.blocks.size() * bs) {
         r.blocks.push_back(take());
         r.host.push_back(-1);
       }
@@ -181,12 +180,14 @@ struct pa_block_manager {
 
 extern "C" {
 
-pa_block_manager_t *pa_bm_create(int32_t num_blocks, int32_t num_host_blocks) {
-  if (num_blocks <= 0 || num_host_blocks < 0) return nullptr;
+pa_block_manager_t *pa_bm_create(int32_t num_blocks, int32_t num_host_blocks, int32_t block_size) {
+  if (num_blocks <= 0 || num_host_blocks < 0 || (block_size != 16 && block_size != 32))
+    return nullptr;
   pa_block_manager *bm = new (std::nothrow) pa_block_manager();
   if (bm == nullptr) return nullptr;
   try {
     bm->num_blocks = num_blocks;
+    bm->bs = block_size;
     bm->free_list.resize(num_blocks);
     for (int32_t i = 0; i < num_blocks; ++i) bm->free_list[i] = num_blocks - 1 - i;  // 0 first
     bm->refs.assign(num_blocks, 0);
@@ -224,24 +225,25 @@ pa_status_t pa_bm_add(pa_block_manager_t *bm, int64_t req, const int32_t *tokens
   if (bm->reqs.count(req)) return pa::set_error(PA_E_ARG, "pa_bm_add: request id already in use");
   // leading full blocks found in the prefix cache; a hit must hold the same 16
   // tokens and follow the block matched before it, so the whole prefix is equal.
-  // The last prompt token is always computed: at most (n - 1) / 16 blocks reused.
-  const int32_t max_hit = (n - 1) / kBlockSize;
+  // The last prompt token is always computed: at most (n - 1) / bs blocks reused.
+  const int bs = bm->bs;
+  const int32_t max_hit = (n - 1) / bs;
   std::vector<int32_t> shared;
   uint64_t h = kSeed;
   for (int32_t i = 0; i < max_hit; ++i) {
-    const uint64_t key = chain(h, tokens + (size_t)i * kBlockSize);
+    const uint64_t key = chain(h, tokens + (size_t)i * bs, bs);
     auto it = bm->cache.find(key);
     if (it == bm->cache.end()) break;
     const int32_t b = it->second;
     if (bm->cached_parent[b] != (i == 0 ? -1 : shared.back())) break;
     if (!std::equal(bm->cached_tokens[b].begin(), bm->cached_tokens[b].end(),
-                    tokens + (size_t)i * kBlockSize))
+                    tokens + (size_t)i * bs))
       break;
     shared.push_back(b);
     h = key;
   }
   const int32_t hit = (int32_t)shared.size();
-  const int32_t fresh = (n + kBlockSize - 1) / kBlockSize - hit;
+  const int32_t fresh = (n + bs - 1) / bs - hit;
   if (fresh > (int32_t)bm->free_list.size())
     return pa::set_error(PA_E_NO_BLOCKS, "pa_bm_add: not enough free blocks for the prompt");
   for (int32_t b : shared) ++bm->refs[b];
@@ -249,13 +251,13 @@ pa_status_t pa_bm_add(pa_block_manager_t *bm, int64_t req, const int32_t *tokens
   r.blocks = shared;
   r.host.assign(shared.size(), -1);
   r.stamp = bm->steps;
-  r.tokens.assign(tokens, tokens + (size_t)hit * kBlockSize);
-  r.written = hit * kBlockSize;
+  r.tokens.assign(tokens, tokens + (size_t)hit * bs);
+  r.written = hit * bs;
   r.published = hit;
   r.hash = h;
   Request &rr = bm->reqs.emplace(req, std::move(r)).first->second;
-  bm->append(rr, tokens + (size_t)hit * kBlockSize, n - hit * kBlockSize);  // fits: checked
-  if (cached) *cached = hit * kBlockSize;
+  bm->append(rr, tokens + (size_t)hit * bs, n - hit * bs);  // fits: checked
+  if (cached) *cached = hit * bs;
   return PA_OK;
 }
 

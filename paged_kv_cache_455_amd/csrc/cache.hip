@@ -14,9 +14,9 @@
 namespace pa {
 
 // Logical position of query row t of sequence s is seq_len - q_len + i; its
-// slot is block_table[s][pos / 16] * 16 + pos % 16.
+// slot is block_table[s][pos / bs] * bs + pos % bs (bs = 16 or 32 tokens).
 __global__ __launch_bounds__(256) void pa_slot_mapping_kernel(const int32_t *bt, int32_t mbps,
-                                                              const int32_t *qsl,
+                                                              int32_t bs, const int32_t *qsl,
                                                               const int32_t *seq_lens,
                                                               int64_t *slots) {
   const int s = blockIdx.x;
@@ -26,7 +26,7 @@ __global__ __launch_bounds__(256) void pa_slot_mapping_kernel(const int32_t *bt,
   const int32_t *row = bt + (int64_t)s * mbps;
   for (int i = threadIdx.x; i < q_len; i += blockDim.x) {
     const int pos = first + i;
-    slots[a + i] = (int64_t)row[pos / kBlock] * kBlock + pos % kBlock;
+    slots[a + i] = (int64_t)row[pos / bs] * bs + pos % bs;
   }
 }
 
@@ -44,12 +44,12 @@ __global__ __launch_bounds__(256) void kv_cache_write_kernel(CacheWriteArgs a, i
     const int64_t t = row / a.num_kv_heads;
     const int64_t slot = a.slots[t];
     if (slot < 0) continue;
-    const int64_t blk = slot / kBlock;
-    const int off = (int)(slot % kBlock);
+    const int64_t blk = slot / a.block_size;
+    const int off = (int)(slot % a.block_size);
     const char *src = reinterpret_cast<const char *>(is_v ? a.v_new : a.k_new) +
                       row * a.row_bytes + c * 16;
     char *dst = reinterpret_cast<char *>(is_v ? a.v : a.k) +
-                ((blk * a.num_kv_heads + h) * kBlock + off) * (int64_t)a.row_bytes + c * 16;
+                ((blk * a.num_kv_heads + h) * a.block_size + off) * (int64_t)a.row_bytes + c * 16;
     *reinterpret_cast<u32x4 *>(dst) = *reinterpret_cast<const u32x4 *>(src);
   }
 }
@@ -102,20 +102,21 @@ __global__ __launch_bounds__(64) void kv_cache_write_quant_kernel(CacheWriteArgs
   const bool is_v = blockIdx.z != 0;
   const int64_t slot = a.slots[t];
   if (slot < 0) return;
-  const int64_t blk = slot / kBlock;
-  const int off = (int)(slot % kBlock);
+  const int bs = a.block_size;
+  const int64_t blk = slot / bs;
+  const int off = (int)(slot % bs);
   if (t > 0) {  // not the first row of its run: the run's first row does the work
     const int64_t prev = a.slots[t - 1];
-    if (prev >= 0 && prev / kBlock == blk) return;
+    if (prev >= 0 && prev / bs == blk) return;
   }
   int len = 1;
-  while (len < kBlock - off && t + len < a.num_tokens && a.slots[t + len] >= 0 &&
-         a.slots[t + len] / kBlock == blk)
+  while (len < bs - off && t + len < a.num_tokens && a.slots[t + len] >= 0 &&
+         a.slots[t + len] / bs == blk)
     ++len;
 
   const void *src = is_v ? a.v_new : a.k_new;
   uint8_t *tile = reinterpret_cast<uint8_t *>(is_v ? a.v : a.k) +
-                  (blk * a.num_kv_heads + h) * (int64_t)(kBlock * D);
+                  (blk * a.num_kv_heads + h) * (int64_t)(bs * D);
   float *scale = (is_v ? a.v_scale : a.k_scale) + blk * a.num_kv_heads + h;
   const int d0 = lane * EPL;
 
@@ -178,10 +179,12 @@ static int grid_for(int64_t total) {
   return (int)(g < 8192 ? (g < 1 ? 1 : g) : 8192);
 }
 
-hipError_t launch_slot_mapping(const int32_t *bt, int32_t mbps, const int32_t *qsl,
+hipError_t launch_slot_mapping(const int32_t *bt, int32_t mbps, int32_t block_size,
+                               const int32_t *qsl,
                                const int32_t *seq_lens, int32_t num_seqs, int64_t *slots,
                                hipStream_t st) {
-  hipLaunchKernelGGL(pa_slot_mapping_kernel, dim3(num_seqs), dim3(256), 0, st, bt, mbps, qsl,
+  hipLaunchKernelGGL(pa_slot_mapping_kernel, dim3(num_seqs), dim3(256), 0, st, bt, mbps,
+                     block_size, qsl,
                      seq_lens, slots);
   return hipGetLastError();
 }

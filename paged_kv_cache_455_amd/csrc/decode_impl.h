@@ -438,7 +438,7 @@ __device__ __forceinline__ void decode_partition(const DecodeArgs &a, int s, int
   float ksA = 1.f, vsA = 1.f, ksB = 1.f, vsB = 1.f;
 
   auto load_tile = [&](int j, Chunk<W32> *kc, Chunk<W32> *vc, float &ks, float &vs) {
-    const int64_t tile = (int64_t)bt[j] * a.num_kv_heads + h;
+    const int64_t tile = tile_index(bt[j >> a.bs_shift], a.num_kv_heads, h, j, a.bs_shift);
     const char *kp = kbase + tile * Gm::TILE_BYTES + lane_off;
     const char *vp = vbase + tile * Gm::TILE_BYTES + lane_off;
 #pragma unroll
@@ -446,8 +446,8 @@ __device__ __forceinline__ void decode_partition(const DecodeArgs &a, int s, int
 #pragma unroll
     for (int i = 0; i < NL; ++i) vc[i] = load_chunk<W32>(vp + i * kWave * Gm::CB);
     if (quant) {
-      ks = a.k_scale[tile];
-      vs = a.v_scale[tile];
+      ks = a.k_scale[tile >> a.bs_shift];
+      vs = a.v_scale[tile >> a.bs_shift];
     }
   };
   constexpr bool kFast = FastGeom<KV, D, G>::kOn;
@@ -798,11 +798,12 @@ __device__ __forceinline__ void stream_run(const DecodeArgs &a, P &path, int w, 
   const int Hkv = a.num_kv_heads, n = rg.n;
   SeqWindow win;
   win.load(a, rg.seg.s, lane);
+  const int sh = a.bs_shift;
   auto bt_of = [&](const StreamSeg &sg, int j) {
-    return a.bt[(int64_t)sg.s * a.max_blocks_per_seq + j];
+    return a.bt[(int64_t)sg.s * a.max_blocks_per_seq + (j >> sh)];
   };
-  auto tile_of = [&](int bt, const StreamSeg &sg) {
-    return (int64_t)__builtin_amdgcn_readfirstlane(bt) * Hkv + sg.h;
+  auto tile_of = [&](int bt, const StreamSeg &sg, int j) {
+    return tile_index(__builtin_amdgcn_readfirstlane(bt), Hkv, sg.h, j, sh);
   };
 
   // stage 0 (compute): sg0, j0; stage 1 (loads in flight): sg1, j1, bt1
@@ -813,7 +814,7 @@ __device__ __forceinline__ void stream_run(const DecodeArgs &a, P &path, int w, 
   if (n > 1) stream_step(a, win, sg1, j1, lane);
   int bt1 = bt_of(sg1, j1);
   typename P::Tile tA, tB;
-  path.load(tA, tile_of(bt0, sg0));
+  path.load(tA, tile_of(bt0, sg0, j0));
   path.begin_segment();
 
   // compute tile (sg0, j0); emit its segment when it ends there or the range does
@@ -834,7 +835,7 @@ __device__ __forceinline__ void stream_run(const DecodeArgs &a, P &path, int w, 
     if (k + 2 < n) stream_step(a, win, sg2, j2, lane);
     const int bt2 = bt_of(sg2, j2);  // (a repeat of tile k+1's entry at the end)
     if (j1 == 0) path.prefetch_q(sg1);
-    path.load(nxt, tile_of(bt1, sg1));
+    path.load(nxt, tile_of(bt1, sg1, j1));
     finish(cur, true);
     sg0 = sg1;
     j0 = j1;
@@ -888,8 +889,8 @@ struct GenericPath {
 #pragma unroll
     for (int i = 0; i < NL; ++i) t.v[i] = load_chunk<W32, NT>(vp + i * kWave * Gm::CB);
     if constexpr (kQuant) {
-      t.ks = a.k_scale[tile];
-      t.vs = a.v_scale[tile];
+      t.ks = a.k_scale[tile >> a.bs_shift];
+      t.vs = a.v_scale[tile >> a.bs_shift];
     } else {
       t.ks = t.vs = 1.f;
     }
@@ -1180,8 +1181,8 @@ struct Q8Path {
     const char *vp = vbase + tile * kTileBytes;
 #pragma unroll
     for (int i = 0; i < 4; ++i) t.v[i] = load_tile_part<u32x2, NT>(vp + i * D);
-    t.ks = a.k_scale[tile];
-    t.vs = a.v_scale[tile];
+    t.ks = a.k_scale[tile >> a.bs_shift];
+    t.vs = a.v_scale[tile >> a.bs_shift];
   }
   __device__ __forceinline__ void prefetch_q(const StreamSeg &sg) {
 #pragma unroll

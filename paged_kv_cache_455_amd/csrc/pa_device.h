@@ -8,9 +8,17 @@
 
 namespace pa {
 
-constexpr int kBlock = 16;            // tokens per physical block
+constexpr int kBlock = 16;            // rows per tile (a physical block holds 1 or 2 tiles)
 constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
+
+// A physical block holds 16 << sh tokens (16 or 32, 5688vip chapter 3, section
+// 3.2): per kv head, 1 << sh tiles of 16 rows, contiguous.  The 16-row tile
+// index of a sequence's logical tile j, whose table entry is blk; the
+// (block, kv head) scale of a 1-byte pool sits at index tile >> sh.
+__device__ __forceinline__ int64_t tile_index(int blk, int hkv, int h, int j, int sh) {
+  return (((int64_t)blk * hkv + h) << sh) + (j & ((1 << sh) - 1));
+}
 // Running-max sentinel: finite so that exp2(sentinel - sentinel) = 1 keeps an
 // empty lane's (m, l, acc) = (sentinel, 0, 0) harmless in every merge.
 constexpr float kNegBig = -1.0e30f;

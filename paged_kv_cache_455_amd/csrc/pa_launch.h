@@ -33,6 +33,7 @@ struct DecodeArgs {
   int32_t num_waves;    // waves launched
   int32_t min_tpw;      // lower bound on cost units per wave
   int32_t seg_cost;     // cost units charged for each (sequence, kv head) segment start
+  int32_t bs_shift;     // log2(block size / 16): tiles of 16 rows per block, as a shift
   // mixed step: [num_seqs + 1] query starts; only q_len == 1 sequences are decoded,
   // sequence s's query/output row being qsl[s] (nullptr: every sequence, row s)
   const int32_t *qsl;
@@ -60,7 +61,8 @@ struct CacheWriteArgs {
   int64_t num_blocks;
   int32_t num_tokens;
   int32_t num_kv_heads;
-  int32_t row_bytes;  // head_dim * element bytes
+  int32_t row_bytes;   // head_dim * element bytes
+  int32_t block_size;  // tokens per physical block (16 or 32)
 };
 
 // Block tiles (and scales) copied from one pool to another of the same geometry;
@@ -102,7 +104,8 @@ hipError_t launch_cache_write(const CacheWriteArgs &a, hipStream_t st);
 hipError_t launch_cache_write_quant(const CacheWriteArgs &a, int kv_dtype, int src_dtype,
                                     int head_dim, hipStream_t st);
 hipError_t launch_block_copy(const BlockCopyArgs &a, hipStream_t st);
-hipError_t launch_slot_mapping(const int32_t *bt, int32_t mbps, const int32_t *qsl,
+hipError_t launch_slot_mapping(const int32_t *bt, int32_t mbps, int32_t block_size,
+                               const int32_t *qsl,
                                const int32_t *seq_lens, int32_t num_seqs, int64_t *slots,
                                hipStream_t st);
 

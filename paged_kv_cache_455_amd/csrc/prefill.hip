@@ -155,20 +155,21 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
   // ---- global -> registers -> LDS staging of one 32-key step ----
   const char *kpool = reinterpret_cast<const char *>(d.k);
   const char *vpool = reinterpret_cast<const char *>(d.v);
-  // block-table entries of step n's two blocks (clamped to the last block)
+  // 16-row tile indices of step n's two tiles (clamped to the last tile)
   struct StepBt {
-    int b0, b1;
+    int64_t u0, u1;
   };
+  const int sh = d.bs_shift;
   auto bt_load = [&](int n) {
+    const int j0 = min(2 * n, nblk - 1), j1 = min(2 * n + 1, nblk - 1);
     StepBt r;
-    r.b0 = bt[min(2 * n, nblk - 1)];
-    r.b1 = bt[min(2 * n + 1, nblk - 1)];
+    r.u0 = tile_index(bt[j0 >> sh], Hkv, h, j0, sh);
+    r.u1 = tile_index(bt[j1 >> sh], Hkv, h, j1, sh);
     return r;
   };
-  // byte offset of key row `key` (0..31 within the step) in its (block, h) tile
+  // byte offset of key row `key` (0..31 within the step) in its 16-row tile
   auto row_off = [&](const StepBt &b, int key) {
-    const int64_t tile = (int64_t)(key < kBlock ? b.b0 : b.b1) * Hkv + h;
-    return (tile * kBlock + (key % kBlock)) * D * 2;
+    return ((key < kBlock ? b.u0 : b.u1) * kBlock + (key % kBlock)) * D * 2;
   };
   // K: chunk q of the step = key q / CPR, 16-byte column q % CPR.
   // V: thread tid < NVB owns dims 4*(tid % (D/4)) .. +3 of keys 4*(tid / (D/4)) .. +3

@@ -59,7 +59,7 @@ class PagedBatch:
     head_dim: int
     scale: float
     q: torch.Tensor                # [T][Hq][D]
-    k_pool: torch.Tensor           # [NB][Hkv][16][D]
+    k_pool: torch.Tensor           # [NB][Hkv][block_size][D]
     v_pool: torch.Tensor
     block_tables: torch.Tensor     # int32 [S][MB], -1 past the last used block
     seq_lens: torch.Tensor         # int32 [S], KV length including this step's tokens
@@ -70,6 +70,7 @@ class PagedBatch:
     v_new: Optional[torch.Tensor] = None
     copy_pairs: Optional[torch.Tensor] = None  # int32 [P][2] (src, dst)
     extra: dict = field(default_factory=dict)
+    block_size: int = BLOCK        # tokens per block, 16 or 32 (the pools' third axis)
 
     @property
     def num_seqs(self) -> int:
@@ -93,7 +94,7 @@ class PagedBatch:
         entries (prefix sharing): the pool is then declared with shared blocks."""
         used = []
         for s in range(self.num_seqs):
-            nb = (int(self.seq_lens[s]) + 15) // 16
+            nb = -(-int(self.seq_lens[s]) // self.block_size)
             used.append(self.block_tables[s, :nb])
         ids = torch.cat(used) if used else torch.empty(0, dtype=torch.int32)
         return int(torch.unique(ids).numel()) < int(ids.numel())
@@ -130,16 +131,16 @@ def _deal_tables(perm: np.ndarray, blocks_per_seq: List[int], start: int = 0):
     return bt, i
 
 
-def _float_pool(rng, nb, hkv, d, div, dt, chunk=2048):
-    """[nb][hkv][16][d] of N(0,1)/div, drawn in chunks to bound host memory."""
-    out = torch.empty((nb, hkv, BLOCK, d), dtype=TORCH_DTYPE[dt])
+def _float_pool(rng, nb, hkv, d, div, dt, chunk=2048, bs=BLOCK):
+    """[nb][hkv][bs][d] of N(0,1)/div, drawn in chunks to bound host memory."""
+    out = torch.empty((nb, hkv, bs, d), dtype=TORCH_DTYPE[dt])
     for a in range(0, nb, chunk):
         b = min(nb, a + chunk)
-        out[a:b] = _cast(_normal(rng, (b - a, hkv, BLOCK, d), div), dt)
+        out[a:b] = _cast(_normal(rng, (b - a, hkv, bs, d), div), dt)
     return out
 
 
-def _quantised_pool(rng, nb, hkv, d, div, kv, chunk=2048):
+def _quantised_pool(rng, nb, hkv, d, div, kv, chunk=2048, bs=BLOCK):
     """Codes and per-(block, kv head) scales for N(0,1)/div data.
 
     Each (block, head) tile gets ``scale = amax(|tile|) / qmax`` (qmax 448 for
@@ -149,11 +150,11 @@ def _quantised_pool(rng, nb, hkv, d, div, kv, chunk=2048):
     does not enter the comparison, which decodes the same stored codes.
     """
     qmax = 448.0 if kv == "fp8" else 127.0
-    codes = torch.empty((nb, hkv, BLOCK, d), dtype=TORCH_DTYPE[kv])
+    codes = torch.empty((nb, hkv, bs, d), dtype=TORCH_DTYPE[kv])
     scales = torch.empty((nb, hkv), dtype=torch.float32)
     for a in range(0, nb, chunk):
         b = min(nb, a + chunk)
-        x = torch.from_numpy(_normal(rng, (b - a, hkv, BLOCK, d), div))
+        x = torch.from_numpy(_normal(rng, (b - a, hkv, bs, d), div))
         amax = x.abs().amax(dim=(2, 3))
         sc = torch.where(amax > 0, amax / qmax, torch.ones_like(amax))
         y = x / sc[:, :, None, None]
@@ -191,7 +192,7 @@ def _used_mask(bt: np.ndarray, nb: int) -> np.ndarray:
 def decode_batch(seed: int, ctx, hq: int, hkv: int, d: int, kv: str, qd: str, *,
                  div: float = 1.0, pool_blocks: Optional[int] = None, pool_extra: float = 0.10,
                  scale: Optional[float] = None, poison: bool = False, name: str = "decode",
-                 with_new: bool = True) -> PagedBatch:
+                 with_new: bool = True, block_size: int = BLOCK) -> PagedBatch:
     """One query token per sequence against ``ctx[s]`` cached tokens.
 
     Physical blocks come from one seeded permutation of the pool, dealt in
@@ -201,7 +202,8 @@ def decode_batch(seed: int, ctx, hq: int, hkv: int, d: int, kv: str, qd: str, *,
     """
     rng = np.random.default_rng(seed)
     ctx = np.asarray(ctx, dtype=np.int64)
-    nbs = [int(-(-int(n) // BLOCK)) for n in ctx]
+    bs = block_size
+    nbs = [int(-(-int(n) // bs)) for n in ctx]
     need = sum(nbs)
     nb = pool_blocks if pool_blocks is not None else int(math.ceil((1.0 + pool_extra) * need))
     assert nb >= need
@@ -212,16 +214,16 @@ def decode_batch(seed: int, ctx, hq: int, hkv: int, d: int, kv: str, qd: str, *,
     if kv in QUANTISED:
         # the draw order does not depend on kv, so an fp8 and an int8 batch with the
         # same seed quantise the same N(0,1) data
-        k_pool, k_scale = _quantised_pool(rng, nb, hkv, d, div, kv)
-        v_pool, v_scale = _quantised_pool(rng, nb, hkv, d, div, kv)
+        k_pool, k_scale = _quantised_pool(rng, nb, hkv, d, div, kv, bs=bs)
+        v_pool, v_scale = _quantised_pool(rng, nb, hkv, d, div, kv, bs=bs)
         if with_new:  # this step's K/V in the model's dtype, quantised on write
             k_new = _cast(_normal(rng, (S, hkv, d), div), qd)
             v_new = _cast(_normal(rng, (S, hkv, d), div), qd)
         else:
             k_new = v_new = None
     else:
-        k_pool = _float_pool(rng, nb, hkv, d, div, kv)
-        v_pool = _float_pool(rng, nb, hkv, d, div, kv)
+        k_pool = _float_pool(rng, nb, hkv, d, div, kv, bs=bs)
+        v_pool = _float_pool(rng, nb, hkv, d, div, kv, bs=bs)
         k_scale = v_scale = None
         if with_new:
             k_new = _cast(_normal(rng, (S, hkv, d), div), kv)
@@ -238,7 +240,7 @@ def decode_batch(seed: int, ctx, hq: int, hkv: int, d: int, kv: str, qd: str, *,
         k_pool=k_pool, v_pool=v_pool, block_tables=torch.from_numpy(bt),
         seq_lens=torch.from_numpy(ctx.astype(np.int32)),
         query_start_loc=torch.arange(S + 1, dtype=torch.int32),
-        k_scale=k_scale, v_scale=v_scale, k_new=k_new, v_new=v_new)
+        k_scale=k_scale, v_scale=v_scale, k_new=k_new, v_new=v_new, block_size=bs)
 
 
 # ----------------------------------------------------------------------------------
@@ -246,7 +248,8 @@ def decode_batch(seed: int, ctx, hq: int, hkv: int, d: int, kv: str, qd: str, *,
 # ----------------------------------------------------------------------------------
 def fork_batch(seed: int, n_req: int, prefix_tokens: int, suffix_lo: int, suffix_hi: int,
                n_forks: int, hq: int, hkv: int, d: int, kv: str, qd: str, *, div: float = 1.0,
-               pool_extra: float = 0.10, poison: bool = False, name: str = "fork") -> PagedBatch:
+               pool_extra: float = 0.10, poison: bool = False, name: str = "fork",
+               block_size: int = BLOCK) -> PagedBatch:
     """Requests over one shared prefix; some are forked just before a decode step.
 
     Request ``r`` holds ``L_r = prefix + suffix_r`` cached tokens; the prefix's
@@ -258,15 +261,16 @@ def fork_batch(seed: int, n_req: int, prefix_tokens: int, suffix_lo: int, suffix
     batch has ``n_req + n_forks`` decode rows (parents first, then children in
     fork order), each with context ``L + 1``.
     """
-    assert prefix_tokens % BLOCK == 0
+    bs = block_size
+    assert prefix_tokens % bs == 0
     rng = np.random.default_rng(seed)
     suffix = rng.integers(suffix_lo, suffix_hi, size=n_req, endpoint=True)
     L = prefix_tokens + suffix
-    eligible = np.nonzero(L % BLOCK != 0)[0]
+    eligible = np.nonzero(L % bs != 0)[0]
     forks = np.sort(rng.choice(eligible, size=n_forks, replace=False)) if n_forks else np.zeros(0, np.int64)
-    pre_blocks = prefix_tokens // BLOCK
-    # blocks each request needs after its new token: ceil((L+1)/16)
-    own = [int(-(-(int(l) + 1) // BLOCK)) - pre_blocks for l in L]
+    pre_blocks = prefix_tokens // bs
+    # blocks each request needs after its new token: ceil((L+1)/bs)
+    own = [int(-(-(int(l) + 1) // bs)) - pre_blocks for l in L]
     need = pre_blocks + sum(own) + n_forks
     nb = int(math.ceil((1.0 + pool_extra) * need))
     perm = rng.permutation(nb).astype(np.int32)
@@ -289,8 +293,8 @@ def fork_batch(seed: int, n_req: int, prefix_tokens: int, suffix_lo: int, suffix
     ctx = np.concatenate([L + 1, L[forks] + 1]).astype(np.int32)
     S = len(ctx)
     q = _cast(_normal(rng, (S, hq, d), div), qd)
-    k_pool = _float_pool(rng, nb, hkv, d, div, kv)
-    v_pool = _float_pool(rng, nb, hkv, d, div, kv)
+    k_pool = _float_pool(rng, nb, hkv, d, div, kv, bs=bs)
+    v_pool = _float_pool(rng, nb, hkv, d, div, kv, bs=bs)
     k_new = _cast(_normal(rng, (S, hkv, d), div), kv)
     v_new = _cast(_normal(rng, (S, hkv, d), div), kv)
     if poison:
@@ -303,7 +307,7 @@ def fork_batch(seed: int, n_req: int, prefix_tokens: int, suffix_lo: int, suffix
         block_tables=torch.from_numpy(bt), seq_lens=torch.from_numpy(ctx),
         query_start_loc=torch.arange(S + 1, dtype=torch.int32), k_new=k_new, v_new=v_new,
         copy_pairs=torch.tensor(pairs, dtype=torch.int32).reshape(-1, 2),
-        extra={"forks": forks, "n_req": n_req, "shared_blocks": shared.copy()})
+        extra={"forks": forks, "n_req": n_req, "shared_blocks": shared.copy()}, block_size=bs)
 
 
 # ----------------------------------------------------------------------------------
@@ -313,7 +317,7 @@ def mixed_batch(seed: int, n_chunks: int, chunk_len: int, prior_lo: int, prior_h
                 n_dec: int, dec_median: float, dec_sigma: float, dec_lo: int, dec_hi: int,
                 hq: int, hkv: int, d: int, kv: str, qd: str, *, div: float = 1.0,
                 pool_extra: float = 0.10, poison: bool = False, priors=None, dec_ctx=None,
-                name: str = "mixed") -> PagedBatch:
+                name: str = "mixed", block_size: int = BLOCK) -> PagedBatch:
     """Chunked prefills and decodes in one batch.
 
     Chunk ``i`` adds ``chunk_len`` tokens on top of ``prior_i`` cached tokens
@@ -332,15 +336,16 @@ def mixed_batch(seed: int, n_chunks: int, chunk_len: int, prior_lo: int, prior_h
     seq_lens = np.concatenate([priors + chunk_len, dec_ctx]).astype(np.int32)
     q_lens = np.concatenate([np.full(len(priors), chunk_len), np.ones(len(dec_ctx))]).astype(np.int32)
     qsl = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
-    nbs = [int(-(-int(n) // BLOCK)) for n in seq_lens]
+    bs = block_size
+    nbs = [int(-(-int(n) // bs)) for n in seq_lens]
     need = sum(nbs)
     nb = int(math.ceil((1.0 + pool_extra) * need))
     perm = rng.permutation(nb).astype(np.int32)
     bt, _ = _deal_tables(perm, nbs)
     T = int(qsl[-1])
     q = _cast(_normal(rng, (T, hq, d), div), qd)
-    k_pool = _float_pool(rng, nb, hkv, d, div, kv)
-    v_pool = _float_pool(rng, nb, hkv, d, div, kv)
+    k_pool = _float_pool(rng, nb, hkv, d, div, kv, bs=bs)
+    v_pool = _float_pool(rng, nb, hkv, d, div, kv, bs=bs)
     k_new = _cast(_normal(rng, (T, hkv, d), div), kv)
     v_new = _cast(_normal(rng, (T, hkv, d), div), kv)
     if poison:
@@ -352,50 +357,52 @@ def mixed_batch(seed: int, n_chunks: int, chunk_len: int, prior_lo: int, prior_h
         head_dim=d, scale=1.0 / math.sqrt(d), q=q, k_pool=k_pool, v_pool=v_pool,
         block_tables=torch.from_numpy(bt), seq_lens=torch.from_numpy(seq_lens),
         query_start_loc=torch.from_numpy(qsl), k_new=k_new, v_new=v_new,
-        extra={"n_chunks": len(priors), "chunk_len": chunk_len})
+        extra={"n_chunks": len(priors), "chunk_len": chunk_len}, block_size=bs)
 
 
 # ----------------------------------------------------------------------------------
 # the five named workloads
 # ----------------------------------------------------------------------------------
-def tiny_fp32(poison: bool = True) -> PagedBatch:
+def tiny_fp32(poison: bool = True, block_size: int = BLOCK) -> PagedBatch:
     """Contexts {5,16,17,40}, Hq 4 / Hkv 2, D 64, fp32, pool 32 blocks."""
     return decode_batch(1, [5, 16, 17, 40], 4, 2, 64, "f32", "f32", pool_blocks=32,
-                        scale=1.0 / 8.0, poison=poison, name="tiny-fp32")
+                        scale=1.0 / 8.0, poison=poison, name="tiny-fp32", block_size=block_size)
 
 
 def llama3_8b_decode(batch: int = 64, ctx_lo: int = 128, ctx_hi: int = 4096, seed: int = 2,
-                     poison: bool = False) -> PagedBatch:
+                     poison: bool = False, block_size: int = BLOCK) -> PagedBatch:
     """Llama-3-8B-shaped decode layer: Hq 32 / Hkv 8, D 128, fp16, N(0,1)/sqrt(128)."""
     rng = np.random.default_rng(seed)
     ctx = rng.integers(ctx_lo, ctx_hi, size=batch, endpoint=True)
     return decode_batch(seed + 1000, ctx, 32, 8, 128, "f16", "f16", div=math.sqrt(128.0),
-                        poison=poison, name=f"llama3-8b-decode-b{batch}")
+                        poison=poison, name=f"llama3-8b-decode-b{batch}", block_size=block_size)
 
 
 def prefix_cow(n_req: int = 128, suffix_hi: int = 2048, n_forks: int = 16, seed: int = 3,
-               poison: bool = False) -> PagedBatch:
+               poison: bool = False, block_size: int = BLOCK) -> PagedBatch:
     """128 requests over a 1024-token shared prefix, 16 forks, bf16, Llama-3-8B heads."""
     return fork_batch(seed, n_req, 1024, 16, suffix_hi, n_forks, 32, 8, 128, "bf16", "bf16",
-                      div=math.sqrt(128.0), poison=poison, name=f"prefix-cow-r{n_req}")
+                      div=math.sqrt(128.0), poison=poison, name=f"prefix-cow-r{n_req}",
+                      block_size=block_size)
 
 
 def mixed_step(n_chunks: int = 8, chunk_len: int = 512, n_dec: int = 256, seed: int = 4,
-               poison: bool = False, priors=None) -> PagedBatch:
+               poison: bool = False, priors=None, block_size: int = BLOCK) -> PagedBatch:
     """8 chunks x 512 over 0..2048 prior tokens + 256 lognormal decodes, fp16."""
     return mixed_batch(seed, n_chunks, chunk_len, 0, 2048, n_dec, 600.0, 1.0, 16, 8192,
                        32, 8, 128, "f16", "f16", div=math.sqrt(128.0), poison=poison,
-                       priors=priors, name=f"mixed-c{n_chunks}x{chunk_len}-d{n_dec}")
+                       priors=priors, name=f"mixed-c{n_chunks}x{chunk_len}-d{n_dec}",
+                       block_size=block_size)
 
 
 def long_quantised(kv: str = "fp8", batch: int = 16, ctx: int = 32768, seed: int = 5,
-                   poison: bool = False) -> PagedBatch:
+                   poison: bool = False, block_size: int = BLOCK) -> PagedBatch:
     """16 x 32768 tokens, Hq 64 / Hkv 8, D 128, fp8 or int8 KV, bf16 q/out.
 
     The int8 batch quantises the same N(0,1) draws as the fp8 batch.
     """
     return decode_batch(seed, [ctx] * batch, 64, 8, 128, kv, "bf16", poison=poison,
-                        name=f"long-{kv}-b{batch}x{ctx}")
+                        name=f"long-{kv}-b{batch}x{ctx}", block_size=block_size)
 
 
 WORKLOADS = {

@@ -37,13 +37,14 @@ def poison_tails(b: W.PagedBatch):
     vf = b.v_pool.view(-1, b.head_dim)
     hkv = b.num_kv_heads
     bad = 0x7F if b.kv_dtype == "fp8" else (127 if b.kv_dtype == "i8" else float("nan"))
+    bs = b.block_size
     for s, n in enumerate(b.seq_lens.tolist()):
-        nb = -(-n // W.BLOCK)
-        for pos in range(n, nb * W.BLOCK):
-            slot = oracle.slot_for_position(bt[s], pos)
-            blk, off = divmod(slot, W.BLOCK)
+        nb = -(-n // bs)
+        for pos in range(n, nb * bs):
+            slot = oracle.slot_for_position(bt[s], pos, bs)
+            blk, off = divmod(slot, bs)
             for h in range(hkv):
-                r = (blk * hkv + h) * W.BLOCK + off
+                r = (blk * hkv + h) * bs + off
                 kf[r] = bad
                 vf[r] = bad
     return b
@@ -56,7 +57,7 @@ def oracle_slots(b: W.PagedBatch) -> np.ndarray:
     for s, n in enumerate(b.seq_lens.tolist()):
         q_len = int(qsl[s + 1] - qsl[s])
         for i in range(q_len):
-            out.append(oracle.slot_for_position(bt[s], n - q_len + i))
+            out.append(oracle.slot_for_position(bt[s], n - q_len + i, b.block_size))
     return np.array(out, dtype=np.int64)
 
 

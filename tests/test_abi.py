@@ -60,7 +60,7 @@ def decode(lib, p, q_dtype=pa.PA_F16, hq=32, S=4, max_ctx=100, mbps=10, ws=None,
 
 
 def test_decode_argument_checks(lib):
-    assert decode(lib, pool(block=32)) == PA_E_UNSUPPORTED
+    assert decode(lib, pool(block=24)) == PA_E_UNSUPPORTED
     assert decode(lib, pool(head_dim=96)) == PA_E_UNSUPPORTED
     assert decode(lib, pool(), hq=30) == PA_E_ARG                      # 30 % 8 != 0
     assert decode(lib, pool(), hq=8 * 16) == PA_E_UNSUPPORTED         # group 16
@@ -112,7 +112,8 @@ def test_write_copy_slot_checks(lib):
     assert lib.kv_block_copy(ctypes.byref(p), None, 3, None) == PA_E_ARG
     assert lib.kv_block_copy(ctypes.byref(p), FAKE, 0, None) == PA_OK
     assert lib.kv_block_copy(ctypes.byref(pool(kv=pa.PA_FP8_E4M3)), FAKE, 2, None) == PA_E_ARG
-    assert lib.pa_slot_mapping(None, 4, FAKE, FAKE, 3, 3, FAKE, None) == PA_E_ARG
+    assert lib.pa_slot_mapping(None, 4, 16, FAKE, FAKE, 3, 3, FAKE, None) == PA_E_ARG
+    assert lib.pa_slot_mapping(FAKE, 4, 24, FAKE, FAKE, 3, 3, FAKE, None) == PA_E_UNSUPPORTED
     # quantise-on-write: 1-byte pools only, float sources only, scales required
     qw = lambda pl, sd=pa.PA_BF16, n=4: lib.kv_cache_write_quant(ctypes.byref(pl), FAKE, FAKE, sd,
                                                                  FAKE, n, None)
@@ -121,7 +122,7 @@ def test_write_copy_slot_checks(lib):
     assert qw(pool(kv=pa.PA_FP8_E4M3, scales=True), sd=pa.PA_I8) == PA_E_UNSUPPORTED
     assert qw(pool(kv=pa.PA_I8, scales=True), n=-1) == PA_E_ARG
     assert qw(pool(kv=pa.PA_I8, scales=True), n=0) == PA_OK
-    assert lib.pa_slot_mapping(FAKE, 4, FAKE, FAKE, 0, 0, FAKE, None) == PA_OK
+    assert lib.pa_slot_mapping(FAKE, 4, 16, FAKE, FAKE, 0, 0, FAKE, None) == PA_OK
 
 
 def test_prefill_argument_checks(lib):

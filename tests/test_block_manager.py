@@ -35,9 +35,10 @@ def lib():
 class DevicePoolModel:
     """The device side of the step protocol on pools of prefix ids."""
 
-    def __init__(self, num_blocks, num_host=0):
-        self.cells = [[None] * BS for _ in range(num_blocks)]
-        self.host = [[None] * BS for _ in range(num_host)]
+    def __init__(self, num_blocks, num_host=0, bs=BS):
+        self.bs = bs
+        self.cells = [[None] * bs for _ in range(num_blocks)]
+        self.host = [[None] * bs for _ in range(num_host)]
         self.prefix_ids = {}
 
     def pid(self, prefix):
@@ -56,13 +57,14 @@ class DevicePoolModel:
 
     def read_back(self, bm, r, toks):
         """Every written row of request r, found on the device or in a host slot."""
+        bs = self.bs
         dev, host = bm.blocks(r)
-        assert len(dev) == -(-len(toks) // BS)
+        assert len(dev) == -(-len(toks) // bs)
         for pos in range(len(toks)):
-            i = pos // BS
+            i = pos // bs
             cell = self.cells[dev[i]] if dev[i] >= 0 else self.host[host[i]]
             assert (dev[i] >= 0) != (host[i] >= 0)
-            assert cell[pos % BS] == self.pid(toks[:pos + 1]), (r, pos, dev[i], host[i])
+            assert cell[pos % bs] == self.pid(toks[:pos + 1]), (r, pos, dev[i], host[i])
 
     def run_step(self, reqs, history, bt, lens, qsl, pairs):
         srcs, dsts = [int(p[0]) for p in pairs], [int(p[1]) for p in pairs]
@@ -72,20 +74,21 @@ class DevicePoolModel:
         for s, d in zip(srcs, dsts):
             self.cells[d] = list(rows[s])
         written = set()
+        bs = self.bs
         for i, r in enumerate(reqs):
             toks, n = history[r], int(lens[i])
             assert n == len(toks)
             for pos in range(n - (qsl[i + 1] - qsl[i]), n):   # the query rows
-                slot = int(bt[i][pos // BS]) * BS + pos % BS
+                slot = int(bt[i][pos // bs]) * bs + pos % bs
                 assert slot not in written, "slot written twice in one step"
                 written.add(slot)
-                self.cells[slot // BS][slot % BS] = self.pid(toks[:pos + 1])
+                self.cells[slot // bs][slot % bs] = self.pid(toks[:pos + 1])
         for i, r in enumerate(reqs):                           # attention reads
             toks = history[r]
             for pos in range(len(toks)):
-                b = int(bt[i][pos // BS])
-                assert self.cells[b][pos % BS] == self.pid(toks[:pos + 1]), (r, pos, b)
-            assert (bt[i][-(-len(toks) // BS):] == -1).all()
+                b = int(bt[i][pos // bs])
+                assert self.cells[b][pos % bs] == self.pid(toks[:pos + 1]), (r, pos, b)
+            assert (bt[i][-(-len(toks) // bs):] == -1).all()
 
 
 def step(bm, reqs, mb=64):
@@ -494,12 +497,12 @@ def test_lru_picks_the_least_recently_stepped():
     assert e.value.status == 5
 
 
-@pytest.mark.parametrize("seed", [0, 1, 2, 3])
-def test_random_workload_with_swaps_against_the_model(seed):
+@pytest.mark.parametrize("seed,bs", [(0, 16), (1, 16), (2, 16), (3, 16), (4, 32), (5, 32)])
+def test_random_workload_with_swaps_against_the_model(seed, bs):
     rng = np.random.default_rng(100 + seed)
-    NB, NH = 64, 48
-    bm = pa.BlockManager(NB, NH)
-    model = DevicePoolModel(NB, NH)
+    NB, NH = 64 * 16 // bs, 48 * 16 // bs
+    bm = pa.BlockManager(NB, NH, block_size=bs)
+    model = DevicePoolModel(NB, NH, bs)
     hist, unwritten, swapped, next_id = {}, set(), set(), 1
     moved = set()
     prompts = [list(rng.integers(0, 30, int(rng.integers(1, 60)))) for _ in range(4)]
@@ -569,3 +572,15 @@ def test_random_workload_with_swaps_against_the_model(seed):
         except pa.PagedAttentionError as e:
             assert e.status == 5, e                # only "out of blocks / slots"
     assert steps > 50 and swaps > 20
+
+
+def test_32_token_blocks_and_bad_sizes():
+    bm = pa.BlockManager(10, 0, block_size=32)
+    assert bm.add(1, list(range(40))) == 0
+    (t,), (n,), (q,), _ = step(bm, [1])
+    assert len(t) == 2 and n == 40 and q == 40
+    assert bm.add(2, list(range(40))) == 32        # one full 32-token block reused
+    assert bm.add(3, list(range(32))) == 0         # the last prompt token is computed
+    for bad in (0, 8, 24, 64):
+        with pytest.raises(pa.PagedAttentionError):
+            pa.BlockManager(10, 0, block_size=bad)

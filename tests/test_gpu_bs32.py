@@ -1,0 +1,173 @@
+"""The device path at 32 tokens per block (5688vip chapter 3, section 3.2 allows
+16 or 32), against the oracle, whose pools carry the block size as their third
+axis.  Bit-exact for slot mapping, cache writes (plain and quantised), block
+copies and swaps; the storage type's tolerance for decode and mixed steps, on
+contexts around 16- and 32-token edges with NaN in every slot past a context.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_455_amd as pa
+from paged_kv_cache_455_amd import workloads as W
+
+from .pa_testlib import (TOL, Dev, max_err, np_of, oracle_decode_rows, oracle_mixed, oracle_slots,
+                         poison_tails)
+
+pytestmark = pytest.mark.gpu
+BS = 32
+EDGES = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 511, 512, 513, 2049, 3333]
+
+
+def say(*a):
+    print("[case bs32]", *a, flush=True)
+
+
+def _raw(t):
+    t = t.detach().cpu()
+    return t.view(torch.int16).numpy() if t.dtype == torch.bfloat16 else t.numpy()
+
+
+@pytest.mark.parametrize("kv,hd", [("f32", 64), ("f16", 128), ("bf16", 128)])
+def test_slot_mapping_and_cache_write_bit_exact(kv, hd):
+    b = W.decode_batch(131, [1, 15, 16, 17, 31, 32, 33, 200], 8, 4, hd, kv, kv, poison=True,
+                       name=f"bs32-write-{kv}", block_size=BS)
+    say("write", b.name)
+    d = Dev(b)
+    got = pa.pa_slot_mapping(d.bt, d.qsl, d.lens, b.num_tokens, block_size=BS)
+    torch.cuda.synchronize()
+    want = oracle_slots(b)
+    assert np.array_equal(got.cpu().numpy(), want)
+    want[3] = -1  # a padding row is skipped
+    pa.kv_cache_write(d.pool, d.k_new, d.v_new, torch.from_numpy(want).cuda())
+    torch.cuda.synchronize()
+    rk, rv = oracle.cache_write(_raw(b.k_pool), _raw(b.v_pool), _raw(b.k_new), _raw(b.v_new), want)
+    assert _raw(d.k).tobytes() == np.ascontiguousarray(rk).tobytes()
+    assert _raw(d.v).tobytes() == np.ascontiguousarray(rv).tobytes()
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_block_copy_and_swap_bit_exact(kv):
+    b = W.decode_batch(141, [40, 70, 5], 8, 8, 128, kv, "bf16", pool_blocks=24,
+                       name=f"bs32-copy-{kv}", block_size=BS)
+    say("copy/swap", b.name)
+    d = Dev(b)
+    pairs = np.array([[0, 9], [3, 12], [7, 20], [1, 2]], dtype=np.int32)
+    pa.kv_block_copy(d.pool, torch.from_numpy(pairs).cuda())
+    torch.cuda.synchronize()
+    ks = None if b.k_scale is None else b.k_scale.numpy()
+    vs = None if b.v_scale is None else b.v_scale.numpy()
+    dev0 = oracle.block_copy(_raw(b.k_pool), _raw(b.v_pool), pairs, ks, vs)
+    assert _raw(d.k).tobytes() == dev0[0].tobytes() and _raw(d.v).tobytes() == dev0[1].tobytes()
+    host = [torch.zeros_like(t).pin_memory() for t in (b.k_pool[:10], b.v_pool[:10])]
+    hs = [None, None] if ks is None else [torch.zeros(10, 8).pin_memory() for _ in range(2)]
+    hpool = pa.KVPool(host[0], host[1], hs[0], hs[1])
+    out_pairs = np.array([[9, 0], [12, 4], [2, 9]], dtype=np.int32)
+    pa.kv_swap(hpool, d.pool, torch.from_numpy(out_pairs).cuda())
+    torch.cuda.synchronize()
+    h0 = (np.zeros_like(dev0[0][:10]), np.zeros_like(dev0[1][:10]),
+          None if ks is None else np.zeros((10, 8), np.float32),
+          None if ks is None else np.zeros((10, 8), np.float32))
+    want = oracle.swap_blocks(h0, dev0, out_pairs)
+    assert _raw(host[0]).tobytes() == want[0].tobytes() and _raw(host[1]).tobytes() == want[1].tobytes()
+    if ks is not None:
+        assert np.array_equal(hs[0].numpy(), want[2]) and np.array_equal(hs[1].numpy(), want[3])
+
+
+@pytest.mark.parametrize("kind", ["fp8", "i8"])
+def test_quantised_write_bit_exact(kind):
+    rng = np.random.default_rng(21)
+    nb, hkv, hd = 24, 4, 128
+    say("quant-write", kind)
+    cdt = torch.uint8 if kind == "fp8" else torch.int8
+    codes0 = torch.from_numpy(rng.integers(-100, 100, (nb, hkv, BS, hd)).astype(np.int8)).view(cdt)
+    if kind == "fp8":
+        codes0 = codes0 & 0x7E | (codes0 & 0x80)
+    scales0 = torch.from_numpy(rng.uniform(0.001, 0.01, (nb, hkv)).astype(np.float32))
+    kc, vc = codes0.clone().cuda(), codes0.clone().cuda()
+    ks, vs = scales0.clone().cuda(), scales0.clone().cuda()
+    pool = pa.KVPool(kc, vc, ks, vs)
+    ok, oks = codes0.numpy().copy(), scales0.numpy().copy()
+    ov, ovs = codes0.numpy().copy(), scales0.numpy().copy()
+    perm = list(rng.permutation(nb))
+    seqs = [[perm.pop()] for _ in range(5)]
+    fill = {s: int(rng.integers(0, 31)) for s in range(5)}
+
+    def take(s, k):
+        out = []
+        for _ in range(k):
+            if fill[s] == BS * len(seqs[s]):
+                seqs[s].append(perm.pop())
+            out.append(seqs[s][fill[s] // BS] * BS + fill[s] % BS)
+            fill[s] += 1
+        return out
+
+    calls = [sum((take(s, 1) for s in range(5)), []) for _ in range(4)]
+    calls.append(take(0, 45) + [-1] + take(3, 20))   # chunks crossing 32-token blocks
+    for i, slots in enumerate(calls):
+        n = len(slots)
+        mag = rng.uniform(0.2, 8.0, (n, 1, 1)) * (0.004 if i % 2 else 0.02)
+        kx = torch.from_numpy((rng.standard_normal((n, hkv, hd)) * mag).astype(np.float32)).to(torch.bfloat16)
+        vx = torch.from_numpy((rng.standard_normal((n, hkv, hd)) * mag).astype(np.float32)).to(torch.bfloat16)
+        sl = torch.tensor(slots, dtype=torch.int64)
+        pa.kv_cache_write_quant(pool, kx.cuda(), vx.cuda(), sl.cuda())
+        torch.cuda.synchronize()
+        ok, oks = oracle.quantised_cache_write(ok, oks, kx.float().numpy(), sl.numpy(), kind)
+        ov, ovs = oracle.quantised_cache_write(ov, ovs, vx.float().numpy(), sl.numpy(), kind)
+        assert np.array_equal(ks.cpu().numpy().view(np.uint32), oks.view(np.uint32)), i
+        assert np.array_equal(vs.cpu().numpy().view(np.uint32), ovs.view(np.uint32)), i
+        assert np.array_equal(kc.cpu().numpy(), ok) and np.array_equal(vc.cpu().numpy(), ov), i
+
+
+@pytest.mark.parametrize("kv,qd,hq,hkv,hd,shared", [
+    ("f32", "f32", 4, 2, 64, False), ("f16", "f16", 32, 8, 128, False),
+    ("f16", "f16", 32, 8, 128, True), ("bf16", "bf16", 16, 2, 128, False),
+    ("f16", "f16", 8, 8, 64, False), ("fp8", "bf16", 64, 8, 128, False),
+    ("fp8", "f16", 8, 4, 64, False), ("i8", "bf16", 64, 8, 128, False),
+    ("i8", "f16", 32, 4, 128, True),
+])
+def test_decode_ragged(kv, qd, hq, hkv, hd, shared):
+    b = W.decode_batch(hq * 11 + hd, EDGES, hq, hkv, hd, kv, qd, poison=True, div=hd ** 0.5,
+                       name=f"bs32-ragged-{kv}-{qd}-{hq}x{hkv}x{hd}", block_size=BS)
+    b = poison_tails(b)
+    say("decode", b.name, "shared" if shared else "")
+    d = Dev(b, shared_blocks=shared)
+    out = pa.pa_decode(d.pool, d.q, d.bt, d.lens, b.max_seq_len, b.scale)
+    torch.cuda.synchronize()
+    err = max_err(out, oracle_decode_rows(b))
+    say("decode", b.name, "max_err", err)
+    assert err <= TOL[kv]
+
+
+def test_decode_llama3_shape():
+    b = W.llama3_8b_decode(batch=8, block_size=BS)
+    d = Dev(b)
+    out = pa.pa_decode(d.pool, d.q, d.bt, d.lens, b.max_seq_len, b.scale)
+    torch.cuda.synchronize()
+    assert max_err(out, oracle_decode_rows(b)) <= TOL["f16"]
+
+
+@pytest.mark.parametrize("kv", ["f16", "bf16", "f32"])
+def test_mixed_with_edges(kv):
+    # f16/bf16: MFMA prefill tiles + streamed decode rows; f32: the rows path
+    b = W.mixed_batch(151, 10, 37, 0, 0, 12, 600.0, 1.0, 16, 3000, 32 if kv != "f32" else 8, 8,
+                      128 if kv != "f32" else 64, kv, kv, div=(128 if kv != "f32" else 64) ** 0.5,
+                      poison=True, priors=[0, 1, 15, 16, 17, 31, 32, 33, 100, 511],
+                      name=f"bs32-mixed-{kv}", block_size=BS)
+    b = poison_tails(b)
+    say("mixed", b.name)
+    d = Dev(b)
+    slots = pa.pa_slot_mapping(d.bt, d.qsl, d.lens, b.num_tokens, block_size=BS)
+    pa.kv_cache_write(d.pool, d.k_new, d.v_new, slots)
+    out = pa.pa_prefill_chunk(d.pool, d.q, d.qsl, d.lens, d.bt, b.max_query_len, b.max_seq_len,
+                              b.scale)
+    torch.cuda.synchronize()
+    rk, rv = oracle.cache_write(np_of(b.k_pool), np_of(b.v_pool), np_of(b.k_new), np_of(b.v_new),
+                                oracle_slots(b))
+    after = W.PagedBatch(**{**b.__dict__, "k_pool": torch.from_numpy(rk).to(b.k_pool.dtype),
+                            "v_pool": torch.from_numpy(rv).to(b.v_pool.dtype)})
+    rows, ref = oracle_mixed(after)
+    err = max_err(out[torch.from_numpy(rows).cuda()], ref)
+    say("mixed", b.name, "max_err", err)
+    assert err <= TOL[kv]

@@ -31,7 +31,7 @@ from .pa_testlib import err_over_bar, max_err, np_of
 
 pytestmark = pytest.mark.gpu
 
-BS, NB, NH, MB = 16, 64, 24, 16
+NB, NH, MB = 64, 24, 16
 HQ, HKV, D = 16, 2, 128
 SCALE = 1.0 / np.sqrt(D)
 TORCH = {"f16": torch.float16, "bf16": torch.bfloat16}
@@ -84,18 +84,18 @@ def scenario():
     return steps
 
 
-def _pool(kv, n=NB, device="cuda"):
+def _pool(kv, bs, n=NB, device="cuda"):
     pin = device == "cpu"
     if kv in TORCH:
-        z = lambda: torch.zeros((n, HKV, BS, D), dtype=TORCH[kv], device=device, pin_memory=pin)
+        z = lambda: torch.zeros((n, HKV, bs, D), dtype=TORCH[kv], device=device, pin_memory=pin)
         return pa.KVPool(z(), z(), shared_blocks=True), None
-    z = lambda: torch.zeros((n, HKV, BS, D), dtype=torch.uint8, device=device, pin_memory=pin)
+    z = lambda: torch.zeros((n, HKV, bs, D), dtype=torch.uint8, device=device, pin_memory=pin)
     s = lambda: torch.zeros((n, HKV), dtype=torch.float32, device=device, pin_memory=pin)
     return pa.KVPool(z(), z(), s(), s(), shared_blocks=True), "e4m3fn"
 
 
-def _mirror(codec, n):
-    mk = np.zeros((n, HKV, BS, D), dtype=np.uint8 if codec else np.float32)
+def _mirror(codec, n, bs):
+    mk = np.zeros((n, HKV, bs, D), dtype=np.uint8 if codec else np.float32)
     return dict(k=mk.copy(), v=mk.copy(), ks=np.zeros((n, HKV), np.float32),
                 vs=np.zeros((n, HKV), np.float32))
 
@@ -108,14 +108,14 @@ def _untup(t):
     return dict(k=t[0], v=t[1], ks=t[2], vs=t[3])
 
 
-@pytest.mark.parametrize("kv", ["f16", "bf16", "fp8"])
-def test_block_manager_drives_the_device_path(kv):
-    say(f"[serving] kv={kv}")
-    pool, codec = _pool(kv)
-    hpool, _ = _pool(kv, NH, "cpu")
+@pytest.mark.parametrize("kv,bs", [("f16", 16), ("bf16", 16), ("fp8", 16), ("f16", 32), ("fp8", 32)])
+def test_block_manager_drives_the_device_path(kv, bs):
+    say(f"[serving] kv={kv} block_size={bs}")
+    pool, codec = _pool(kv, bs)
+    hpool, _ = _pool(kv, bs, NH, "cpu")
     qdt = TORCH.get(kv, torch.float16)
-    mirror, hmirror = _mirror(codec, NB), _mirror(codec, NH)
-    bm = pa.BlockManager(NB, NH)
+    mirror, hmirror = _mirror(codec, NB, bs), _mirror(codec, NH, bs)
+    bm = pa.BlockManager(NB, NH, block_size=bs)
     hist, live, unwritten = History(), {}, set()
     rng = np.random.default_rng(11)
     ws = None
@@ -159,7 +159,7 @@ def test_block_manager_drives_the_device_path(kv):
             pa.kv_swap(pool, hpool, torch.from_numpy(in_np.copy()).cuda())
         if len(pairs_np):
             pa.kv_block_copy(pool, torch.from_numpy(pairs_np.copy()).cuda())
-        slots = pa.pa_slot_mapping(bt, qsl, lens, T)
+        slots = pa.pa_slot_mapping(bt, qsl, lens, T, block_size=bs)
         pos = [(i, r, int(lens_np[i]) - int(q_lens[i]) + j)
                for i, r in enumerate(reqs) for j in range(int(q_lens[i]))]
         kv_new = np.stack([hist.kv(live[r], p) for _, r, p in pos])       # [T][2][HKV][D]
@@ -182,7 +182,7 @@ def test_block_manager_drives_the_device_path(kv):
         torch.cuda.synchronize()
 
         # oracle: slots, mirror pools, attention
-        want_slots = [oracle.slot_for_position(bt_np[i], p) for i, _, p in pos]
+        want_slots = [oracle.slot_for_position(bt_np[i], p, bs) for i, _, p in pos]
         assert slots.cpu().tolist() == want_slots
         if len(out_np):
             hmirror = _untup(oracle.swap_blocks(_tup(hmirror), _tup(mirror), out_np))
