@@ -45,6 +45,8 @@ def parse():
                     help="only run a 256 MiB device copy three times (byte-counter calibration)")
     ap.add_argument("--block-size", type=int, default=16, choices=[16, 32],
                     help="tokens per KV block (the pages allow 16 or 32)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the decode step eagerly and as a replayed HIP graph")
     ap.add_argument("--swap", action="store_true",
                     help="measure kv_swap (device pool <-> pinned host pool) instead of the step")
     return ap.parse_args()
@@ -218,6 +220,67 @@ def swap_bench(args):
     }), flush=True)
 
 
+def graph_bench(args):
+    """The decode step (slot mapping -> K/V write -> decode + merge) of a decode
+    workload, eager against a captured HIP graph replayed on the same buffers.
+    Both are timed with HIP events over K back-to-back steps on one stream."""
+    import torch
+
+    import paged_kv_cache_455_amd as pa
+    b = make_batch(args.workload, args.block_size)
+    if b.kind != "decode" or b.k_new is None:
+        print("--graph takes a decode workload", file=sys.stderr)
+        sys.exit(2)
+    to = lambda t: None if t is None else t.cuda().contiguous()
+    k, v, ks, vs = to(b.k_pool), to(b.v_pool), to(b.k_scale), to(b.v_scale)
+    pool = pa.KVPool(k, v, ks, vs, shared_blocks=b.shares_blocks)
+    q, kn, vn, bt, lens = to(b.q), to(b.k_new), to(b.v_new), to(b.block_tables), to(b.seq_lens)
+    qsl = torch.arange(b.num_seqs + 1, dtype=torch.int32, device="cuda")
+    slots = torch.empty(b.num_seqs, dtype=torch.int64, device="cuda")
+    out = torch.empty_like(q)
+    need = pa.pa_decode_workspace_size(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim,
+                                       b.max_seq_len)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    write = pa.kv_cache_write_quant if b.kv_dtype in ("fp8", "i8") else pa.kv_cache_write
+    stream = torch.cuda.current_stream()
+
+    def eager():
+        pa.pa_slot_mapping(bt, qsl, lens, b.num_seqs, out=slots, block_size=b.block_size,
+                           stream=stream)
+        write(pool, kn, vn, slots, stream=stream)
+        pa.pa_decode(pool, q, bt, lens, b.max_seq_len, b.scale, out=out, workspace=ws,
+                     stream=stream)
+
+    g = pa.DecodeStepGraph(pool, q, kn, vn, bt, lens, b.max_seq_len, b.scale)
+
+    def timed(fn):
+        for _ in range(max(1, args.warmup)):
+            fn()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / args.steps * 1e3
+
+    us_eager = timed(eager)
+    us_graph = timed(lambda: g.replay(stream=stream))
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out.view(torch.int16) if out.element_size() == 2 else out,
+                            g.out.view(torch.int16) if out.element_size() == 2 else g.out))
+    print(json.dumps({
+        "metric": "decode step time, eager vs replayed HIP graph",
+        "value": round(us_graph, 2), "unit": "us/step", "higher_is_better": False,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "dtype": b.kv_dtype,
+        "data": "synthetic",
+        "config": {"workload": b.name, "block_size": b.block_size, "num_seqs": b.num_seqs},
+        "eager_us_per_step": round(us_eager, 2), "graph_us_per_step": round(us_graph, 2),
+        "speedup": round(us_eager / us_graph, 3), "outputs_equal": same,
+    }), flush=True)
+
+
 def cpu_baseline(b, budget_s):
     """The oracle as it stands, timed on this host over a bounded sample of the batch."""
     import numpy as np
@@ -289,6 +352,9 @@ def main():
         return
     if args.swap:
         swap_bench(args)
+        return
+    if args.graph:
+        graph_bench(args)
         return
     pa.load_library()
     dev = torch.device("cuda:0")

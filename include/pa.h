@@ -231,6 +231,38 @@ pa_status_t pa_prefill_chunk(const pa_kv_pool_t *pool, const void *q, int32_t q_
                              void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * ---- A captured decode step ([P3] 4.2: the serving engine builds graphs of
+ * its step at start-up; 6.2: running eagerly instead saves that memory but adds
+ * latency to every step; here a HIP graph). ----
+ * pa_decode_step_graph records, on a stream of its own, the calls of one
+ * decode step over fixed buffers: pa_slot_mapping (block_size from the pool),
+ * the write of each sequence's new K/V row (kv_cache_write; kv_cache_write_quant
+ * from new_dtype for 1-byte pools), then pa_decode with its merge.  Arguments
+ * mean what they mean in those calls (one query row per sequence:
+ * query_start_loc is 0, 1, .., num_seqs; slot_mapping int64 [num_seqs] is the
+ * step's scratch for the slots) and are validated at capture; nothing runs
+ * then.  pa_graph_launch replays the step on `stream`, reading the buffers'
+ * contents at that time: q, k_new, v_new, block tables and context lengths may
+ * change between replays (contexts >= 1 and within max_blocks_per_seq *
+ * block_size -- longer than max_context_len only costs balance, the split keeps
+ * its pieces within the workspace); the buffers, num_seqs and the pool must
+ * stay as captured.  Copy-on-write pairs vary in number per step and are not
+ * part of the graph: run kv_block_copy before the replay.  Replays on one
+ * stream run in order; the caller owns every buffer.
+ */
+typedef struct pa_graph pa_graph_t;
+pa_status_t pa_decode_step_graph(const pa_kv_pool_t *pool, const void *q, int32_t q_dtype,
+                                 const void *k_new, const void *v_new, int32_t new_dtype,
+                                 void *out, const int32_t *block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                 const int32_t *query_start_loc, int64_t *slot_mapping,
+                                 int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                                 float scale, void *workspace, size_t workspace_bytes,
+                                 pa_graph_t **graph);
+pa_status_t pa_graph_launch(pa_graph_t *graph, hipStream_t stream);
+void pa_graph_destroy(pa_graph_t *graph);
+
+/*
  * ---- Host block manager ([P1] PagedAttention, Prefix Sharing, Continuous
  * Batching; [P2] 3.2) -- host memory only, no device calls. ----
  * A request's cache is a list of physical blocks of block_size (16 or 32)

@@ -18,7 +18,8 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "KVPool", "PA_POOL_SHARED_BLOCKS", "PagedAttentionError", "BlockManager", "kv_swap", "library_path", "load_library",
+    "KVPool", "PA_POOL_SHARED_BLOCKS", "PagedAttentionError", "BlockManager", "kv_swap",
+    "DecodeStepGraph", "library_path", "load_library",
     "pa_slot_mapping", "kv_cache_write", "kv_cache_write_quant", "kv_block_copy", "pa_decode",
     "pa_prefill_chunk",
     "pa_decode_workspace_size", "pa_prefill_workspace_size", "PA_DTYPE",
@@ -83,6 +84,13 @@ _SIGS = {
                                _c.c_int32, _c.c_void_p]),
     "kv_swap": (_c.c_int, [_c.POINTER(_Pool), _c.POINTER(_Pool), _c.c_void_p, _c.c_int32,
                            _c.c_void_p]),
+    "pa_decode_step_graph": (_c.c_int, [_c.POINTER(_Pool), _c.c_void_p, _c.c_int32, _c.c_void_p,
+                                        _c.c_void_p, _c.c_int32, _c.c_void_p, _c.c_void_p,
+                                        _c.c_int32, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                        _c.c_int32, _c.c_int32, _c.c_int32, _c.c_float,
+                                        _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "pa_graph_launch": (_c.c_int, [_c.c_void_p, _c.c_void_p]),
+    "pa_graph_destroy": (None, [_c.c_void_p]),
     "pa_bm_destroy": (None, [_c.c_void_p]),
     "pa_bm_num_free": (_c.c_int32, [_c.c_void_p]),
     "pa_bm_refcount": (_c.c_int32, [_c.c_void_p, _c.c_int32]),
@@ -281,6 +289,43 @@ def pa_prefill_chunk(pool: KVPool, q, query_start_loc, seq_lens, block_tables, m
         _ptr(block_tables), int(block_tables.shape[1]), S, int(T), int(hq), int(max_query_len),
         int(max_seq_len), float(scale), _ptr(workspace), wbytes, _stream(q, stream)))
     return out
+
+
+class DecodeStepGraph:
+    """A decode step captured once and replayed (``pa_decode_step_graph``): slot
+    mapping, the new K/V rows' write and the decode, over the tensors given
+    here.  ``replay()`` reads their contents at that time, so refresh q, k_new,
+    v_new, block_tables and context_lens in place between replays.  The tensors
+    are held here so they outlive the graph."""
+
+    def __init__(self, pool: KVPool, q, k_new, v_new, block_tables, context_lens,
+                 max_context_len: int, scale: float, out=None):
+        lib = load_library()
+        self._lib = lib
+        S, hq, _ = q.shape
+        self.out = torch.empty_like(q) if out is None else out
+        self.slots = torch.empty(S, dtype=torch.int64, device=q.device)
+        self.qsl = torch.arange(S + 1, dtype=torch.int32, device=q.device)
+        need = pa_decode_workspace_size(S, hq, pool.num_kv_heads, pool.head_dim, max_context_len)
+        self.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        self._keep = (pool, q, k_new, v_new, block_tables, context_lens)
+        h = ctypes.c_void_p()
+        _check("pa_decode_step_graph", lib.pa_decode_step_graph(
+            pool.ref(), _ptr(q), _dt(q), _ptr(k_new), _ptr(v_new), _dt(k_new), _ptr(self.out),
+            _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), _ptr(self.qsl),
+            _ptr(self.slots), int(S), int(hq), int(max_context_len), float(scale),
+            _ptr(self.workspace), int(need), ctypes.byref(h)))
+        self._h = h
+
+    def replay(self, stream=None):
+        _check("pa_graph_launch", self._lib.pa_graph_launch(self._h, _stream(self.out, stream)))
+        return self.out
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            self._lib.pa_graph_destroy(h)
+            self._h = None
 
 
 class BlockManager:

@@ -6,6 +6,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <new>
+
 #include "pa_launch.h"
 #include "../../include/pa.h"
 
@@ -529,6 +531,90 @@ pa_status_t pa_prefill_chunk(const pa_kv_pool_t *pool, const void *q, int32_t q_
   return hip_status(pa::launch_mixed(m, pool->kv_dtype, q_dtype, pool->head_dim, group,
                                      num_q_tokens, stream_loads, stream),
                     "pa_prefill_chunk launch");
+}
+
+}  // extern "C"
+
+struct pa_graph {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+extern "C" {
+
+// Capture one decode step -- slot mapping, the new rows' K/V write (quantising
+// for 1-byte pools), the balanced-split decode and its merge -- into a HIP graph,
+// built once and replayed every step ("从KV Cache到vLLM" 4.2, 6.2).  Every launch
+// is validated as in the eager calls; no memset node is recorded.
+pa_status_t pa_decode_step_graph(const pa_kv_pool_t *pool, const void *q, int32_t q_dtype,
+                                 const void *k_new, const void *v_new, int32_t new_dtype,
+                                 void *out, const int32_t *block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                 const int32_t *query_start_loc, int64_t *slot_mapping,
+                                 int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                                 float scale, void *workspace, size_t workspace_bytes,
+                                 pa_graph_t **graph) {
+  if (!graph) return fail(PA_E_ARG, "graph is NULL");
+  *graph = nullptr;
+  if (num_seqs <= 0) return fail(PA_E_ARG, "num_seqs must be > 0");
+  pa_status_t st = check_pool(pool, true);
+  if (st != PA_OK) return st;
+  if (!is_quantised(pool->kv_dtype) && new_dtype != pool->kv_dtype)
+    return fail(PA_E_UNSUPPORTED, "new_dtype %d must equal kv_dtype %d for float KV", new_dtype,
+                pool->kv_dtype);
+  hipStream_t cs = nullptr;
+  if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess)
+    return hip_status(hipGetLastError(), "capture stream");
+  // relaxed: the first launch of a kernel instantiation queries its occupancy
+  hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeRelaxed);
+  if (e != hipSuccess) {
+    (void)hipStreamDestroy(cs);
+    return hip_status(e, "hipStreamBeginCapture");
+  }
+  st = pa_slot_mapping(block_tables, max_blocks_per_seq, pool->block_size, query_start_loc,
+                       context_lens, num_seqs, num_seqs, slot_mapping, cs);
+  if (st == PA_OK)
+    st = is_quantised(pool->kv_dtype)
+             ? kv_cache_write_quant(pool, k_new, v_new, new_dtype, slot_mapping, num_seqs, cs)
+             : kv_cache_write(pool, k_new, v_new, slot_mapping, num_seqs, cs);
+  if (st == PA_OK)
+    st = pa_decode(pool, q, q_dtype, out, block_tables, max_blocks_per_seq, context_lens,
+                   num_seqs, num_q_heads, max_context_len, scale, workspace, workspace_bytes, cs);
+  hipGraph_t g = nullptr;
+  e = hipStreamEndCapture(cs, &g);
+  (void)hipStreamDestroy(cs);
+  if (st != PA_OK || e != hipSuccess) {
+    if (g) (void)hipGraphDestroy(g);
+    return st != PA_OK ? st : hip_status(e, "hipStreamEndCapture");
+  }
+  hipGraphExec_t x = nullptr;
+  e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    return hip_status(e, "hipGraphInstantiate");
+  }
+  pa_graph *h = new (std::nothrow) pa_graph();
+  if (!h) {
+    (void)hipGraphExecDestroy(x);
+    (void)hipGraphDestroy(g);
+    return fail(PA_E_ARG, "out of host memory");
+  }
+  h->graph = g;
+  h->exec = x;
+  *graph = h;
+  return PA_OK;
+}
+
+pa_status_t pa_graph_launch(pa_graph_t *graph, hipStream_t stream) {
+  if (!graph || !graph->exec) return fail(PA_E_ARG, "graph is NULL");
+  return hip_status(hipGraphLaunch(graph->exec, stream), "hipGraphLaunch");
+}
+
+void pa_graph_destroy(pa_graph_t *graph) {
+  if (!graph) return;
+  if (graph->exec) (void)hipGraphExecDestroy(graph->exec);
+  if (graph->graph) (void)hipGraphDestroy(graph->graph);
+  delete graph;
 }
 
 }  // extern "C"

@@ -569,6 +569,11 @@ __device__ __forceinline__ void merge_partitions(const DecodeArgs &a, int r, int
 // touches: the final output when it owns the whole segment, else a partial
 // (m, l, acc) for "piece" w - first_wave(segment), combined by the merge kernel.
 
+__device__ __forceinline__ int wave_max_i(int x) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) x = max(x, __shfl_xor(x, m, kWave));
+  return x;
+}
 __device__ __forceinline__ int wave_sum_i(int x) {
 #pragma unroll
   for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m, kWave);
@@ -692,12 +697,13 @@ __device__ __forceinline__ void next_sequence(const DecodeArgs &a, SeqWindow &wi
 __device__ __forceinline__ bool stream_range(const DecodeArgs &a, int w, int lane, StreamRange &r) {
   const int Hkv = a.num_kv_heads, S = a.num_seqs, c = a.seg_cost;
   auto seq_cost = [&](int nb) { return nb > 0 ? Hkv * (nb + c) : 0; };
-  int TC = 0;
+  int TC = 0, mxnb = 0;
   int nb0 = 0, incl0 = 0;  // first 64 sequences, kept for the locate pass
   for (int c0 = 0; c0 < S; c0 += kWave) {
     const int sq = c0 + lane;
     const int n = sq < S ? decode_len(a, sq) : 0;
     const int nb = n > 0 ? (n + kBlock - 1) / kBlock : 0;
+    mxnb = max(mxnb, nb);
     const int incl = wave_incl_scan_i(seq_cost(nb), lane);
     if (c0 == 0) {
       nb0 = nb;
@@ -707,6 +713,13 @@ __device__ __forceinline__ bool stream_range(const DecodeArgs &a, int w, int lan
     TC += __builtin_amdgcn_readlane(incl, kWave - 1);
   }
   r.tpw = max(a.min_tpw, (TC + a.num_waves - 1) / a.num_waves);
+  // A segment of nblk tiles meets at most floor((nblk - 1) / tpw) + 2 waves; so
+  // with tpw >= ceil(max nblk / (max_parts - 1)) its pieces fit the workspace's
+  // max_parts rows whatever the lengths (max_parts >= 2 by construction), also
+  // when the host's length bound is low or a captured step is replayed on
+  // longer contexts.
+  mxnb = wave_max_i(mxnb);
+  r.tpw = max(r.tpw, (mxnb + a.max_parts - 2) / (a.max_parts - 1));
   if (w == 0 && lane == 0) a.hdr[0] = r.tpw;
   const int t = w * r.tpw;
   const int tend = min(t + r.tpw, TC);

@@ -39,7 +39,7 @@ def test_header_declares_the_entry_points():
               "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free", "pa_bm_refcount", "pa_bm_add",
               "pa_bm_fork", "pa_bm_append", "pa_bm_release", "pa_bm_step", "pa_bm_num_free_host",
               "pa_bm_swap_out", "pa_bm_swap_in", "pa_bm_lru", "pa_bm_blocks", "pa_bm_swaps",
-              "kv_swap"):
+              "kv_swap", "pa_decode_step_graph", "pa_graph_launch", "pa_graph_destroy"):
         assert n in names, n
 
 
