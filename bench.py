@@ -3,7 +3,10 @@
 
 A step is one pass of the whole path over one synthetic batch already resident
 in HBM: slot mapping -> (copy-on-write block copies) -> cache write of this
-step's K/V -> paged attention (decode, or the mixed prefill+decode launch).
+step's K/V -> paged attention (decode, or the mixed prefill+decode launch).  A
+decode step on a float pool runs slot mapping, write and decode as one
+pa_decode_append call (``--unfused``: three calls); 1-byte pools quantise on
+write (kv_cache_write_quant) before pa_decode.
 
 Default workload: the Llama-3-8B-shaped decode layer (64 sequences, contexts
 uniform in [128, 4096], 32 query / 8 KV heads, head_dim 128, fp16 KV, fp32
@@ -47,6 +50,9 @@ def parse():
                     help="tokens per KV block (the pages allow 16 or 32)")
     ap.add_argument("--graph", action="store_true",
                     help="time the decode step eagerly and as a replayed HIP graph")
+    ap.add_argument("--unfused", action="store_true",
+                    help="decode step as separate slot-mapping, cache-write and decode calls "
+                         "instead of pa_decode_append")
     ap.add_argument("--swap", action="store_true",
                     help="measure kv_swap (device pool <-> pinned host pool) instead of the step")
     return ap.parse_args()
@@ -106,6 +112,62 @@ def side_bytes(b):
 
 
 # ---------------------------------------------------------------------------------------
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+class TimingEvent:
+    """A HIP event used only to time work on one stream, created with
+    hipEventDisableSystemFence: recording it skips the system-scope cache writeback
+    and invalidation of a default event (torch.cuda.Event), which leaves the GPU
+    idle for several microseconds at every record and would be counted in the
+    bracketed time.  Called on the HIP runtime torch has loaded."""
+    _hip = None
+
+    @classmethod
+    def _runtime(cls):
+        if cls._hip is None:
+            import ctypes
+            path = "libamdhip64.so.7"  # the soname: dlopen returns the loaded copy
+            for line in open("/proc/self/maps"):
+                if "/libamdhip64.so" in line:
+                    path = line.split()[-1]
+                    break
+            h = ctypes.CDLL(path)
+            vp, P = ctypes.c_void_p, ctypes.POINTER
+            h.hipEventCreateWithFlags.argtypes = [P(vp), ctypes.c_uint]
+            h.hipEventRecord.argtypes = [vp, vp]
+            h.hipEventElapsedTime.argtypes = [P(ctypes.c_float), vp, vp]
+            h.hipEventDestroy.argtypes = [vp]
+            cls._hip = h
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self._ct = ctypes
+        self._h = self._runtime()
+        self._e = ctypes.c_void_p()
+        rc = self._h.hipEventCreateWithFlags(ctypes.byref(self._e), HIP_EVENT_DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self, stream):
+        rc = self._h.hipEventRecord(self._e, self._ct.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end) -> float:
+        """Milliseconds from this event to ``end`` (both complete)."""
+        ms = self._ct.c_float()
+        rc = self._h.hipEventElapsedTime(self._ct.byref(ms), self._e, end._e)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if getattr(self, "_e", None) and self._e.value:
+            self._h.hipEventDestroy(self._e)
+
+
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "paged_kv_cache_455_amd", "csrc")
 
@@ -186,7 +248,7 @@ def swap_bench(args):
         for _ in range(max(1, args.warmup)):
             fn()
         torch.cuda.synchronize()
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0, t1 = TimingEvent(), TimingEvent()
         t0.record(stream)
         for _ in range(reps):
             fn()
@@ -257,7 +319,7 @@ def graph_bench(args):
         for _ in range(max(1, args.warmup)):
             fn()
         torch.cuda.synchronize()
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0, t1 = TimingEvent(), TimingEvent()
         t0.record(stream)
         for _ in range(args.steps):
             fn()
@@ -385,11 +447,21 @@ def main():
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     quantised = b.k_scale is not None
+    # decode steps on float pools write the new rows inside the decode call
+    fused = b.kind == "decode" and k_new is not None and not quantised and not args.unfused
 
     def step(i, ev=None):
         pool = pools[i % R]
         if pairs is not None:
             pa.kv_block_copy(pool, pairs)
+        if fused:
+            if ev is not None:
+                ev[0].record(stream)
+            pa.pa_decode_append(pool, q, k_new, v_new, bt, lens, b.max_seq_len, b.scale, out=out,
+                                slot_mapping=slots, workspace=ws)
+            if ev is not None:
+                ev[1].record(stream)
+            return
         pa.pa_slot_mapping(bt, qsl, lens, b.num_tokens, out=slots, block_size=b.block_size)
         if k_new is not None:
             if quantised:  # 1-byte pool: quantise this step's K/V on the way in
@@ -409,8 +481,7 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    evs = [(TimingEvent(), TimingEvent()) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -426,7 +497,10 @@ def main():
     s_bytes = side_bytes(b)
     flops = attention_flops(b)
     step_gbps = (a_bytes + s_bytes) / (ms_per_step * 1e-3) / 1e9
-    attn_gbps = a_bytes / (attn_ms_avg * 1e-3) / 1e9
+    # the timed call: the attention, plus (fused) the new rows' read, store and slots
+    call_bytes = a_bytes + (b.num_tokens * 8 + 2 * b.num_tokens * b.num_kv_heads * b.head_dim *
+                            2 * ELEM[b.kv_dtype] if fused else 0)
+    attn_gbps = call_bytes / (attn_ms_avg * 1e-3) / 1e9
     tokens = b.num_seqs if b.kind == "decode" else b.num_tokens
     rec = {
         "metric": METRIC,
@@ -453,12 +527,17 @@ def main():
                          "p10": round(attn_ms_sorted[len(attn_ms) // 10] * 1e3, 2),
                          "p50": round(attn_ms_sorted[len(attn_ms) // 2] * 1e3, 2),
                          "p90": round(attn_ms_sorted[(9 * len(attn_ms)) // 10] * 1e3, 2)},
-        "algorithmic": {"attention_bytes": a_bytes, "side_bytes": s_bytes, "attention_flops": flops},
+        "algorithmic": {"attention_bytes": a_bytes, "side_bytes": s_bytes, "timed_call_bytes": call_bytes,
+                        "attention_flops": flops},
         "roofline": {"bound": "hbm", "achieved": round(attn_gbps, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": profiled_traffic(args.workload) if b.block_size == 16 else None,
-                     "kernel": "pa_decode (balanced-split kernel + piece merge)" if b.kind == "decode"
-                     else "pa_prefill_chunk"},
+                     "traffic": (profiled_traffic(args.workload + ("-unfused" if args.unfused else ""))
+                                 if b.block_size == 16 else None),
+                     "kernel": ("pa_decode_append (balanced-split kernel + piece merge storing the "
+                                "new rows)" if fused else
+                                "pa_decode (balanced-split kernel + piece merge)" if b.kind == "decode"
+                                else "pa_prefill_chunk")},
+        "fused_append": fused,
     }
     if b.kind != "decode":
         rec["attention_tflops"] = round(flops / (attn_ms_avg * 1e-3) / 1e12, 2)

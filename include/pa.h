@@ -205,6 +205,34 @@ pa_status_t pa_decode(const pa_kv_pool_t *pool, const void *q, int32_t q_dtype, 
                       int32_t max_context_len, float scale, void *workspace,
                       size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * pa_decode_append -- a decode step with its cache write fused in: for every
+ * sequence the new token's K/V row goes to the end of its last block ([P2] 3.2:
+ * compute the token's K/V, write it at the end of the current block, then
+ * attend) and its query attends to all context_lens[s] tokens, the new one
+ * included.  The result equals pa_slot_mapping (one row per sequence at
+ * position context_lens[s] - 1), kv_cache_write and pa_decode run in that order:
+ * out is bit-identical and the pools byte-identical.  The attention reads the
+ * new rows from k_new / v_new, so the write needs no launch of its own; the
+ * pool rows are stored within the call, after every read of the pool.
+ *   k_new, v_new  [num_seqs][num_kv_heads][head_dim], the pool's kv_dtype,
+ *                 16-byte aligned
+ *   slot_mapping  int64 [num_seqs] receives each row's slot
+ *                 (block * block_size + offset); may be NULL
+ *   the rest      as pa_decode; the workspace is pa_decode_workspace_size's
+ * Errors as pa_decode, plus PA_E_UNSUPPORTED for fp8/int8 pools (their write
+ * quantises and may re-encode the block: kv_cache_write_quant, then pa_decode)
+ * and PA_E_ARG for NULL or misaligned k_new / v_new.  Slots must be distinct
+ * across sequences (no two sequences own one block's same row).
+ */
+pa_status_t pa_decode_append(const pa_kv_pool_t *pool, const void *q, int32_t q_dtype,
+                             const void *k_new, const void *v_new, void *out,
+                             const int32_t *block_tables, int32_t max_blocks_per_seq,
+                             const int32_t *context_lens, int64_t *slot_mapping,
+                             int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                             float scale, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
 /* Workspace bytes pa_prefill_chunk needs for these sizes and KV storage type
  * (0 for invalid sizes). */
 size_t pa_prefill_workspace_size(int32_t num_seqs, int32_t num_q_tokens, int32_t num_q_heads,
@@ -235,9 +263,10 @@ pa_status_t pa_prefill_chunk(const pa_kv_pool_t *pool, const void *q, int32_t q_
  * its step at start-up; 6.2: running eagerly instead saves that memory but adds
  * latency to every step; here a HIP graph). ----
  * pa_decode_step_graph records, on a stream of its own, the calls of one
- * decode step over fixed buffers: pa_slot_mapping (block_size from the pool),
- * the write of each sequence's new K/V row (kv_cache_write; kv_cache_write_quant
- * from new_dtype for 1-byte pools), then pa_decode with its merge.  Arguments
+ * decode step over fixed buffers: for float pools pa_decode_append (slot
+ * mapping, the write of each sequence's new K/V row and the decode with its
+ * merge, in two launches); for 1-byte pools pa_slot_mapping (block_size from
+ * the pool), kv_cache_write_quant from new_dtype, then pa_decode.  Arguments
  * mean what they mean in those calls (one query row per sequence:
  * query_start_loc is 0, 1, .., num_seqs; slot_mapping int64 [num_seqs] is the
  * step's scratch for the slots) and are validated at capture; nothing runs

@@ -6,7 +6,8 @@ the HIP kernels; PyTorch only provides device memory and the current stream.
 There is no CPU fallback: without the built library every call raises.
 
 Entry points (same names as the C ABI): ``pa_slot_mapping``,
-``kv_cache_write``, ``kv_cache_write_quant``, ``kv_block_copy``, ``pa_decode``, ``pa_prefill_chunk``,
+``kv_cache_write``, ``kv_cache_write_quant``, ``kv_block_copy``, ``pa_decode``,
+``pa_decode_append``, ``pa_prefill_chunk``,
 ``pa_decode_workspace_size``, ``pa_prefill_workspace_size``.
 """
 from __future__ import annotations
@@ -21,7 +22,7 @@ __all__ = [
     "KVPool", "PA_POOL_SHARED_BLOCKS", "PagedAttentionError", "BlockManager", "kv_swap",
     "DecodeStepGraph", "library_path", "load_library",
     "pa_slot_mapping", "kv_cache_write", "kv_cache_write_quant", "kv_block_copy", "pa_decode",
-    "pa_prefill_chunk",
+    "pa_decode_append", "pa_prefill_chunk",
     "pa_decode_workspace_size", "pa_prefill_workspace_size", "PA_DTYPE",
 ]
 
@@ -72,6 +73,10 @@ _SIGS = {
     "pa_decode": (_c.c_int, [_c.POINTER(_Pool), _c.c_void_p, _c.c_int32, _c.c_void_p, _c.c_void_p,
                              _c.c_int32, _c.c_void_p, _c.c_int32, _c.c_int32, _c.c_int32,
                              _c.c_float, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "pa_decode_append": (_c.c_int, [_c.POINTER(_Pool), _c.c_void_p, _c.c_int32, _c.c_void_p,
+                                    _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int32,
+                                    _c.c_void_p, _c.c_void_p, _c.c_int32, _c.c_int32, _c.c_int32,
+                                    _c.c_float, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "pa_prefill_workspace_size": (_c.c_size_t, [_c.c_int32] * 8),
     "pa_bm_create": (_c.c_void_p, [_c.c_int32, _c.c_int32, _c.c_int32]),
     "pa_bm_num_free_host": (_c.c_int32, [_c.c_void_p]),
@@ -270,6 +275,26 @@ def pa_decode(pool: KVPool, q, block_tables, context_lens, max_context_len: int,
         pool.ref(), _ptr(q), _dt(q), _ptr(out), _ptr(block_tables), int(block_tables.shape[1]),
         _ptr(context_lens), int(S), int(hq), int(max_context_len), float(scale),
         _ptr(workspace), wbytes, _stream(q, stream)))
+    return out
+
+
+def pa_decode_append(pool: KVPool, q, k_new, v_new, block_tables, context_lens,
+                     max_context_len: int, scale: float, out=None, slot_mapping=None,
+                     workspace=None, stream=None):
+    """Decode with the new rows' cache write fused in: equals pa_slot_mapping (row s at
+    position context_lens[s] - 1), kv_cache_write and pa_decode in that order.
+    ``slot_mapping`` (int64 [num_seqs]), when given, receives the slots."""
+    lib = load_library()
+    S, hq, _ = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    need = pa_decode_workspace_size(S, hq, pool.num_kv_heads, pool.head_dim, max_context_len)
+    workspace = _workspace(need, q.device, workspace)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pa_decode_append", lib.pa_decode_append(
+        pool.ref(), _ptr(q), _dt(q), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(block_tables),
+        int(block_tables.shape[1]), _ptr(context_lens), _ptr(slot_mapping), int(S), int(hq),
+        int(max_context_len), float(scale), _ptr(workspace), wbytes, _stream(q, stream)))
     return out
 
 

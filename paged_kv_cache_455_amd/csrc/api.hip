@@ -396,11 +396,15 @@ static pa_status_t fill_decode_args(const pa_kv_pool_t *pool, const void *q, int
   return PA_OK;
 }
 
-pa_status_t pa_decode(const pa_kv_pool_t *pool, const void *q, int32_t q_dtype, void *out,
-                      const int32_t *block_tables, int32_t max_blocks_per_seq,
-                      const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
-                      int32_t max_context_len, float scale, void *workspace,
-                      size_t workspace_bytes, hipStream_t stream) {
+// pa_decode, and pa_decode_append when k_new is set (new rows read by the decode,
+// stored into the pool by its merge kernel).
+static pa_status_t decode_call(const pa_kv_pool_t *pool, const void *q, int32_t q_dtype,
+                               const void *k_new, const void *v_new, void *out,
+                               const int32_t *block_tables, int32_t max_blocks_per_seq,
+                               const int32_t *context_lens, int64_t *slot_mapping,
+                               int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                               float scale, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
   if (num_seqs < 0) return fail(PA_E_ARG, "num_seqs must be >= 0");
   if (num_seqs == 0) return PA_OK;
   pa::DecodeArgs a;
@@ -422,10 +426,49 @@ pa_status_t pa_decode(const pa_kv_pool_t *pool, const void *q, int32_t q_dtype, 
   a.num_seqs = num_seqs;
   a.min_tpw = kMinTilesPerWave;
   a.seg_cost = seg_cost();
+  if (k_new != nullptr) {
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.pool_k = pool->k;
+    a.pool_v = pool->v;
+    a.slots_out = slot_mapping;
+  }
   const bool stream_loads = (pool->flags & PA_POOL_SHARED_BLOCKS) == 0;
   return hip_status(pa::launch_decode_stream(a, pool->kv_dtype, q_dtype, pool->head_dim, group,
                                              num_seqs, stream_loads, stream),
-                    "pa_decode launch");
+                    k_new ? "pa_decode_append launch" : "pa_decode launch");
+}
+
+pa_status_t pa_decode(const pa_kv_pool_t *pool, const void *q, int32_t q_dtype, void *out,
+                      const int32_t *block_tables, int32_t max_blocks_per_seq,
+                      const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t max_context_len, float scale, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  return decode_call(pool, q, q_dtype, nullptr, nullptr, out, block_tables, max_blocks_per_seq,
+                     context_lens, nullptr, num_seqs, num_q_heads, max_context_len, scale,
+                     workspace, workspace_bytes, stream);
+}
+
+pa_status_t pa_decode_append(const pa_kv_pool_t *pool, const void *q, int32_t q_dtype,
+                             const void *k_new, const void *v_new, void *out,
+                             const int32_t *block_tables, int32_t max_blocks_per_seq,
+                             const int32_t *context_lens, int64_t *slot_mapping,
+                             int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                             float scale, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  pa_status_t st = check_pool(pool, true);
+  if (st != PA_OK) return st;
+  if (is_quantised(pool->kv_dtype))
+    return fail(PA_E_UNSUPPORTED,
+                "pa_decode_append takes f32/f16/bf16 pools; 1-byte pools quantise on write "
+                "(kv_cache_write_quant, then pa_decode)");
+  if (!k_new || !v_new) return fail(PA_E_ARG, "NULL k_new / v_new");
+  if (((uintptr_t)k_new | (uintptr_t)v_new) & 15)
+    return fail(PA_E_ARG, "k_new and v_new must be 16-byte aligned");
+  if ((uintptr_t)slot_mapping & 7) return fail(PA_E_ARG, "slot_mapping must be 8-byte aligned");
+  return decode_call(pool, q, q_dtype, k_new, v_new, out, block_tables, max_blocks_per_seq,
+                     context_lens, slot_mapping, num_seqs, num_q_heads, max_context_len, scale,
+                     workspace, workspace_bytes, stream);
 }
 
 // Workspace of the mixed step.  f16/bf16 KV: a header int, the prefill tile list,
@@ -571,15 +614,20 @@ pa_status_t pa_decode_step_graph(const pa_kv_pool_t *pool, const void *q, int32_
     (void)hipStreamDestroy(cs);
     return hip_status(e, "hipStreamBeginCapture");
   }
-  st = pa_slot_mapping(block_tables, max_blocks_per_seq, pool->block_size, query_start_loc,
-                       context_lens, num_seqs, num_seqs, slot_mapping, cs);
-  if (st == PA_OK)
-    st = is_quantised(pool->kv_dtype)
-             ? kv_cache_write_quant(pool, k_new, v_new, new_dtype, slot_mapping, num_seqs, cs)
-             : kv_cache_write(pool, k_new, v_new, slot_mapping, num_seqs, cs);
-  if (st == PA_OK)
-    st = pa_decode(pool, q, q_dtype, out, block_tables, max_blocks_per_seq, context_lens,
-                   num_seqs, num_q_heads, max_context_len, scale, workspace, workspace_bytes, cs);
+  if (is_quantised(pool->kv_dtype)) {
+    st = pa_slot_mapping(block_tables, max_blocks_per_seq, pool->block_size, query_start_loc,
+                         context_lens, num_seqs, num_seqs, slot_mapping, cs);
+    if (st == PA_OK)
+      st = kv_cache_write_quant(pool, k_new, v_new, new_dtype, slot_mapping, num_seqs, cs);
+    if (st == PA_OK)
+      st = pa_decode(pool, q, q_dtype, out, block_tables, max_blocks_per_seq, context_lens,
+                     num_seqs, num_q_heads, max_context_len, scale, workspace, workspace_bytes,
+                     cs);
+  } else {  // float pools: the write rides in the decode (pa_decode_append)
+    st = pa_decode_append(pool, q, q_dtype, k_new, v_new, out, block_tables, max_blocks_per_seq,
+                          context_lens, slot_mapping, num_seqs, num_q_heads, max_context_len,
+                          scale, workspace, workspace_bytes, cs);
+  }
   hipGraph_t g = nullptr;
   e = hipStreamEndCapture(cs, &g);
   (void)hipStreamDestroy(cs);

@@ -827,7 +827,7 @@ __device__ __forceinline__ void stream_run(const DecodeArgs &a, P &path, int w, 
   if (n > 1) stream_step(a, win, sg1, j1, lane);
   int bt1 = bt_of(sg1, j1);
   typename P::Tile tA, tB;
-  path.load(tA, tile_of(bt0, sg0, j0));
+  path.load(tA, tile_of(bt0, sg0, j0), sg0, j0);
   path.begin_segment();
 
   // compute tile (sg0, j0); emit its segment when it ends there or the range does
@@ -848,7 +848,7 @@ __device__ __forceinline__ void stream_run(const DecodeArgs &a, P &path, int w, 
     if (k + 2 < n) stream_step(a, win, sg2, j2, lane);
     const int bt2 = bt_of(sg2, j2);  // (a repeat of tile k+1's entry at the end)
     if (j1 == 0) path.prefetch_q(sg1);
-    path.load(nxt, tile_of(bt1, sg1, j1));
+    path.load(nxt, tile_of(bt1, sg1, j1), sg1, j1);
     finish(cur, true);
     sg0 = sg1;
     j0 = j1;
@@ -894,13 +894,22 @@ struct GenericPath {
         kbase(reinterpret_cast<const char *>(args.k) + ln * Gm::CB),
         vbase(reinterpret_cast<const char *>(args.v) + ln * Gm::CB) {}
 
-  __device__ __forceinline__ void load(Tile &t, int64_t tile) {
+  // Tile j of segment sg.  With a fused append (k_new set) the newest row of the
+  // segment -- row tail - 1 of its last tile, not yet in the pool -- is read from
+  // k_new / v_new instead; every load is still issued, only its address differs.
+  __device__ __forceinline__ void load(Tile &t, int64_t tile, const StreamSeg &sg, int j) {
     const char *kp = kbase + tile * Gm::TILE_BYTES;
     const char *vp = vbase + tile * Gm::TILE_BYTES;
+    const int nr = (a.k_new != nullptr && j == sg.nblk - 1) ? sg.tail - 1 : -1;
+    const int64_t no = ((int64_t)sg.s * a.num_kv_heads + sg.h) * (D * Gm::E) + cidx * Gm::CB;
+    const char *kn = reinterpret_cast<const char *>(a.k_new) + no;
+    const char *vn = reinterpret_cast<const char *>(a.v_new) + no;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) t.k[i] = load_chunk<W32, NT>(kp + i * kWave * Gm::CB);
+    for (int i = 0; i < NL; ++i)
+      t.k[i] = load_chunk<W32, NT>(i * Gm::TPI + tg == nr ? kn : kp + i * kWave * Gm::CB);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) t.v[i] = load_chunk<W32, NT>(vp + i * kWave * Gm::CB);
+    for (int i = 0; i < NL; ++i)
+      t.v[i] = load_chunk<W32, NT>(i * Gm::TPI + tg == nr ? vn : vp + i * kWave * Gm::CB);
     if constexpr (kQuant) {
       t.ks = a.k_scale[tile >> a.bs_shift];
       t.vs = a.v_scale[tile >> a.bs_shift];
@@ -1187,7 +1196,7 @@ struct Q8Path {
         kbase(reinterpret_cast<const char *>(args.k) + (ln & 15) * D + 16 * (ln >> 4)),
         vbase(reinterpret_cast<const char *>(args.v) + 4 * (ln >> 4) * D + 8 * (ln & 15)) {}
 
-  __device__ __forceinline__ void load(Tile &t, int64_t tile) {
+  __device__ __forceinline__ void load(Tile &t, int64_t tile, const StreamSeg &, int) {
     const char *kp = kbase + tile * kTileBytes;
     t.k0 = load_tile_part<u32x4, NT>(kp);
     t.k1 = load_tile_part<u32x4, NT>(kp + 64);
@@ -1236,6 +1245,29 @@ __device__ __forceinline__ void decode_stream_q8(const DecodeArgs &a) {
 }
 
 
+// Fused append, after the decode has read the rows: store sequence s's new K and V
+// row of kv head h at its slot, the pool position of token n - 1 ("5688vip" chapter
+// 3, section 3.2: a new token's K/V goes at the end of the request's last block),
+// slot = block_tables[s][(n - 1) / bs] * bs + (n - 1) % bs.  Lanes 0..31 move K,
+// lanes 32..63 V, 16 bytes each (a row is at most 512 bytes).
+template <int D, int E>
+__device__ __forceinline__ void append_new_row(const DecodeArgs &a, int s, int h, int n, int lane) {
+  constexpr int RB = D * E, CPR = RB / 16;
+  static_assert(CPR <= 32, "row too wide");
+  const int bs = kBlock << a.bs_shift, p = n - 1;
+  const int64_t blk = a.bt[(int64_t)s * a.max_blocks_per_seq + p / bs];
+  const int64_t slot = blk * bs + p % bs;
+  if (a.slots_out != nullptr && h == 0 && lane == 0) a.slots_out[s] = slot;
+  const int c = lane & 31;
+  if (c >= CPR) return;
+  const bool is_v = lane >= 32;
+  const int64_t src = ((int64_t)s * a.num_kv_heads + h) * RB + c * 16;
+  const int64_t dst = ((blk * a.num_kv_heads + h) * bs + p % bs) * RB + c * 16;
+  const char *from = reinterpret_cast<const char *>(is_v ? a.v_new : a.k_new) + src;
+  char *to = reinterpret_cast<char *>(is_v ? a.pool_v : a.pool_k) + dst;
+  *reinterpret_cast<u32x4 *>(to) = *reinterpret_cast<const u32x4 *>(from);
+}
+
 // Second pass of the balanced split.  One wave per (sequence s, query head hq):
 // lane p reads piece p's (m, l) (all pieces in flight at once), wave reductions
 // give M = max_p m_p and L = sum_p 2^(m_p - M) l_p, then every lane combines its
@@ -1249,10 +1281,12 @@ __device__ __forceinline__ void merge_stream(const DecodeArgs &a, int s, int hq,
   const int64_t o = (decode_row(a, s) * a.num_q_heads + hq) * D;
   if (n <= 0) {  // undefined input; keep the output finite and defined
     for (int d = lane; d < D; d += kWave) store_out<QT>(a.out, o + d, 0.f);
+    if (a.slots_out != nullptr && hq == 0 && lane == 0) a.slots_out[s] = -1;
     return;
   }
   const int G = a.num_q_heads / a.num_kv_heads;
   const int h = hq / G;
+  if (a.k_new != nullptr && hq % G == 0) append_new_row<D, dtype_bytes(QT)>(a, s, h, n, lane);
   const int nblk = (n + kBlock - 1) / kBlock;
   const int tpw = a.hdr[0];  // cost units per wave; the split is described at stream_range
   const int seg0 = a.hdr[1 + s] + h * (nblk + a.seg_cost) + a.seg_cost;

@@ -37,6 +37,15 @@ struct DecodeArgs {
   // mixed step: [num_seqs + 1] query starts; only q_len == 1 sequences are decoded,
   // sequence s's query/output row being qsl[s] (nullptr: every sequence, row s)
   const int32_t *qsl;
+  // fused append (pa_decode_append; nullptr otherwise): each sequence's new K/V row,
+  // [num_seqs][num_kv_heads][head_dim] in the pool's type, at position ctx[s] - 1.
+  // The decode reads it from here in place of the pool row; the merge kernel then
+  // stores it into the pool (pool_k / pool_v) and its slot into slots_out (if set).
+  const void *k_new;
+  const void *v_new;
+  void *pool_k;
+  void *pool_v;
+  int64_t *slots_out;
 };
 
 struct MixedArgs {

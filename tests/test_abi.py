@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("pa_decode", "pa_prefill_chunk", "kv_cache_write", "kv_cache_write_quant",
+    for n in ("pa_decode", "pa_decode_append", "pa_prefill_chunk", "kv_cache_write", "kv_cache_write_quant",
               "kv_block_copy",
               "pa_slot_mapping", "pa_decode_workspace_size", "pa_prefill_workspace_size",
               "pa_status_string", "pa_last_error", "pa_version",
@@ -87,6 +87,23 @@ def test_decode_argument_checks(lib):
     # empty batch: nothing to do
     assert decode(lib, pool(), S=0) == PA_OK
     assert lib.pa_status_string(PA_E_WORKSPACE) == b"workspace too small"
+
+
+def test_decode_append_argument_checks(lib):
+    f = lambda p, kn=FAKE, vn=FAKE, slots=None, S=4, ws=None, wsb=0: lib.pa_decode_append(
+        ctypes.byref(p), FAKE, p.kv_dtype if p.kv_dtype < 3 else pa.PA_F16, kn, vn, FAKE, FAKE,
+        10, FAKE, slots, S, 32, 100, 0.1, ws, wsb, None)
+    # 1-byte pools quantise on write: not fused
+    assert f(pool(kv=pa.PA_FP8_E4M3, scales=True)) == PA_E_UNSUPPORTED
+    assert f(pool(kv=pa.PA_I8, scales=True)) == PA_E_UNSUPPORTED
+    assert f(pool(), kn=None) == PA_E_ARG
+    assert f(pool(), vn=FAKE + 8) == PA_E_ARG
+    assert f(pool(), slots=FAKE + 4) == PA_E_ARG
+    assert b"aligned" in lib.pa_last_error()
+    assert f(pool(block=24)) == PA_E_UNSUPPORTED
+    # the rest is pa_decode's validation: the workspace check comes last
+    assert f(pool()) == PA_E_WORKSPACE
+    assert f(pool(), S=0) == PA_OK
 
 
 def test_workspace_sizes(lib):
