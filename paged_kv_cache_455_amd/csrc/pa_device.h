@@ -175,6 +175,25 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// max(x, x of lane ^ MASK) for MASK 16 or 32: the row swap leaves the lane's own
+// value in one output and its partner's in the other, so no select is needed.
+template <int MASK>
+__device__ __forceinline__ float max_xor_rows(float x) {
+  static_assert(MASK == 16 || MASK == 32, "row swaps only");
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  unsigned a, b;
+  if constexpr (MASK == 16) {
+    auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    a = r[0];
+    b = r[1];
+  } else {
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    a = r[0];
+    b = r[1];
+  }
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 }  // namespace pa

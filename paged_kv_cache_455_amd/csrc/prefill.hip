@@ -21,6 +21,8 @@
 //  * decode rows (q_len == 1): the balanced-split decode of decode_impl.h over
 //    the batch's one-token sequences (query row qsl[s]), with its piece merge.
 // Other KV types run every query row through the partitioned decode path.
+#include <type_traits>
+
 #include "decode_impl.h"
 
 namespace pa {
@@ -63,21 +65,22 @@ __device__ __forceinline__ f4_t mfma32(const u32x4 &a, const u32x4 &b, const f4_
                                                    __builtin_bit_cast(b8_t, b), c, 0, 0, 0);
 }
 
-// Round 8 floats to the MFMA input type and pack them (nearest even).
+typedef float f2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h2v_t __attribute__((ext_vector_type(2)));
+typedef __bf16 b2v_t __attribute__((ext_vector_type(2)));
+
+// Round 8 floats to the MFMA input type and pack them (nearest even; one packed
+// convert per pair on gfx950, v_cvt_pk_{f16,bf16}_f32).
 template <int KV>
 __device__ __forceinline__ u32x4 pack8(const float *p) {
   u32x4 r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    uint32_t lo, hi;
-    if constexpr (KV == PA_F16) {
-      lo = __builtin_bit_cast(uint16_t, (_Float16)p[2 * i]);
-      hi = __builtin_bit_cast(uint16_t, (_Float16)p[2 * i + 1]);
-    } else {
-      lo = __builtin_bit_cast(uint16_t, (__bf16)p[2 * i]);
-      hi = __builtin_bit_cast(uint16_t, (__bf16)p[2 * i + 1]);
-    }
-    r[i] = lo | (hi << 16);
+    const f2_t v = f2_t{p[2 * i], p[2 * i + 1]};
+    if constexpr (KV == PA_F16)
+      r[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2v_t));
+    else
+      r[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2v_t));
   }
   return r;
 }
@@ -142,15 +145,20 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
     }
   }
 
-  f4_t o[RB][NSL];
-  float m[RB], l[RB];
+  // o: O^T slices; lsum: the running softmax denominators, accumulated on the matrix
+  // cores as ones(16 x 32) . P^T, so every element holds its query row's sum of the
+  // (rounded) probabilities the P.V product used
+  f4_t o[RB][NSL], lsum[RB];
+  float m[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     m[rb] = kNegBig;
-    l[rb] = 0.f;
+    lsum[rb] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int sl = 0; sl < NSL; ++sl) o[rb][sl] = f4_t{0.f, 0.f, 0.f, 0.f};
   }
+  constexpr uint32_t kOne2 = KV == PA_F16 ? 0x3C003C00u : 0x3F803F80u;  // two 16-bit 1.0s
+  const u32x4 ones = u32x4{kOne2, kOne2, kOne2, kOne2};
 
   // ---- global -> registers -> LDS staging of one 32-key step ----
   const char *kpool = reinterpret_cast<const char *>(d.k);
@@ -168,9 +176,6 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
     return r;
   };
   // byte offset of key row `key` (0..31 within the step) in its 16-row tile
-  auto row_off = [&](const StepBt &b, int key) {
-    return ((key < kBlock ? b.u0 : b.u1) * kBlock + (key % kBlock)) * D * 2;
-  };
   // K: chunk q of the step = key q / CPR, 16-byte column q % CPR.
   // V: thread tid < NVB owns dims 4*(tid % (D/4)) .. +3 of keys 4*(tid / (D/4)) .. +3
   // (a wave's loads of one key row are contiguous).
@@ -179,17 +184,32 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
     u32x2 v[4];
   };
   const int vdg = tid % (D / 4), vkg = tid / (D / 4);
+  // Which of the step's two 16-row tiles a thread's K chunk or V rows sit in is the
+  // same for the whole wave (2*D key-row chunks per tile is a multiple of 64 lanes,
+  // and so are the D/4 threads per 4 V rows), so it is chosen on the scalar unit
+  // from the wave's first thread; the thread's offset inside the tile is fixed.
+  const int wtid = __builtin_amdgcn_readfirstlane(tid);
+  uint32_t k_off[NCH];
+  bool k_hi[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int q = tid + 256 * c;
+    k_off[c] = (uint32_t)(((q / CPR) % kBlock) * D * 2 + (q % CPR) * 16);
+    k_hi[c] = (wtid + 256 * c) / CPR >= kBlock;
+  }
+  const uint32_t v_off = (uint32_t)((((4 * vkg) % kKeyStep) % kBlock) * D * 2 + vdg * 8);
+  const bool v_hi = ((4 * (wtid / (D / 4))) % kKeyStep) >= kBlock;
   auto gload = [&](const StepBt &b, Stage &st) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const int q = tid + 256 * c;
-      st.k[c] = *reinterpret_cast<const u32x4 *>(kpool + row_off(b, q / CPR) + (q % CPR) * 16);
+      const char *tb = kpool + (k_hi[c] ? b.u1 : b.u0) * (int64_t)(kBlock * D * 2);
+      st.k[c] = *reinterpret_cast<const u32x4 *>(tb + k_off[c]);
     }
     // (threads past NVB, for head_dim 64, load rows of the step's second block too;
     // lstore ignores them)
-    const int64_t vb = row_off(b, (4 * vkg) % kKeyStep) + vdg * 8;
+    const char *vb = vpool + (v_hi ? b.u1 : b.u0) * (int64_t)(kBlock * D * 2) + v_off;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) st.v[r] = *reinterpret_cast<const u32x2 *>(vpool + vb + r * D * 2);
+    for (int r = 0; r < 4; ++r) st.v[r] = *reinterpret_cast<const u32x2 *>(vb + r * D * 2);
   };
   // V^T rows hold the 32 keys in 4 groups of 8; group gk of dim row d sits at
   // position gk ^ ((d / 8) & 3) so that the operand reads spread over banks.  A
@@ -197,7 +217,7 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
   // permutes) and written as four 8-byte rows.
   // Keys at or past nkeys (the tile's reach; they may hold anything, NaN included)
   // are zeroed on the way in.
-  auto lstore = [&](int buf, int kb, const Stage &st) {
+  auto lstore_impl = [&](int buf, int kb, const Stage &st, auto masked) {
     _Float16 *K = lds + buf * L::kBufHalves;
     _Float16 *Vt = K + L::kKHalves;
 #pragma unroll
@@ -205,14 +225,14 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
       const int q = tid + 256 * c;
       const int key = q / CPR, cc = q % CPR;
       const int pc = cc ^ (key & (CPR - 1));  // swizzle: rows hit different banks
-      const bool ok = kb + key < nkeys;
+      const bool ok = !masked.value || kb + key < nkeys;
       *reinterpret_cast<u32x4 *>(K + key * D + pc * 8) = ok ? st.k[c] : u32x4{0, 0, 0, 0};
     }
     if (tid < NVB) {
       uint32_t v[4][2];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const bool ok = kb + 4 * vkg + r < nkeys;
+        const bool ok = !masked.value || kb + 4 * vkg + r < nkeys;
         v[r][0] = ok ? st.v[r][0] : 0u;
         v[r][1] = ok ? st.v[r][1] : 0u;
       }
@@ -228,6 +248,13 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
         *reinterpret_cast<u32x2 *>(Vt + dim * kVtStride + pos) = col;
       }
     }
+  };
+  // only a step that reaches past the tile's keys needs the zeroing (a uniform branch)
+  auto lstore = [&](int buf, int kb, const Stage &st) {
+    if (kb + kKeyStep <= nkeys)
+      lstore_impl(buf, kb, st, std::false_type{});
+    else
+      lstore_impl(buf, kb, st, std::true_type{});
   };
 
   const int key1 = 8 * (c16 >> 2) + (c16 & 3);  // key row of this lane in QK product 1
@@ -273,8 +300,8 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
       float mx = sc[0];
 #pragma unroll
       for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sc[j]);
-      mx = fmaxf(mx, xor_lanes<16>(mx));
-      mx = fmaxf(mx, xor_lanes<32>(mx));
+      mx = max_xor_rows<16>(mx);
+      mx = max_xor_rows<32>(mx);
       // Lazy rescale: the running max moves only when a score exceeds it by more
       // than kLazy (log2 units), so p = 2^(s*c - m) stays below 2^kLazy, well inside
       // the range of the 16-bit P operand and of the fp32 sums; the result does not
@@ -285,21 +312,21 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
       rescale |= grow;
       alpha[rb] = fast_exp2(m[rb] - mn);
       m[rb] = mn;
-      float p[8], ps = 0.f;
+      float p[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        p[j] = fast_exp2(__builtin_fmaf(sc[j], c, -mn));
-        ps += p[j];
-      }
-      l[rb] = l[rb] * alpha[rb] + ps;
+      for (int j = 0; j < 8; ++j) p[j] = fast_exp2(__builtin_fmaf(sc[j], c, -mn));
       pk[rb] = pack8<KV>(p);
     }
     if (__any(rescale)) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
+      for (int rb = 0; rb < RB; ++rb) {
+        lsum[rb] *= alpha[rb];
 #pragma unroll
         for (int sl = 0; sl < NSL; ++sl) o[rb][sl] *= alpha[rb];
+      }
     }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) lsum[rb] = mfma32<KV>(ones, pk[rb], lsum[rb]);
 #pragma unroll
     for (int sl = 0; sl < NSL; ++sl) {
       const int dim = sl * 16 + c16;
@@ -340,11 +367,8 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
   // ---- normalise and store: lane holds dims sl*16 + 4*g16 + i of query row c16 ----
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    float tot = l[rb];
-    tot += xor_lanes<16>(tot);
-    tot += xor_lanes<32>(tot);
     if (!row_ok[rb]) continue;
-    const float inv = 1.f / tot;
+    const float inv = 1.f / lsum[rb][0];
 #pragma unroll
     for (int sl = 0; sl < NSL; ++sl)
 #pragma unroll
