@@ -640,17 +640,6 @@ struct StreamSeg {
   int tail;   // valid rows of its last block
 };
 
-struct StreamRange {
-  int tpw;        // cost units per wave
-  int n;          // tiles of the wave
-  int j;          // block of the wave's first tile inside its segment
-  StreamSeg seg;  // the first tile's segment
-};
-
-__device__ __forceinline__ int stream_tail(const DecodeArgs &a, int s, int nblk) {
-  return a.ctx[s] - (nblk - 1) * kBlock;
-}
-
 // Context lengths of the sequences [s0, s0 + 64), one per lane (0 past the batch),
 // read back by readlane: walking from segment to segment costs no memory round trip
 // until the wave leaves the window.
@@ -664,6 +653,14 @@ struct SeqWindow {
     if (s - s0 >= kWave) load(a, s, lane);
     return __builtin_amdgcn_readlane(ctx_l, s - s0);
   }
+};
+
+struct StreamRange {
+  int tpw;        // cost units per wave
+  int n;          // tiles of the wave
+  int j;          // block of the wave's first tile inside its segment
+  StreamSeg seg;  // the first tile's segment
+  SeqWindow win;  // context lengths of the 64 sequences from the window holding seg.s
 };
 
 // Move sg to the first segment of the next sequence that has blocks (one exists).
@@ -698,7 +695,7 @@ __device__ __forceinline__ bool stream_range(const DecodeArgs &a, int w, int lan
   const int Hkv = a.num_kv_heads, S = a.num_seqs, c = a.seg_cost;
   auto seq_cost = [&](int nb) { return nb > 0 ? Hkv * (nb + c) : 0; };
   int TC = 0, mxnb = 0;
-  int nb0 = 0, incl0 = 0;  // first 64 sequences, kept for the locate pass
+  int n0 = 0, nb0 = 0, incl0 = 0;  // first 64 sequences, kept for the locate pass
   for (int c0 = 0; c0 < S; c0 += kWave) {
     const int sq = c0 + lane;
     const int n = sq < S ? decode_len(a, sq) : 0;
@@ -706,6 +703,7 @@ __device__ __forceinline__ bool stream_range(const DecodeArgs &a, int w, int lan
     mxnb = max(mxnb, nb);
     const int incl = wave_incl_scan_i(seq_cost(nb), lane);
     if (c0 == 0) {
+      n0 = n;
       nb0 = nb;
       incl0 = incl;
     }
@@ -725,16 +723,19 @@ __device__ __forceinline__ bool stream_range(const DecodeArgs &a, int w, int lan
   const int tend = min(t + r.tpw, TC);
   if (t >= tend) return false;
 
-  int s = 0, cum_s = 0, nblk = 1;
+  int s = 0, cum_s = 0, nblk = 1, ns = 1;
   int base = 0;
+  r.win.s0 = 0;  // (a hit always comes: t < TC)
+  r.win.ctx_l = n0;
   for (int c0 = 0; c0 < S; c0 += kWave) {
     const int sq = c0 + lane;
-    int nb, incl;
+    int n, nb, incl;
     if (c0 == 0) {  // already scanned
+      n = n0;
       nb = nb0;
       incl = incl0;
     } else {
-      const int n = sq < S ? decode_len(a, sq) : 0;
+      n = sq < S ? decode_len(a, sq) : 0;
       nb = n > 0 ? (n + kBlock - 1) / kBlock : 0;
       incl = base + wave_incl_scan_i(seq_cost(nb), lane);
     }
@@ -745,6 +746,10 @@ __device__ __forceinline__ bool stream_range(const DecodeArgs &a, int w, int lan
       s = c0 + l;
       cum_s = __builtin_amdgcn_readlane(excl, l);
       nblk = __builtin_amdgcn_readlane(nb, l);
+      ns = __builtin_amdgcn_readlane(n, l);
+      // the window of lengths this pass already holds (no second read)
+      r.win.s0 = c0;
+      r.win.ctx_l = n;
       break;
     }
     base = __builtin_amdgcn_readlane(incl, kWave - 1);
@@ -753,11 +758,10 @@ __device__ __forceinline__ bool stream_range(const DecodeArgs &a, int w, int lan
   const int h = (t - cum_s) / L;
   const int u = (t - cum_s) - h * L;
   r.j = u < c ? 0 : u - c;
-  r.seg = StreamSeg{s, h, nblk, cum_s, stream_tail(a, s, nblk)};
+  r.seg = StreamSeg{s, h, nblk, cum_s, ns - (nblk - 1) * kBlock};
 
   // count the wave's tiles: walk the segments its range touches
-  SeqWindow win;
-  win.load(a, s, lane);
+  SeqWindow win = r.win;
   StreamSeg sg = r.seg;
   int first = sg.cum + sg.h * (sg.nblk + c) + c + r.j;  // unit of the next tile
   int n = 0;
@@ -809,8 +813,7 @@ __device__ __forceinline__ void stream_run(const DecodeArgs &a, P &path, int w, 
   StreamRange rg;
   if (!stream_range(a, w, lane, rg)) return;
   const int Hkv = a.num_kv_heads, n = rg.n;
-  SeqWindow win;
-  win.load(a, rg.seg.s, lane);
+  SeqWindow win = rg.win;
   const int sh = a.bs_shift;
   auto bt_of = [&](const StreamSeg &sg, int j) {
     return a.bt[(int64_t)sg.s * a.max_blocks_per_seq + (j >> sh)];
