@@ -377,34 +377,74 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
   }
 }
 
-// Work list of prefill tiles (heaviest tile of each chunk first).  One workgroup of
-// 256 threads scans the sequences in rounds of 256.
+// Work list of prefill tiles, heaviest first over the whole step (longest
+// processing time first: the tiles of a chunk with a long prior context start in
+// the first round of workgroups, whichever chunk they belong to).  A tile's cost is
+// its number of 32-key steps.  One workgroup of 256 threads: a counting sort of
+// the tiles by cost (costs past kCostBuckets - 1 share the last bucket), in two
+// passes over the sequences in rounds of 256.  Tiles of equal cost land in any
+// order; each tile writes its own rows, so the order never changes a result.
+constexpr int kCostBuckets = 1024;
+
 __global__ __launch_bounds__(256) void pa_mixed_prep_kernel(MixedArgs a) {
-  __shared__ int sp[256];
+  __shared__ int hist[kCostBuckets];
+  __shared__ int part[256];
   const int tid = threadIdx.x;
-  int base_p = 0;
+  for (int b = tid; b < kCostBuckets; b += 256) hist[b] = 0;
+  __syncthreads();
+  // tiles of sequence s (0 for a decode row or a sequence past the batch), and
+  // the cost bucket of its tile t
+  auto tiles_of = [&](int s, int &first, int &ql) {
+    if (s >= a.num_seqs) return 0;
+    ql = a.qsl[s + 1] - a.qsl[s];
+    if (ql <= 1) return 0;
+    first = a.dec.ctx[s] - ql;
+    return min((ql + a.qtok - 1) / a.qtok, (1 << kItemBits));
+  };
+  auto bucket = [&](int first, int ql, int t) {
+    const int nkeys = first + min((t + 1) * a.qtok, ql);
+    return min((nkeys + kKeyStep - 1) / kKeyStep, kCostBuckets - 1);
+  };
   for (int c0 = 0; c0 < a.num_seqs; c0 += 256) {
-    const int s = c0 + tid;
-    int np = 0;
-    if (s < a.num_seqs) {
-      const int ql = a.qsl[s + 1] - a.qsl[s];
-      if (ql > 1) np = min((ql + a.qtok - 1) / a.qtok, (1 << kItemBits));
-    }
-    sp[tid] = np;
+    int first = 0, ql = 0;
+    const int np = tiles_of(c0 + tid, first, ql);
+    for (int t = 0; t < np; ++t) atomicAdd(&hist[bucket(first, ql, t)], 1);
+  }
+  __syncthreads();
+  // start of every bucket in descending cost order: thread i owns buckets
+  // B-1-4i .. B-4-4i (four in a row, highest first); scan the per-thread sums
+  int loc[4], sum = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    loc[k] = hist[kCostBuckets - 1 - (4 * tid + k)];
+    sum += loc[k];
+  }
+  part[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {  // inclusive scan
+    const int v = tid >= off ? part[tid - off] : 0;
     __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {  // inclusive scan
-      const int vp = tid >= off ? sp[tid - off] : 0;
-      __syncthreads();
-      sp[tid] += vp;
-      __syncthreads();
-    }
-    const int ep = base_p + sp[tid] - np;
-    for (int k = 0; k < np && ep + k < a.p_bound; ++k)
-      a.p_items[ep + k] = (s << kItemBits) | (np - 1 - k);
-    base_p += sp[255];
+    part[tid] += v;
     __syncthreads();
   }
-  if (tid == 0) a.hdr[0] = min(base_p, a.p_bound);
+  int run = part[tid] - sum;
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    hist[kCostBuckets - 1 - (4 * tid + k)] = run;  // bucket start
+    run += loc[k];
+  }
+  __syncthreads();
+  for (int c0 = 0; c0 < a.num_seqs; c0 += 256) {
+    const int s = c0 + tid;
+    int first = 0, ql = 0;
+    const int np = tiles_of(s, first, ql);
+    for (int t = 0; t < np; ++t) {
+      const int pos = atomicAdd(&hist[bucket(first, ql, t)], 1);
+      if (pos < a.p_bound) a.p_items[pos] = (s << kItemBits) | t;
+    }
+  }
+  if (tid == 0) a.hdr[0] = min(part[255], a.p_bound);
 }
 
 // Grid (Hkv, items): the kv head is the fastest index, so with workgroups handed to
