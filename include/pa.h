@@ -259,6 +259,40 @@ pa_status_t pa_prefill_chunk(const pa_kv_pool_t *pool, const void *q, int32_t q_
                              void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * ---- Input checks: a debugging aid for the arrays the calls take on trust ----
+ * The calls above never read their index arrays back (that would need a
+ * synchronisation): a block id outside the pool, a length past its table, a
+ * repeated slot or overlapping copy pairs are undefined behaviour there.  These
+ * enqueue a kernel that reads the same arrays, compares values only (no id is used
+ * as an address) and ORs one bit per kind of violation into *flags, an int32 in
+ * device memory that the caller zeroes beforehand and reads after synchronising.
+ * The slot and pair checks compare every two entries (quadratic in the count).
+ * Only num_blocks and block_size of the pool are used.  Errors: PA_E_ARG for NULL
+ * arrays or flags, negative counts or a bad pool geometry; PA_E_HIP on launch.
+ */
+#define PA_CHECK_LEN 1      /* a length < 1, above the bound given, or past its table row */
+#define PA_CHECK_BLOCK 2    /* an id in the used part of a table row outside [0, num_blocks) */
+#define PA_CHECK_QSL 4      /* query_start_loc[0] != 0, or a q_len < 1 or above its seq_len */
+#define PA_CHECK_SLOT 8     /* a slot >= num_blocks * block_size (negative = skipped, allowed) */
+#define PA_CHECK_SLOT_DUP 16 /* two tokens with one slot (>= 0) */
+#define PA_CHECK_PAIR 32    /* a copy pair id out of range, a repeated destination, or a
+                               source that is some pair's destination */
+
+/* block_tables / seq_lens (/ query_start_loc) as pa_decode or pa_prefill_chunk
+ * read them: query_start_loc may be NULL (one row per sequence); max_seq_len is
+ * the host bound passed to those calls. */
+pa_status_t pa_check_tables(const pa_kv_pool_t *pool, const int32_t *block_tables,
+                            int32_t max_blocks_per_seq, const int32_t *seq_lens,
+                            const int32_t *query_start_loc, int32_t num_seqs, int32_t max_seq_len,
+                            int32_t *flags, hipStream_t stream);
+/* slot_mapping as kv_cache_write / kv_cache_write_quant read it. */
+pa_status_t pa_check_slots(const pa_kv_pool_t *pool, const int64_t *slot_mapping,
+                           int32_t num_tokens, int32_t *flags, hipStream_t stream);
+/* src_dst as kv_block_copy reads it. */
+pa_status_t pa_check_copy_pairs(const pa_kv_pool_t *pool, const int32_t *src_dst,
+                                int32_t num_pairs, int32_t *flags, hipStream_t stream);
+
+/*
  * ---- A captured decode step ([P3] 4.2: the serving engine builds graphs of
  * its step at start-up; 6.2: running eagerly instead saves that memory but adds
  * latency to every step; here a HIP graph). ----

@@ -24,6 +24,7 @@ __all__ = [
     "pa_slot_mapping", "kv_cache_write", "kv_cache_write_quant", "kv_block_copy", "pa_decode",
     "pa_decode_append", "pa_prefill_chunk",
     "pa_decode_workspace_size", "pa_prefill_workspace_size", "PA_DTYPE",
+    "pa_check_tables", "pa_check_slots", "pa_check_copy_pairs", "PA_CHECK",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -78,6 +79,12 @@ _SIGS = {
                                     _c.c_void_p, _c.c_void_p, _c.c_int32, _c.c_int32, _c.c_int32,
                                     _c.c_float, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "pa_prefill_workspace_size": (_c.c_size_t, [_c.c_int32] * 8),
+    "pa_check_tables": (_c.c_int, [_c.POINTER(_Pool), _c.c_void_p, _c.c_int32, _c.c_void_p,
+                                   _c.c_void_p, _c.c_int32, _c.c_int32, _c.c_void_p, _c.c_void_p]),
+    "pa_check_slots": (_c.c_int, [_c.POINTER(_Pool), _c.c_void_p, _c.c_int32, _c.c_void_p,
+                                  _c.c_void_p]),
+    "pa_check_copy_pairs": (_c.c_int, [_c.POINTER(_Pool), _c.c_void_p, _c.c_int32, _c.c_void_p,
+                                       _c.c_void_p]),
     "pa_bm_create": (_c.c_void_p, [_c.c_int32, _c.c_int32, _c.c_int32]),
     "pa_bm_num_free_host": (_c.c_int32, [_c.c_void_p]),
     "pa_bm_swap_out": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_void_p]),
@@ -314,6 +321,46 @@ def pa_prefill_chunk(pool: KVPool, q, query_start_loc, seq_lens, block_tables, m
         _ptr(block_tables), int(block_tables.shape[1]), S, int(T), int(hq), int(max_query_len),
         int(max_seq_len), float(scale), _ptr(workspace), wbytes, _stream(q, stream)))
     return out
+
+
+# bits of the input checks' flags word (include/pa.h PA_CHECK_*)
+PA_CHECK = {"len": 1, "block": 2, "qsl": 4, "slot": 8, "slot_dup": 16, "pair": 32}
+
+
+def _flags(device, flags):
+    if flags is None:
+        flags = torch.zeros(1, dtype=torch.int32, device=device)
+    return flags
+
+
+def pa_check_tables(pool: KVPool, block_tables, seq_lens, max_seq_len: int, query_start_loc=None,
+                    flags=None, stream=None):
+    """OR PA_CHECK_* bits for bad lengths, table ids or query starts into ``flags``
+    (int32 [1] on the device, zeroed here when not given); read it after a sync."""
+    lib = load_library()
+    flags = _flags(block_tables.device, flags)
+    _check("pa_check_tables", lib.pa_check_tables(
+        pool.ref(), _ptr(block_tables), int(block_tables.shape[1]), _ptr(seq_lens),
+        _ptr(query_start_loc), int(seq_lens.shape[0]), int(max_seq_len), _ptr(flags),
+        _stream(block_tables, stream)))
+    return flags
+
+
+def pa_check_slots(pool: KVPool, slot_mapping, flags=None, stream=None):
+    lib = load_library()
+    flags = _flags(slot_mapping.device, flags)
+    _check("pa_check_slots", lib.pa_check_slots(
+        pool.ref(), _ptr(slot_mapping), int(slot_mapping.shape[0]), _ptr(flags),
+        _stream(slot_mapping, stream)))
+    return flags
+
+
+def pa_check_copy_pairs(pool: KVPool, src_dst, flags=None, stream=None):
+    lib = load_library()
+    flags = _flags(src_dst.device, flags)
+    _check("pa_check_copy_pairs", lib.pa_check_copy_pairs(
+        pool.ref(), _ptr(src_dst), int(src_dst.shape[0]), _ptr(flags), _stream(src_dst, stream)))
+    return flags
 
 
 class DecodeStepGraph:

@@ -209,6 +209,53 @@ pa_status_t pa_slot_mapping(const int32_t *block_tables, int32_t max_blocks_per_
                     "pa_slot_mapping launch");
 }
 
+// The input checks need the pool's geometry only.
+static pa_status_t check_geometry(const pa_kv_pool_t *pool, int32_t *flags) {
+  if (!pool || !flags) return fail(PA_E_ARG, "NULL pool or flags");
+  if (pool->num_blocks <= 0) return fail(PA_E_ARG, "num_blocks must be > 0");
+  if (pool->block_size != 16 && pool->block_size != 32)
+    return fail(PA_E_ARG, "block_size %d (16 or 32)", pool->block_size);
+  return PA_OK;
+}
+
+pa_status_t pa_check_tables(const pa_kv_pool_t *pool, const int32_t *block_tables,
+                            int32_t max_blocks_per_seq, const int32_t *seq_lens,
+                            const int32_t *query_start_loc, int32_t num_seqs, int32_t max_seq_len,
+                            int32_t *flags, hipStream_t stream) {
+  pa_status_t st = check_geometry(pool, flags);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0) return fail(PA_E_ARG, "num_seqs must be >= 0");
+  if (num_seqs == 0) return PA_OK;
+  if (!block_tables || !seq_lens) return fail(PA_E_ARG, "NULL array argument");
+  if (max_blocks_per_seq <= 0) return fail(PA_E_ARG, "max_blocks_per_seq must be > 0");
+  pa::CheckTablesArgs a{block_tables, seq_lens, query_start_loc, flags, pool->num_blocks,
+                        max_blocks_per_seq, pool->block_size, max_seq_len};
+  return hip_status(pa::launch_check_tables(a, num_seqs, stream), "pa_check_tables launch");
+}
+
+pa_status_t pa_check_slots(const pa_kv_pool_t *pool, const int64_t *slot_mapping,
+                           int32_t num_tokens, int32_t *flags, hipStream_t stream) {
+  pa_status_t st = check_geometry(pool, flags);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return fail(PA_E_ARG, "num_tokens must be >= 0");
+  if (num_tokens == 0) return PA_OK;
+  if (!slot_mapping) return fail(PA_E_ARG, "NULL slot_mapping");
+  return hip_status(pa::launch_check_slots(slot_mapping, num_tokens,
+                                           pool->num_blocks * pool->block_size, flags, stream),
+                    "pa_check_slots launch");
+}
+
+pa_status_t pa_check_copy_pairs(const pa_kv_pool_t *pool, const int32_t *src_dst,
+                                int32_t num_pairs, int32_t *flags, hipStream_t stream) {
+  pa_status_t st = check_geometry(pool, flags);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0) return fail(PA_E_ARG, "num_pairs must be >= 0");
+  if (num_pairs == 0) return PA_OK;
+  if (!src_dst) return fail(PA_E_ARG, "NULL src_dst");
+  return hip_status(pa::launch_check_pairs(src_dst, num_pairs, pool->num_blocks, flags, stream),
+                    "pa_check_copy_pairs launch");
+}
+
 pa_status_t kv_cache_write(const pa_kv_pool_t *pool, const void *k_new, const void *v_new,
                            const int64_t *slot_mapping, int32_t num_tokens, hipStream_t stream) {
   pa_status_t st = check_pool(pool, false);

@@ -92,6 +92,23 @@ struct BlockCopyArgs {
   int32_t tile_bytes;  // 16 * head_dim * element bytes
 };
 
+// Input checks (debugging aid): tables and lengths of one call.
+struct CheckTablesArgs {
+  const int32_t *bt;    // [num_seqs][mbps]
+  const int32_t *lens;  // [num_seqs]
+  const int32_t *qsl;   // [num_seqs + 1] or nullptr
+  int32_t *flags;       // OR-ed PA_CHECK_* bits
+  int64_t num_blocks;
+  int32_t mbps;
+  int32_t block_size;
+  int32_t max_len;
+};
+hipError_t launch_check_tables(const CheckTablesArgs &a, int32_t num_seqs, hipStream_t st);
+hipError_t launch_check_slots(const int64_t *slots, int32_t n, int64_t num_slots, int32_t *flags,
+                              hipStream_t st);
+hipError_t launch_check_pairs(const int32_t *pairs, int32_t n, int64_t num_blocks,
+                              int32_t *flags, hipStream_t st);
+
 // stream_loads: read K/V tiles with the nontemporal hint (off when blocks are shared)
 hipError_t launch_decode_stream(const DecodeArgs &a, int kv_dtype, int q_dtype, int head_dim,
                                 int group, int num_seqs, bool stream_loads, hipStream_t st);

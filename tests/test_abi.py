@@ -39,7 +39,8 @@ def test_header_declares_the_entry_points():
               "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free", "pa_bm_refcount", "pa_bm_add",
               "pa_bm_fork", "pa_bm_append", "pa_bm_release", "pa_bm_step", "pa_bm_num_free_host",
               "pa_bm_swap_out", "pa_bm_swap_in", "pa_bm_lru", "pa_bm_blocks", "pa_bm_swaps",
-              "kv_swap", "pa_decode_step_graph", "pa_graph_launch", "pa_graph_destroy"):
+              "kv_swap", "pa_decode_step_graph", "pa_graph_launch", "pa_graph_destroy",
+              "pa_check_tables", "pa_check_slots", "pa_check_copy_pairs"):
         assert n in names, n
 
 
@@ -104,6 +105,25 @@ def test_decode_append_argument_checks(lib):
     # the rest is pa_decode's validation: the workspace check comes last
     assert f(pool()) == PA_E_WORKSPACE
     assert f(pool(), S=0) == PA_OK
+
+
+def test_input_check_argument_checks(lib):
+    p = pool()
+    t = lambda pl=p, bt=FAKE, fl=FAKE, S=3: lib.pa_check_tables(
+        ctypes.byref(pl) if pl is not None else None, bt, 8, FAKE, None, S, 100, fl, None)
+    assert t(fl=None) == PA_E_ARG
+    assert t(pl=None) == PA_E_ARG
+    assert t(bt=None) == PA_E_ARG
+    assert t(S=-1) == PA_E_ARG
+    assert t(S=0) == PA_OK
+    assert t(pl=pool(block=24)) == PA_E_ARG
+    assert t(pl=pool(nb=0)) == PA_E_ARG
+    assert lib.pa_check_slots(ctypes.byref(p), None, 4, FAKE, None) == PA_E_ARG
+    assert lib.pa_check_slots(ctypes.byref(p), FAKE, 0, FAKE, None) == PA_OK
+    assert lib.pa_check_slots(ctypes.byref(p), FAKE, 4, None, None) == PA_E_ARG
+    assert lib.pa_check_copy_pairs(ctypes.byref(p), FAKE, -2, FAKE, None) == PA_E_ARG
+    assert lib.pa_check_copy_pairs(ctypes.byref(p), None, 2, FAKE, None) == PA_E_ARG
+    assert lib.pa_check_copy_pairs(ctypes.byref(p), FAKE, 0, FAKE, None) == PA_OK
 
 
 def test_workspace_sizes(lib):
