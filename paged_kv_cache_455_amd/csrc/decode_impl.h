@@ -1298,7 +1298,7 @@ __device__ __forceinline__ void merge_stream(const DecodeArgs &a, int s, int hq,
   const int64_t r0 = ((int64_t)s * a.num_q_heads + hq) * a.max_parts;
   constexpr int PER = (D + kWave - 1) / kWave;  // output elements per lane
   constexpr int PB = 8;                         // pieces whose acc loads are in flight together
-  // Round 1 of loads: (m, l) of every piece (lane p) and the acc of the first PB pieces
+  // First batch of loads: (m, l) of every piece (lane p) and the acc of the first PB pieces
   // (the acc loads do not wait for the weights).
   float mp = kNegBig, lp = 0.f;
   if (lane < pieces) {
