@@ -116,3 +116,43 @@ def test_fused_refuses_quantised_pools():
     with pytest.raises(pa.PagedAttentionError, match="unsupported"):
         pa.pa_decode_append(pool, dev(b.q), dev(b.k_new), dev(b.v_new), dev(b.block_tables),
                             dev(b.seq_lens), b.max_seq_len, b.scale)
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_fused_prefix_sharing_cow_step(bs):
+    """Prefix sharing + copy-on-write ("uml.org.cn" Prefix Sharing): the copies run
+    first, then the fused step writes each row into its (possibly fresh) last block
+    and attends, on a pool declared to share blocks (cached loads).  Pools and slots
+    must equal the separate calls bit for bit, the output too."""
+    b = W.prefix_cow(n_req=24, n_forks=6, suffix_hi=400, block_size=bs)
+    say(b.name, "block", bs)
+    dev = lambda t: t.clone().cuda()
+    kA, vA, kB, vB = dev(b.k_pool), dev(b.v_pool), dev(b.k_pool), dev(b.v_pool)
+    poolA = pa.KVPool(kA, vA, shared_blocks=True)
+    poolB = pa.KVPool(kB, vB, shared_blocks=True)
+    q, kn, vn, bt, lens = dev(b.q), dev(b.k_new), dev(b.v_new), dev(b.block_tables), dev(b.seq_lens)
+    pairs = dev(b.copy_pairs)
+    S = b.num_seqs
+    qsl = torch.arange(S + 1, dtype=torch.int32, device="cuda")
+    pa.kv_block_copy(poolA, pairs)
+    slotsA = pa.pa_slot_mapping(bt, qsl, lens, S, block_size=bs)
+    pa.kv_cache_write(poolA, kn, vn, slotsA)
+    outA = pa.pa_decode(poolA, q, bt, lens, b.max_seq_len, b.scale)
+    pa.kv_block_copy(poolB, pairs)
+    slotsB = torch.empty_like(slotsA)
+    outB = pa.pa_decode_append(poolB, q, kn, vn, bt, lens, b.max_seq_len, b.scale,
+                               slot_mapping=slotsB)
+    torch.cuda.synchronize()
+    assert torch.equal(slotsA, slotsB)
+    assert torch.equal(_bits(kA), _bits(kB)) and torch.equal(_bits(vA), _bits(vB))
+    assert torch.equal(_bits(outA), _bits(outB))
+    # and the oracle on a few rows, parents and forks
+    kp, vp, _, _ = oracle.block_copy(np_of(b.k_pool), np_of(b.v_pool), b.copy_pairs.numpy())
+    kp, vp = oracle.cache_write(kp, vp, np_of(b.k_new), np_of(b.v_new), oracle_slots(b))
+    assert np.array_equal(np_of(kB), kp) and np.array_equal(np_of(vB), vp)
+    rows = [0, 1, S // 2, S - 2, S - 1]
+    ref = oracle.decode(np_of(b.q).astype(np.float64)[rows], kp, vp, b.block_tables.numpy()[rows],
+                        b.seq_lens.numpy()[rows], b.scale)
+    err = max_err(outB[rows], ref)
+    say("max err", err)
+    assert err <= TOL["bf16"]
