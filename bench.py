@@ -4,9 +4,9 @@
 A step is one pass of the whole path over one synthetic batch already resident
 in HBM: slot mapping -> (copy-on-write block copies) -> cache write of this
 step's K/V -> paged attention (decode, or the mixed prefill+decode launch).  A
-decode step on a float pool runs slot mapping, write and decode as one
-pa_decode_append call (``--unfused``: three calls); 1-byte pools quantise on
-write (kv_cache_write_quant) before pa_decode.
+decode step runs slot mapping, write and decode as one pa_decode_append call
+(``--unfused``: separate calls); 1-byte pools quantise the new rows on write
+inside it.
 
 Default workload: the Llama-3-8B-shaped decode layer (64 sequences, contexts
 uniform in [128, 4096], 32 query / 8 KV heads, head_dim 128, fp16 KV, fp32
@@ -449,8 +449,9 @@ def main():
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     quantised = b.k_scale is not None
-    # decode steps on float pools write the new rows inside the decode call
-    fused = b.kind == "decode" and k_new is not None and not quantised and not args.unfused
+    # decode steps write the new rows inside the decode call (1-byte pools quantise
+    # them there, in a launch of their own)
+    fused = b.kind == "decode" and k_new is not None and not args.unfused
 
     def step(i, ev=None):
         pool = pools[i % R]
@@ -512,7 +513,7 @@ def main():
     step_gbps = (a_bytes + s_bytes) / (ms_per_step * 1e-3) / 1e9
     # the timed call: the attention, plus (fused) the new rows' read, store and slots
     call_bytes = a_bytes + (b.num_tokens * 8 + 2 * b.num_tokens * b.num_kv_heads * b.head_dim *
-                            2 * ELEM[b.kv_dtype] if fused else 0)
+                            (b.k_new.element_size() + ELEM[b.kv_dtype]) if fused else 0)
     attn_gbps = call_bytes / (attn_ms_avg * 1e-3) / 1e9
     tokens = b.num_seqs if b.kind == "decode" else b.num_tokens
     rec = {

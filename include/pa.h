@@ -215,15 +215,19 @@ pa_status_t pa_decode(const pa_kv_pool_t *pool, const void *q, int32_t q_dtype, 
  * out is bit-identical and the pools byte-identical.  The attention reads the
  * new rows from k_new / v_new, so the write needs no launch of its own; the
  * pool rows are stored within the call, after every read of the pool.
- *   k_new, v_new  [num_seqs][num_kv_heads][head_dim], the pool's kv_dtype,
- *                 16-byte aligned
+ *   k_new, v_new  [num_seqs][num_kv_heads][head_dim], 16-byte aligned: the
+ *                 pool's kv_dtype for f32/f16/bf16 pools; for fp8/int8 pools
+ *                 q_dtype, quantised on write by kv_cache_write_quant's policy
+ *                 (the result then equals pa_slot_mapping, kv_cache_write_quant
+ *                 and pa_decode; three launches, the write's slots taken from the
+ *                 block tables)
  *   slot_mapping  int64 [num_seqs] receives each row's slot
- *                 (block * block_size + offset); may be NULL
+ *                 (block * block_size + offset; -1 for a context length < 1);
+ *                 may be NULL
  *   the rest      as pa_decode; the workspace is pa_decode_workspace_size's
- * Errors as pa_decode, plus PA_E_UNSUPPORTED for fp8/int8 pools (their write
- * quantises and may re-encode the block: kv_cache_write_quant, then pa_decode)
- * and PA_E_ARG for NULL or misaligned k_new / v_new.  Slots must be distinct
- * across sequences (no two sequences own one block's same row).
+ * Errors as pa_decode, plus PA_E_ARG for NULL or misaligned k_new / v_new.
+ * Sequences' new rows must sit in distinct blocks (each writes the end of a last
+ * block it owns alone, as copy-on-write guarantees).
  */
 pa_status_t pa_decode_append(const pa_kv_pool_t *pool, const void *q, int32_t q_dtype,
                              const void *k_new, const void *v_new, void *out,

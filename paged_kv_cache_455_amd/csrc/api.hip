@@ -505,16 +505,51 @@ pa_status_t pa_decode_append(const pa_kv_pool_t *pool, const void *q, int32_t q_
                              hipStream_t stream) {
   pa_status_t st = check_pool(pool, true);
   if (st != PA_OK) return st;
-  if (is_quantised(pool->kv_dtype))
-    return fail(PA_E_UNSUPPORTED,
-                "pa_decode_append takes f32/f16/bf16 pools; 1-byte pools quantise on write "
-                "(kv_cache_write_quant, then pa_decode)");
   if (!k_new || !v_new) return fail(PA_E_ARG, "NULL k_new / v_new");
   if (((uintptr_t)k_new | (uintptr_t)v_new) & 15)
     return fail(PA_E_ARG, "k_new and v_new must be 16-byte aligned");
   if ((uintptr_t)slot_mapping & 7) return fail(PA_E_ARG, "slot_mapping must be 8-byte aligned");
-  return decode_call(pool, q, q_dtype, k_new, v_new, out, block_tables, max_blocks_per_seq,
-                     context_lens, slot_mapping, num_seqs, num_q_heads, max_context_len, scale,
+  if (!is_quantised(pool->kv_dtype))
+    return decode_call(pool, q, q_dtype, k_new, v_new, out, block_tables, max_blocks_per_seq,
+                       context_lens, slot_mapping, num_seqs, num_q_heads, max_context_len, scale,
+                       workspace, workspace_bytes, stream);
+  // 1-byte pools: the new rows (in q's dtype) are quantised on write, their slots
+  // taken from the tables, then the decode reads them from the pool
+  if (num_seqs < 0) return fail(PA_E_ARG, "num_seqs must be >= 0");
+  if (num_seqs == 0) return PA_OK;
+  pa::DecodeArgs probe;
+  int group = 0;
+  st = fill_decode_args(pool, q, q_dtype, out, block_tables, max_blocks_per_seq, context_lens,
+                        num_seqs, num_q_heads, max_context_len, scale, nullptr, 0, probe, group,
+                        /*partitioned=*/false);
+  if (st != PA_OK) return st;
+  if (workspace == nullptr ||
+      workspace_bytes < stream_layout(num_seqs, num_q_heads, pool->head_dim, max_context_len).total)
+    return decode_call(pool, q, q_dtype, nullptr, nullptr, out, block_tables, max_blocks_per_seq,
+                       context_lens, nullptr, num_seqs, num_q_heads, max_context_len, scale,
+                       workspace, workspace_bytes, stream);  // reports the workspace error
+  pa::CacheWriteArgs w{};
+  w.k = pool->k;
+  w.v = pool->v;
+  w.k_scale = pool->k_scale;
+  w.v_scale = pool->v_scale;
+  w.k_new = k_new;
+  w.v_new = v_new;
+  w.slots = nullptr;
+  w.num_blocks = pool->num_blocks;
+  w.num_tokens = num_seqs;
+  w.num_kv_heads = pool->num_kv_heads;
+  w.row_bytes = pool->head_dim;
+  w.block_size = pool->block_size;
+  w.bt = block_tables;
+  w.ctx = context_lens;
+  w.slots_out = slot_mapping;
+  w.mbps = max_blocks_per_seq;
+  st = hip_status(pa::launch_cache_write_quant(w, pool->kv_dtype, q_dtype, pool->head_dim, stream),
+                  "pa_decode_append quantised write");
+  if (st != PA_OK) return st;
+  return decode_call(pool, q, q_dtype, nullptr, nullptr, out, block_tables, max_blocks_per_seq,
+                     context_lens, nullptr, num_seqs, num_q_heads, max_context_len, scale,
                      workspace, workspace_bytes, stream);
 }
 

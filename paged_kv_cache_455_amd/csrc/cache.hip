@@ -100,19 +100,27 @@ __global__ __launch_bounds__(64) void kv_cache_write_quant_kernel(CacheWriteArgs
   constexpr int EPL = D / 64;  // dims per lane
   const int t = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
   const bool is_v = blockIdx.z != 0;
-  const int64_t slot = a.slots[t];
-  if (slot < 0) return;
   const int bs = a.block_size;
+  int64_t slot;
+  int len = 1;
+  if (a.slots == nullptr) {  // decode append: one row per sequence, each a run of its own
+    const int n = a.ctx[t];
+    slot = n > 0 ? (int64_t)a.bt[(int64_t)t * a.mbps + (n - 1) / bs] * bs + (n - 1) % bs : -1;
+    if (a.slots_out != nullptr && h == 0 && !is_v && lane == 0) a.slots_out[t] = slot;
+    if (slot < 0) return;
+  } else {
+    slot = a.slots[t];
+    if (slot < 0) return;
+    if (t > 0) {  // not the first row of its run: the run's first row does the work
+      const int64_t prev = a.slots[t - 1];
+      if (prev >= 0 && prev / bs == slot / bs) return;
+    }
+    while (len < bs - (int)(slot % bs) && t + len < a.num_tokens && a.slots[t + len] >= 0 &&
+           a.slots[t + len] / bs == slot / bs)
+      ++len;
+  }
   const int64_t blk = slot / bs;
   const int off = (int)(slot % bs);
-  if (t > 0) {  // not the first row of its run: the run's first row does the work
-    const int64_t prev = a.slots[t - 1];
-    if (prev >= 0 && prev / bs == blk) return;
-  }
-  int len = 1;
-  while (len < bs - off && t + len < a.num_tokens && a.slots[t + len] >= 0 &&
-         a.slots[t + len] / bs == blk)
-    ++len;
 
   const void *src = is_v ? a.v_new : a.k_new;
   uint8_t *tile = reinterpret_cast<uint8_t *>(is_v ? a.v : a.k) +

@@ -72,6 +72,12 @@ struct CacheWriteArgs {
   int32_t num_kv_heads;
   int32_t row_bytes;   // head_dim * element bytes
   int32_t block_size;  // tokens per physical block (16 or 32)
+  // decode append (slots == nullptr): token t is sequence t's new row at position
+  // ctx[t] - 1 of its table row; its slot is computed here and stored to slots_out
+  const int32_t *bt;
+  const int32_t *ctx;
+  int64_t *slots_out;
+  int32_t mbps;
 };
 
 // Block tiles (and scales) copied from one pool to another of the same geometry;

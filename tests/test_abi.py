@@ -94,9 +94,10 @@ def test_decode_append_argument_checks(lib):
     f = lambda p, kn=FAKE, vn=FAKE, slots=None, S=4, ws=None, wsb=0: lib.pa_decode_append(
         ctypes.byref(p), FAKE, p.kv_dtype if p.kv_dtype < 3 else pa.PA_F16, kn, vn, FAKE, FAKE,
         10, FAKE, slots, S, 32, 100, 0.1, ws, wsb, None)
-    # 1-byte pools quantise on write: not fused
-    assert f(pool(kv=pa.PA_FP8_E4M3, scales=True)) == PA_E_UNSUPPORTED
-    assert f(pool(kv=pa.PA_I8, scales=True)) == PA_E_UNSUPPORTED
+    # 1-byte pools quantise on write (q's dtype): the same checks, then the workspace
+    assert f(pool(kv=pa.PA_FP8_E4M3, scales=True)) == PA_E_WORKSPACE
+    assert f(pool(kv=pa.PA_I8, scales=True)) == PA_E_WORKSPACE
+    assert f(pool(kv=pa.PA_I8)) == PA_E_ARG                              # scales missing
     assert f(pool(), kn=None) == PA_E_ARG
     assert f(pool(), vn=FAKE + 8) == PA_E_ARG
     assert f(pool(), slots=FAKE + 4) == PA_E_ARG

@@ -18,7 +18,7 @@ import oracle
 import paged_kv_cache_455_amd as pa
 from paged_kv_cache_455_amd import workloads as W
 
-from .pa_testlib import TOL, max_err, np_of, oracle_slots, sample_rows
+from .pa_testlib import TOL, max_err, np_of, oracle_decode_rows, oracle_slots, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -109,13 +109,47 @@ def test_fused_llama_decode_layer(bs):
     assert err <= TOL["f16"]
 
 
-def test_fused_refuses_quantised_pools():
-    b = W.decode_batch(5, [20, 40], 64, 8, 128, "fp8", "bf16", name="append-fp8")
+@pytest.mark.parametrize("kv,qd,hq,bs", [("fp8", "bf16", 64, 16), ("i8", "f16", 32, 32),
+                                         ("fp8", "f16", 16, 32), ("i8", "bf16", 64, 16)])
+def test_fused_quantised_equals_separate_and_oracle(kv, qd, hq, bs):
+    """1-byte pools: the new rows (in q's dtype) are quantised on write with the slots
+    taken from the tables; codes, scales, slots and output must equal
+    pa_slot_mapping + kv_cache_write_quant + pa_decode bit for bit."""
+    ctx = [1, 2, 15, 16, 17, 33, 100, 511, 1000, 1500]
+    b = W.decode_batch(91, ctx, hq, 8, 128, kv, qd, name=f"append-{kv}", block_size=bs)
+    say(b.name, qd, "block", bs)
     dev = lambda t: t.clone().cuda()
-    pool = pa.KVPool(dev(b.k_pool), dev(b.v_pool), dev(b.k_scale), dev(b.v_scale))
-    with pytest.raises(pa.PagedAttentionError, match="unsupported"):
-        pa.pa_decode_append(pool, dev(b.q), dev(b.k_new), dev(b.v_new), dev(b.block_tables),
-                            dev(b.seq_lens), b.max_seq_len, b.scale)
+    kA, vA, ksA, vsA = dev(b.k_pool), dev(b.v_pool), dev(b.k_scale), dev(b.v_scale)
+    kB, vB, ksB, vsB = dev(b.k_pool), dev(b.v_pool), dev(b.k_scale), dev(b.v_scale)
+    poolA, poolB = pa.KVPool(kA, vA, ksA, vsA), pa.KVPool(kB, vB, ksB, vsB)
+    q, kn, vn, bt, lens = dev(b.q), dev(b.k_new), dev(b.v_new), dev(b.block_tables), dev(b.seq_lens)
+    S = b.num_seqs
+    qsl = torch.arange(S + 1, dtype=torch.int32, device="cuda")
+    slotsA = pa.pa_slot_mapping(bt, qsl, lens, S, block_size=bs)
+    pa.kv_cache_write_quant(poolA, kn, vn, slotsA)
+    outA = pa.pa_decode(poolA, q, bt, lens, b.max_seq_len, b.scale)
+    slotsB = torch.full((S,), -7, dtype=torch.int64, device="cuda")
+    outB = pa.pa_decode_append(poolB, q, kn, vn, bt, lens, b.max_seq_len, b.scale,
+                               slot_mapping=slotsB)
+    torch.cuda.synchronize()
+    assert torch.equal(slotsA, slotsB)
+    for x, y in ((kA, kB), (vA, vB), (ksA, ksB), (vsA, vsB)):
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+    assert torch.equal(_bits(outA), _bits(outB))
+    # the oracle: its quantised write, then decode over the codes it stored
+    slots = oracle_slots(b)
+    kc, ksc = oracle.quantised_cache_write(b.k_pool.numpy(), b.k_scale.numpy(),
+                                           b.k_new.float().numpy(), slots, kv)
+    vc, vsc = oracle.quantised_cache_write(b.v_pool.numpy(), b.v_scale.numpy(),
+                                           b.v_new.float().numpy(), slots, kv)
+    assert np.array_equal(kB.cpu().numpy(), kc) and np.array_equal(vB.cpu().numpy(), vc)
+    assert np.array_equal(ksB.cpu().numpy().view(np.uint32), ksc.view(np.uint32))
+    b2 = W.PagedBatch(**{**b.__dict__, "k_pool": torch.from_numpy(kc), "v_pool": torch.from_numpy(vc),
+                         "k_scale": torch.from_numpy(ksc), "v_scale": torch.from_numpy(vsc)})
+    ref = oracle_decode_rows(b2)
+    err = max_err(outB, ref)
+    say("max err", err)
+    assert err <= TOL[kv]
 
 
 @pytest.mark.parametrize("bs", [16, 32])
