@@ -7,21 +7,25 @@
 // cached values.  Keys and values live in 16-token physical blocks found through
 // the sequence's block table.
 //
-// Work decomposition (MI355X, wave64):
-//  * one workgroup per (query row, kv head, context partition of part_blocks
-//    blocks); the GQA group of G query heads shares every K/V tile load;
-//  * 4 waves per workgroup; wave w takes blocks w, w+4, ... of the partition,
-//    double-buffering the next tile's loads in registers while it computes;
-//  * one (block, kv head) tile is 16 x head_dim contiguous elements; a
-//    wave-wide load instruction reads 64 x 16 bytes (8 bytes for 1-byte codes)
-//    contiguous, so lane l owns the same CB-byte column chunk of every token row
-//    it touches, for K and V alike;
-//  * q.k partial sums are completed with DPP adds inside each row of LPT lanes,
-//    after which every lane holds the finished scores of its own tokens for all
-//    G heads: the P.V update needs no further data exchange;
-//  * each lane keeps its own running (max, sum, acc) over the tokens it saw; the
-//    lanes' and waves' states are merged once at the end (LDS), and partitions
-//    in a second kernel (or directly to the output when there is only one).
+// Work decomposition (MI355X, wave64).  Two forms share the per-tile code:
+//  * the balanced split (pa_decode, the mixed step's one-token rows; see
+//    stream_range / stream_run below): every (sequence, kv head, 16-row tile) of
+//    the batch forms one list and each wave of a grid sized to the resident
+//    capacity streams an equal share of it, emitting a finished output for a
+//    segment it owns alone and a partial (m, l, acc) piece otherwise, merged by a
+//    second kernel;
+//  * the partitioned form (decode_partition; the mixed step's rows for fp32 and
+//    1-byte KV): one workgroup per (query row, kv head, context partition), 4
+//    waves taking blocks w, w+4, ... and merging through LDS.
+// In both, the GQA group of G query heads shares every K/V tile load; one
+// (block, kv head) tile is 16 x head_dim contiguous elements, and a wave-wide
+// load instruction reads 64 x 16 bytes (8 bytes for 1-byte codes) contiguous, so
+// lane l owns the same CB-byte column chunk of every token row it touches, for K
+// and V alike; q.k partial sums are completed with DPP adds inside each row of
+// LPT lanes, after which the lanes hold finished scores for the P.V update; each
+// lane keeps its own running (max, sum, acc), merged across lanes at the end.
+// 1-byte KV with a GQA group of 8 runs both products of a tile on MFMA instead
+// (Q8Path below).
 #pragma once
 
 #include "pa_device.h"
