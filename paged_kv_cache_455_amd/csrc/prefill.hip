@@ -7,7 +7,7 @@
 // keys 0 .. that position.
 //
 // For f16 / bf16 KV the step is two launches (after a small one that lists the
-// prefill tiles on the device):
+// prefill tiles on the device, heaviest first over the whole step):
 //  * prefill tiles: 64 * RB query rows -- (token, head) pairs of one kv head's GQA
 //    group -- against 32-key steps of the chunk's context, with the dense products
 //    on MFMA (v_mfma_f32_16x16x32_{f16,bf16}):
@@ -17,7 +17,8 @@
 //    The two QK products of a step take their 16 key rows in an interleaved order
 //    (first: keys 8(r/4) + r%4, second: the same + 4) so that each lane's 8 scores
 //    are the 8 consecutive keys its P^T operand needs; computing O^T rather than O
-//    keeps each query row's running max, sum and rescale inside one lane.
+//    keeps each query row's running max, sum and rescale inside one lane; the
+//    running sums come from the matrix cores too, as ones . P^T.
 //  * decode rows (q_len == 1): the balanced-split decode of decode_impl.h over
 //    the batch's one-token sequences (query row qsl[s]), with its piece merge.
 // Other KV types run every query row through the partitioned decode path.
