@@ -301,10 +301,11 @@ pa_status_t pa_check_copy_pairs(const pa_kv_pool_t *pool, const int32_t *src_dst
  * its step at start-up; 6.2: running eagerly instead saves that memory but adds
  * latency to every step; here a HIP graph). ----
  * pa_decode_step_graph records, on a stream of its own, the calls of one
- * decode step over fixed buffers: for float pools pa_decode_append (slot
- * mapping, the write of each sequence's new K/V row and the decode with its
- * merge, in two launches); for 1-byte pools pa_slot_mapping (block_size from
- * the pool), kv_cache_write_quant from new_dtype, then pa_decode.  Arguments
+ * decode step over fixed buffers: pa_decode_append (slot mapping, the write of
+ * each sequence's new K/V row -- quantised for 1-byte pools -- and the decode
+ * with its merge); for a 1-byte pool whose new rows are not in q_dtype,
+ * pa_slot_mapping (block_size from the pool), kv_cache_write_quant from
+ * new_dtype, then pa_decode.  Arguments
  * mean what they mean in those calls (one query row per sequence:
  * query_start_loc is 0, 1, .., num_seqs; slot_mapping int64 [num_seqs] is the
  * step's scratch for the slots) and are validated at capture; nothing runs

@@ -696,7 +696,7 @@ pa_status_t pa_decode_step_graph(const pa_kv_pool_t *pool, const void *q, int32_
     (void)hipStreamDestroy(cs);
     return hip_status(e, "hipStreamBeginCapture");
   }
-  if (is_quantised(pool->kv_dtype)) {
+  if (is_quantised(pool->kv_dtype) && new_dtype != q_dtype) {
     st = pa_slot_mapping(block_tables, max_blocks_per_seq, pool->block_size, query_start_loc,
                          context_lens, num_seqs, num_seqs, slot_mapping, cs);
     if (st == PA_OK)
@@ -705,7 +705,7 @@ pa_status_t pa_decode_step_graph(const pa_kv_pool_t *pool, const void *q, int32_
       st = pa_decode(pool, q, q_dtype, out, block_tables, max_blocks_per_seq, context_lens,
                      num_seqs, num_q_heads, max_context_len, scale, workspace, workspace_bytes,
                      cs);
-  } else {  // float pools: the write rides in the decode (pa_decode_append)
+  } else {  // the write rides in the decode call (pa_decode_append)
     st = pa_decode_append(pool, q, q_dtype, k_new, v_new, out, block_tables, max_blocks_per_seq,
                           context_lens, slot_mapping, num_seqs, num_q_heads, max_context_len,
                           scale, workspace, workspace_bytes, cs);
