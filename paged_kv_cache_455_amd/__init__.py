@@ -289,7 +289,8 @@ def pa_decode_append(pool: KVPool, q, k_new, v_new, block_tables, context_lens,
                      max_context_len: int, scale: float, out=None, slot_mapping=None,
                      workspace=None, stream=None):
     """Decode with the new rows' cache write fused in: equals pa_slot_mapping (row s at
-    position context_lens[s] - 1), kv_cache_write and pa_decode in that order.
+    position context_lens[s] - 1), kv_cache_write (kv_cache_write_quant for fp8/int8
+    pools, whose new rows come in q's dtype) and pa_decode in that order.
     ``slot_mapping`` (int64 [num_seqs]), when given, receives the slots."""
     lib = load_library()
     S, hq, _ = q.shape
