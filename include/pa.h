@@ -212,9 +212,10 @@ pa_status_t pa_decode(const pa_kv_pool_t *pool, const void *q, int32_t q_dtype, 
  * attend) and its query attends to all context_lens[s] tokens, the new one
  * included.  The result equals pa_slot_mapping (one row per sequence at
  * position context_lens[s] - 1), kv_cache_write and pa_decode run in that order:
- * out is bit-identical and the pools byte-identical.  The attention reads the
- * new rows from k_new / v_new, so the write needs no launch of its own; the
- * pool rows are stored within the call, after every read of the pool.
+ * out is bit-identical and the pools byte-identical.  For f32/f16/bf16 pools
+ * the attention reads the new rows from k_new / v_new, so the write needs no
+ * launch of its own (two launches); the pool rows are stored within the call,
+ * after every read of the pool.
  *   k_new, v_new  [num_seqs][num_kv_heads][head_dim], 16-byte aligned: the
  *                 pool's kv_dtype for f32/f16/bf16 pools; for fp8/int8 pools
  *                 q_dtype, quantised on write by kv_cache_write_quant's policy
