@@ -698,22 +698,29 @@ __device__ __forceinline__ void next_sequence(const DecodeArgs &a, SeqWindow &wi
 __device__ __forceinline__ bool stream_range(const DecodeArgs &a, int w, int lane, StreamRange &r) {
   const int Hkv = a.num_kv_heads, S = a.num_seqs, c = a.seg_cost;
   auto seq_cost = [&](int nb) { return nb > 0 ? Hkv * (nb + c) : 0; };
+  auto blocks = [](int n) { return n > 0 ? (n + kBlock - 1) / kBlock : 0; };
+  // The lengths of the first kHeld windows of 64 sequences are read together (one
+  // round trip, indices clamped into the batch) and kept, with their scan, for the
+  // locate pass; longer batches read the rest window by window.
+  constexpr int kHeld = 8;
+  int held_n[kHeld], held_incl[kHeld];
+#pragma unroll
+  for (int i = 0; i < kHeld; ++i) held_n[i] = decode_len(a, min(i * kWave + lane, S - 1));
   int TC = 0, mxnb = 0;
-  int n0 = 0, nb0 = 0, incl0 = 0;  // first 64 sequences, kept for the locate pass
-  for (int c0 = 0; c0 < S; c0 += kWave) {
+  auto scan_window = [&](int c0, int n) {
     const int sq = c0 + lane;
-    const int n = sq < S ? decode_len(a, sq) : 0;
-    const int nb = n > 0 ? (n + kBlock - 1) / kBlock : 0;
+    const int nb = sq < S ? blocks(n) : 0;
     mxnb = max(mxnb, nb);
-    const int incl = wave_incl_scan_i(seq_cost(nb), lane);
-    if (c0 == 0) {
-      n0 = n;
-      nb0 = nb;
-      incl0 = incl;
-    }
-    if (w == 0 && sq < S) a.hdr[1 + sq] = TC + incl - seq_cost(nb);
-    TC += __builtin_amdgcn_readlane(incl, kWave - 1);
-  }
+    const int incl = TC + wave_incl_scan_i(seq_cost(nb), lane);
+    if (w == 0 && sq < S) a.hdr[1 + sq] = incl - seq_cost(nb);
+    TC = __builtin_amdgcn_readlane(incl, kWave - 1);
+    return incl;
+  };
+#pragma unroll
+  for (int i = 0; i < kHeld; ++i)
+    if (i * kWave < S) held_incl[i] = scan_window(i * kWave, held_n[i]);
+  for (int c0 = kHeld * kWave; c0 < S; c0 += kWave)
+    scan_window(c0, c0 + lane < S ? decode_len(a, c0 + lane) : 0);
   r.tpw = max(a.min_tpw, (TC + a.num_waves - 1) / a.num_waves);
   // A segment of nblk tiles meets at most floor((nblk - 1) / tpw) + 2 waves; so
   // with tpw >= ceil(max nblk / (max_parts - 1)) its pieces fit the workspace's
@@ -727,22 +734,14 @@ __device__ __forceinline__ bool stream_range(const DecodeArgs &a, int w, int lan
   const int tend = min(t + r.tpw, TC);
   if (t >= tend) return false;
 
+  // locate the sequence holding unit t (a hit always comes: t < TC)
   int s = 0, cum_s = 0, nblk = 1, ns = 1;
-  int base = 0;
-  r.win.s0 = 0;  // (a hit always comes: t < TC)
-  r.win.ctx_l = n0;
-  for (int c0 = 0; c0 < S; c0 += kWave) {
+  bool found = false;
+  r.win.s0 = 0;
+  r.win.ctx_l = held_n[0];
+  auto try_window = [&](int c0, int n, int incl) {
     const int sq = c0 + lane;
-    int n, nb, incl;
-    if (c0 == 0) {  // already scanned
-      n = n0;
-      nb = nb0;
-      incl = incl0;
-    } else {
-      n = sq < S ? decode_len(a, sq) : 0;
-      nb = n > 0 ? (n + kBlock - 1) / kBlock : 0;
-      incl = base + wave_incl_scan_i(seq_cost(nb), lane);
-    }
+    const int nb = sq < S ? blocks(n) : 0;
     const int excl = incl - seq_cost(nb);
     const unsigned long long hit = __ballot(sq < S && nb > 0 && excl <= t && t < incl);
     if (hit) {
@@ -751,12 +750,22 @@ __device__ __forceinline__ bool stream_range(const DecodeArgs &a, int w, int lan
       cum_s = __builtin_amdgcn_readlane(excl, l);
       nblk = __builtin_amdgcn_readlane(nb, l);
       ns = __builtin_amdgcn_readlane(n, l);
-      // the window of lengths this pass already holds (no second read)
-      r.win.s0 = c0;
-      r.win.ctx_l = n;
-      break;
+      r.win.s0 = c0;  // the window of lengths in hand (no second read)
+      r.win.ctx_l = sq < S ? n : 0;
+      found = true;
     }
-    base = __builtin_amdgcn_readlane(incl, kWave - 1);
+  };
+#pragma unroll
+  for (int i = 0; i < kHeld; ++i)
+    if (!found && i * kWave < S) try_window(i * kWave, held_n[i], held_incl[i]);
+  if (!found) {
+    int base = __builtin_amdgcn_readlane(held_incl[kHeld - 1], kWave - 1);
+    for (int c0 = kHeld * kWave; c0 < S && !found; c0 += kWave) {
+      const int n = c0 + lane < S ? decode_len(a, c0 + lane) : 0;
+      const int incl = base + wave_incl_scan_i(seq_cost(c0 + lane < S ? blocks(n) : 0), lane);
+      try_window(c0, n, incl);
+      base = __builtin_amdgcn_readlane(incl, kWave - 1);
+    }
   }
   const int L = nblk + c;
   const int h = (t - cum_s) / L;
