@@ -38,7 +38,10 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=600)
+    ap.add_argument("--min-warm-ms", type=float, default=100.0,
+                    help="untimed steps continue past --warmup until this much time has "
+                         "passed: the GPU needs tens of ms of load to reach its clocks")
     ap.add_argument("--workload", default="llama3-decode",
                     choices=["llama3-decode", "tiny", "prefix-cow", "mixed", "long-fp8", "long-i8"])
     ap.add_argument("--rotate", type=int, default=4, help="pool copies cycled between steps")
@@ -247,7 +250,7 @@ def swap_bench(args):
     reps = max(1, args.steps)
 
     def timed(fn):
-        for _ in range(max(1, args.warmup)):
+        for _ in range(max(1, min(args.warmup, 10))):  # PCIe-bound: a few suffice
             fn()
         torch.cuda.synchronize()
         t0, t1 = TimingEvent(), TimingEvent()
@@ -481,9 +484,16 @@ def main():
         if ev is not None:
             ev[1].record(stream)
 
+    t_warm = time.perf_counter()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    extra_warm = 0
+    while (time.perf_counter() - t_warm) * 1e3 < args.min_warm_ms:
+        for _ in range(10):
+            step(args.warmup + extra_warm)
+            extra_warm += 1
+        torch.cuda.synchronize()
     # A step that is the timed call alone (fused decode, no copies) is bracketed once
     # around all K steps: an event record between launches still costs GPU time.
     # Otherwise each step's timed call gets its own pair.
@@ -523,6 +533,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "extra_warm_steps": extra_warm,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
