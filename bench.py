@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=600)
     ap.add_argument("--min-warm-ms", type=float, default=100.0,
                     help="untimed steps continue past --warmup until this much time has "
-                         "passed: the GPU needs tens of ms of load to reach its clocks")
+                         "passed: the first tens of ms of steps run slower")
     ap.add_argument("--workload", default="llama3-decode",
                     choices=["llama3-decode", "tiny", "prefix-cow", "mixed", "long-fp8", "long-i8"])
     ap.add_argument("--rotate", type=int, default=4, help="pool copies cycled between steps")
