@@ -289,8 +289,9 @@ def swap_bench(args):
 
 def graph_bench(args):
     """The decode step (slot mapping -> K/V write -> decode + merge) of a decode
-    workload, eager against a captured HIP graph replayed on the same buffers.
-    Both are timed with HIP events over K back-to-back steps on one stream."""
+    workload: the fused call launched directly against the captured HIP graph of
+    it replayed on the same buffers (and, for reference, the separate calls).
+    All are timed with HIP events over K back-to-back steps on one stream."""
     import torch
 
     import paged_kv_cache_455_amd as pa
@@ -311,12 +312,16 @@ def graph_bench(args):
     write = pa.kv_cache_write_quant if b.kv_dtype in ("fp8", "i8") else pa.kv_cache_write
     stream = torch.cuda.current_stream()
 
-    def eager():
+    def separate():
         pa.pa_slot_mapping(bt, qsl, lens, b.num_seqs, out=slots, block_size=b.block_size,
                            stream=stream)
         write(pool, kn, vn, slots, stream=stream)
         pa.pa_decode(pool, q, bt, lens, b.max_seq_len, b.scale, out=out, workspace=ws,
                      stream=stream)
+
+    def eager():  # the calls the graph holds (pa_decode_append), launched directly
+        pa.pa_decode_append(pool, q, kn, vn, bt, lens, b.max_seq_len, b.scale, out=out,
+                            slot_mapping=slots, workspace=ws, stream=stream)
 
     g = pa.DecodeStepGraph(pool, q, kn, vn, bt, lens, b.max_seq_len, b.scale)
 
@@ -332,6 +337,7 @@ def graph_bench(args):
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / args.steps * 1e3
 
+    us_separate = timed(separate)
     us_eager = timed(eager)
     us_graph = timed(lambda: g.replay(stream=stream))
     torch.cuda.synchronize()
@@ -344,6 +350,7 @@ def graph_bench(args):
         "data": "synthetic",
         "config": {"workload": b.name, "block_size": b.block_size, "num_seqs": b.num_seqs},
         "eager_us_per_step": round(us_eager, 2), "graph_us_per_step": round(us_graph, 2),
+        "separate_calls_us_per_step": round(us_separate, 2),
         "speedup": round(us_eager / us_graph, 3), "outputs_equal": same,
     }), flush=True)
 
