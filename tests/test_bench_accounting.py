@@ -79,3 +79,14 @@ def test_side_bytes_count_writes_and_copies():
               + 2 * 2 * int(b.copy_pairs.shape[0]) * b.num_kv_heads * b.block_size * b.head_dim * e)
     assert bench.side_bytes(b) == expect
     assert np.all(b.copy_pairs.numpy() >= 0)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
