@@ -109,15 +109,16 @@ def test_fused_llama_decode_layer(bs):
     assert err <= TOL["f16"]
 
 
-@pytest.mark.parametrize("kv,qd,hq,bs", [("fp8", "bf16", 64, 16), ("i8", "f16", 32, 32),
-                                         ("fp8", "f16", 16, 32), ("i8", "bf16", 64, 16)])
-def test_fused_quantised_equals_separate_and_oracle(kv, qd, hq, bs):
+@pytest.mark.parametrize("kv,qd,hq,bs,d", [("fp8", "bf16", 64, 16, 128), ("i8", "f16", 32, 32, 128),
+                                           ("fp8", "f16", 16, 32, 128), ("i8", "bf16", 64, 16, 128),
+                                           ("fp8", "bf16", 32, 16, 64), ("i8", "f16", 8, 32, 64)])
+def test_fused_quantised_equals_separate_and_oracle(kv, qd, hq, bs, d):
     """1-byte pools: the new rows (in q's dtype) are quantised on write with the slots
     taken from the tables; codes, scales, slots and output must equal
     pa_slot_mapping + kv_cache_write_quant + pa_decode bit for bit."""
     ctx = [1, 2, 15, 16, 17, 33, 100, 511, 1000, 1500]
-    b = W.decode_batch(91, ctx, hq, 8, 128, kv, qd, name=f"append-{kv}", block_size=bs)
-    say(b.name, qd, "block", bs)
+    b = W.decode_batch(91, ctx, hq, 8, d, kv, qd, name=f"append-{kv}", block_size=bs)
+    say(b.name, qd, "block", bs, "head_dim", d)
     dev = lambda t: t.clone().cuda()
     kA, vA, ksA, vsA = dev(b.k_pool), dev(b.v_pool), dev(b.k_scale), dev(b.v_scale)
     kB, vB, ksB, vsB = dev(b.k_pool), dev(b.v_pool), dev(b.k_scale), dev(b.v_scale)
