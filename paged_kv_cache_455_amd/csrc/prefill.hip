@@ -12,8 +12,10 @@
 //    group -- against 32-key steps of the chunk's context, with the dense products
 //    on MFMA (v_mfma_f32_16x16x32_{f16,bf16}):
 //      S^T = K . Q^T   (A = 16 keys x 32 dims from LDS, B = q rows in registers)
-//      O^T += V^T . P^T (A = 16 dims x 32 keys of the transposed V tile in LDS,
-//                        B = the probabilities straight from S^T's registers)
+//      O^T += V^T . P^T (A = 16 dims x 32 keys of V: V sits in LDS row-major like
+//                        K, and gfx950's transposed 16-bit LDS read hands each lane
+//                        the key-consecutive values of one dim; B = the
+//                        probabilities straight from S^T's registers)
 //    The two QK products of a step take their 16 key rows in an interleaved order
 //    (first: keys 8(r/4) + r%4, second: the same + 4) so that each lane's 8 scores
 //    are the 8 consecutive keys its P^T operand needs; computing O^T rather than O
@@ -38,7 +40,6 @@ typedef float f4_t __attribute__((ext_vector_type(4)));
 constexpr int kRowBlocks = PA_PREFILL_RB;       // 16-row MFMA blocks per wave
 constexpr int kTileRows = 4 * 16 * kRowBlocks;  // query rows (token, head) per prefill workgroup
 constexpr int kKeyStep = 32;    // keys per step (two blocks)
-constexpr int kVtStride = 40;   // halves per transposed-V row: 32 keys + 8 pad (80 bytes)
 constexpr int kItemBits = 12;   // item = (sequence << 12) | tile or partition index
 #ifndef PA_PREFILL_STAGES
 #define PA_PREFILL_STAGES 3
@@ -51,8 +52,8 @@ int mixed_tile_rows() { return kTileRows; }
 template <int D>
 struct PrefillLds {
   static constexpr int kKHalves = kKeyStep * D;     // K: [32 keys][D], chunks swizzled
-  static constexpr int kVtHalves = D * kVtStride;   // V^T: [D][32 keys + pad], groups swizzled
-  static constexpr int kBufHalves = kKHalves + kVtHalves;
+  static constexpr int kVHalves = kKeyStep * D;     // V: [32 keys][D], chunks swizzled
+  static constexpr int kBufHalves = kKHalves + kVHalves;
   static constexpr int kBytes = 2 * kBufHalves * 2;  // two K/V buffers
 };
 
@@ -86,6 +87,31 @@ __device__ __forceinline__ u32x4 pack8(const float *p) {
   return r;
 }
 
+// gfx950's transposed LDS read of 16-bit values (ds_read_b64_tr_b16).  Each lane
+// names 8 bytes; inside each 16-lane group, lane i receives element i % 4 of the
+// reads of lanes 4e + i / 4 (e = 0 .. 3).  So when those lanes read 4 rows of a
+// row-major tile, 4 lanes per row side by side over 16 columns, lane i gets
+// column i of the 4 rows.
+typedef short s4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const _Float16 *p) {
+  return __builtin_bit_cast(
+      u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4_t *)p));
+}
+
+// XOR swizzle of a V row's 16-byte chunks (an even value below D/8).  A
+// transposed V operand read touches keys 8g + r (g = 0..3, r = 0..3; +4 for its
+// second half) at the same two chunks of every row; the swizzle puts each half
+// wave's 8 rows on 8 disjoint 32-byte bank ranges (and each 16-lane group's 4 rows
+// on 4), with 32 or 64 four-byte banks.  Row writes stay a permutation of chunks.
+template <int D>
+__device__ __forceinline__ int v_swizzle(int key) {
+  static_assert(D == 64 || D == 128, "prefill tiles take head_dim 64 or 128");
+  if constexpr (D == 128)
+    return 2 * ((key & 3) | (((key >> 3) & 1) << 2));
+  else
+    return 2 * ((((key >> 1) & 1) | (((key >> 3) & 1) << 1)) ^ ((key & 1) << 1));
+}
+
 // One prefill tile: query tokens [qt*QTOK, ...) of sequence s, kv head h.
 // Rows: wave w, row block rb, lane column c16 -> row (w*RB + rb)*16 + c16 = token*G + head.
 // Pipeline, per 32-key step n (NS = kStages): the two block-table entries of step
@@ -102,9 +128,7 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
   constexpr int NKK = D / 32;        // QK MFMAs along head_dim
   constexpr int NSL = D / 16;        // 16-dim output slices
   constexpr int CPR = D / 8;         // 16-byte chunks per key row
-  constexpr int NCH = kKeyStep * CPR / 256;  // K chunks per thread per step
-  constexpr int NVB = (kKeyStep / 4) * (D / 4);  // V blocks of 4 keys x 4 dims per step
-  static_assert(NVB <= 256, "one V block per thread");
+  constexpr int NCH = kKeyStep * CPR / 256;  // K (and V) chunks per thread per step
   using L = PrefillLds<D>;
   _Float16 *lds = reinterpret_cast<_Float16 *>(smem);
   const DecodeArgs &d = a.dec;
@@ -176,19 +200,15 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
     r.u1 = tile_index(bt[j1 >> sh], Hkv, h, j1, sh);
     return r;
   };
-  // byte offset of key row `key` (0..31 within the step) in its 16-row tile
-  // K: chunk q of the step = key q / CPR, 16-byte column q % CPR.
-  // V: thread tid < NVB owns dims 4*(tid % (D/4)) .. +3 of keys 4*(tid / (D/4)) .. +3
+  // K and V alike: chunk q of the step = key q / CPR, 16-byte column q % CPR
   // (a wave's loads of one key row are contiguous).
   struct Stage {
-    u32x4 k[NCH];
-    u32x2 v[4];
+    u32x4 k[NCH], v[NCH];
   };
-  const int vdg = tid % (D / 4), vkg = tid / (D / 4);
-  // Which of the step's two 16-row tiles a thread's K chunk or V rows sit in is the
-  // same for the whole wave (2*D key-row chunks per tile is a multiple of 64 lanes,
-  // and so are the D/4 threads per 4 V rows), so it is chosen on the scalar unit
-  // from the wave's first thread; the thread's offset inside the tile is fixed.
+  // Which of the step's two 16-row tiles a thread's chunk sits in is the same for
+  // the whole wave (2*D key-row chunks per tile is a multiple of 64 lanes), so it is
+  // chosen on the scalar unit from the wave's first thread; the thread's offset
+  // inside the tile is fixed.
   const int wtid = __builtin_amdgcn_readfirstlane(tid);
   uint32_t k_off[NCH];
   bool k_hi[NCH];
@@ -198,56 +218,28 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
     k_off[c] = (uint32_t)(((q / CPR) % kBlock) * D * 2 + (q % CPR) * 16);
     k_hi[c] = (wtid + 256 * c) / CPR >= kBlock;
   }
-  const uint32_t v_off = (uint32_t)((((4 * vkg) % kKeyStep) % kBlock) * D * 2 + vdg * 8);
-  const bool v_hi = ((4 * (wtid / (D / 4))) % kKeyStep) >= kBlock;
   auto gload = [&](const StepBt &b, Stage &st) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const char *tb = kpool + (k_hi[c] ? b.u1 : b.u0) * (int64_t)(kBlock * D * 2);
-      st.k[c] = *reinterpret_cast<const u32x4 *>(tb + k_off[c]);
+      const int64_t tile = (k_hi[c] ? b.u1 : b.u0) * (int64_t)(kBlock * D * 2);
+      st.k[c] = *reinterpret_cast<const u32x4 *>(kpool + tile + k_off[c]);
+      st.v[c] = *reinterpret_cast<const u32x4 *>(vpool + tile + k_off[c]);
     }
-    // (threads past NVB, for head_dim 64, load rows of the step's second block too;
-    // lstore ignores them)
-    const char *vb = vpool + (v_hi ? b.u1 : b.u0) * (int64_t)(kBlock * D * 2) + v_off;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) st.v[r] = *reinterpret_cast<const u32x2 *>(vb + r * D * 2);
   };
-  // V^T rows hold the 32 keys in 4 groups of 8; group gk of dim row d sits at
-  // position gk ^ ((d / 8) & 3) so that the operand reads spread over banks.  A
-  // thread's 4 x 4 block is transposed in registers (16-bit halves picked by byte
-  // permutes) and written as four 8-byte rows.
-  // Keys at or past nkeys (the tile's reach; they may hold anything, NaN included)
-  // are zeroed on the way in.
+  // Both go to LDS as 16-byte chunks, row-major, swizzled so that the operand reads
+  // spread over the banks (K by key % CPR, V by v_swizzle).  Keys at or past nkeys
+  // (the tile's reach; they may hold anything, NaN included) are zeroed on the way in.
   auto lstore_impl = [&](int buf, int kb, const Stage &st, auto masked) {
     _Float16 *K = lds + buf * L::kBufHalves;
-    _Float16 *Vt = K + L::kKHalves;
+    _Float16 *V = K + L::kKHalves;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int q = tid + 256 * c;
       const int key = q / CPR, cc = q % CPR;
-      const int pc = cc ^ (key & (CPR - 1));  // swizzle: rows hit different banks
       const bool ok = !masked.value || kb + key < nkeys;
-      *reinterpret_cast<u32x4 *>(K + key * D + pc * 8) = ok ? st.k[c] : u32x4{0, 0, 0, 0};
-    }
-    if (tid < NVB) {
-      uint32_t v[4][2];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool ok = !masked.value || kb + 4 * vkg + r < nkeys;
-        v[r][0] = ok ? st.v[r][0] : 0u;
-        v[r][1] = ok ? st.v[r][1] : 0u;
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const int w = e >> 1;
-        u32x2 col;
-        col[0] = __builtin_amdgcn_perm(v[1][w], v[0][w], sel);  // keys 0, 1
-        col[1] = __builtin_amdgcn_perm(v[3][w], v[2][w], sel);  // keys 2, 3
-        const int dim = 4 * vdg + e;
-        const int pos = (((vkg >> 1) ^ ((dim >> 3) & 3)) * 8) + (vkg & 1) * 4;
-        *reinterpret_cast<u32x2 *>(Vt + dim * kVtStride + pos) = col;
-      }
+      const u32x4 zero = u32x4{0, 0, 0, 0};
+      *reinterpret_cast<u32x4 *>(K + key * D + (cc ^ (key & (CPR - 1))) * 8) = ok ? st.k[c] : zero;
+      *reinterpret_cast<u32x4 *>(V + key * D + (cc ^ v_swizzle<D>(key)) * 8) = ok ? st.v[c] : zero;
     }
   };
   // only a step that reaches past the tile's keys needs the zeroing (a uniform branch)
@@ -260,10 +252,15 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
 
   const int key1 = 8 * (c16 >> 2) + (c16 & 3);  // key row of this lane in QK product 1
   const int key2 = key1 + 4;                      // ... in product 2
+  // V^T operand of slice sl: this lane reads dims 16 sl + vcol .. +3 of key rows
+  // vrow (keys 8 g16 .. +3 of the operand) and vrow + 4 (keys + 4 .. +7); the
+  // transposed read returns dim 16 sl + c16 of the 4 keys.  vrow + 4 shares vrow's
+  // swizzle (bit 2 of the key is not in it).
+  const int vrow = 8 * g16 + (c16 >> 2), vcol = 4 * (c16 & 3);
   auto compute = [&](int buf, int kb) {
     if (kb > wave_max_pos) return;  // every key of the step is in the future of every row
     const _Float16 *K = lds + buf * L::kBufHalves;
-    const _Float16 *Vt = K + L::kKHalves;
+    const _Float16 *V = K + L::kKHalves;
     f4_t s1[RB], s2[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -330,9 +327,10 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
     for (int rb = 0; rb < RB; ++rb) lsum[rb] = mfma32<KV>(ones, pk[rb], lsum[rb]);
 #pragma unroll
     for (int sl = 0; sl < NSL; ++sl) {
-      const int dim = sl * 16 + c16;
-      const u32x4 va = *reinterpret_cast<const u32x4 *>(
-          Vt + dim * kVtStride + ((g16 ^ ((dim >> 3) & 3)) * 8));
+      const int d0 = sl * 16 + vcol;
+      const _Float16 *vp = V + vrow * D + ((d0 >> 3) ^ v_swizzle<D>(vrow)) * 8 + (d0 & 7);
+      const u32x2 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 4 * D);
+      const u32x4 va = u32x4{lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) o[rb][sl] = mfma32<KV>(va, pk[rb], o[rb][sl]);
     }
