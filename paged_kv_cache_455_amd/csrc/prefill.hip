@@ -42,9 +42,11 @@ constexpr int kTileRows = 4 * 16 * kRowBlocks;  // query rows (token, head) per 
 constexpr int kKeyStep = 32;    // keys per step (two blocks)
 constexpr int kItemBits = 12;   // item = (sequence << 12) | tile or partition index
 #ifndef PA_PREFILL_STAGES
-#define PA_PREFILL_STAGES 3
+#define PA_PREFILL_STAGES 2
 #endif
-constexpr int kStages = PA_PREFILL_STAGES;  // key steps whose K/V loads are in flight in registers
+// key steps whose K/V loads are in flight in registers (3 would need 258 VGPRs at
+// head_dim 128: one workgroup per CU instead of two)
+constexpr int kStages = PA_PREFILL_STAGES;
 constexpr float kLazy = 8.f;    // running-max slack before a rescale (log2 units)
 
 int mixed_tile_rows() { return kTileRows; }
@@ -357,11 +359,18 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
     if (n + 1 < nsteps) lstore((n + 1) & 1, (n + 1) * kKeyStep, next);
     __syncthreads();
   };
-  for (int n0 = 0; n0 < nsteps; n0 += U) {
+  // Whole groups of U steps in an unguarded loop, then the (< U) remaining steps
+  // once.  With a per-step guard inside the loop, its header gets several entries
+  // and the compiler's wait counting, merging them, drains every load in flight
+  // before each step issues its own: the ring would be one step deep instead of NS.
+  int n0 = 0;
+  for (; n0 + U <= nsteps; n0 += U) {
 #pragma unroll
-    for (int i = 0; i < U; ++i)
-      if (n0 + i < nsteps) iter(n0 + i, st[i % NS], st[(i + 1) % NS]);
+    for (int i = 0; i < U; ++i) iter(n0 + i, st[i % NS], st[(i + 1) % NS]);
   }
+#pragma unroll
+  for (int i = 0; i < U - 1; ++i)
+    if (n0 + i < nsteps) iter(n0 + i, st[i % NS], st[(i + 1) % NS]);
 
   // ---- normalise and store: lane holds dims sl*16 + 4*g16 + i of query row c16 ----
 #pragma unroll
