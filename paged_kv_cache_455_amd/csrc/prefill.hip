@@ -100,6 +100,20 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const _Float16 *p) {
       u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4_t *)p));
 }
 
+// XOR swizzle of a K row's 16-byte chunks (a value below D/8).  A K operand read
+// takes, in each 16-lane group, the same chunk of keys 8(c/4) + c%4 (c = 0..15;
+// +4 for the second product); the swizzle gives those 16 rows distinct bank ranges
+// per 16 lanes, and per 8, with 64 or 32 four-byte banks (key % (D/8), its simpler
+// form, left keys k and k + 16 on one range).  Row writes stay a permutation.
+template <int D>
+__device__ __forceinline__ int k_swizzle(int key) {
+  static_assert(D == 64 || D == 128, "prefill tiles take head_dim 64 or 128");
+  if constexpr (D == 128)
+    return (key & 3) | (((key >> 3) & 3) << 2);
+  else
+    return ((key >> 1) & 1) | (((key >> 3) & 1) << 1) | (((key & 1) ^ ((key >> 4) & 1)) << 2);
+}
+
 // XOR swizzle of a V row's 16-byte chunks (an even value below D/8).  A
 // transposed V operand read touches keys 8g + r (g = 0..3, r = 0..3; +4 for its
 // second half) at the same two chunks of every row; the swizzle puts each half
@@ -229,7 +243,7 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
     }
   };
   // Both go to LDS as 16-byte chunks, row-major, swizzled so that the operand reads
-  // spread over the banks (K by key % CPR, V by v_swizzle).  Keys at or past nkeys
+  // spread over the banks (K by k_swizzle, V by v_swizzle).  Keys at or past nkeys
   // (the tile's reach; they may hold anything, NaN included) are zeroed on the way in.
   auto lstore_impl = [&](int buf, int kb, const Stage &st, auto masked) {
     _Float16 *K = lds + buf * L::kBufHalves;
@@ -240,7 +254,7 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
       const int key = q / CPR, cc = q % CPR;
       const bool ok = !masked.value || kb + key < nkeys;
       const u32x4 zero = u32x4{0, 0, 0, 0};
-      *reinterpret_cast<u32x4 *>(K + key * D + (cc ^ (key & (CPR - 1))) * 8) = ok ? st.k[c] : zero;
+      *reinterpret_cast<u32x4 *>(K + key * D + (cc ^ k_swizzle<D>(key)) * 8) = ok ? st.k[c] : zero;
       *reinterpret_cast<u32x4 *>(V + key * D + (cc ^ v_swizzle<D>(key)) * 8) = ok ? st.v[c] : zero;
     }
   };
@@ -272,8 +286,8 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const int cc = 4 * kk + g16;
-      const u32x4 a1 = *reinterpret_cast<const u32x4 *>(K + key1 * D + ((cc ^ (key1 & (CPR - 1))) * 8));
-      const u32x4 a2 = *reinterpret_cast<const u32x4 *>(K + key2 * D + ((cc ^ (key2 & (CPR - 1))) * 8));
+      const u32x4 a1 = *reinterpret_cast<const u32x4 *>(K + key1 * D + ((cc ^ k_swizzle<D>(key1)) * 8));
+      const u32x4 a2 = *reinterpret_cast<const u32x4 *>(K + key2 * D + ((cc ^ k_swizzle<D>(key2)) * 8));
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         s1[rb] = mfma32<KV>(a1, qop[rb][kk], s1[rb]);
