@@ -195,7 +195,9 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
  *   context_lens int32 [num_seqs], >= 1: cached tokens including this step's
  *                token, whose K/V must already be written
  *   max_context_len  host upper bound of context_lens (sizes the split)
- *   scale        softmax scale applied to q.k (1/sqrt(head_dim) usually)
+ *   scale        softmax scale applied to q.k (1/sqrt(head_dim) usually); it
+ *                must be positive and finite (PA_E_ARG otherwise), here and in
+ *                pa_decode_append and pa_prefill_chunk
  * dtypes: kv f32/f16/bf16 need q_dtype == kv_dtype; fp8/int8 KV take f16 or
  * bf16 queries.  num_q_heads / num_kv_heads must be 1, 2, 4 or 8.
  */
@@ -239,7 +241,8 @@ pa_status_t pa_decode_append(const pa_kv_pool_t *pool, const void *q, int32_t q_
                              hipStream_t stream);
 
 /* Workspace bytes pa_prefill_chunk needs for these sizes and KV storage type
- * (0 for invalid sizes). */
+ * (0 for invalid sizes, including a GQA group num_q_heads / num_kv_heads other
+ * than 1, 2, 4 or 8). */
 size_t pa_prefill_workspace_size(int32_t num_seqs, int32_t num_q_tokens, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim, int32_t max_query_len,
                                  int32_t max_seq_len, int32_t kv_dtype);

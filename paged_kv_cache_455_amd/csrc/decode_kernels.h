@@ -3,8 +3,6 @@
 // kernel instantiations compile in parallel translation units.
 #pragma once
 
-#include <stdlib.h>
-
 #include "decode_impl.h"
 
 namespace pa {
@@ -56,12 +54,8 @@ static int resident_groups() {
 template <int KV, int QT, int D, int G, bool NT>
 static hipError_t launch_stream_kg(DecodeArgs a, int num_seqs, hipStream_t st) {
   auto kern = stream_kernel<KV, QT, D, G, NT>();
-  static const int oversub = [] {
-    const char *v = getenv("PA_STREAM_OVERSUB");
-    const int x = v ? atoi(v) : 0;
-    return x > 0 ? x : 1;
-  }();
-  const int groups = resident_groups<KV, QT, D, G, NT>() * oversub;
+  // one workgroup per resident slot: every wave streams one equal share of the work
+  const int groups = resident_groups<KV, QT, D, G, NT>();
   if (groups <= 0) return hipErrorInvalidDeviceFunction;
   a.num_waves = groups * kDecodeWaves;
   hipLaunchKernelGGL(kern, dim3(groups), dim3(kDecodeWaves * kWave), 0, st, a);

@@ -20,7 +20,9 @@
 //    (first: keys 8(r/4) + r%4, second: the same + 4) so that each lane's 8 scores
 //    are the 8 consecutive keys its P^T operand needs; computing O^T rather than O
 //    keeps each query row's running max, sum and rescale inside one lane; the
-//    running sums come from the matrix cores too, as ones . P^T.
+//    running sums come from the matrix cores too, as ones . P^T.  P enters both
+//    products as two 16-bit parts, hi + lo (split8), so the weights are not
+//    rounded to the 16-bit type.
 //  * decode rows (q_len == 1): the balanced-split decode of decode_impl.h over
 //    the batch's one-token sequences (query row qsl[s]), with its piece merge.
 // Other KV types run every query row through the partitioned decode path.
@@ -34,19 +36,13 @@ typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 
-#ifndef PA_PREFILL_RB
-#define PA_PREFILL_RB 2
-#endif
-constexpr int kRowBlocks = PA_PREFILL_RB;       // 16-row MFMA blocks per wave
+constexpr int kRowBlocks = 2;                   // 16-row MFMA blocks per wave
 constexpr int kTileRows = 4 * 16 * kRowBlocks;  // query rows (token, head) per prefill workgroup
 constexpr int kKeyStep = 32;    // keys per step (two blocks)
 constexpr int kItemBits = 12;   // item = (sequence << 12) | tile or partition index
-#ifndef PA_PREFILL_STAGES
-#define PA_PREFILL_STAGES 2
-#endif
-// key steps whose K/V loads are in flight in registers (3 would need 258 VGPRs at
-// head_dim 128: one workgroup per CU instead of two)
-constexpr int kStages = PA_PREFILL_STAGES;
+// key steps whose K/V loads are in flight in registers (3 would need more than 256
+// VGPRs at head_dim 128: one workgroup per CU instead of two)
+constexpr int kStages = 2;
 constexpr float kLazy = 8.f;    // running-max slack before a rescale (log2 units)
 
 int mixed_tile_rows() { return kTileRows; }
@@ -73,20 +69,35 @@ typedef float f2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h2v_t __attribute__((ext_vector_type(2)));
 typedef __bf16 b2v_t __attribute__((ext_vector_type(2)));
 
-// Round 8 floats to the MFMA input type and pack them (nearest even; one packed
-// convert per pair on gfx950, v_cvt_pk_{f16,bf16}_f32).
+// Split 8 probabilities into two 16-bit parts each, p ~= hi + lo, packed as MFMA
+// operands.  One 16-bit rounding of p (up to 2^-8 relative for bf16, 2^-11 for f16)
+// would perturb each weight of the softmax average by that much, which rows that see
+// a few keys do not average out; with the remainder carried in lo the pair holds p
+// to 2^-15 relative (bf16) or 2^-22 (f16), and both products, O^T += V^T . hi^T +
+// V^T . lo^T and the row sums, see the same pair.
+//  f16:  hi = p rounded to nearest even; lo = (p - hi) rounded (the difference is
+//        exact in fp32)
+//  bf16: hi = p truncated to its upper 16 bits (a byte permute of two values); lo =
+//        (p - hi) rounded to nearest even, the difference exact in fp32
 template <int KV>
-__device__ __forceinline__ u32x4 pack8(const float *p) {
-  u32x4 r;
+__device__ __forceinline__ void split8(const float *p, u32x4 &hi, u32x4 &lo) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const f2_t v = f2_t{p[2 * i], p[2 * i + 1]};
-    if constexpr (KV == PA_F16)
-      r[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2v_t));
-    else
-      r[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2v_t));
+    const float a = p[2 * i], b = p[2 * i + 1];
+    if constexpr (KV == PA_F16) {
+      const h2v_t h = __builtin_convertvector(f2_t{a, b}, h2v_t);
+      const float ra = __builtin_fmaf((float)h[0], -1.f, a);
+      const float rb = __builtin_fmaf((float)h[1], -1.f, b);
+      hi[i] = __builtin_bit_cast(uint32_t, h);
+      lo[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{ra, rb}, h2v_t));
+    } else {
+      const uint32_t ua = __builtin_bit_cast(uint32_t, a), ub = __builtin_bit_cast(uint32_t, b);
+      hi[i] = __builtin_amdgcn_perm(ub, ua, 0x07060302u);  // upper halves of a (low), b (high)
+      const float ra = a - __builtin_bit_cast(float, ua & 0xFFFF0000u);
+      const float rb = b - __builtin_bit_cast(float, ub & 0xFFFF0000u);
+      lo[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{ra, rb}, b2v_t));
+    }
   }
-  return r;
 }
 
 // gfx950's transposed LDS read of 16-bit values (ds_read_b64_tr_b16).  Each lane
@@ -187,8 +198,8 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
   }
 
   // o: O^T slices; lsum: the running softmax denominators, accumulated on the matrix
-  // cores as ones(16 x 32) . P^T, so every element holds its query row's sum of the
-  // (rounded) probabilities the P.V product used
+  // cores as ones(16 x 32) . (hi + lo)^T, so every element holds its query row's sum
+  // of the probabilities as the P.V product used them
   f4_t o[RB][NSL], lsum[RB];
   float m[RB];
 #pragma unroll
@@ -296,7 +307,7 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
     }
     const bool need_mask = kb + kKeyStep - 1 > wave_min_pos;
     const float c = d.qk_scale;  // softmax scale * log2(e); m is kept in these units
-    u32x4 pk[RB];
+    u32x4 pk[RB], pl[RB];  // P^T operands: hi and lo parts
     bool rescale = false;
     float alpha[RB];
 #pragma unroll
@@ -329,7 +340,7 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
       float p[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) p[j] = fast_exp2(__builtin_fmaf(sc[j], c, -mn));
-      pk[rb] = pack8<KV>(p);
+      split8<KV>(p, pk[rb], pl[rb]);
     }
     if (__any(rescale)) {
 #pragma unroll
@@ -340,7 +351,10 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
       }
     }
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) lsum[rb] = mfma32<KV>(ones, pk[rb], lsum[rb]);
+    for (int rb = 0; rb < RB; ++rb) {
+      lsum[rb] = mfma32<KV>(ones, pk[rb], lsum[rb]);
+      lsum[rb] = mfma32<KV>(ones, pl[rb], lsum[rb]);
+    }
 #pragma unroll
     for (int sl = 0; sl < NSL; ++sl) {
       const int d0 = sl * 16 + vcol;
@@ -349,6 +363,8 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
       const u32x4 va = u32x4{lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) o[rb][sl] = mfma32<KV>(va, pk[rb], o[rb][sl]);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) o[rb][sl] = mfma32<KV>(va, pl[rb], o[rb][sl]);
     }
   };
 

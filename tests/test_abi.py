@@ -69,8 +69,10 @@ def test_decode_argument_checks(lib):
     assert decode(lib, pool(kv=pa.PA_FP8_E4M3)) == PA_E_ARG            # scales missing
     assert decode(lib, pool(kv=pa.PA_FP8_E4M3, scales=True), q_dtype=pa.PA_F32) == PA_E_UNSUPPORTED
     assert decode(lib, pool(), max_ctx=161, mbps=10) == PA_E_ARG       # > 10 blocks * 16
-    assert decode(lib, pool(), scale=float("nan")) == PA_E_ARG
-    assert b"NaN" in lib.pa_last_error()
+    # the softmax scale must be positive and finite
+    for bad in (float("nan"), float("inf"), 0.0, -0.1):
+        assert decode(lib, pool(), scale=bad) == PA_E_ARG
+        assert b"scale" in lib.pa_last_error()
     # a split context needs a workspace; too small is reported, nothing launched
     need = pa.pa_decode_workspace_size(4, 32, 8, 128, 4096)
     assert need > 0
@@ -137,6 +139,9 @@ def test_workspace_sizes(lib):
     assert pa.pa_prefill_workspace_size(10, 100, 32, 8, 128, 64, 4096, pa.PA_F16) > 0
     assert pa.pa_prefill_workspace_size(10, 100, 32, 8, 128, 64, 4096, pa.PA_F32) > 0
     assert pa.pa_prefill_workspace_size(10, 100, 30, 8, 128, 64, 4096, pa.PA_F16) == 0
+    # GQA groups other than 1, 2, 4, 8 (here 256 query heads over one kv head) size nothing
+    assert pa.pa_prefill_workspace_size(10, 100, 256, 1, 128, 64, 4096, pa.PA_F16) == 0
+    assert pa.pa_prefill_workspace_size(10, 100, 48, 4, 128, 64, 4096, pa.PA_BF16) == 0
 
 
 def test_write_copy_slot_checks(lib):
@@ -173,3 +178,6 @@ def test_prefill_argument_checks(lib):
     assert f(mql=200) == PA_E_ARG          # longer than max_seq_len
     assert f(qd=pa.PA_F32) == PA_E_UNSUPPORTED
     assert f(msl=4096, mbps=256) == PA_E_WORKSPACE
+    g = lambda sc: lib.pa_prefill_chunk(ctypes.byref(p), FAKE, pa.PA_F16, FAKE, FAKE, FAKE, FAKE,
+                                        10, 3, 40, 32, 20, 100, sc, None, 0, None)
+    assert g(0.0) == PA_E_ARG and g(-1.0) == PA_E_ARG and g(float("inf")) == PA_E_ARG
