@@ -240,6 +240,34 @@ pa_status_t pa_decode_append(const pa_kv_pool_t *pool, const void *q, int32_t q_
                              float scale, void *workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+/*
+ * pa_decode_append_noalloc -- pa_decode_append for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  It takes no workspace: the decode's scratch (its
+ * partial pieces, their (m, l) and the split header) lives in a static device
+ * array of pa_noalloc_scratch_bytes() bytes (64 MiB) that the library holds on
+ * every GPU it runs on until the process ends.  Arguments, results and errors
+ * are pa_decode_append's (bit-identical outputs, pools and slots), plus
+ * PA_E_WORKSPACE, with nothing enqueued, when the sizes need more scratch than
+ * that (pa_decode_workspace_size of the same sizes > pa_noalloc_scratch_bytes();
+ * e.g. 64 sequences x 32 query heads x head_dim 128 up to 4096 tokens need 35 MB).
+ * The call allocates nothing and calls no allocating routine.  Every call on one
+ * GPU shares that GPU's array, which keeps the last call's contents (nothing in
+ * it needs to start at zero): calls that overlap on one GPU (other streams,
+ * other threads) race and give undefined results; serialise them.  The first
+ * call on each device looks up the array's device address
+ * (hipGetSymbolAddress) with that device current.
+ */
+pa_status_t pa_decode_append_noalloc(const pa_kv_pool_t *pool, const void *q, int32_t q_dtype,
+                                     const void *k_new, const void *v_new, void *out,
+                                     const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t *context_lens, int64_t *slot_mapping,
+                                     int32_t num_seqs, int32_t num_q_heads,
+                                     int32_t max_context_len, float scale, hipStream_t stream);
+
+/* Bytes of the static scratch pa_decode_append_noalloc uses (a host constant). */
+size_t pa_noalloc_scratch_bytes(void);
+
 /* Workspace bytes pa_prefill_chunk needs for these sizes and KV storage type
  * (0 for invalid sizes, including a GQA group num_q_heads / num_kv_heads other
  * than 1, 2, 4 or 8). */

@@ -78,6 +78,11 @@ _SIGS = {
                                     _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int32,
                                     _c.c_void_p, _c.c_void_p, _c.c_int32, _c.c_int32, _c.c_int32,
                                     _c.c_float, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "pa_decode_append_noalloc": (_c.c_int, [_c.POINTER(_Pool), _c.c_void_p, _c.c_int32,
+                                            _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                            _c.c_int32, _c.c_void_p, _c.c_void_p, _c.c_int32,
+                                            _c.c_int32, _c.c_int32, _c.c_float, _c.c_void_p]),
+    "pa_noalloc_scratch_bytes": (_c.c_size_t, []),
     "pa_prefill_workspace_size": (_c.c_size_t, [_c.c_int32] * 8),
     "pa_check_tables": (_c.c_int, [_c.POINTER(_Pool), _c.c_void_p, _c.c_int32, _c.c_void_p,
                                    _c.c_void_p, _c.c_int32, _c.c_int32, _c.c_void_p, _c.c_void_p]),
@@ -304,6 +309,25 @@ def pa_decode_append(pool: KVPool, q, k_new, v_new, block_tables, context_lens,
         int(block_tables.shape[1]), _ptr(context_lens), _ptr(slot_mapping), int(S), int(hq),
         int(max_context_len), float(scale), _ptr(workspace), wbytes, _stream(q, stream)))
     return out
+
+
+def pa_decode_append_noalloc(pool: KVPool, q, k_new, v_new, block_tables, context_lens,
+                             max_context_len: int, scale: float, out, slot_mapping=None,
+                             stream=None):
+    """pa_decode_append with its scratch in the library's static device array: no
+    workspace argument and nothing allocated, here or in the library (``out`` must be
+    given).  Calls that overlap on one GPU share that array and race."""
+    lib = load_library()
+    S, hq, _ = q.shape
+    _check("pa_decode_append_noalloc", lib.pa_decode_append_noalloc(
+        pool.ref(), _ptr(q), _dt(q), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(block_tables),
+        int(block_tables.shape[1]), _ptr(context_lens), _ptr(slot_mapping), int(S), int(hq),
+        int(max_context_len), float(scale), _stream(q, stream)))
+    return out
+
+
+def pa_noalloc_scratch_bytes() -> int:
+    return int(load_library().pa_noalloc_scratch_bytes())
 
 
 def pa_prefill_chunk(pool: KVPool, q, query_start_loc, seq_lens, block_tables, max_query_len: int,

@@ -7,6 +7,7 @@
 #include <string.h>
 #include <float.h>
 
+#include <mutex>
 #include <new>
 
 #include "pa_launch.h"
@@ -539,6 +540,69 @@ pa_status_t pa_decode_append(const pa_kv_pool_t *pool, const void *q, int32_t q_
   return decode_call(pool, q, q_dtype, nullptr, nullptr, out, block_tables, max_blocks_per_seq,
                      context_lens, nullptr, num_seqs, num_q_heads, max_context_len, scale,
                      workspace, workspace_bytes, stream);
+}
+
+// ---- pa_decode_append_noalloc: the same call with its scratch in a static array ----
+// Device memory of fixed size that the library holds for the life of the process
+// (the code object's static data: one copy on every GPU the library runs on).  In
+// host code `scratch` names a host-side stand-in, never the device copy: its device
+// address comes from hipGetSymbolAddress, once per device with that device current,
+// and only that address is handed to kernels.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
+static pa_status_t scratch_address(void **out) {
+  static std::mutex mu;
+  static void *addr[kMaxDevices];  // device address of scratch on each device, or null
+  *out = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PA_E_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", dev,
+                kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                        "hipGetSymbolAddress(scratch)");
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return PA_OK;
+}
+
+size_t pa_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+pa_status_t pa_decode_append_noalloc(const pa_kv_pool_t *pool, const void *q, int32_t q_dtype,
+                                     const void *k_new, const void *v_new, void *out,
+                                     const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t *context_lens, int64_t *slot_mapping,
+                                     int32_t num_seqs, int32_t num_q_heads,
+                                     int32_t max_context_len, float scale, hipStream_t stream) {
+  if (num_seqs < 0) return fail(PA_E_ARG, "num_seqs must be >= 0");
+  if (num_seqs == 0) return PA_OK;
+  pa_status_t st = check_pool(pool, true);
+  if (st != PA_OK) return st;
+  if (num_q_heads <= 0 || max_context_len <= 0)
+    return fail(PA_E_ARG, "num_q_heads and max_context_len must be > 0");
+  // the decode's pieces, (m, l) and split header, as pa_decode_workspace_size counts
+  // them; nothing in that region needs to start at zero
+  const size_t need = stream_layout(num_seqs, num_q_heads, pool->head_dim, max_context_len).total;
+  if (need > kScratchBytes)
+    return fail(PA_E_WORKSPACE,
+                "pa_decode_append_noalloc: these sizes need %zu bytes of scratch, the static "
+                "scratch holds %zu (use pa_decode_append with a workspace)",
+                need, kScratchBytes);
+  void *ws = nullptr;
+  if ((st = scratch_address(&ws)) != PA_OK) return st;
+  return pa_decode_append(pool, q, q_dtype, k_new, v_new, out, block_tables, max_blocks_per_seq,
+                          context_lens, slot_mapping, num_seqs, num_q_heads, max_context_len,
+                          scale, ws, kScratchBytes, stream);
 }
 
 // Workspace of the mixed step.  f16/bf16 KV: a header int, the prefill tile list,

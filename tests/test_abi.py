@@ -92,6 +92,24 @@ def test_decode_argument_checks(lib):
     assert lib.pa_status_string(PA_E_WORKSPACE) == b"workspace too small"
 
 
+def test_noalloc_checks_before_touching_the_gpu(lib):
+    """pa_decode_append_noalloc validates on the host first: sizes whose scratch
+    exceeds the static array are refused (PA_E_WORKSPACE) with nothing enqueued."""
+    cap = lib.pa_noalloc_scratch_bytes()
+    assert cap == 64 << 20
+    f = lambda p, S=16, hq=64, ctx=32768: lib.pa_decode_append_noalloc(
+        ctypes.byref(p), FAKE, pa.PA_BF16, FAKE, FAKE, FAKE, FAKE, 2048, FAKE, None, S, hq, ctx,
+        0.1, None)
+    big = pool(kv=pa.PA_FP8_E4M3, scales=True)
+    assert pa.pa_decode_workspace_size(16, 64, 8, 128, 32768) > cap
+    assert f(big) == PA_E_WORKSPACE
+    assert b"static" in lib.pa_last_error()
+    assert f(big, S=0) == PA_OK
+    assert f(big, S=-1) == PA_E_ARG
+    assert f(pool(block=24)) == PA_E_UNSUPPORTED
+    assert f(big, ctx=0) == PA_E_ARG
+
+
 def test_decode_append_argument_checks(lib):
     f = lambda p, kn=FAKE, vn=FAKE, slots=None, S=4, ws=None, wsb=0: lib.pa_decode_append(
         ctypes.byref(p), FAKE, p.kv_dtype if p.kv_dtype < 3 else pa.PA_F16, kn, vn, FAKE, FAKE,
