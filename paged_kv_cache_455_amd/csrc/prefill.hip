@@ -20,9 +20,9 @@
 //    (first: keys 8(r/4) + r%4, second: the same + 4) so that each lane's 8 scores
 //    are the 8 consecutive keys its P^T operand needs; computing O^T rather than O
 //    keeps each query row's running max, sum and rescale inside one lane; the
-//    running sums come from the matrix cores too, as ones . P^T.  P enters both
-//    products as two 16-bit parts, hi + lo (split8), so the weights are not
-//    rounded to the 16-bit type.
+//    running sums come from the matrix cores too, as ones . P^T.  For bf16 KV, P
+//    enters both products as two 16-bit parts, hi + lo (p_operands), so the weights
+//    are not rounded to bf16's 8 bits.
 //  * decode rows (q_len == 1): the balanced-split decode of decode_impl.h over
 //    the batch's one-token sequences (query row qsl[s]), with its piece merge.
 // Other KV types run every query row through the partitioned decode path.
@@ -69,27 +69,30 @@ typedef float f2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h2v_t __attribute__((ext_vector_type(2)));
 typedef __bf16 b2v_t __attribute__((ext_vector_type(2)));
 
-// Split 8 probabilities into two 16-bit parts each, p ~= hi + lo, packed as MFMA
-// operands.  One 16-bit rounding of p (up to 2^-8 relative for bf16, 2^-11 for f16)
-// would perturb each weight of the softmax average by that much, which rows that see
-// a few keys do not average out; with the remainder carried in lo the pair holds p
-// to 2^-15 relative (bf16) or 2^-22 (f16), and both products, O^T += V^T . hi^T +
-// V^T . lo^T and the row sums, see the same pair.
-//  f16:  hi = p rounded to nearest even; lo = (p - hi) rounded (the difference is
-//        exact in fp32)
-//  bf16: hi = p truncated to its upper 16 bits (a byte permute of two values); lo =
-//        (p - hi) rounded to nearest even, the difference exact in fp32
+// P^T operands of 8 probabilities.  The P.V product and the row sums see the same
+// operands, so the output is sum(p~ v) / sum(p~) for the weights p~ as the MFMA
+// inputs hold them.
+//  f16: p rounded to nearest even (lo unused).  Each weight then carries a
+//       relative error below 2^-11, which moves the output by less than 2^-11 of
+//       the weighted spread |v - out| of the values -- the order of V's own f16
+//       storage precision, and inside the f16 tolerance (a simulation of 25.6 M
+//       outputs on unscaled N(0,1) data, few to hundreds of keys, peaked at 0.72
+//       of the bar: max(2e-3, one ulp)).
+//  bf16: one rounding would be 2^-8 relative (3x the bar on such data), so p is
+//       split into two parts, p ~= hi + lo: hi = p truncated to its upper 16 bits
+//       (a byte permute of two values), lo = (p - hi) rounded to nearest even, the
+//       difference exact in fp32; the pair holds p to 2^-15 relative and every
+//       product runs twice (hi, then lo).
 template <int KV>
-__device__ __forceinline__ void split8(const float *p, u32x4 &hi, u32x4 &lo) {
+constexpr bool kSplitP = KV == PA_BF16;
+
+template <int KV>
+__device__ __forceinline__ void p_operands(const float *p, u32x4 &hi, u32x4 &lo) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float a = p[2 * i], b = p[2 * i + 1];
-    if constexpr (KV == PA_F16) {
-      const h2v_t h = __builtin_convertvector(f2_t{a, b}, h2v_t);
-      const float ra = __builtin_fmaf((float)h[0], -1.f, a);
-      const float rb = __builtin_fmaf((float)h[1], -1.f, b);
-      hi[i] = __builtin_bit_cast(uint32_t, h);
-      lo[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{ra, rb}, h2v_t));
+    if constexpr (!kSplitP<KV>) {
+      hi[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{a, b}, h2v_t));
     } else {
       const uint32_t ua = __builtin_bit_cast(uint32_t, a), ub = __builtin_bit_cast(uint32_t, b);
       hi[i] = __builtin_amdgcn_perm(ub, ua, 0x07060302u);  // upper halves of a (low), b (high)
@@ -159,7 +162,8 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
   using L = PrefillLds<D>;
   _Float16 *lds = reinterpret_cast<_Float16 *>(smem);
   const DecodeArgs &d = a.dec;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the wave's bounds stay scalar
   const int g16 = lane >> 4, c16 = lane & 15;
   const int q0 = a.qsl[s], q_len = a.qsl[s + 1] - q0;
   const int first_pos = d.ctx[s] - q_len;
@@ -198,8 +202,8 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
   }
 
   // o: O^T slices; lsum: the running softmax denominators, accumulated on the matrix
-  // cores as ones(16 x 32) . (hi + lo)^T, so every element holds its query row's sum
-  // of the probabilities as the P.V product used them
+  // cores as ones(16 x 32) . P^T (hi and lo parts for bf16), so every element holds
+  // its query row's sum of the probabilities as the P.V product used them
   f4_t o[RB][NSL], lsum[RB];
   float m[RB];
 #pragma unroll
@@ -284,8 +288,13 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
   // transposed read returns dim 16 sl + c16 of the 4 keys.  vrow + 4 shares vrow's
   // swizzle (bit 2 of the key is not in it).
   const int vrow = 8 * g16 + (c16 >> 2), vcol = 4 * (c16 & 3);
+  // One 32-key step from LDS buffer buf (keys kb ..): S^T = K . Q^T, the online
+  // softmax, O^T += V^T . P^T.
   auto compute = [&](int buf, int kb) {
     if (kb > wave_max_pos) return;  // every key of the step is in the future of every row
+    // some key of the step lies past some row's position (the causal diagonal, or
+    // the tile's reach); uniform per wave, a scalar branch
+    const bool need_mask = kb + kKeyStep - 1 > wave_min_pos;
     const _Float16 *K = lds + buf * L::kBufHalves;
     const _Float16 *V = K + L::kKHalves;
     f4_t s1[RB], s2[RB];
@@ -305,9 +314,8 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
         s2[rb] = mfma32<KV>(a2, qop[rb][kk], s2[rb]);
       }
     }
-    const bool need_mask = kb + kKeyStep - 1 > wave_min_pos;
-    const float c = d.qk_scale;  // softmax scale * log2(e); m is kept in these units
-    u32x4 pk[RB], pl[RB];  // P^T operands: hi and lo parts
+    const float c = d.qk_scale;  // softmax scale * log2(e) (> 0); m is kept in these units
+    u32x4 pk[RB], pl[RB];  // P^T operands: p (f16), or its hi and lo parts (bf16)
     bool rescale = false;
     float alpha[RB];
 #pragma unroll
@@ -340,7 +348,7 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
       float p[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) p[j] = fast_exp2(__builtin_fmaf(sc[j], c, -mn));
-      split8<KV>(p, pk[rb], pl[rb]);
+      p_operands<KV>(p, pk[rb], pl[rb]);
     }
     if (__any(rescale)) {
 #pragma unroll
@@ -353,21 +361,28 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       lsum[rb] = mfma32<KV>(ones, pk[rb], lsum[rb]);
-      lsum[rb] = mfma32<KV>(ones, pl[rb], lsum[rb]);
+      if constexpr (kSplitP<KV>) lsum[rb] = mfma32<KV>(ones, pl[rb], lsum[rb]);
     }
-#pragma unroll
-    for (int sl = 0; sl < NSL; ++sl) {
+    // V^T operand of slice sl, read one slice ahead of the products that use it
+    auto vread = [&](int sl) {
       const int d0 = sl * 16 + vcol;
       const _Float16 *vp = V + vrow * D + ((d0 >> 3) ^ v_swizzle<D>(vrow)) * 8 + (d0 & 7);
       const u32x2 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 4 * D);
-      const u32x4 va = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    u32x4 va[2];
+    va[0] = vread(0);
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) o[rb][sl] = mfma32<KV>(va, pk[rb], o[rb][sl]);
+    for (int sl = 0; sl < NSL; ++sl) {
+      if (sl + 1 < NSL) va[(sl + 1) & 1] = vread(sl + 1);
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) o[rb][sl] = mfma32<KV>(va, pl[rb], o[rb][sl]);
+      for (int rb = 0; rb < RB; ++rb) o[rb][sl] = mfma32<KV>(va[sl & 1], pk[rb], o[rb][sl]);
+      if constexpr (kSplitP<KV>) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) o[rb][sl] = mfma32<KV>(va[sl & 1], pl[rb], o[rb][sl]);
+      }
     }
   };
-
   constexpr int NS = kStages;
   constexpr int U = NS % 2 ? 2 * NS : NS;  // unroll: stage ring and LDS buffer parity
   const int nsteps = (nkeys + kKeyStep - 1) / kKeyStep;
