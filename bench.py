@@ -355,6 +355,33 @@ def graph_bench(args):
     }), flush=True)
 
 
+STREAM_READ_BYTES = 1 << 32  # 4 GiB: far past the 256 MB Infinity Cache
+
+
+def hbm_read_reference(stream, passes=10):
+    """Achievable HBM read rate in this run: pa_stream_read (16-byte nontemporal
+    loads, grid-stride) over a 4 GiB buffer, timed with HIP events."""
+    import torch
+
+    import paged_kv_cache_455_amd as pa
+    buf = torch.empty(STREAM_READ_BYTES, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        pa.pa_stream_read(buf, sink, stream=stream)
+    torch.cuda.synchronize()
+    t0, t1 = TimingEvent(), TimingEvent()
+    t0.record(stream)
+    for _ in range(passes):
+        pa.pa_stream_read(buf, sink, stream=stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / passes
+    del buf
+    return {"GBps": round(STREAM_READ_BYTES / (ms * 1e-3) / 1e9, 1), "bytes": STREAM_READ_BYTES,
+            "passes": passes, "us_per_pass": round(ms * 1e3, 1),
+            "kernel": "pa_stream_read (one read of a 4 GiB buffer, 16-byte nontemporal loads)"}
+
+
 def cpu_baseline(b, budget_s):
     """The oracle as it stands, timed on this host over a bounded sample of the batch."""
     import numpy as np
@@ -577,9 +604,13 @@ def main():
     }
     if b.kind != "decode":
         rec["attention_tflops"] = round(flops / (attn_ms_avg * 1e-3) / 1e12, 2)
+    del pools, k0, v0
+    torch.cuda.synchronize()
+    ref = hbm_read_reference(stream)
+    rec["hbm_read_reference"] = ref
+    # the timed call's rate against the read rate measured beside it
+    rec["pct_measured_peak"] = round(100.0 * attn_gbps / ref["GBps"], 2)
     if not args.no_cpu_baseline:
-        del pools, k0, v0
-        torch.cuda.synchronize()
         rec["cpu_baseline"] = cpu_baseline(b, args.cpu_budget_s)
     print(json.dumps(rec), flush=True)
 

@@ -268,6 +268,17 @@ pa_status_t pa_decode_append_noalloc(const pa_kv_pool_t *pool, const void *q, in
 /* Bytes of the static scratch pa_decode_append_noalloc uses (a host constant). */
 size_t pa_noalloc_scratch_bytes(void);
 
+/*
+ * pa_stream_read -- a measurement reference, not part of the attention path:
+ * reads `bytes` of device memory at src once (16-byte nontemporal loads, the
+ * cache hint the decode kernels use for K/V tiles) and XORs the words into
+ * *sink (a device uint32; its old value is folded in, nothing needs zeroing),
+ * so the achievable HBM read rate can be timed beside the attention calls in
+ * the same run.  src 16-byte aligned, bytes a multiple of 16 (PA_E_ARG
+ * otherwise); bytes == 0 enqueues nothing.
+ */
+pa_status_t pa_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream);
+
 /* Workspace bytes pa_prefill_chunk needs for these sizes and KV storage type
  * (0 for invalid sizes, including a GQA group num_q_heads / num_kv_heads other
  * than 1, 2, 4 or 8). */

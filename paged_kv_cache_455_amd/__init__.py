@@ -83,6 +83,7 @@ _SIGS = {
                                             _c.c_int32, _c.c_void_p, _c.c_void_p, _c.c_int32,
                                             _c.c_int32, _c.c_int32, _c.c_float, _c.c_void_p]),
     "pa_noalloc_scratch_bytes": (_c.c_size_t, []),
+    "pa_stream_read": (_c.c_int, [_c.c_void_p, _c.c_size_t, _c.c_void_p, _c.c_void_p]),
     "pa_prefill_workspace_size": (_c.c_size_t, [_c.c_int32] * 8),
     "pa_check_tables": (_c.c_int, [_c.POINTER(_Pool), _c.c_void_p, _c.c_int32, _c.c_void_p,
                                    _c.c_void_p, _c.c_int32, _c.c_int32, _c.c_void_p, _c.c_void_p]),
@@ -141,7 +142,11 @@ def load_library() -> ctypes.CDLL:
                            "`python -m paged_kv_cache_455_amd._build`")
     lib = ctypes.CDLL(path)
     for name, (res, args) in _SIGS.items():
-        fn = getattr(lib, name)
+        # a library built from part of the sources (the sanitized host-only build)
+        # lacks some entry points: calling one of those raises AttributeError
+        fn = getattr(lib, name, None)
+        if fn is None:
+            continue
         fn.restype = res
         fn.argtypes = args
     _LIB = lib
@@ -324,6 +329,14 @@ def pa_decode_append_noalloc(pool: KVPool, q, k_new, v_new, block_tables, contex
         int(block_tables.shape[1]), _ptr(context_lens), _ptr(slot_mapping), int(S), int(hq),
         int(max_context_len), float(scale), _stream(q, stream)))
     return out
+
+
+def pa_stream_read(src, sink, stream=None):
+    """One streaming read of ``src`` (a 16-byte aligned device tensor) folded into the
+    device uint32 ``sink``: the achievable HBM read rate, timed beside the path."""
+    lib = load_library()
+    _check("pa_stream_read", lib.pa_stream_read(_ptr(src), src.numel() * src.element_size(),
+                                                _ptr(sink), _stream(src, stream)))
 
 
 def pa_noalloc_scratch_bytes() -> int:

@@ -70,5 +70,25 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+# Host modules that need no HIP runtime: they also build with g++ on their own.
+HOST_ONLY = ("status.cpp", "block_manager.cpp")
+
+
+def build_host_sanitized(out_path: str) -> str:
+    """The host-only modules (the block manager and status reporting) as a shared
+    library built by g++ with AddressSanitizer and UndefinedBehaviorSanitizer, for
+    CPU test runs of the block manager (load it with the sanitizer runtimes
+    preloaded; it exports only the pa_bm_* and status calls)."""
+    srcs = [os.path.join(CSRC, f) for f in HOST_ONLY]
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-fPIC", "-shared",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include", "-I", os.path.join(ROOT, "include"),
+           *srcs, "-o", out_path]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized host build failed:\n{r.stdout}\n{r.stderr}")
+    return out_path
+
+
 if __name__ == "__main__":
     build()

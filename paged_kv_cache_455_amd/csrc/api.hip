@@ -11,17 +11,16 @@
 #include <new>
 
 #include "pa_launch.h"
+#include "status.h"
 #include "../../include/pa.h"
 
 namespace {
-
-thread_local char g_last_error[512] = "";
 
 pa_status_t fail(pa_status_t st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 pa_status_t fail(pa_status_t st, const char *fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  pa::set_errorv(st, fmt, ap);
   va_end(ap);
   return st;
 }
@@ -151,34 +150,7 @@ int max_parts_for(int max_ctx, int part_blocks) {
 
 }  // namespace
 
-namespace pa {
-// Record a failure for pa_last_error() (used by the host-side modules).
-pa_status_t set_error(pa_status_t st, const char *fmt, ...) {
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
-  va_end(ap);
-  return st;
-}
-}  // namespace pa
-
 extern "C" {
-
-const char *pa_version(void) { return "paged_kv_cache_455_amd 0.1 (gfx950)"; }
-
-const char *pa_status_string(pa_status_t s) {
-  switch (s) {
-    case PA_OK: return "ok";
-    case PA_E_ARG: return "invalid argument";
-    case PA_E_UNSUPPORTED: return "unsupported shape or dtype";
-    case PA_E_WORKSPACE: return "workspace too small";
-    case PA_E_HIP: return "HIP error";
-    case PA_E_NO_BLOCKS: return "no free block";
-  }
-  return "unknown status";
-}
-
-const char *pa_last_error(void) { return g_last_error; }
 
 pa_status_t pa_slot_mapping(const int32_t *block_tables, int32_t max_blocks_per_seq,
                             int32_t block_size, const int32_t *query_start_loc, const int32_t *seq_lens,
@@ -540,6 +512,14 @@ pa_status_t pa_decode_append(const pa_kv_pool_t *pool, const void *q, int32_t q_
   return decode_call(pool, q, q_dtype, nullptr, nullptr, out, block_tables, max_blocks_per_seq,
                      context_lens, nullptr, num_seqs, num_q_heads, max_context_len, scale,
                      workspace, workspace_bytes, stream);
+}
+
+pa_status_t pa_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream) {
+  if (bytes == 0) return PA_OK;
+  if (!src || !sink) return fail(PA_E_ARG, "NULL src or sink");
+  if (((uintptr_t)src & 15) || (bytes & 15))
+    return fail(PA_E_ARG, "src must be 16-byte aligned and bytes a multiple of 16");
+  return hip_status(pa::launch_stream_read(src, bytes, sink, stream), "pa_stream_read launch");
 }
 
 // ---- pa_decode_append_noalloc: the same call with its scratch in a static array ----

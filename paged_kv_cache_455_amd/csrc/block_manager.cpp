@@ -45,7 +45,7 @@
 #include <vector>
 
 #include "../../include/pa.h"
-#include "pa_launch.h"
+#include "status.h"
 
 namespace {
 

@@ -136,12 +136,11 @@ hipError_t launch_cache_write(const CacheWriteArgs &a, hipStream_t st);
 hipError_t launch_cache_write_quant(const CacheWriteArgs &a, int kv_dtype, int src_dtype,
                                     int head_dim, hipStream_t st);
 hipError_t launch_block_copy(const BlockCopyArgs &a, hipStream_t st);
+hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t st);
 hipError_t launch_slot_mapping(const int32_t *bt, int32_t mbps, int32_t block_size,
                                const int32_t *qsl,
                                const int32_t *seq_lens, int32_t num_seqs, int64_t *slots,
                                hipStream_t st);
 
-// Record a failure for pa_last_error(); returns st.
-pa_status_t set_error(pa_status_t st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 
 }  // namespace pa

@@ -110,6 +110,15 @@ def test_noalloc_checks_before_touching_the_gpu(lib):
     assert f(big, ctx=0) == PA_E_ARG
 
 
+def test_stream_read_argument_checks(lib):
+    sink = FAKE
+    assert lib.pa_stream_read(None, 64, sink, None) == PA_E_ARG
+    assert lib.pa_stream_read(FAKE, 64, None, None) == PA_E_ARG
+    assert lib.pa_stream_read(FAKE + 4, 64, sink, None) == PA_E_ARG   # misaligned
+    assert lib.pa_stream_read(FAKE, 60, sink, None) == PA_E_ARG       # not whole chunks
+    assert lib.pa_stream_read(FAKE, 0, sink, None) == PA_OK
+
+
 def test_decode_append_argument_checks(lib):
     f = lambda p, kn=FAKE, vn=FAKE, slots=None, S=4, ws=None, wsb=0: lib.pa_decode_append(
         ctypes.byref(p), FAKE, p.kv_dtype if p.kv_dtype < 3 else pa.PA_F16, kn, vn, FAKE, FAKE,
