@@ -40,9 +40,6 @@ constexpr int kRowBlocks = 2;                   // 16-row MFMA blocks per wave
 constexpr int kTileRows = 4 * 16 * kRowBlocks;  // query rows (token, head) per prefill workgroup
 constexpr int kKeyStep = 32;    // keys per step (two blocks)
 constexpr int kItemBits = 12;   // item = (sequence << 12) | tile or partition index
-// key steps whose K/V loads are in flight in registers (3 would need more than 256
-// VGPRs at head_dim 128: one workgroup per CU instead of two)
-constexpr int kStages = 2;
 constexpr float kLazy = 8.f;    // running-max slack before a rescale (log2 units)
 
 int mixed_tile_rows() { return kTileRows; }
@@ -52,7 +49,10 @@ struct PrefillLds {
   static constexpr int kKHalves = kKeyStep * D;     // K: [32 keys][D], chunks swizzled
   static constexpr int kVHalves = kKeyStep * D;     // V: [32 keys][D], chunks swizzled
   static constexpr int kBufHalves = kKHalves + kVHalves;
-  static constexpr int kBytes = 2 * kBufHalves * 2;  // two K/V buffers
+  // four K/V buffers: a step's loads are issued two iterations ahead, and its V is
+  // still read (by the deferred P.V) one iteration after its scores
+  static constexpr int kBufs = 4;
+  static constexpr int kBytes = kBufs * kBufHalves * 2;
 };
 
 template <int KV>
@@ -144,12 +144,13 @@ __device__ __forceinline__ int v_swizzle(int key) {
 
 // One prefill tile: query tokens [qt*QTOK, ...) of sequence s, kv head h.
 // Rows: wave w, row block rb, lane column c16 -> row (w*RB + rb)*16 + c16 = token*G + head.
-// Pipeline, per 32-key step n (NS = kStages): the two block-table entries of step
-// n+NS+1 are read, K/V of step n+NS are loaded into registers, step n is computed
-// from LDS and step n+1 is written to the other LDS buffer.  Every load is issued unconditionally
-// (indices clamped to the tile's last block, keys past its reach zeroed when they
-// reach LDS) so that the compiler's waits count loads instead of draining them.
-// Each K or V operand read from LDS serves all RB row blocks of the wave.
+// Pipeline, per 32-key step n: K/V of step n+2 go from HBM straight into the LDS
+// buffer (n+2) mod 4 (LDS-DMA, no registers), the block-table entries of step n+3
+// are read, the scores and softmax of step n run beside the P.V product of step n-1
+// (whose V still sits in buffer (n-1) mod 4), and the wave waits for its loads of
+// step n+1 before the barrier that hands them to every wave.  Every load is issued
+// unconditionally (indices clamped to the tile's last block) so the wait counts are
+// fixed.  Each K or V operand read from LDS serves all RB row blocks of the wave.
 template <int KV, int D, int G>
 __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, int qt,
                                              char *smem) {
@@ -157,8 +158,6 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
   constexpr int QTOK = kTileRows / G;
   constexpr int NKK = D / 32;        // QK MFMAs along head_dim
   constexpr int NSL = D / 16;        // 16-dim output slices
-  constexpr int CPR = D / 8;         // 16-byte chunks per key row
-  constexpr int NCH = kKeyStep * CPR / 256;  // K (and V) chunks per thread per step
   using L = PrefillLds<D>;
   _Float16 *lds = reinterpret_cast<_Float16 *>(smem);
   const DecodeArgs &d = a.dec;
@@ -175,7 +174,6 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
   // the wave's rows: tokens t0 + (wave*RB*16) / G ... ; positions bound its keys
   const int wave_tok0 = t0 + (wave * RB * 16) / G;
   const int wave_min_pos = first_pos + wave_tok0;
-  const int wave_max_pos = first_pos + min(t0 + ((wave + 1) * RB * 16 - 1) / G, q_len - 1);
 
   const int nblk = (nkeys + kBlock - 1) / kBlock;
 
@@ -216,7 +214,12 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
   constexpr uint32_t kOne2 = KV == PA_F16 ? 0x3C003C00u : 0x3F803F80u;  // two 16-bit 1.0s
   const u32x4 ones = u32x4{kOne2, kOne2, kOne2, kOne2};
 
-  // ---- global -> registers -> LDS staging of one 32-key step ----
+  // ---- global -> LDS staging of one 32-key step (LDS-DMA) ----
+  // gfx950's global_load_lds_dwordx4: each lane's 16 bytes land at m0 + 16 * lane
+  // (checked on the MI355X), so a wave-wide load fills 1 KiB of LDS -- RPW whole key
+  // rows -- with no registers in between.  A lane picks the global chunk whose
+  // swizzled position is its slot: chunk p ^ swizzle(key) of its key row (the same
+  // row, so the wave's reads stay contiguous).
   const char *kpool = reinterpret_cast<const char *>(d.k);
   const char *vpool = reinterpret_cast<const char *>(d.v);
   // 16-row tile indices of step n's two tiles (clamped to the last tile)
@@ -224,61 +227,83 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
     int64_t u0, u1;
   };
   const int sh = d.bs_shift;
+  // The table row is read through the constant address space: nothing writes it
+  // during the kernel, and these reads (uniform per wave) then stay scalar loads --
+  // the compiler would otherwise make vector loads of them after the LDS-DMA
+  // statements below, which it cannot prove write no global memory, and a wait for
+  // those would also wait for every load in flight.
+  const __attribute__((address_space(4))) int32_t *btc =
+      (const __attribute__((address_space(4))) int32_t *)(uintptr_t)bt;
   auto bt_load = [&](int n) {
     const int j0 = min(2 * n, nblk - 1), j1 = min(2 * n + 1, nblk - 1);
     StepBt r;
-    r.u0 = tile_index(bt[j0 >> sh], Hkv, h, j0, sh);
-    r.u1 = tile_index(bt[j1 >> sh], Hkv, h, j1, sh);
+    r.u0 = tile_index(btc[j0 >> sh], Hkv, h, j0, sh);
+    r.u1 = tile_index(btc[j1 >> sh], Hkv, h, j1, sh);
     return r;
   };
-  // K and V alike: chunk q of the step = key q / CPR, 16-byte column q % CPR
-  // (a wave's loads of one key row are contiguous).
-  struct Stage {
-    u32x4 k[NCH], v[NCH];
-  };
-  // Which of the step's two 16-row tiles a thread's chunk sits in is the same for
-  // the whole wave (2*D key-row chunks per tile is a multiple of 64 lanes), so it is
-  // chosen on the scalar unit from the wave's first thread; the thread's offset
-  // inside the tile is fixed.
-  const int wtid = __builtin_amdgcn_readfirstlane(tid);
-  uint32_t k_off[NCH];
-  bool k_hi[NCH];
+  constexpr int CPR = D / 8;                    // 16-byte chunks per key row
+  constexpr int RPW = 64 / CPR;                 // key rows per wave-wide load
+  constexpr int NL = kKeyStep / RPW / 4;        // wave-wide loads of K (and of V) per wave
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
+  uint32_t koff[NL], voff[NL];  // byte offset of the lane's chunk inside its 16-row tile
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const int q = tid + 256 * c;
-    k_off[c] = (uint32_t)(((q / CPR) % kBlock) * D * 2 + (q % CPR) * 16);
-    k_hi[c] = (wtid + 256 * c) / CPR >= kBlock;
+  for (int j = 0; j < NL; ++j) {
+    const int key = (wave * NL + j) * RPW + lane / CPR, p = lane % CPR;
+    koff[j] = (uint32_t)((key % kBlock) * D * 2 + (p ^ k_swizzle<D>(key)) * 16);
+    voff[j] = (uint32_t)((key % kBlock) * D * 2 + (p ^ v_swizzle<D>(key)) * 16);
   }
-  auto gload = [&](const StepBt &b, Stage &st) {
+  auto dma1 = [&](const char *gbase, uint32_t off, uint32_t lds_addr) {
+    const uint64_t g = (uint64_t)(uintptr_t)gbase;
+    const uint32_t glo = __builtin_amdgcn_readfirstlane((uint32_t)g);
+    const uint32_t ghi = __builtin_amdgcn_readfirstlane((uint32_t)(g >> 32));
+    const uint64_t gu = ((uint64_t)ghi << 32) | glo;
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
+    // No memory clobber: the compiler must keep its block-table reads scalar, which
+    // it does only while no write to global memory may precede them.  The load's
+    // LDS writes are ordered by the waits and barriers around it (both have side
+    // effects, as this statement does, so none of them is moved across another).
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0v), "v"(off),
+                 "s"(gu));
+  };
+  // the step's K and V tiles into LDS buffer bi: NL wave-wide loads of each per wave
+  auto dma_step = [&](const StepBt &b, int bi) {
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int64_t tile = (k_hi[c] ? b.u1 : b.u0) * (int64_t)(kBlock * D * 2);
-      st.k[c] = *reinterpret_cast<const u32x4 *>(kpool + tile + k_off[c]);
-      st.v[c] = *reinterpret_cast<const u32x4 *>(vpool + tile + k_off[c]);
+    for (int j = 0; j < NL; ++j) {
+      const int lw = wave * NL + j;                // this load's 1 KiB of the tile pair
+      const int64_t tile = ((lw * RPW) / kBlock ? b.u1 : b.u0) * (int64_t)(kBlock * D * 2);
+      const uint32_t at = lds_base + (uint32_t)((bi * L::kBufHalves) * 2 + lw * 1024);
+      dma1(kpool + tile, koff[j], at);
+      dma1(vpool + tile, voff[j], at + L::kKHalves * 2);
     }
   };
-  // Both go to LDS as 16-byte chunks, row-major, swizzled so that the operand reads
-  // spread over the banks (K by k_swizzle, V by v_swizzle).  Keys at or past nkeys
-  // (the tile's reach; they may hold anything, NaN included) are zeroed on the way in.
-  auto lstore_impl = [&](int buf, int kb, const Stage &st, auto masked) {
-    _Float16 *K = lds + buf * L::kBufHalves;
-    _Float16 *V = K + L::kKHalves;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int q = tid + 256 * c;
-      const int key = q / CPR, cc = q % CPR;
-      const bool ok = !masked.value || kb + key < nkeys;
-      const u32x4 zero = u32x4{0, 0, 0, 0};
-      *reinterpret_cast<u32x4 *>(K + key * D + (cc ^ k_swizzle<D>(key)) * 8) = ok ? st.k[c] : zero;
-      *reinterpret_cast<u32x4 *>(V + key * D + (cc ^ v_swizzle<D>(key)) * 8) = ok ? st.v[c] : zero;
-    }
+  // s_waitcnt vmcnt(c) (the other counters left alone): the loads this wave issued,
+  // all but the newest c, have landed in LDS.  The library code in the step loop
+  // issues no other vector-memory instruction, so the count is exact.
+  auto wait_loads = [&](auto c) {
+    constexpr int n = decltype(c)::value;
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
   };
-  // only a step that reaches past the tile's keys needs the zeroing (a uniform branch)
-  auto lstore = [&](int buf, int kb, const Stage &st) {
-    if (kb + kKeyStep <= nkeys)
-      lstore_impl(buf, kb, st, std::false_type{});
-    else
-      lstore_impl(buf, kb, st, std::true_type{});
+  // V rows of step n at or past nkeys (the tile's reach; they may hold anything, NaN
+  // included) are zeroed after this wave's own loads of them have landed: their
+  // weights are zero, and 0 * NaN would not be.  K needs no fix: those keys are
+  // masked by selection.  The store is written out with its waits (all loads, then
+  // the store itself) so that the compiler, which does not see the loads, cannot
+  // place it before them.  Only the step that reaches past nkeys takes this path.
+  auto fix_tail = [&](int n, int bi) {
+    const int kb = n * kKeyStep;
+    if (kb + kKeyStep <= nkeys) return;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int lw = wave * NL + j;
+      const int key = lw * RPW + lane / CPR;
+      const uint32_t at = lds_base + (uint32_t)((bi * L::kBufHalves + L::kKHalves) * 2 + lw * 1024 +
+                                                lane * 16);
+      const u32x4 z = u32x4{0, 0, 0, 0};
+      if (kb + key >= nkeys)
+        asm volatile("s_waitcnt vmcnt(0)\n\tds_write_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(at),
+                     "v"(z));
+    }
   };
 
   const int key1 = 8 * (c16 >> 2) + (c16 & 3);  // key row of this lane in QK product 1
@@ -288,15 +313,55 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
   // transposed read returns dim 16 sl + c16 of the 4 keys.  vrow + 4 shares vrow's
   // swizzle (bit 2 of the key is not in it).
   const int vrow = 8 * g16 + (c16 >> 2), vcol = 4 * (c16 & 3);
-  // One 32-key step from LDS buffer buf (keys kb ..): S^T = K . Q^T, the online
-  // softmax, O^T += V^T . P^T.
-  auto compute = [&](int buf, int kb) {
-    if (kb > wave_max_pos) return;  // every key of the step is in the future of every row
+  // LDS buffer of the step with index i modulo the unroll (i >= -1; i = -1 at step
+  // 0 is the zeroed V that the first step's deferred product reads); U is a multiple
+  // of kBufs, so i modulo kBufs is the step's buffer
+  auto buf_of = [&](int i) { return lds + ((i + L::kBufs) % L::kBufs) * L::kBufHalves; };
+  // P^T operands of the step whose P.V product is still to run (deferred by one
+  // step), zero before the first
+  u32x4 pp[RB], ppl[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    pp[rb] = u32x4{0, 0, 0, 0};
+    ppl[rb] = u32x4{0, 0, 0, 0};
+  }
+  // O^T += V^T . P^T and the row sums for the held P^T operands, V from buffer Vb
+  auto pv_product = [&](const _Float16 *Vb) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      lsum[rb] = mfma32<KV>(ones, pp[rb], lsum[rb]);
+      if constexpr (kSplitP<KV>) lsum[rb] = mfma32<KV>(ones, ppl[rb], lsum[rb]);
+    }
+    // V^T operand of slice sl, read one slice ahead of the products that use it
+    auto vread = [&](int sl) {
+      const int d0 = sl * 16 + vcol;
+      const _Float16 *vp = Vb + vrow * D + ((d0 >> 3) ^ v_swizzle<D>(vrow)) * 8 + (d0 & 7);
+      const u32x2 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 4 * D);
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    u32x4 va[2];
+    va[0] = vread(0);
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl) {
+      if (sl + 1 < NSL) va[(sl + 1) & 1] = vread(sl + 1);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) o[rb][sl] = mfma32<KV>(va[sl & 1], pp[rb], o[rb][sl]);
+      if constexpr (kSplitP<KV>) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) o[rb][sl] = mfma32<KV>(va[sl & 1], ppl[rb], o[rb][sl]);
+      }
+    }
+  };
+  // Step n (keys kb ..): S^T = K . Q^T and the online softmax of step n, and the
+  // P.V product of step n-1.  The two are independent, so the softmax's VALU work
+  // and the previous step's MFMAs can interleave; the rescale of the accumulators
+  // by step n's factor follows the product of step n-1 (whose P was relative to the
+  // old maximum).
+  auto full_step = [&](int i, int kb) {
     // some key of the step lies past some row's position (the causal diagonal, or
     // the tile's reach); uniform per wave, a scalar branch
     const bool need_mask = kb + kKeyStep - 1 > wave_min_pos;
-    const _Float16 *K = lds + buf * L::kBufHalves;
-    const _Float16 *V = K + L::kKHalves;
+    const _Float16 *K = buf_of(i);
     f4_t s1[RB], s2[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -314,8 +379,19 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
         s2[rb] = mfma32<KV>(a2, qop[rb][kk], s2[rb]);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);  // the score products stay ahead of the block below
+    if (need_mask) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const bool vis = kb + 8 * g16 + j <= row_pos[rb];
+          if (j < 4) s1[rb][j] = vis ? s1[rb][j] : -INFINITY;
+          else s2[rb][j - 4] = vis ? s2[rb][j - 4] : -INFINITY;
+        }
+    }
     const float c = d.qk_scale;  // softmax scale * log2(e) (> 0); m is kept in these units
-    u32x4 pk[RB], pl[RB];  // P^T operands: p (f16), or its hi and lo parts (bf16)
+    u32x4 pn[RB], pnl[RB];  // P^T operands of step n: p (f16), or its hi and lo parts (bf16)
     bool rescale = false;
     float alpha[RB];
 #pragma unroll
@@ -325,10 +401,6 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
       for (int i = 0; i < 4; ++i) {
         sc[i] = s1[rb][i];
         sc[4 + i] = s2[rb][i];
-      }
-      if (need_mask) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) sc[j] = (kb + 8 * g16 + j <= row_pos[rb]) ? sc[j] : -INFINITY;
       }
       float mx = sc[0];
 #pragma unroll
@@ -343,79 +415,96 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
       const bool grow = mt > m[rb] + kLazy;
       const float mn = grow ? mt : m[rb];
       rescale |= grow;
-      alpha[rb] = fast_exp2(m[rb] - mn);
+      alpha[rb] = m[rb] - mn;  // log2 of the rescale factor, 0 when the max stays
       m[rb] = mn;
       float p[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) p[j] = fast_exp2(__builtin_fmaf(sc[j], c, -mn));
-      p_operands<KV>(p, pk[rb], pl[rb]);
+      p_operands<KV>(p, pn[rb], pnl[rb]);
+    }
+    pv_product(buf_of(i - 1) + L::kKHalves);
+    // Order this block (the softmax above and the product): the V reads of two
+    // slices first, then one MFMA of the product after every few VALU instructions
+    // of the softmax, the other V reads two at a time in between, so the matrix
+    // cores run the previous step's product while the vector unit works.
+    {
+      constexpr int kMf = (kSplitP<KV> ? 2 : 1) * RB * (NSL + 1);  // product MFMAs
+      constexpr int kReads = 2 * NSL;                              // transposed V reads
+      constexpr int kValuPer = kSplitP<KV> ? 3 : 4;
+      constexpr int kEvery = kMf / (kReads / 2 - 1);  // MFMAs between later read pairs
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int j = 0; j < kMf; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, kValuPer, 0);
+        if (j % kEvery == kEvery - 1 && j / kEvery < kReads / 2 - 2)
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
     }
     if (__any(rescale)) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        lsum[rb] *= alpha[rb];
+        const float f = fast_exp2(alpha[rb]);
+        lsum[rb] *= f;
 #pragma unroll
-        for (int sl = 0; sl < NSL; ++sl) o[rb][sl] *= alpha[rb];
+        for (int sl = 0; sl < NSL; ++sl) o[rb][sl] *= f;
       }
     }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      lsum[rb] = mfma32<KV>(ones, pk[rb], lsum[rb]);
-      if constexpr (kSplitP<KV>) lsum[rb] = mfma32<KV>(ones, pl[rb], lsum[rb]);
-    }
-    // V^T operand of slice sl, read one slice ahead of the products that use it
-    auto vread = [&](int sl) {
-      const int d0 = sl * 16 + vcol;
-      const _Float16 *vp = V + vrow * D + ((d0 >> 3) ^ v_swizzle<D>(vrow)) * 8 + (d0 & 7);
-      const u32x2 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 4 * D);
-      return u32x4{lo[0], lo[1], hi[0], hi[1]};
-    };
-    u32x4 va[2];
-    va[0] = vread(0);
-#pragma unroll
-    for (int sl = 0; sl < NSL; ++sl) {
-      if (sl + 1 < NSL) va[(sl + 1) & 1] = vread(sl + 1);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) o[rb][sl] = mfma32<KV>(va[sl & 1], pk[rb], o[rb][sl]);
-      if constexpr (kSplitP<KV>) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) o[rb][sl] = mfma32<KV>(va[sl & 1], pl[rb], o[rb][sl]);
-      }
+      pp[rb] = pn[rb];
+      ppl[rb] = pnl[rb];
     }
   };
-  constexpr int NS = kStages;
-  constexpr int U = NS % 2 ? 2 * NS : NS;  // unroll: stage ring and LDS buffer parity
+
+  constexpr int kAhead = 2;  // a step's loads go out this many iterations before its scores
+  constexpr int U = L::kBufs;  // unroll: every unrolled step's buffers are compile-time
+  static_assert(kAhead + 2 <= L::kBufs, "buffers of the steps in flight, scored and deferred");
   const int nsteps = (nkeys + kKeyStep - 1) / kKeyStep;
-  Stage st[NS];
-  StepBt bnext = bt_load(NS);  // clamped when the tile has fewer steps
+  // this wave's loads of kAhead - 1 steps: what may still be in flight when a step's
+  // loads must have landed
+  using AheadLess1 = std::integral_constant<int, 2 * NL * (kAhead - 1)>;
+  // The q operands have landed before the first LDS-DMA load is issued: the
+  // compiler's own waits for them would otherwise sit inside the step loop and,
+  // counting loads it cannot see, drain the prefetch every time round.
+  wait_loads(std::integral_constant<int, 0>{});
+  {  // the V that step 0's deferred product (with P = 0) reads: zeros, never NaN
+    _Float16 *Vz = buf_of(-1) + L::kKHalves;
 #pragma unroll
-  for (int i = 0; i < NS; ++i) gload(bt_load(i), st[i]);
-  lstore(0, 0, st[0]);
+    for (int c = tid; c < L::kVHalves / 8; c += 256)
+      *reinterpret_cast<u32x4 *>(Vz + 8 * c) = u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) dma_step(bt_load(i), i);  // clamped past the last step
+  StepBt bnext = bt_load(kAhead);
+  wait_loads(AheadLess1{});
+  fix_tail(0, 0);
   __syncthreads();
-  // iteration n: read step n+NS+1's block-table entries, load step n+NS into the
-  // stage step n used, compute step n from LDS, then move step n+1 (already in
-  // registers) into the other LDS buffer.  Past the last step the loads repeat
-  // the last block.
-  auto iter = [&](int n, Stage &mine, const Stage &next) {
-    const StepBt bn = bt_load(n + NS + 1);
-    gload(bnext, mine);
-    bnext = bn;
-    compute(n & 1, n * kKeyStep);
-    if (n + 1 < nsteps) lstore((n + 1) & 1, (n + 1) * kKeyStep, next);
+  // iteration n (i = n mod U): issue step n+kAhead's loads, read the block-table
+  // entries of the step after, run step n (with the product of step n-1), then wait
+  // for step n+1's loads.  A wave whose rows end before the tile's last step runs
+  // its remaining steps fully masked (zero weights): it would otherwise wait at the
+  // barriers, and one code path keeps its registers within two waves per SIMD.
+  // Past the last step the loads repeat the last block into free buffers.
+  auto iter = [&](int n, int i) {
+    dma_step(bnext, (i + kAhead) % L::kBufs);
+    bnext = bt_load(n + kAhead + 1);
+    full_step(i, n * kKeyStep);
+    wait_loads(AheadLess1{});  // step n+1's loads have landed; step n+2's may be in flight
+    if (n + 1 < nsteps) fix_tail(n + 1, (i + 1) % L::kBufs);
     __syncthreads();
   };
-  // Whole groups of U steps in an unguarded loop, then the (< U) remaining steps
-  // once.  With a per-step guard inside the loop, its header gets several entries
-  // and the compiler's wait counting, merging them, drains every load in flight
-  // before each step issues its own: the ring would be one step deep instead of NS.
   int n0 = 0;
   for (; n0 + U <= nsteps; n0 += U) {
 #pragma unroll
-    for (int i = 0; i < U; ++i) iter(n0 + i, st[i % NS], st[(i + 1) % NS]);
+    for (int i = 0; i < U; ++i) iter(n0 + i, i);
   }
 #pragma unroll
   for (int i = 0; i < U - 1; ++i)
-    if (n0 + i < nsteps) iter(n0 + i, st[i % NS], st[(i + 1) % NS]);
+    if (n0 + i < nsteps) iter(n0 + i, i);
+  pv_product(lds + ((nsteps - 1) % L::kBufs) * L::kBufHalves + L::kKHalves);  // the last product
+  // no load may still be writing this workgroup's LDS when it exits
+  wait_loads(std::integral_constant<int, 0>{});
 
   // ---- normalise and store: lane holds dims sl*16 + 4*g16 + i of query row c16 ----
 #pragma unroll
