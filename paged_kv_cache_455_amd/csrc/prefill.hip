@@ -103,6 +103,24 @@ __device__ __forceinline__ void p_operands(const float *p, u32x4 &hi, u32x4 &lo)
   }
 }
 
+// The same for 4 probabilities: words 2*half and 2*half + 1 of the operands.
+template <int KV>
+__device__ __forceinline__ void p_operands_half(const float *p, u32x4 &hi, u32x4 &lo, int half) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float a = p[2 * i], b = p[2 * i + 1];
+    if constexpr (!kSplitP<KV>) {
+      hi[2 * half + i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{a, b}, h2v_t));
+    } else {
+      const uint32_t ua = __builtin_bit_cast(uint32_t, a), ub = __builtin_bit_cast(uint32_t, b);
+      hi[2 * half + i] = __builtin_amdgcn_perm(ub, ua, 0x07060302u);
+      const float ra = a - __builtin_bit_cast(float, ua & 0xFFFF0000u);
+      const float rb = b - __builtin_bit_cast(float, ub & 0xFFFF0000u);
+      lo[2 * half + i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{ra, rb}, b2v_t));
+    }
+  }
+}
+
 // gfx950's transposed LDS read of 16-bit values (ds_read_b64_tr_b16).  Each lane
 // names 8 bytes; inside each 16-lane group, lane i receives element i % 4 of the
 // reads of lanes 4e + i / 4 (e = 0 .. 3).  So when those lanes read 4 rows of a
@@ -390,56 +408,91 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
           else s2[rb][j - 4] = vis ? s2[rb][j - 4] : -INFINITY;
         }
     }
+    // The softmax of step n and the P.V product of step n-1 (independent) run as
+    // NSL + 1 phases, each holding a share of both: the product's MFMAs of one V
+    // slice (the row sums first) and a piece of the softmax's VALU work, the V
+    // reads two phases ahead of their products.  A scheduling fence closes each
+    // phase, so the compiler cannot regroup the MFMAs into one run and the VALU work
+    // into another: inside a phase the matrix cores run the MFMAs while the vector
+    // unit works through its piece.
     const float c = d.qk_scale;  // softmax scale * log2(e) (> 0); m is kept in these units
     u32x4 pn[RB], pnl[RB];  // P^T operands of step n: p (f16), or its hi and lo parts (bf16)
     bool rescale = false;
-    float alpha[RB];
+    float alpha[RB], mx[RB], mnew[RB];
+    // softmax pieces in order: local maxima (one per row block), the cross-lane max
+    // and the running-max update (one per row block), then the weights and their
+    // operands a half (4 keys) at a time
+    constexpr int kPieces = 4 * RB;
+    auto softmax_piece = [&](int k) {
+      if (k < RB) {
+        const int rb = k;
+        float v = fmaxf(s1[rb][0], s1[rb][1]);
+        v = fmaxf(v, fmaxf(s1[rb][2], s1[rb][3]));
+        v = fmaxf(v, fmaxf(s2[rb][0], s2[rb][1]));
+        mx[rb] = fmaxf(v, fmaxf(s2[rb][2], s2[rb][3]));
+      } else if (k < 2 * RB) {
+        const int rb = k - RB;
+        const float v = max_xor_rows<32>(max_xor_rows<16>(mx[rb]));
+        // Lazy rescale: the running max moves only when a score exceeds it by more
+        // than kLazy (log2 units), so p = 2^(s*c - m) stays below 2^kLazy, well
+        // inside the range of the 16-bit P operand and of the fp32 sums; the result
+        // does not depend on m (numerator and denominator carry the same factor).
+        const float mt = v * c;
+        const bool grow = mt > m[rb] + kLazy;
+        mnew[rb] = grow ? mt : m[rb];
+        rescale |= grow;
+        alpha[rb] = m[rb] - mnew[rb];  // log2 of the rescale factor, 0 when the max stays
+        m[rb] = mnew[rb];
+      } else {
+        const int rb = (k - 2 * RB) >> 1, half = (k - 2 * RB) & 1;
+        const f4_t &sv = half ? s2[rb] : s1[rb];
+        float p[4];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float sc[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sc[i] = s1[rb][i];
-        sc[4 + i] = s2[rb][i];
+        for (int j = 0; j < 4; ++j) p[j] = fast_exp2(__builtin_fmaf(sv[j], c, -mnew[rb]));
+        p_operands_half<KV>(p, pn[rb], pnl[rb], half);
+        // The operands are used only by the next step's product; without a use
+        // here the compiler sinks their computation there, out of this phase.
+        asm volatile("" ::"v"(pn[rb][2 * half]), "v"(pn[rb][2 * half + 1]));
+        if constexpr (kSplitP<KV>)
+          asm volatile("" ::"v"(pnl[rb][2 * half]), "v"(pnl[rb][2 * half + 1]));
       }
-      float mx = sc[0];
+    };
+    const _Float16 *Vb = buf_of(i - 1) + L::kKHalves;  // step n-1's V
+    auto vread = [&](int sl) {
+      const int d0 = sl * 16 + vcol;
+      const _Float16 *vp = Vb + vrow * D + ((d0 >> 3) ^ v_swizzle<D>(vrow)) * 8 + (d0 & 7);
+      const u32x2 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 4 * D);
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    constexpr int NPH = NSL + 1;
+    u32x4 va[3];
 #pragma unroll
-      for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sc[j]);
-      mx = max_xor_rows<16>(mx);
-      mx = max_xor_rows<32>(mx);
-      // Lazy rescale: the running max moves only when a score exceeds it by more
-      // than kLazy (log2 units), so p = 2^(s*c - m) stays below 2^kLazy, well inside
-      // the range of the 16-bit P operand and of the fp32 sums; the result does not
-      // depend on m (numerator and denominator carry the same factor).
-      const float mt = mx * c;
-      const bool grow = mt > m[rb] + kLazy;
-      const float mn = grow ? mt : m[rb];
-      rescale |= grow;
-      alpha[rb] = m[rb] - mn;  // log2 of the rescale factor, 0 when the max stays
-      m[rb] = mn;
-      float p[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) p[j] = fast_exp2(__builtin_fmaf(sc[j], c, -mn));
-      p_operands<KV>(p, pn[rb], pnl[rb]);
-    }
-    pv_product(buf_of(i - 1) + L::kKHalves);
-    // Order this block (the softmax above and the product): the V reads of two
-    // slices first, then one MFMA of the product after every few VALU instructions
-    // of the softmax, the other V reads two at a time in between, so the matrix
-    // cores run the previous step's product while the vector unit works.
-    {
-      constexpr int kMf = (kSplitP<KV> ? 2 : 1) * RB * (NSL + 1);  // product MFMAs
-      constexpr int kReads = 2 * NSL;                              // transposed V reads
-      constexpr int kValuPer = kSplitP<KV> ? 3 : 4;
-      constexpr int kEvery = kMf / (kReads / 2 - 1);  // MFMAs between later read pairs
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int j = 0; j < kMf; ++j) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x402, kValuPer, 0);
-        if (j % kEvery == kEvery - 1 && j / kEvery < kReads / 2 - 2)
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    for (int ph = 0; ph < NPH; ++ph) {
+      if (ph == 0) {
+        va[0] = vread(0);
+        if (NSL > 1) va[1] = vread(1);
+      } else if (ph + 1 < NSL) {
+        va[(ph + 1) % 3] = vread(ph + 1);
       }
+      if (ph == 0) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          lsum[rb] = mfma32<KV>(ones, pp[rb], lsum[rb]);
+          if constexpr (kSplitP<KV>) lsum[rb] = mfma32<KV>(ones, ppl[rb], lsum[rb]);
+        }
+      } else {
+        const int sl = ph - 1;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) o[rb][sl] = mfma32<KV>(va[sl % 3], pp[rb], o[rb][sl]);
+        if constexpr (kSplitP<KV>) {
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) o[rb][sl] = mfma32<KV>(va[sl % 3], ppl[rb], o[rb][sl]);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kPieces; ++k)
+        if (k * NPH / kPieces == ph) softmax_piece(k);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (__any(rescale)) {
 #pragma unroll
