@@ -6,7 +6,7 @@
 // sequence to seq_len tokens sits at position seq_len - q_len + i and attends to
 // keys 0 .. that position.
 //
-// For f16 / bf16 KV the step is two launches (after a small one that lists the
+// For f16 / bf16 and fp8 / int8 KV the step is two launches (after a small one that lists the
 // prefill tiles on the device, heaviest first over the whole step):
 //  * prefill tiles: 64 * RB query rows -- (token, head) pairs of one kv head's GQA
 //    group -- against 32-key steps of the chunk's context, with the dense products
@@ -25,7 +25,10 @@
 //    are not rounded to bf16's 8 bits.
 //  * decode rows (q_len == 1): the balanced-split decode of decode_impl.h over
 //    the batch's one-token sequences (query row qsl[s]), with its piece merge.
-// Other KV types run every query row through the partitioned decode path.
+// 1-byte KV (fp8 E4M3FN, int8) runs the same tiles on its codes converted exactly to
+// 16 bits in LDS (q's type for K, bf16 for V), with the scales folded into the score
+// scale and the weights (see prefill_tile).  fp32 KV runs every query row through
+// the partitioned decode path.
 #include <type_traits>
 
 #include "decode_impl.h"
@@ -44,15 +47,20 @@ constexpr float kLazy = 8.f;    // running-max slack before a rescale (log2 unit
 
 int mixed_tile_rows() { return kTileRows; }
 
-template <int D>
+template <int D, bool Q8>
 struct PrefillLds {
   static constexpr int kKHalves = kKeyStep * D;     // K: [32 keys][D], chunks swizzled
   static constexpr int kVHalves = kKeyStep * D;     // V: [32 keys][D], chunks swizzled
   static constexpr int kBufHalves = kKHalves + kVHalves;
-  // four K/V buffers: a step's loads are issued two iterations ahead, and its V is
-  // still read (by the deferred P.V) one iteration after its scores
-  static constexpr int kBufs = 4;
-  static constexpr int kBytes = kBufs * kBufHalves * 2;
+  // 16-bit K/V buffers.  16-bit pools load a step straight into its buffer two
+  // iterations ahead (four: two in flight, the scored step, the deferred V).  1-byte
+  // pools load codes into a ring of their own and convert a step into its buffer
+  // one iteration ahead (three: converted, scored, deferred V).
+  static constexpr int kBufs = Q8 ? 3 : 4;
+  static constexpr int kCodeBytes = Q8 ? 2 * kKeyStep * D : 0;  // K + V codes of a step
+  static constexpr int kCodeBufs = Q8 ? 2 : 0;
+  static constexpr int kCodeOff = kBufs * kBufHalves * 2;       // bytes
+  static constexpr int kBytes = kCodeOff + kCodeBufs * kCodeBytes;
 };
 
 template <int KV>
@@ -69,51 +77,34 @@ typedef float f2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h2v_t __attribute__((ext_vector_type(2)));
 typedef __bf16 b2v_t __attribute__((ext_vector_type(2)));
 
-// P^T operands of 8 probabilities.  The P.V product and the row sums see the same
-// operands, so the output is sum(p~ v) / sum(p~) for the weights p~ as the MFMA
-// inputs hold them.
+// P^T operands of 4 probabilities (words 2*half and 2*half + 1) in the P.V MFMA's
+// 16-bit type T.  The P.V product and the row sums see the same operands, so the
+// output is sum(p~ v) / sum(p~) for the weights p~ as the MFMA inputs hold them.
 //  f16: p rounded to nearest even (lo unused).  Each weight then carries a
 //       relative error below 2^-11, which moves the output by less than 2^-11 of
 //       the weighted spread |v - out| of the values -- the order of V's own f16
 //       storage precision, and inside the f16 tolerance (a simulation of 25.6 M
 //       outputs on unscaled N(0,1) data, few to hundreds of keys, peaked at 0.72
 //       of the bar: max(2e-3, one ulp)).
-//  bf16: one rounding would be 2^-8 relative (3x the bar on such data), so p is
-//       split into two parts, p ~= hi + lo: hi = p truncated to its upper 16 bits
-//       (a byte permute of two values), lo = (p - hi) rounded to nearest even, the
-//       difference exact in fp32; the pair holds p to 2^-15 relative and every
-//       product runs twice (hi, then lo).
-template <int KV>
-constexpr bool kSplitP = KV == PA_BF16;
-
-template <int KV>
-__device__ __forceinline__ void p_operands(const float *p, u32x4 &hi, u32x4 &lo) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float a = p[2 * i], b = p[2 * i + 1];
-    if constexpr (!kSplitP<KV>) {
-      hi[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{a, b}, h2v_t));
-    } else {
-      const uint32_t ua = __builtin_bit_cast(uint32_t, a), ub = __builtin_bit_cast(uint32_t, b);
-      hi[i] = __builtin_amdgcn_perm(ub, ua, 0x07060302u);  // upper halves of a (low), b (high)
-      const float ra = a - __builtin_bit_cast(float, ua & 0xFFFF0000u);
-      const float rb = b - __builtin_bit_cast(float, ub & 0xFFFF0000u);
-      lo[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{ra, rb}, b2v_t));
-    }
-  }
-}
-
-// The same for 4 probabilities: words 2*half and 2*half + 1 of the operands.
-template <int KV>
+//  bf16 pools (SPLIT): one rounding would be 2^-8 relative (3x the bar on such
+//       data), so p is split into two parts, p ~= hi + lo: hi = p truncated to its
+//       upper 16 bits (a byte permute of two values), lo = (p - hi) rounded to
+//       nearest even, the difference exact in fp32; the pair holds p to 2^-15
+//       relative and every product runs twice (hi, then lo).
+//  1-byte pools: bf16, one rounding (2^-8 relative, within their 2e-2 tolerance).
+template <int T, bool SPLIT>
 __device__ __forceinline__ void p_operands_half(const float *p, u32x4 &hi, u32x4 &lo, int half) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const float a = p[2 * i], b = p[2 * i + 1];
-    if constexpr (!kSplitP<KV>) {
-      hi[2 * half + i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{a, b}, h2v_t));
+    if constexpr (!SPLIT) {
+      if constexpr (T == PA_F16)
+        hi[2 * half + i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{a, b}, h2v_t));
+      else
+        hi[2 * half + i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{a, b}, b2v_t));
     } else {
       const uint32_t ua = __builtin_bit_cast(uint32_t, a), ub = __builtin_bit_cast(uint32_t, b);
-      hi[2 * half + i] = __builtin_amdgcn_perm(ub, ua, 0x07060302u);
+      hi[2 * half + i] = __builtin_amdgcn_perm(ub, ua, 0x07060302u);  // upper halves of a, b
       const float ra = a - __builtin_bit_cast(float, ua & 0xFFFF0000u);
       const float rb = b - __builtin_bit_cast(float, ub & 0xFFFF0000u);
       lo[2 * half + i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{ra, rb}, b2v_t));
@@ -162,21 +153,33 @@ __device__ __forceinline__ int v_swizzle(int key) {
 
 // One prefill tile: query tokens [qt*QTOK, ...) of sequence s, kv head h.
 // Rows: wave w, row block rb, lane column c16 -> row (w*RB + rb)*16 + c16 = token*G + head.
-// Pipeline, per 32-key step n: K/V of step n+2 go from HBM straight into the LDS
-// buffer (n+2) mod 4 (LDS-DMA, no registers), the block-table entries of step n+3
-// are read, the scores and softmax of step n run beside the P.V product of step n-1
-// (whose V still sits in buffer (n-1) mod 4), and the wave waits for its loads of
-// step n+1 before the barrier that hands them to every wave.  Every load is issued
-// unconditionally (indices clamped to the tile's last block) so the wait counts are
-// fixed.  Each K or V operand read from LDS serves all RB row blocks of the wave.
-template <int KV, int D, int G>
+// Pipeline, per 32-key step n: K/V of step n+2 go from HBM straight into LDS
+// (LDS-DMA, no registers), the block-table entries of step n+3 are read, the scores
+// and softmax of step n run beside the P.V product of step n-1 (whose V is still in
+// LDS), and the wave waits for its loads of step n+1 before the barrier that hands
+// them to every wave.  16-bit pools: the loads land in step n+2's 16-bit buffer.
+// 1-byte pools (fp8 E4M3FN, int8): the codes land in a ring of code buffers, and
+// each wave converts the rows it loaded itself -- exactly, to q's type for K and to
+// bf16 for V -- into step n+1's 16-bit buffer once they have landed; the
+// per-(block, kv head) scales are folded in afterwards: the key scale into each
+// lane's score scale (a lane's 8 keys lie in one block), the value scale into the
+// weights (p' = p * vs through the exponent), and the row sums are kept per lane in
+// fp32 as sum(p' / vs).  Every load is issued unconditionally (indices clamped to the
+// tile's last block) so the wait counts are fixed.  Each K or V operand read from
+// LDS serves all RB row blocks of the wave.
+template <int KV, int QT, int D, int G>
 __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, int qt,
                                              char *smem) {
+  constexpr bool Q8 = KV == PA_FP8_E4M3 || KV == PA_I8;
+  static_assert(Q8 || KV == QT, "16-bit pools take queries of their own type");
+  constexpr int MQ = QT;                     // QK MFMA type (q's type; K converted to it)
+  constexpr int MP = Q8 ? PA_BF16 : KV;      // P.V MFMA type (V as stored, or codes as bf16)
+  constexpr bool kSplit = KV == PA_BF16;     // P as hi + lo parts
   constexpr int RB = kRowBlocks;
   constexpr int QTOK = kTileRows / G;
   constexpr int NKK = D / 32;        // QK MFMAs along head_dim
   constexpr int NSL = D / 16;        // 16-dim output slices
-  using L = PrefillLds<D>;
+  using L = PrefillLds<D, Q8>;
   _Float16 *lds = reinterpret_cast<_Float16 *>(smem);
   const DecodeArgs &d = a.dec;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -217,27 +220,28 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
     }
   }
 
-  // o: O^T slices; lsum: the running softmax denominators, accumulated on the matrix
-  // cores as ones(16 x 32) . P^T (hi and lo parts for bf16), so every element holds
-  // its query row's sum of the probabilities as the P.V product used them
+  // o: O^T slices.  lsum (16-bit pools): the running softmax denominators,
+  // accumulated on the matrix cores as ones(16 x 32) . P^T (hi and lo parts for
+  // bf16), so every element holds its query row's sum of the probabilities as the
+  // P.V product used them.  lrow (1-byte pools): this lane's share of its row's sum
+  // of the unscaled weights, in fp32.
   f4_t o[RB][NSL], lsum[RB];
-  float m[RB];
+  float m[RB], lrow[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     m[rb] = kNegBig;
+    lrow[rb] = 0.f;
     lsum[rb] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int sl = 0; sl < NSL; ++sl) o[rb][sl] = f4_t{0.f, 0.f, 0.f, 0.f};
   }
-  constexpr uint32_t kOne2 = KV == PA_F16 ? 0x3C003C00u : 0x3F803F80u;  // two 16-bit 1.0s
+  constexpr uint32_t kOne2 = MP == PA_F16 ? 0x3C003C00u : 0x3F803F80u;  // two 16-bit 1.0s
   const u32x4 ones = u32x4{kOne2, kOne2, kOne2, kOne2};
 
   // ---- global -> LDS staging of one 32-key step (LDS-DMA) ----
   // gfx950's global_load_lds_dwordx4: each lane's 16 bytes land at m0 + 16 * lane
-  // (checked on the MI355X), so a wave-wide load fills 1 KiB of LDS -- RPW whole key
-  // rows -- with no registers in between.  A lane picks the global chunk whose
-  // swizzled position is its slot: chunk p ^ swizzle(key) of its key row (the same
-  // row, so the wave's reads stay contiguous).
+  // (checked on the MI355X), so a wave-wide load fills 1 KiB of LDS with no
+  // registers in between.
   const char *kpool = reinterpret_cast<const char *>(d.k);
   const char *vpool = reinterpret_cast<const char *>(d.v);
   // 16-row tile indices of step n's two tiles (clamped to the last tile)
@@ -245,13 +249,14 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
     int64_t u0, u1;
   };
   const int sh = d.bs_shift;
-  // The table row is read through the constant address space: nothing writes it
-  // during the kernel, and these reads (uniform per wave) then stay scalar loads --
-  // the compiler would otherwise make vector loads of them after the LDS-DMA
-  // statements below, which it cannot prove write no global memory, and a wait for
-  // those would also wait for every load in flight.
-  const __attribute__((address_space(4))) int32_t *btc =
-      (const __attribute__((address_space(4))) int32_t *)(uintptr_t)bt;
+  // The table row (and the scales) are read through the constant address space:
+  // nothing writes them during the kernel, and these reads (uniform per wave) then
+  // stay scalar loads -- the compiler would otherwise make vector loads of them after
+  // the LDS-DMA statements below, which it cannot prove write no global memory, and a
+  // wait for those would also wait for every load in flight.
+  typedef const __attribute__((address_space(4))) int32_t *cint_p;
+  typedef const __attribute__((address_space(4))) float *cfloat_p;
+  const cint_p btc = (cint_p)(uintptr_t)bt;
   auto bt_load = [&](int n) {
     const int j0 = min(2 * n, nblk - 1), j1 = min(2 * n + 1, nblk - 1);
     StepBt r;
@@ -259,17 +264,7 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
     r.u1 = tile_index(btc[j1 >> sh], Hkv, h, j1, sh);
     return r;
   };
-  constexpr int CPR = D / 8;                    // 16-byte chunks per key row
-  constexpr int RPW = 64 / CPR;                 // key rows per wave-wide load
-  constexpr int NL = kKeyStep / RPW / 4;        // wave-wide loads of K (and of V) per wave
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
-  uint32_t koff[NL], voff[NL];  // byte offset of the lane's chunk inside its 16-row tile
-#pragma unroll
-  for (int j = 0; j < NL; ++j) {
-    const int key = (wave * NL + j) * RPW + lane / CPR, p = lane % CPR;
-    koff[j] = (uint32_t)((key % kBlock) * D * 2 + (p ^ k_swizzle<D>(key)) * 16);
-    voff[j] = (uint32_t)((key % kBlock) * D * 2 + (p ^ v_swizzle<D>(key)) * 16);
-  }
   auto dma1 = [&](const char *gbase, uint32_t off, uint32_t lds_addr) {
     const uint64_t g = (uint64_t)(uintptr_t)gbase;
     const uint32_t glo = __builtin_amdgcn_readfirstlane((uint32_t)g);
@@ -283,15 +278,58 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0v), "v"(off),
                  "s"(gu));
   };
-  // the step's K and V tiles into LDS buffer bi: NL wave-wide loads of each per wave
-  auto dma_step = [&](const StepBt &b, int bi) {
+
+  // 16-bit pools: a wave-wide load is RPW whole key rows; a lane picks the global
+  // chunk whose swizzled position is its slot: chunk p ^ swizzle(key) of its key row
+  // (the same row, so the wave's reads stay contiguous).  NL loads of K and NL of V
+  // per wave and step.
+  constexpr int CPR = D / 8;                    // 16-byte chunks per key row
+  constexpr int RPW = 64 / CPR;                 // key rows per wave-wide load
+  constexpr int NL = Q8 ? 0 : kKeyStep / RPW / 4;
+  // 1-byte pools: the step's K and V codes are D/16 wave-wide loads, K first; wave w
+  // issues QPW of them (K for half the waves, V for the other half), each 1 KiB =
+  // RPQ key rows, the lane's 16 codes being chunk p of row r.
+  constexpr int QPW = Q8 ? D / 64 : 0;
+  constexpr int RPQ = 1024 / D;                 // key rows per code load
+  constexpr int CPQ = D / 16;                   // 16-code chunks per key row
+  constexpr int KLD = D / 32;                   // code loads of K per step
+  constexpr int LPW = Q8 ? QPW : 2 * NL;        // loads per wave and step
+  uint32_t koff[Q8 ? 1 : NL], voff[Q8 ? 1 : NL];  // 16-bit: the lane's chunk in its tile
+  uint32_t qoff[Q8 ? QPW : 1];                    // 1-byte: the lane's code chunk in its tile
+  if constexpr (!Q8) {
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
-      const int lw = wave * NL + j;                // this load's 1 KiB of the tile pair
-      const int64_t tile = ((lw * RPW) / kBlock ? b.u1 : b.u0) * (int64_t)(kBlock * D * 2);
-      const uint32_t at = lds_base + (uint32_t)((bi * L::kBufHalves) * 2 + lw * 1024);
-      dma1(kpool + tile, koff[j], at);
-      dma1(vpool + tile, voff[j], at + L::kKHalves * 2);
+      const int key = (wave * NL + j) * RPW + lane / CPR, p = lane % CPR;
+      koff[j] = (uint32_t)((key % kBlock) * D * 2 + (p ^ k_swizzle<D>(key)) * 16);
+      voff[j] = (uint32_t)((key % kBlock) * D * 2 + (p ^ v_swizzle<D>(key)) * 16);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < QPW; ++j) {
+      const int lw = wave * QPW + j;
+      const int r = (lw % KLD) * RPQ + lane / CPQ, p = lane % CPQ;
+      qoff[j] = (uint32_t)((r % kBlock) * D + p * 16);
+    }
+  }
+  // the step's K and V tiles: into 16-bit buffer bi, or (1-byte) into code buffer bi
+  auto dma_step = [&](const StepBt &b, int bi) {
+    if constexpr (!Q8) {
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        const int lw = wave * NL + j;                // this load's 1 KiB of the tile pair
+        const int64_t tile = ((lw * RPW) / kBlock ? b.u1 : b.u0) * (int64_t)(kBlock * D * 2);
+        const uint32_t at = lds_base + (uint32_t)((bi * L::kBufHalves) * 2 + lw * 1024);
+        dma1(kpool + tile, koff[j], at);
+        dma1(vpool + tile, voff[j], at + L::kKHalves * 2);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < QPW; ++j) {
+        const int lw = wave * QPW + j;
+        const int64_t tile = (((lw % KLD) * RPQ) / kBlock ? b.u1 : b.u0) * (int64_t)(kBlock * D);
+        const uint32_t at = lds_base + (uint32_t)(L::kCodeOff + bi * L::kCodeBytes + lw * 1024);
+        dma1((lw < KLD ? kpool : vpool) + tile, qoff[j], at);
+      }
     }
   };
   // s_waitcnt vmcnt(c) (the other counters left alone): the loads this wave issued,
@@ -302,12 +340,13 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
     static_assert(n >= 0 && n < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
   };
-  // V rows of step n at or past nkeys (the tile's reach; they may hold anything, NaN
-  // included) are zeroed after this wave's own loads of them have landed: their
-  // weights are zero, and 0 * NaN would not be.  K needs no fix: those keys are
-  // masked by selection.  The store is written out with its waits (all loads, then
-  // the store itself) so that the compiler, which does not see the loads, cannot
-  // place it before them.  Only the step that reaches past nkeys takes this path.
+  // 16-bit pools: V rows of step n at or past nkeys (the tile's reach; they may hold
+  // anything, NaN included) are zeroed after this wave's own loads of them have
+  // landed: their weights are zero, and 0 * NaN would not be.  K needs no fix: those
+  // keys are masked by selection.  The store is written out with its waits (all
+  // loads, then the store itself) so that the compiler, which does not see the
+  // loads, cannot place it before them.  Only the step that reaches past nkeys takes
+  // this path.
   auto fix_tail = [&](int n, int bi) {
     const int kb = n * kKeyStep;
     if (kb + kKeyStep <= nkeys) return;
@@ -323,6 +362,62 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
                      "v"(z));
     }
   };
+  // 1-byte pools: after this wave's code loads of step n have landed (the caller
+  // waits), its lanes convert their own 16 codes each into step n's 16-bit buffer bi
+  // (K in q's type, V in bf16; both exact), in the same swizzled layout the 16-bit
+  // pools load; rows at or past nkeys become zeros.  The read of the codes is written
+  // out with its wait, so the compiler (which does not see the loads) keeps it after
+  // the wait for them.
+  auto convert_step = [&](int n, int bi, int ci) {
+    const int kb = n * kKeyStep;
+#pragma unroll
+    for (int j = 0; j < QPW; ++j) {
+      const int lw = wave * QPW + j;
+      const bool is_k = lw < KLD;
+      const int r = (lw % KLD) * RPQ + lane / CPQ, p = lane % CPQ;
+      const uint32_t at = lds_base + (uint32_t)(L::kCodeOff + ci * L::kCodeBytes + lw * 1024 + lane * 16);
+      u32x4 c;
+      asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(c) : "v"(at));
+      uint32_t w[8];
+      if (is_k) {  // uniform per load
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w[2 * e] = codes2_to_16<KV, MQ, false>(c[e]);
+          w[2 * e + 1] = codes2_to_16<KV, MQ, true>(c[e]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w[2 * e] = codes2_to_16<KV, PA_BF16, false>(c[e]);
+          w[2 * e + 1] = codes2_to_16<KV, PA_BF16, true>(c[e]);
+        }
+      }
+      if (kb + r >= nkeys) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = 0u;
+      }
+      _Float16 *dst = lds + bi * L::kBufHalves + (is_k ? 0 : L::kKHalves) + r * D;
+      const int sw = is_k ? k_swizzle<D>(r) : v_swizzle<D>(r);
+      *reinterpret_cast<u32x4 *>(dst + ((2 * p) ^ sw) * 8) = u32x4{w[0], w[1], w[2], w[3]};
+      *reinterpret_cast<u32x4 *>(dst + ((2 * p + 1) ^ sw) * 8) = u32x4{w[4], w[5], w[6], w[7]};
+    }
+  };
+  // 1-byte pools: the step's key and value scales (per tile), for the lane's keys
+  struct StepScale {
+    float k0, k1, v0, v1;
+  };
+  const cfloat_p ksc = (cfloat_p)(uintptr_t)d.k_scale;
+  const cfloat_p vsc = (cfloat_p)(uintptr_t)d.v_scale;
+  auto scale_load = [&](const StepBt &b) {
+    StepScale r{1.f, 1.f, 1.f, 1.f};
+    if constexpr (Q8) {
+      r.k0 = ksc[b.u0 >> sh];
+      r.k1 = ksc[b.u1 >> sh];
+      r.v0 = vsc[b.u0 >> sh];
+      r.v1 = vsc[b.u1 >> sh];
+    }
+    return r;
+  };
 
   const int key1 = 8 * (c16 >> 2) + (c16 & 3);  // key row of this lane in QK product 1
   const int key2 = key1 + 4;                      // ... in product 2
@@ -331,9 +426,9 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
   // transposed read returns dim 16 sl + c16 of the 4 keys.  vrow + 4 shares vrow's
   // swizzle (bit 2 of the key is not in it).
   const int vrow = 8 * g16 + (c16 >> 2), vcol = 4 * (c16 & 3);
-  // LDS buffer of the step with index i modulo the unroll (i >= -1; i = -1 at step
-  // 0 is the zeroed V that the first step's deferred product reads); U is a multiple
-  // of kBufs, so i modulo kBufs is the step's buffer
+  // 16-bit buffer of the step with index i modulo the unroll (i >= -1; i = -1 at step
+  // 0 is the zeroed V that the first step's deferred product reads); the unroll is a
+  // multiple of kBufs, so i modulo kBufs is the step's buffer
   auto buf_of = [&](int i) { return lds + ((i + L::kBufs) % L::kBufs) * L::kBufHalves; };
   // P^T operands of the step whose P.V product is still to run (deferred by one
   // step), zero before the first
@@ -343,39 +438,42 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
     pp[rb] = u32x4{0, 0, 0, 0};
     ppl[rb] = u32x4{0, 0, 0, 0};
   }
-  // O^T += V^T . P^T and the row sums for the held P^T operands, V from buffer Vb
+  auto vread_from = [&](const _Float16 *Vb, int sl) {
+    const int d0 = sl * 16 + vcol;
+    const _Float16 *vp = Vb + vrow * D + ((d0 >> 3) ^ v_swizzle<D>(vrow)) * 8 + (d0 & 7);
+    const u32x2 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 4 * D);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+  // O^T += V^T . P^T and (16-bit pools) the row sums for the held P^T operands, V
+  // from buffer Vb
   auto pv_product = [&](const _Float16 *Vb) {
+    if constexpr (!Q8) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      lsum[rb] = mfma32<KV>(ones, pp[rb], lsum[rb]);
-      if constexpr (kSplitP<KV>) lsum[rb] = mfma32<KV>(ones, ppl[rb], lsum[rb]);
+      for (int rb = 0; rb < RB; ++rb) {
+        lsum[rb] = mfma32<MP>(ones, pp[rb], lsum[rb]);
+        if constexpr (kSplit) lsum[rb] = mfma32<MP>(ones, ppl[rb], lsum[rb]);
+      }
     }
     // V^T operand of slice sl, read one slice ahead of the products that use it
-    auto vread = [&](int sl) {
-      const int d0 = sl * 16 + vcol;
-      const _Float16 *vp = Vb + vrow * D + ((d0 >> 3) ^ v_swizzle<D>(vrow)) * 8 + (d0 & 7);
-      const u32x2 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 4 * D);
-      return u32x4{lo[0], lo[1], hi[0], hi[1]};
-    };
     u32x4 va[2];
-    va[0] = vread(0);
+    va[0] = vread_from(Vb, 0);
 #pragma unroll
     for (int sl = 0; sl < NSL; ++sl) {
-      if (sl + 1 < NSL) va[(sl + 1) & 1] = vread(sl + 1);
+      if (sl + 1 < NSL) va[(sl + 1) & 1] = vread_from(Vb, sl + 1);
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) o[rb][sl] = mfma32<KV>(va[sl & 1], pp[rb], o[rb][sl]);
-      if constexpr (kSplitP<KV>) {
+      for (int rb = 0; rb < RB; ++rb) o[rb][sl] = mfma32<MP>(va[sl & 1], pp[rb], o[rb][sl]);
+      if constexpr (kSplit) {
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) o[rb][sl] = mfma32<KV>(va[sl & 1], ppl[rb], o[rb][sl]);
+        for (int rb = 0; rb < RB; ++rb) o[rb][sl] = mfma32<MP>(va[sl & 1], ppl[rb], o[rb][sl]);
       }
     }
   };
-  // Step n (keys kb ..): S^T = K . Q^T and the online softmax of step n, and the
-  // P.V product of step n-1.  The two are independent, so the softmax's VALU work
-  // and the previous step's MFMAs can interleave; the rescale of the accumulators
-  // by step n's factor follows the product of step n-1 (whose P was relative to the
-  // old maximum).
-  auto full_step = [&](int i, int kb) {
+  // Step n (keys kb ..; i = n modulo the unroll, sc = its scales): S^T = K . Q^T and
+  // the online softmax of step n, and the P.V product of step n-1.  The two are
+  // independent, so the softmax's VALU work and the previous step's MFMAs can
+  // interleave; the rescale of the accumulators by step n's factor follows the
+  // product of step n-1 (whose P was relative to the old maximum).
+  auto full_step = [&](int i, int kb, const StepScale &sc) {
     // some key of the step lies past some row's position (the causal diagonal, or
     // the tile's reach); uniform per wave, a scalar branch
     const bool need_mask = kb + kKeyStep - 1 > wave_min_pos;
@@ -393,8 +491,8 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
       const u32x4 a2 = *reinterpret_cast<const u32x4 *>(K + key2 * D + ((cc ^ k_swizzle<D>(key2)) * 8));
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        s1[rb] = mfma32<KV>(a1, qop[rb][kk], s1[rb]);
-        s2[rb] = mfma32<KV>(a2, qop[rb][kk], s2[rb]);
+        s1[rb] = mfma32<MQ>(a1, qop[rb][kk], s1[rb]);
+        s2[rb] = mfma32<MQ>(a2, qop[rb][kk], s2[rb]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);  // the score products stay ahead of the block below
@@ -408,6 +506,19 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
           else s2[rb][j - 4] = vis ? s2[rb][j - 4] : -INFINITY;
         }
     }
+    // Score scale of this lane's keys (softmax scale * log2(e), > 0; m is kept in
+    // these units), for 1-byte pools times the key scale of their block.  The value
+    // scale enters the weights through the exponent: p' = 2^(s*c - m + log2 vs).  A
+    // zero scale (an all-zero tile) is taken as 1e-30: its codes give zero scores and
+    // values either way, and the weights stay finite.
+    float c = d.qk_scale, lvs = 0.f, ivs = 1.f;
+    if constexpr (Q8) {
+      const bool hi = g16 >= 2;  // keys 8*g16 .. +7 lie in the step's second block
+      c *= fmaxf(hi ? sc.k1 : sc.k0, 1e-30f);
+      const float vs = fmaxf(hi ? sc.v1 : sc.v0, 1e-30f);
+      lvs = __builtin_amdgcn_logf(vs);
+      ivs = __builtin_amdgcn_rcpf(vs);
+    }
     // The softmax of step n and the P.V product of step n-1 (independent) run as
     // NSL + 1 phases, each holding a share of both: the product's MFMAs of one V
     // slice (the row sums first) and a piece of the softmax's VALU work, the V
@@ -415,10 +526,14 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
     // phase, so the compiler cannot regroup the MFMAs into one run and the VALU work
     // into another: inside a phase the matrix cores run the MFMAs while the vector
     // unit works through its piece.
-    const float c = d.qk_scale;  // softmax scale * log2(e) (> 0); m is kept in these units
-    u32x4 pn[RB], pnl[RB];  // P^T operands of step n: p (f16), or its hi and lo parts (bf16)
+    u32x4 pn[RB], pnl[RB];  // P^T operands of step n (and lo parts for bf16 pools)
     bool rescale = false;
     float alpha[RB], mx[RB], mnew[RB];
+    // 1-byte pools: this lane's sum of step n's weights (relative to the new max);
+    // added to lrow only after lrow has been rescaled to that max
+    float lstep[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) lstep[rb] = 0.f;
     // softmax pieces in order: local maxima (one per row block), the cross-lane max
     // and the running-max update (one per row block), then the weights and their
     // operands a half (4 keys) at a time
@@ -429,15 +544,14 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
         float v = fmaxf(s1[rb][0], s1[rb][1]);
         v = fmaxf(v, fmaxf(s1[rb][2], s1[rb][3]));
         v = fmaxf(v, fmaxf(s2[rb][0], s2[rb][1]));
-        mx[rb] = fmaxf(v, fmaxf(s2[rb][2], s2[rb][3]));
+        mx[rb] = fmaxf(v, fmaxf(s2[rb][2], s2[rb][3])) * c;  // c > 0 keeps the order
       } else if (k < 2 * RB) {
         const int rb = k - RB;
-        const float v = max_xor_rows<32>(max_xor_rows<16>(mx[rb]));
         // Lazy rescale: the running max moves only when a score exceeds it by more
         // than kLazy (log2 units), so p = 2^(s*c - m) stays below 2^kLazy, well
         // inside the range of the 16-bit P operand and of the fp32 sums; the result
         // does not depend on m (numerator and denominator carry the same factor).
-        const float mt = v * c;
+        const float mt = max_xor_rows<32>(max_xor_rows<16>(mx[rb]));
         const bool grow = mt > m[rb] + kLazy;
         mnew[rb] = grow ? mt : m[rb];
         rescale |= grow;
@@ -448,45 +562,42 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
         const f4_t &sv = half ? s2[rb] : s1[rb];
         float p[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) p[j] = fast_exp2(__builtin_fmaf(sv[j], c, -mnew[rb]));
-        p_operands_half<KV>(p, pn[rb], pnl[rb], half);
+        for (int j = 0; j < 4; ++j) p[j] = fast_exp2(__builtin_fmaf(sv[j], c, lvs - mnew[rb]));
+        if constexpr (Q8) lstep[rb] = __builtin_fmaf((p[0] + p[1]) + (p[2] + p[3]), ivs, lstep[rb]);
+        p_operands_half<MP, kSplit>(p, pn[rb], pnl[rb], half);
         // The operands are used only by the next step's product; without a use
         // here the compiler sinks their computation there, out of this phase.
         asm volatile("" ::"v"(pn[rb][2 * half]), "v"(pn[rb][2 * half + 1]));
-        if constexpr (kSplitP<KV>)
+        if constexpr (kSplit)
           asm volatile("" ::"v"(pnl[rb][2 * half]), "v"(pnl[rb][2 * half + 1]));
       }
     };
     const _Float16 *Vb = buf_of(i - 1) + L::kKHalves;  // step n-1's V
-    auto vread = [&](int sl) {
-      const int d0 = sl * 16 + vcol;
-      const _Float16 *vp = Vb + vrow * D + ((d0 >> 3) ^ v_swizzle<D>(vrow)) * 8 + (d0 & 7);
-      const u32x2 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 4 * D);
-      return u32x4{lo[0], lo[1], hi[0], hi[1]};
-    };
     constexpr int NPH = NSL + 1;
     u32x4 va[3];
 #pragma unroll
     for (int ph = 0; ph < NPH; ++ph) {
       if (ph == 0) {
-        va[0] = vread(0);
-        if (NSL > 1) va[1] = vread(1);
+        va[0] = vread_from(Vb, 0);
+        if (NSL > 1) va[1] = vread_from(Vb, 1);
       } else if (ph + 1 < NSL) {
-        va[(ph + 1) % 3] = vread(ph + 1);
+        va[(ph + 1) % 3] = vread_from(Vb, ph + 1);
       }
       if (ph == 0) {
+        if constexpr (!Q8) {
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          lsum[rb] = mfma32<KV>(ones, pp[rb], lsum[rb]);
-          if constexpr (kSplitP<KV>) lsum[rb] = mfma32<KV>(ones, ppl[rb], lsum[rb]);
+          for (int rb = 0; rb < RB; ++rb) {
+            lsum[rb] = mfma32<MP>(ones, pp[rb], lsum[rb]);
+            if constexpr (kSplit) lsum[rb] = mfma32<MP>(ones, ppl[rb], lsum[rb]);
+          }
         }
       } else {
         const int sl = ph - 1;
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) o[rb][sl] = mfma32<KV>(va[sl % 3], pp[rb], o[rb][sl]);
-        if constexpr (kSplitP<KV>) {
+        for (int rb = 0; rb < RB; ++rb) o[rb][sl] = mfma32<MP>(va[sl % 3], pp[rb], o[rb][sl]);
+        if constexpr (kSplit) {
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) o[rb][sl] = mfma32<KV>(va[sl % 3], ppl[rb], o[rb][sl]);
+          for (int rb = 0; rb < RB; ++rb) o[rb][sl] = mfma32<MP>(va[sl % 3], ppl[rb], o[rb][sl]);
         }
       }
 #pragma unroll
@@ -499,24 +610,32 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
       for (int rb = 0; rb < RB; ++rb) {
         const float f = fast_exp2(alpha[rb]);
         lsum[rb] *= f;
+        lrow[rb] *= f;
 #pragma unroll
         for (int sl = 0; sl < NSL; ++sl) o[rb][sl] *= f;
       }
     }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
+      if constexpr (Q8) lrow[rb] += lstep[rb];
       pp[rb] = pn[rb];
       ppl[rb] = pnl[rb];
     }
   };
 
   constexpr int kAhead = 2;  // a step's loads go out this many iterations before its scores
-  constexpr int U = L::kBufs;  // unroll: every unrolled step's buffers are compile-time
-  static_assert(kAhead + 2 <= L::kBufs, "buffers of the steps in flight, scored and deferred");
+  // unroll: a multiple of every ring (16-bit buffers, code buffers, scales), so every
+  // unrolled step's slots are compile-time
+  constexpr int U = Q8 ? 6 : L::kBufs;
+  static_assert(U % L::kBufs == 0 && U % (Q8 ? L::kCodeBufs : 1) == 0, "unroll cycles the rings");
+  static_assert(Q8 ? L::kBufs >= 3 : kAhead + 2 <= L::kBufs, "buffers of the steps in use");
+  constexpr int kScaleRing = Q8 ? kAhead + 1 : 1;  // 1-byte pools: scales of steps n .. n+kAhead
+  constexpr int kCB = Q8 ? L::kCodeBufs : 1;       // code buffers (none for 16-bit pools)
+  static_assert(U % kScaleRing == 0, "unroll cycles the scale ring");
   const int nsteps = (nkeys + kKeyStep - 1) / kKeyStep;
   // this wave's loads of kAhead - 1 steps: what may still be in flight when a step's
   // loads must have landed
-  using AheadLess1 = std::integral_constant<int, 2 * NL * (kAhead - 1)>;
+  using AheadLess1 = std::integral_constant<int, LPW * (kAhead - 1)>;
   // The q operands have landed before the first LDS-DMA load is issued: the
   // compiler's own waits for them would otherwise sit inside the step loop and,
   // counting loads it cannot see, drain the prefetch every time round.
@@ -527,24 +646,39 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
     for (int c = tid; c < L::kVHalves / 8; c += 256)
       *reinterpret_cast<u32x4 *>(Vz + 8 * c) = u32x4{0, 0, 0, 0};
   }
+  StepScale scl[kScaleRing];
 #pragma unroll
-  for (int i = 0; i < kAhead; ++i) dma_step(bt_load(i), i);  // clamped past the last step
+  for (int i = 0; i < kAhead; ++i) {  // clamped past the last step
+    const StepBt b = bt_load(i);
+    dma_step(b, Q8 ? i % kCB : i);
+    scl[i] = scale_load(b);
+  }
   StepBt bnext = bt_load(kAhead);
   wait_loads(AheadLess1{});
-  fix_tail(0, 0);
+  if constexpr (Q8)
+    convert_step(0, 0, 0);
+  else
+    fix_tail(0, 0);
   __syncthreads();
-  // iteration n (i = n mod U): issue step n+kAhead's loads, read the block-table
-  // entries of the step after, run step n (with the product of step n-1), then wait
-  // for step n+1's loads.  A wave whose rows end before the tile's last step runs
-  // its remaining steps fully masked (zero weights): it would otherwise wait at the
-  // barriers, and one code path keeps its registers within two waves per SIMD.
-  // Past the last step the loads repeat the last block into free buffers.
+  // iteration n (i = n mod U): issue step n+kAhead's loads (and read its scales),
+  // read the block-table entries of the step after, run step n (with the product of
+  // step n-1), then wait for step n+1's loads (and convert them, for 1-byte pools).
+  // A wave whose rows end before the tile's last step runs its remaining steps fully
+  // masked (zero weights): it would otherwise wait at the barriers, and one code path
+  // keeps its registers within two waves per SIMD.  Past the last step the loads
+  // repeat the last block into free buffers.
   auto iter = [&](int n, int i) {
-    dma_step(bnext, (i + kAhead) % L::kBufs);
+    dma_step(bnext, Q8 ? (i + kAhead) % kCB : (i + kAhead) % L::kBufs);
+    scl[(i + kAhead) % kScaleRing] = scale_load(bnext);
     bnext = bt_load(n + kAhead + 1);
-    full_step(i, n * kKeyStep);
+    full_step(i, n * kKeyStep, scl[i % kScaleRing]);
     wait_loads(AheadLess1{});  // step n+1's loads have landed; step n+2's may be in flight
-    if (n + 1 < nsteps) fix_tail(n + 1, (i + 1) % L::kBufs);
+    if (n + 1 < nsteps) {
+      if constexpr (Q8)
+        convert_step(n + 1, (i + 1) % L::kBufs, (i + 1) % kCB);
+      else
+        fix_tail(n + 1, (i + 1) % L::kBufs);
+    }
     __syncthreads();
   };
   int n0 = 0;
@@ -562,13 +696,21 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
   // ---- normalise and store: lane holds dims sl*16 + 4*g16 + i of query row c16 ----
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
+    float l;
+    if constexpr (Q8) {  // the row's sum over its four lanes (g16 = 0 .. 3)
+      l = lrow[rb];
+      l += __shfl_xor(l, 16, 64);
+      l += __shfl_xor(l, 32, 64);
+    } else {
+      l = lsum[rb][0];
+    }
     if (!row_ok[rb]) continue;
-    const float inv = 1.f / lsum[rb][0];
+    const float inv = 1.f / l;
 #pragma unroll
     for (int sl = 0; sl < NSL; ++sl)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        store_out<KV>(d.out, row_out[rb] + sl * 16 + 4 * g16 + i, o[rb][sl][i] * inv);
+        store_out<QT>(d.out, row_out[rb] + sl * 16 + 4 * g16 + i, o[rb][sl][i] * inv);
   }
 }
 
@@ -645,17 +787,18 @@ __global__ __launch_bounds__(256) void pa_mixed_prep_kernel(MixedArgs a) {
 // Grid (Hkv, items): the kv head is the fastest index, so with workgroups handed to
 // the 8 XCDs in turn, all tiles of one (sequence, kv head) run on one XCD (for
 // 8 kv heads; on 8 / Hkv of them otherwise) and share its L2 copy of their K/V.
-template <int KV, int D, int G>
+template <int KV, int QT, int D, int G>
 __global__ __launch_bounds__(256) void pa_prefill_tiles_kernel(MixedArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[PrefillLds<D>::kBytes];
+  __shared__ __attribute__((aligned(16)))
+  char smem[PrefillLds<D, KV == PA_FP8_E4M3 || KV == PA_I8>::kBytes];
   const int x = blockIdx.y, h = blockIdx.x;
   if (x >= a.hdr[0]) return;
   const int item = a.p_items[x];
-  prefill_tile<KV, D, G>(a, item >> kItemBits, h, item & ((1 << kItemBits) - 1), smem);
+  prefill_tile<KV, QT, D, G>(a, item >> kItemBits, h, item & ((1 << kItemBits) - 1), smem);
 }
 
-// ---- fallback for KV types without an MFMA tile path (fp32, fp8, int8): every
-// query row runs the decode partition path with its own causal length ----
+// ---- fp32 KV (no MFMA tile path): every query row runs the decode partition path
+// with its own causal length ----
 __device__ __forceinline__ void row_owner(const int32_t *qsl, const int32_t *seq_lens,
                                           int num_seqs, int t, int &s, int &n) {
   int lo = 0, hi = num_seqs;  // invariant: qsl[lo] <= t < qsl[hi]
@@ -692,7 +835,7 @@ template <int KV, int QT, int D, int G>
 static hipError_t launch_tiles(const MixedArgs &a, bool stream_loads, hipStream_t st) {
   hipLaunchKernelGGL(pa_mixed_prep_kernel, dim3(1), dim3(256), 0, st, a);
   dim3 grid(a.dec.num_kv_heads, a.p_bound);
-  hipLaunchKernelGGL((pa_prefill_tiles_kernel<KV, D, G>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((pa_prefill_tiles_kernel<KV, QT, D, G>), grid, dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_decode_stream(a.dec, KV, QT, D, G, a.num_seqs, stream_loads, st);
@@ -713,7 +856,7 @@ static hipError_t launch_rows(const MixedArgs &a, int num_rows, hipStream_t st) 
 template <int KV, int QT, int D>
 static hipError_t launch_g(const MixedArgs &a, int G, int num_rows, bool tiles, bool stream_loads,
                            hipStream_t st) {
-  constexpr bool kMfma = (KV == PA_F16 || KV == PA_BF16);
+  constexpr bool kMfma = KV != PA_F32;  // MFMA prefill tiles: 16-bit and 1-byte pools
 #define PA_CASE(g)                                                              \
   case g:                                                                       \
     if constexpr (kMfma) {                                                      \
@@ -738,7 +881,9 @@ static hipError_t launch_d(const MixedArgs &a, int D, int G, int num_rows, bool 
   return hipErrorInvalidValue;
 }
 
-bool mixed_uses_tiles(int kv_dtype) { return kv_dtype == PA_F16 || kv_dtype == PA_BF16; }
+bool mixed_uses_tiles(int kv_dtype) {
+  return kv_dtype == PA_F16 || kv_dtype == PA_BF16 || kv_dtype == PA_FP8_E4M3 || kv_dtype == PA_I8;
+}
 
 hipError_t launch_mixed(const MixedArgs &a, int kv_dtype, int q_dtype, int head_dim, int group,
                         int num_rows, bool stream_loads, hipStream_t st) {

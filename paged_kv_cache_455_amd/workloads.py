@@ -344,10 +344,17 @@ def mixed_batch(seed: int, n_chunks: int, chunk_len: int, prior_lo: int, prior_h
     bt, _ = _deal_tables(perm, nbs)
     T = int(qsl[-1])
     q = _cast(_normal(rng, (T, hq, d), div), qd)
-    k_pool = _float_pool(rng, nb, hkv, d, div, kv, bs=bs)
-    v_pool = _float_pool(rng, nb, hkv, d, div, kv, bs=bs)
-    k_new = _cast(_normal(rng, (T, hkv, d), div), kv)
-    v_new = _cast(_normal(rng, (T, hkv, d), div), kv)
+    if kv in QUANTISED:  # codes + per-(block, kv head) scales; new rows in q's dtype
+        k_pool, k_scale = _quantised_pool(rng, nb, hkv, d, div, kv, bs=bs)
+        v_pool, v_scale = _quantised_pool(rng, nb, hkv, d, div, kv, bs=bs)
+        k_new = _cast(_normal(rng, (T, hkv, d), div), qd)
+        v_new = _cast(_normal(rng, (T, hkv, d), div), qd)
+    else:
+        k_pool = _float_pool(rng, nb, hkv, d, div, kv, bs=bs)
+        v_pool = _float_pool(rng, nb, hkv, d, div, kv, bs=bs)
+        k_scale = v_scale = None
+        k_new = _cast(_normal(rng, (T, hkv, d), div), kv)
+        v_new = _cast(_normal(rng, (T, hkv, d), div), kv)
     if poison:
         used = _used_mask(bt, nb)
         _poison_unused(k_pool, used, kv)
@@ -356,7 +363,8 @@ def mixed_batch(seed: int, n_chunks: int, chunk_len: int, prior_lo: int, prior_h
         name=name, kind="mixed", kv_dtype=kv, q_dtype=qd, num_q_heads=hq, num_kv_heads=hkv,
         head_dim=d, scale=1.0 / math.sqrt(d), q=q, k_pool=k_pool, v_pool=v_pool,
         block_tables=torch.from_numpy(bt), seq_lens=torch.from_numpy(seq_lens),
-        query_start_loc=torch.from_numpy(qsl), k_new=k_new, v_new=v_new,
+        query_start_loc=torch.from_numpy(qsl), k_scale=k_scale, v_scale=v_scale,
+        k_new=k_new, v_new=v_new,
         extra={"n_chunks": len(priors), "chunk_len": chunk_len}, block_size=bs)
 
 

@@ -388,6 +388,40 @@ def test_mixed_full_size_peaked_every_row(kv):
     rows, ref = oracle_mixed(b)
     check_peaked(b, out, ref, "mixed full peaked")
 
+@pytest.mark.parametrize("kv,qd", [("fp8", "bf16"), ("fp8", "f16"), ("i8", "bf16"), ("i8", "f16")])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("g", [1, 2, 4, 8])
+def test_mixed_quantised_every_head_dim_and_group(kv, qd, d, g):
+    """Mixed steps on fp8 / int8 pools (codes with per-(block, kv head) scales, q in
+    f16 or bf16): unscaled N(0,1) data, chunks over priors at block edges (a 0-prior
+    chunk's first rows see 1, 2, 3 keys), ragged last tiles, decodes beside them,
+    NaN codes in every unused block; every row against the oracle on the same codes
+    and scales, at max(2e-2, one ulp of the output type)."""
+    hkv = 2
+    b = W.mixed_batch(360 + g + d, 5, 150, 0, 0, 6, 300.0, 1.0, 16, 1500, g * hkv, hkv, d, kv, qd,
+                      poison=True, priors=[0, 1, 16, 200, 700],
+                      name=f"quant-{kv}-{qd}-d{d}-g{g}")
+    b = poison_tails(b)
+    out = run_mixed(Dev(b))
+    torch.cuda.synchronize()
+    rows, ref = oracle_mixed(b)
+    assert np.array_equal(rows, np.arange(b.num_tokens))
+    check_peaked(b, out, ref, "mixed quantised")
+
+
+@pytest.mark.parametrize("kv", ["fp8", "i8"])
+def test_mixed_quantised_full_size_every_row(kv):
+    """The mixed step's full size (8 chunks x 512 over 0..2048 prior tokens + 256
+    lognormal decodes, 32 query / 8 kv heads, head_dim 128) on an fp8 / int8 pool with
+    bf16 queries, unscaled N(0,1) data: all 4352 rows against the oracle."""
+    b = W.mixed_batch(4, 8, 512, 0, 2048, 256, 600.0, 1.0, 16, 8192, 32, 8, 128, kv, "bf16",
+                      name=f"mixed-full-{kv}")
+    out = run_mixed(Dev(b))
+    torch.cuda.synchronize()
+    rows, ref = oracle_mixed(b)
+    check_peaked(b, out, ref, "mixed full quantised")
+
+
 def test_mixed_full_step_every_row():
     b = W.mixed_step()
     say("mixed full", b.name)
