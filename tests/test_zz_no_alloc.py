@@ -6,6 +6,7 @@ against pa_decode_append (which takes a caller workspace) on an identical copy
 of the pools: outputs, pools and slots must be bit-identical, since both run the
 same kernels; the second call runs over whatever the first left in the array.
 """
+import gc
 import math
 
 import numpy as np
@@ -40,11 +41,19 @@ def _compare(b):
                                slot_mapping=slotsA)
     outB = torch.full_like(q, float("nan"))
     torch.cuda.synchronize()
-    before = torch.cuda.memory_allocated()
-    pa.pa_decode_append_noalloc(poolB, q, kn, vn, bt, lens, b.max_seq_len, b.scale, outB,
-                                slot_mapping=slotsB)
-    torch.cuda.synchronize()
-    assert torch.cuda.memory_allocated() == before
+    # Tensors of earlier tests that only the cycle collector frees would otherwise
+    # be freed at an arbitrary point, inside the measured call included.
+    gc.collect()
+    gc.disable()
+    try:
+        before = torch.cuda.memory_allocated()
+        pa.pa_decode_append_noalloc(poolB, q, kn, vn, bt, lens, b.max_seq_len, b.scale, outB,
+                                    slot_mapping=slotsB)
+        torch.cuda.synchronize()
+        after = torch.cuda.memory_allocated()
+    finally:
+        gc.enable()
+    assert after == before
     assert torch.equal(slotsA, slotsB), "slots differ"
     for x, y in ((poolA.k, poolB.k), (poolA.v, poolB.v)):
         assert torch.equal(_bits(x), _bits(y)), "pools differ"
