@@ -177,15 +177,38 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "paged_kv_cache_455_amd", "csrc")
 
 
+def _code_tokens(text):
+    """C++ source with its comments and whitespace runs removed (string and
+    character literals kept whole), so that an edit of comments alone leaves it
+    unchanged."""
+    import re
+    tok = re.compile(r'"(?:\\.|[^"\\])*"|\'(?:\\.|[^\'\\])*\'|//[^\n]*|/\*.*?\*/|\s+', re.S)
+    out, pos, gap = [], 0, False
+    for m in tok.finditer(text):
+        if m.start() > pos:  # code between the matches
+            out.append((" " if gap and out else "") + text[pos:m.start()])
+            gap = False
+        if m.group(0)[0] in "\"'":
+            out.append((" " if gap and out else "") + m.group(0))
+            gap = False
+        else:  # a comment or whitespace: at most one space in its place
+            gap = True
+        pos = m.end()
+    if pos < len(text):
+        out.append((" " if gap and out else "") + text[pos:])
+    return "".join(out)
+
+
 def kernel_source_hash():
-    """sha256 over the HIP sources; a profiled byte count is valid only for this hash."""
+    """sha256 over the HIP sources' code (comments and layout ignored); a profiled
+    byte count is valid only for this hash."""
     import hashlib
     h = hashlib.sha256()
     for f in sorted(os.listdir(CSRC)):
         if f.endswith((".h", ".hip")):
             h.update(f.encode())
-            with open(os.path.join(CSRC, f), "rb") as fh:
-                h.update(fh.read())
+            with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+                h.update(_code_tokens(fh.read()).encode())
     return h.hexdigest()
 
 

@@ -585,10 +585,11 @@ pa_status_t pa_decode_append_noalloc(const pa_kv_pool_t *pool, const void *q, in
                           scale, ws, kScratchBytes, stream);
 }
 
-// Workspace of the mixed step.  f16/bf16 KV: a header int, the prefill tile list,
-// then the balanced-split decode workspace of the one-token rows (pieces for every
-// sequence, as pa_decode lays them out).  Other KV types run every query row
-// through the partitioned decode path (per-row partitions).
+// Workspace of the mixed step.  f16, bf16, fp8 and int8 KV (MFMA prefill tiles): a
+// header int, the prefill tile list, then the balanced-split decode workspace of
+// the one-token rows (pieces for every sequence, as pa_decode lays them out).  fp32
+// KV runs every query row through the partitioned decode path (per-row
+// partitions).
 struct MixedLayout {
   size_t hdr_off, p_off, acc_off, m_off, l_off, stream_off, total;
   WsLayout stream;  // offsets relative to stream_off

@@ -49,8 +49,9 @@ struct DecodeArgs {
 };
 
 struct MixedArgs {
-  DecodeArgs dec;       // pools, q/out, tables, seq_lens (as ctx); for f16/bf16 KV also the
-                        // balanced-split decode of the one-token rows (dec.qsl set)
+  DecodeArgs dec;       // pools, q/out, tables, seq_lens (as ctx); with the MFMA tiles (all
+                        // but fp32 KV) also the balanced-split decode of the one-token rows
+                        // (dec.qsl set)
   const int32_t *qsl;   // [num_seqs + 1]
   int32_t *hdr;         // [1]: prefill tiles listed (written by the prep kernel)
   int32_t *p_items;     // [p_bound]
