@@ -202,6 +202,23 @@ def test_decode_peaked_data_within_one_ulp(kv):
     assert np.all(err <= ulp + 1e-6), float(np.max(err / (ulp + 1e-6)))
 
 
+@pytest.mark.parametrize("kv,qd,hq", [("f16", "f16", 32), ("bf16", "bf16", 32), ("fp8", "bf16", 64),
+                                       ("i8", "f16", 64)])
+def test_decode_one_very_long_context(kv, qd, hq):
+    """The longest context here: one sequence of 131072 tokens beside two short ones,
+    8 kv heads, head_dim 128.  Each of its kv heads' segments spans about a hundred
+    waves of the balanced split, so the merge combines more pieces than a wave has
+    lanes.  Unscaled N(0,1) data at softmax scale 1 (scores spread by ~11), so the
+    few largest scores decide each output and every piece's weight matters; every
+    row against the oracle at max(tolerance, one ulp of the output)."""
+    b = W.decode_batch(77, [131072, 5, 1000], hq, 8, 128, kv, qd, scale=1.0, poison=True,
+                       name=f"ctx131072-{kv}")
+    b = poison_tails(b)
+    out = run_decode(Dev(b))
+    torch.cuda.synchronize()
+    check_peaked(b, out, oracle_decode_rows(b), "decode 131072")
+
+
 @pytest.mark.parametrize("kv", ["fp8", "i8"])
 def test_decode_long_quantised_small(kv):
     check_decode(W.long_quantised(kv, batch=2, ctx=4100))
