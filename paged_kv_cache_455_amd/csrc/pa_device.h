@@ -175,6 +175,23 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Maxima as the bare v_max / v_max3 instructions.  Written through fmaxf, every
+// operand that the compiler cannot prove canonical (an MFMA result, a value moved
+// across lanes) first gets a v_max_f32 x, x, x of its own, which quiets a
+// signalling NaN under the IEEE mode the kernels run in.  The callers' operands
+// are scores and running maxima -- finite, or -inf where masked by a select --
+// for which the bare instruction is the same maximum.
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // max(x, x of lane ^ MASK) for MASK 16 or 32: the row swap leaves the lane's own
 // value in one output and its partner's in the other, so no select is needed.
 template <int MASK>
@@ -191,7 +208,7 @@ __device__ __forceinline__ float max_xor_rows(float x) {
     a = r[0];
     b = r[1];
   }
-  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  return max_raw(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

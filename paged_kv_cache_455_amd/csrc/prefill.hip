@@ -541,10 +541,10 @@ __device__ __forceinline__ void prefill_tile(const MixedArgs &a, int s, int h, i
     auto softmax_piece = [&](int k) {
       if (k < RB) {
         const int rb = k;
-        float v = fmaxf(s1[rb][0], s1[rb][1]);
-        v = fmaxf(v, fmaxf(s1[rb][2], s1[rb][3]));
-        v = fmaxf(v, fmaxf(s2[rb][0], s2[rb][1]));
-        mx[rb] = fmaxf(v, fmaxf(s2[rb][2], s2[rb][3])) * c;  // c > 0 keeps the order
+        const float v = max3_raw(max3_raw(s1[rb][0], s1[rb][1], s1[rb][2]),
+                                 max3_raw(s1[rb][3], s2[rb][0], s2[rb][1]),
+                                 max_raw(s2[rb][2], s2[rb][3]));
+        mx[rb] = v * c;  // c > 0 keeps the order
       } else if (k < 2 * RB) {
         const int rb = k - RB;
         // Lazy rescale: the running max moves only when a score exceeds it by more
