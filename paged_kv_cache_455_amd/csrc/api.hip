@@ -123,8 +123,11 @@ WsLayout ws_layout(int64_t rows, int num_q_heads, int head_dim, int max_parts) {
 constexpr int kMinTilesPerWave = 8;
 // Cost, in tiles, of starting a (sequence, kv head) segment in the balanced split
 // (emitting its result, switching q): 0 -> 4 took the Llama-3-8B-shaped decode layer
-// from 110 to 103 us and the mixed step's lognormal decode rows from 224 to 190 us.
-constexpr int kSegCost = 4;
+// from 110 to 103 us and the mixed step's lognormal decode rows from 224 to 190 us;
+// once the emit became a reduce-scatter (0.55 instead of 1.8 us per segment end),
+// 2 beat 1, 3 and 4 (stream kernel 95.0 vs 95.9 us at 4, mixed decode rows 185.5 vs
+// 188.0 us, prefix-sharing decode 162.8 vs 164.2 us).
+constexpr int kSegCost = 2;
 
 int stream_pieces(int max_ctx) {
   const int max_blocks = (max_ctx + kTileRows - 1) / kTileRows;

@@ -602,6 +602,14 @@ __device__ __forceinline__ int decode_len(const DecodeArgs &a, int s) {
 __device__ __forceinline__ int64_t decode_row(const DecodeArgs &a, int s) {
   return a.qsl != nullptr ? a.qsl[s] : s;
 }
+// The same for a wave-uniform s, by a scalar load: its wait counts scalar loads only,
+// so it does not drain the K/V loads in flight (a vector load behind the test of
+// qsl makes the compiler wait for every vector load on both paths).
+__device__ __forceinline__ int64_t decode_row_uniform(const DecodeArgs &a, int s) {
+  if (a.qsl == nullptr) return s;
+  using cint = const __attribute__((address_space(4))) int;
+  return *(cint *)(a.qsl + __builtin_amdgcn_readfirstlane(s));
+}
 
 // Write this wave's state for (s, kv head h): normalised output when single,
 // else the partial for `piece`.  Lanes of token group 0 hold every column chunk.
@@ -631,6 +639,66 @@ __device__ __forceinline__ void emit_segment(const DecodeArgs &a, DecodeState<KV
       if (c == 0) {
         a.ws_m[r] = st.m[g];
         a.ws_l[r] = st.l[g];
+      }
+    }
+  }
+}
+
+// emit_segment for waves of four token groups (rows of 16 lanes) and a group of
+// 4 or 8 heads, by reduce-scatter instead of the all-reduce above: step 1 merges
+// rows r and r^1, the even row keeping heads [0, G/2) and the odd row heads
+// [G/2, G); step 2 merges the halves, the lower keeping the first half of what is
+// left.  Each lane ends with G/4 heads (head q + G/4*(r>>1) + G/2*(r&1) in slot q)
+// for its column chunk, and every lane stores: a quarter of the cross-lane moves
+// and merge arithmetic of the all-reduce, which kept four copies of everything.
+template <int KV, int QT, int D, int G>
+__device__ __forceinline__ void emit_segment_rs(const DecodeArgs &a, DecodeState<KV, QT, D, G> &st,
+                                                int s, int h, bool single, int piece, int lane) {
+  constexpr int EPC = Geom<KV, D>::EPC, G2 = G / 2, G4 = G / 4;
+  static_assert(Geom<KV, D>::LPT == 16 && G % 4 == 0, "four token rows, G a multiple of 4");
+  // merge state (mx, lx, ax) with (my, ly, ay) into x
+  auto merge = [](float &mx, float my, float &lx, float ly, float *ax, const float *ay) {
+    const float mn = fmaxf(mx, my);
+    const float wx = fast_exp2(mx - mn), wy = fast_exp2(my - mn);
+    mx = mn;
+    lx = lx * wx + ly * wy;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) ax[e] = ax[e] * wx + ay[e] * wy;
+  };
+#pragma unroll
+  for (int p = 0; p < G2; ++p) {
+    swap_rows<16>(st.m[p], st.m[p + G2]);
+    swap_rows<16>(st.l[p], st.l[p + G2]);
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) swap_rows<16>(st.acc[p][e], st.acc[p + G2][e]);
+    merge(st.m[p], st.m[p + G2], st.l[p], st.l[p + G2], st.acc[p], st.acc[p + G2]);
+  }
+#pragma unroll
+  for (int q = 0; q < G4; ++q) {
+    swap_rows<32>(st.m[q], st.m[q + G4]);
+    swap_rows<32>(st.l[q], st.l[q + G4]);
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) swap_rows<32>(st.acc[q][e], st.acc[q + G4][e]);
+    merge(st.m[q], st.m[q + G4], st.l[q], st.l[q + G4], st.acc[q], st.acc[q + G4]);
+  }
+  const int r = lane >> 4, c = lane & 15;
+  const int g0 = G4 * (r >> 1) + G2 * (r & 1);
+#pragma unroll
+  for (int q = 0; q < G4; ++q) {
+    const int g = g0 + q;
+    if (single) {
+      const float inv = 1.f / st.l[q];
+      const int64_t o = (decode_row_uniform(a, s) * a.num_q_heads + h * G + g) * D + c * EPC;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) store_out<QT>(a.out, o + e, st.acc[q][e] * inv);
+    } else {
+      const int64_t w = ((int64_t)s * a.num_q_heads + h * G + g) * a.max_parts + piece;
+      float *dst = a.ws_acc + w * D + c * EPC;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) dst[e] = st.acc[q][e];
+      if (c == 0) {
+        a.ws_m[w] = st.m[q];
+        a.ws_l[w] = st.l[q];
       }
     }
   }
@@ -969,7 +1037,10 @@ struct GenericPath {
   }
   __device__ __forceinline__ void emit(const StreamSeg &sg, bool single, int piece) {
     if constexpr (kFast) fast_to_generic(st, fs);
-    emit_segment<KV, QT, D, G>(a, st, sg.s, sg.h, single, piece, lane);
+    if constexpr (LPT == 16 && G % 4 == 0)
+      emit_segment_rs<KV, QT, D, G>(a, st, sg.s, sg.h, single, piece, lane);
+    else
+      emit_segment<KV, QT, D, G>(a, st, sg.s, sg.h, single, piece, lane);
   }
 };
 

@@ -211,6 +211,26 @@ __device__ __forceinline__ float max_xor_rows(float x) {
   return max_raw(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
 }
 
+// Row swap of two values (MASK 16: rows r and r^1; MASK 32: halves): afterwards x
+// holds, in the even row (lower half), its own x and in the odd row (upper half) the
+// partner's y, and y the partner's x in the even row and its own y in the odd one.
+// So x and y are the two states of one value pair-wise: x (+) y merges x's value in
+// the even rows and y's in the odd rows, with no select.
+template <int MASK>
+__device__ __forceinline__ void swap_rows(float &x, float &y) {
+  static_assert(MASK == 16 || MASK == 32, "row swaps only");
+  const unsigned u = __builtin_bit_cast(unsigned, x), v = __builtin_bit_cast(unsigned, y);
+  if constexpr (MASK == 16) {
+    auto r = __builtin_amdgcn_permlane16_swap(u, v, false, false);
+    x = __builtin_bit_cast(float, (unsigned)r[0]);
+    y = __builtin_bit_cast(float, (unsigned)r[1]);
+  } else {
+    auto r = __builtin_amdgcn_permlane32_swap(u, v, false, false);
+    x = __builtin_bit_cast(float, (unsigned)r[0]);
+    y = __builtin_bit_cast(float, (unsigned)r[1]);
+  }
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 }  // namespace pa
