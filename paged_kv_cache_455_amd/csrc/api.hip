@@ -142,7 +142,7 @@ WsLayout stream_layout(int64_t num_seqs, int num_q_heads, int head_dim, int max_
   w.m_off = align256(n_ml * head_dim * sizeof(float));
   w.l_off = w.m_off + align256(n_ml * sizeof(float));
   w.hdr_off = w.l_off + align256(n_ml * sizeof(float));
-  w.total = w.hdr_off + align256((size_t)(num_seqs + 1) * sizeof(int32_t));
+  w.total = w.hdr_off + align256((size_t)(num_seqs + 2) * sizeof(int32_t));
   return w;
 }
 

@@ -569,9 +569,11 @@ __device__ __forceinline__ void merge_partitions(const DecodeArgs &a, int r, int
 //   [Hkv*cum[s] + h*nblk_s, Hkv*cum[s] + (h+1)*nblk_s).
 // Wave w of the grid takes the tiles [w*tpw, (w+1)*tpw), tpw = max(min_tpw,
 // ceil(T / waves)): every wave streams the same number of K/V bytes whatever the
-// context lengths.  A wave emits one result per (sequence, kv head) segment it
-// touches: the final output when it owns the whole segment, else a partial
-// (m, l, acc) for "piece" w - first_wave(segment), combined by the merge kernel.
+// context lengths (with two workgroups per CU, the first round's waves a few
+// percent more and the second round's as many fewer; see stream_range).  A wave
+// emits one result per (sequence, kv head) segment it touches: the final output
+// when it owns the whole segment, else a partial (m, l, acc) for "piece"
+// w - first_wave(segment), combined by the merge kernel.
 
 __device__ __forceinline__ int wave_max_i(int x) {
 #pragma unroll
@@ -727,8 +729,21 @@ struct SeqWindow {
   }
 };
 
+// The split of the cost units over the waves: waves [0, H) take t1 units each and
+// waves [H, W) t2 (t1 = t2, H = W without a skew).
+struct SplitGeom {
+  int t1, t2, H;
+  __device__ __forceinline__ int start(int w) const {
+    return w < H ? w * t1 : H * t1 + (w - H) * t2;
+  }
+  __device__ __forceinline__ int wave_of(int u) const {  // the wave owning unit u
+    const int b = H * t1;
+    return u < b ? u / t1 : H + (u - b) / t2;
+  }
+};
+
 struct StreamRange {
-  int tpw;        // cost units per wave
+  SplitGeom sp;   // cost units per wave
   int n;          // tiles of the wave
   int j;          // block of the wave's first tile inside its segment
   StreamSeg seg;  // the first tile's segment
@@ -757,8 +772,9 @@ __device__ __forceinline__ void next_sequence(const DecodeArgs &a, SeqWindow &wi
 // at cum_s + h*L_s + seg_cost + j; a wave owns the tiles whose units fall in its
 // range.
 //
-// stream_range counts the batch's cost, records tpw and every sequence's first
-// cost unit (wave 0 does), finds wave w's first tile and counts its tiles.  False
+// stream_range counts the batch's cost, records the units per wave (both rounds)
+// and every sequence's first cost unit (wave 0 does), finds wave w's first tile
+// and counts its tiles.  False
 // when the wave has no tiles.  Everything it returns is wave-uniform and taken
 // from lanes by readlane, so the compiler keeps the tile cursor in scalar
 // registers: block-table entries, context lengths and scales are then scalar loads,
@@ -789,17 +805,28 @@ __device__ __forceinline__ bool stream_range(const DecodeArgs &a, int w, int lan
     if (i * kWave < S) held_incl[i] = scan_window(i * kWave, held_n[i]);
   for (int c0 = kHeld * kWave; c0 < S; c0 += kWave)
     scan_window(c0, c0 + lane < S ? decode_len(a, c0 + lane) : 0);
-  r.tpw = max(a.min_tpw, (TC + a.num_waves - 1) / a.num_waves);
-  // A segment of nblk tiles meets at most floor((nblk - 1) / tpw) + 2 waves; so
-  // with tpw >= ceil(max nblk / (max_parts - 1)) its pieces fit the workspace's
+  const int base = max(a.min_tpw, (TC + a.num_waves - 1) / a.num_waves);
+  // A segment of nblk tiles meets at most floor((nblk - 1) / t) + 2 waves of t units
+  // or more; so with t >= ceil(max nblk / (max_parts - 1)) its pieces fit the workspace's
   // max_parts rows whatever the lengths (max_parts >= 2 by construction), also
   // when the host's length bound is low or a captured step is replayed on
   // longer contexts.
   mxnb = wave_max_i(mxnb);
-  r.tpw = max(r.tpw, (mxnb + a.max_parts - 2) / (a.max_parts - 1));
-  if (w == 0 && lane == 0) a.hdr[0] = r.tpw;
-  const int t = w * r.tpw;
-  const int tend = min(t + r.tpw, TC);
+  const int bound = (mxnb + a.max_parts - 2) / (a.max_parts - 1);
+  // With two workgroups per CU the second wave of each SIMD issues behind the first
+  // and streams slower, so the first round (waves [0, W/2): the grid's first
+  // workgroups) takes d units more and the second d fewer; W/2 (t1 + t2) = W base
+  // still covers TC (W is even), and t2 >= bound keeps the pieces bound.
+  const int d = (base * a.skew) >> 8;
+  r.sp.t1 = max(base + d, bound);
+  r.sp.t2 = max(base - d, bound);
+  r.sp.H = a.skew > 0 ? a.num_waves / 2 : a.num_waves;
+  if (w == 0 && lane == 0) {
+    a.hdr[0] = r.sp.t1;
+    a.hdr[1 + S] = r.sp.t2;
+  }
+  const int t = r.sp.start(w);
+  const int tend = min(t + (w < r.sp.H ? r.sp.t1 : r.sp.t2), TC);
   if (t >= tend) return false;
 
   // locate the sequence holding unit t (a hit always comes: t < TC)
@@ -871,10 +898,10 @@ __device__ __forceinline__ void stream_step(const DecodeArgs &a, SeqWindow &win,
 }
 
 // True when one wave owns all of sg's tiles; piece = this wave's index among them.
-__device__ __forceinline__ bool stream_single(const DecodeArgs &a, const StreamSeg &sg, int tpw,
-                                              int w, int &piece) {
+__device__ __forceinline__ bool stream_single(const DecodeArgs &a, const StreamSeg &sg,
+                                              const SplitGeom &sp, int w, int &piece) {
   const int first = sg.cum + sg.h * (sg.nblk + a.seg_cost) + a.seg_cost;  // first tile's unit
-  const int wfirst = first / tpw, wlast = (first + sg.nblk - 1) / tpw;
+  const int wfirst = sp.wave_of(first), wlast = sp.wave_of(first + sg.nblk - 1);
   piece = w - wfirst;
   return wfirst == wlast;
 }
@@ -920,7 +947,7 @@ __device__ __forceinline__ void stream_run(const DecodeArgs &a, P &path, int w, 
     path.compute(cur, masked ? sg0.tail : kBlock, masked);
     if (j0 == sg0.nblk - 1 || !has_next) {
       int piece;
-      const bool single = stream_single(a, sg0, rg.tpw, w, piece);
+      const bool single = stream_single(a, sg0, rg.sp, w, piece);
       path.emit(sg0, single, piece);
       if (has_next) path.begin_segment();
     }
@@ -1375,9 +1402,10 @@ __device__ __forceinline__ void merge_stream(const DecodeArgs &a, int s, int hq,
   const int h = hq / G;
   if (a.k_new != nullptr && hq % G == 0) append_new_row<D, dtype_bytes(QT)>(a, s, h, n, lane);
   const int nblk = (n + kBlock - 1) / kBlock;
-  const int tpw = a.hdr[0];  // cost units per wave; the split is described at stream_range
+  // the split as stream_range made it
+  const SplitGeom sp{a.hdr[0], a.hdr[1 + a.num_seqs], a.skew > 0 ? a.num_waves / 2 : a.num_waves};
   const int seg0 = a.hdr[1 + s] + h * (nblk + a.seg_cost) + a.seg_cost;
-  const int pieces = (seg0 + nblk - 1) / tpw - seg0 / tpw + 1;
+  const int pieces = sp.wave_of(seg0 + nblk - 1) - sp.wave_of(seg0) + 1;
   if (pieces <= 1) return;
   const int64_t r0 = ((int64_t)s * a.num_q_heads + hq) * a.max_parts;
   constexpr int PER = (D + kWave - 1) / kWave;  // output elements per lane

@@ -35,29 +35,44 @@ static constexpr auto stream_kernel() {
     return pa_decode_stream_kernel<KV, QT, D, G, NT>;
 }
 
-// Workgroups of one balanced-split kernel instantiation that fit on the device at once.
+// Workgroups of one balanced-split kernel instantiation that fit on the device at
+// once, and how many of them share a CU.
+struct Residency {
+  int groups, per_cu;
+};
 template <int KV, int QT, int D, int G, bool NT>
-static int resident_groups() {
-  static int cached = 0;  // one value per instantiation
-  if (cached > 0) return cached;
+static Residency resident_groups() {
+  static Residency cached{0, 0};  // one value per instantiation
+  if (cached.groups > 0) return cached;
   auto kernel = stream_kernel<KV, QT, D, G, NT>();
   int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipGetDevice(&dev) != hipSuccess) return Residency{0, 0};
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return Residency{0, 0};
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kDecodeWaves * kWave, 0) !=
       hipSuccess)
-    return 0;
-  cached = cus * (per_cu > 0 ? per_cu : 1);
+    return Residency{0, 0};
+  per_cu = per_cu > 0 ? per_cu : 1;
+  cached = Residency{cus * per_cu, per_cu};
   return cached;
 }
+
+// Two workgroups per CU: the waves of the grid's second round (the second wave on
+// each SIMD) stream slower than the first's, which the instruction arbiter serves
+// first; per-wave timestamps of the 16 x 32768-token fp8 decode put their median
+// end 5-17 us later.  The first round takes skew/256 of its share more, the second
+// as much less.
+constexpr int kTwoRoundSkew = 6;
 
 template <int KV, int QT, int D, int G, bool NT>
 static hipError_t launch_stream_kg(DecodeArgs a, int num_seqs, hipStream_t st) {
   auto kern = stream_kernel<KV, QT, D, G, NT>();
   // one workgroup per resident slot: every wave streams one equal share of the work
-  const int groups = resident_groups<KV, QT, D, G, NT>();
+  const Residency res = resident_groups<KV, QT, D, G, NT>();
+  const int groups = res.groups;
   if (groups <= 0) return hipErrorInvalidDeviceFunction;
   a.num_waves = groups * kDecodeWaves;
+  a.skew = res.per_cu == 2 ? kTwoRoundSkew : 0;
   hipLaunchKernelGGL(kern, dim3(groups), dim3(kDecodeWaves * kWave), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -28,11 +28,14 @@ struct DecodeArgs {
   int32_t max_parts;    // partitions (or pieces) of the longest context
   float qk_scale;       // softmax scale * log2(e)
   // balanced split: waves share the work evenly; see decode_stream
-  int32_t *hdr;         // [1 + num_seqs]: tiles per wave, then each sequence's first block index
+  int32_t *hdr;         // [2 + num_seqs]: cost units per first-round wave, each sequence's
+                        // first cost unit, cost units per later wave
   int32_t num_seqs;
   int32_t num_waves;    // waves launched
   int32_t min_tpw;      // lower bound on cost units per wave
   int32_t seg_cost;     // cost units charged for each (sequence, kv head) segment start
+  int32_t skew;         // two workgroups per CU: the first round's waves take tpw + d cost
+                        // units and the second round's tpw - d, d = tpw * skew / 256
   int32_t bs_shift;     // log2(block size / 16): tiles of 16 rows per block, as a shift
   // mixed step: [num_seqs + 1] query starts; only q_len == 1 sequences are decoded,
   // sequence s's query/output row being qsl[s] (nullptr: every sequence, row s)
