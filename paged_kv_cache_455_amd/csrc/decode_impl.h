@@ -1384,8 +1384,8 @@ __device__ __forceinline__ void append_new_row(const DecodeArgs &a, int s, int h
 
 // Second pass of the balanced split.  One wave per (sequence s, query head hq):
 // lane p reads piece p's (m, l) (all pieces in flight at once), wave reductions
-// give M = max_p m_p and L = sum_p 2^(m_p - M) l_p, then every lane combines its
-// output elements d, issuing the pieces' acc loads eight at a time:
+// give M = max_p m_p and L = sum_p 2^(m_p - M) l_p, then the pieces' acc rows come
+// in 16-byte lane slices, several pieces per wave-wide load, and are combined as
 //   out[d] = sum_p 2^(m_p - M) acc_p[d] / L.
 // Nothing to do where one wave owned the whole segment (pieces == 1).
 template <int QT, int D>
@@ -1408,23 +1408,30 @@ __device__ __forceinline__ void merge_stream(const DecodeArgs &a, int s, int hq,
   const int pieces = sp.wave_of(seg0 + nblk - 1) - sp.wave_of(seg0) + 1;
   if (pieces <= 1) return;
   const int64_t r0 = ((int64_t)s * a.num_q_heads + hq) * a.max_parts;
-  constexpr int PER = (D + kWave - 1) / kWave;  // output elements per lane
-  constexpr int PB = 8;                         // pieces whose acc loads are in flight together
-  // First batch of loads: (m, l) of every piece (lane p) and the acc of the first PB pieces
-  // (the acc loads do not wait for the weights).
+  // acc: each wave-wide load brings PPL whole pieces, lane l taking dims
+  // 4*(l % LP) .. +3 of piece PPL*j + l / LP (16 bytes a lane), so the NB loads in
+  // flight cover PPL*NB pieces (16 at D = 128): one round trip for the pieces of a
+  // long context's segment instead of one per eight.
+  constexpr int LP = D / 4, PPL = kWave / LP, NB = 8;
+  static_assert(D % 4 == 0 && kWave % LP == 0, "head_dim splits into 16-byte lane slices");
+  const int sub = lane / LP, dq = 4 * (lane % LP);
+  // First batch of loads: (m, l) of every piece (lane p) and the acc of the first
+  // PPL*NB pieces (the acc loads do not wait for the weights).
   float mp = kNegBig, lp = 0.f;
   if (lane < pieces) {
     mp = a.ws_m[r0 + lane];
     lp = a.ws_l[r0 + lane];
   }
-  float v[PB][PER];
+  f4v_t v[NB];
+  auto load_acc = [&](int p0) {
 #pragma unroll
-  for (int j = 0; j < PB; ++j)
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int d = lane + i * kWave;
-      v[j][i] = (j < pieces && d < D) ? a.ws_acc[(r0 + j) * D + d] : 0.f;
+    for (int j = 0; j < NB; ++j) {
+      const int p = p0 + PPL * j + sub;
+      v[j] = p < pieces ? *reinterpret_cast<const f4v_t *>(a.ws_acc + (r0 + p) * D + dq)
+                        : f4v_t{0.f, 0.f, 0.f, 0.f};
     }
+  };
+  load_acc(0);
   float M = mp;
   for (int p = lane + kWave; p < pieces; p += kWave) M = fmaxf(M, a.ws_m[r0 + p]);
   M = fmaxf(M, xor_lanes<1>(M));
@@ -1437,33 +1444,28 @@ __device__ __forceinline__ void merge_stream(const DecodeArgs &a, int s, int hq,
   for (int p = lane + kWave; p < pieces; p += kWave) L += fast_exp2(a.ws_m[r0 + p] - M) * a.ws_l[r0 + p];
   L = group_sum<64>(L);
   const float invL = 1.f / L;
-  float acc[PER];
+  f4v_t acc = f4v_t{0.f, 0.f, 0.f, 0.f};
+  for (int p0 = 0; p0 < pieces; p0 += PPL * NB) {
+    if (p0 > 0) load_acc(p0);
 #pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  for (int p0 = 0; p0 < pieces; p0 += PB) {
-    if (p0 > 0) {
-#pragma unroll
-      for (int j = 0; j < PB; ++j)
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-          const int d = lane + i * kWave;
-          v[j][i] = (p0 + j < pieces && d < D) ? a.ws_acc[(r0 + p0 + j) * D + d] : 0.f;
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < PB; ++j) {
-      // weight of piece p0 + j: lane (p0 + j) % 64 holds its m when p0 + j < 64
-      const int p = p0 + j;
-      const float mpj = p < kWave ? __shfl(mp, p, kWave) : (p < pieces ? a.ws_m[r0 + p] : kNegBig);
-      const float wt = p < pieces ? fast_exp2(mpj - M) : 0.f;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] += wt * v[j][i];
+    for (int j = 0; j < NB; ++j) {
+      // weight of this lane's piece p: lane p holds its m when p < 64
+      const int p = p0 + PPL * j + sub;
+      const float mpj = __shfl(mp, p & (kWave - 1), kWave);
+      const float mq = p < kWave ? mpj : (p < pieces ? a.ws_m[r0 + p] : kNegBig);
+      const float wt = p < pieces ? fast_exp2(mq - M) : 0.f;
+      acc += wt * v[j];
     }
   }
+  // add up the PPL lane groups that hold the same dims
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int d = lane + i * kWave;
-    if (d < D) store_out<QT>(a.out, o + d, acc[i] * invL);
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (LP <= 16) acc[i] += xor_lanes<16>(acc[i]);
+    acc[i] += xor_lanes<32>(acc[i]);
+  }
+  if (lane < LP) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) store_out<QT>(a.out, o + dq + i, acc[i] * invL);
   }
 }
 
