@@ -44,8 +44,8 @@ def run_decode(d: Dev, out=None):
     return pa.pa_decode(d.pool, d.q, d.bt, d.lens, b.max_seq_len, b.scale, out=out)
 
 
-def check_decode(b, rows=None, tol=None):
-    d = Dev(b)
+def check_decode(b, rows=None, tol=None, shared_blocks=None):
+    d = Dev(b, shared_blocks=shared_blocks)
     out = run_decode(d)
     torch.cuda.synchronize()
     rows = list(range(b.num_seqs)) if rows is None else rows
@@ -150,6 +150,26 @@ def test_decode_shapes_ragged(kv, qd, hq, hkv, hd):
     b = W.decode_batch(hq * 7 + hd, ctx, hq, hkv, hd, kv, qd, poison=True, div=hd ** 0.5,
                        name=f"ragged-{kv}-{qd}-{hq}x{hkv}x{hd}")
     check_decode(poison_tails(b))
+
+
+@pytest.mark.parametrize("kv,qd,hq,hkv,hd", [
+    ("f16", "f16", 32, 8, 128), ("f16", "f16", 8, 8, 64), ("f16", "f16", 16, 2, 128),
+    ("bf16", "bf16", 32, 8, 128), ("bf16", "bf16", 4, 4, 128), ("bf16", "bf16", 3, 3, 64),
+    ("fp8", "bf16", 64, 8, 128), ("fp8", "f16", 8, 4, 64),
+    ("i8", "bf16", 64, 8, 128), ("i8", "f16", 16, 16, 128),
+])
+def test_decode_shapes_ragged_shared_pool(kv, qd, hq, hkv, hd):
+    # A pool flagged as holding shared blocks (cached K/V loads): the same contexts as
+    # above across 1..16 kv heads, and a batch of 150 sequences (more than one window
+    # of 64 lengths in the split).
+    ctx = [1, 2, 15, 16, 17, 31, 127, 128, 129, 511, 512, 513, 1000, 2049, 3333]
+    b = W.decode_batch(hq * 5 + hd, ctx, hq, hkv, hd, kv, qd, poison=True, div=hd ** 0.5,
+                       name=f"ragged-shared-{kv}-{qd}-{hq}x{hkv}x{hd}")
+    check_decode(poison_tails(b), shared_blocks=True)
+    long = [1 + (37 * i) % 700 for i in range(150)]
+    b = W.decode_batch(hq * 5 + hd + 1, long, hq, hkv, hd, kv, qd, poison=True, div=hd ** 0.5,
+                       name=f"many-shared-{kv}-{qd}-{hq}x{hkv}x{hd}")
+    check_decode(poison_tails(b), shared_blocks=True)
 
 
 def test_decode_llama3_small():
