@@ -1423,9 +1423,12 @@ __device__ __forceinline__ void merge_stream(const DecodeArgs &a, int s, int hq,
     lp = a.ws_l[r0 + lane];
   }
   f4v_t v[NB];
+  // (slots past the last piece are skipped by a uniform test: a segment of a short
+  // context has two or three pieces)
   auto load_acc = [&](int p0) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
+      if (p0 + PPL * j >= pieces) break;
       const int p = p0 + PPL * j + sub;
       v[j] = p < pieces ? *reinterpret_cast<const f4v_t *>(a.ws_acc + (r0 + p) * D + dq)
                         : f4v_t{0.f, 0.f, 0.f, 0.f};
@@ -1449,6 +1452,7 @@ __device__ __forceinline__ void merge_stream(const DecodeArgs &a, int s, int hq,
     if (p0 > 0) load_acc(p0);
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
+      if (p0 + PPL * j >= pieces) break;
       // weight of this lane's piece p: lane p holds its m when p < 64
       const int p = p0 + PPL * j + sub;
       const float mpj = __shfl(mp, p & (kWave - 1), kWave);
