@@ -111,3 +111,24 @@ def test_eager_decode_with_an_understated_length_bound():
         torch.cuda.synchronize()
         err = max_err(out, oracle_decode_rows(b))
         assert err <= TOL["f16"], (bound, err)
+
+
+def test_eager_decode_two_rounds_with_an_understated_length_bound():
+    # The 1-byte decode runs two workgroups per CU, and the split gives the first
+    # round tpw + d cost units per wave and the second tpw - d.  On the 16 x 32768
+    # fp8 batch tpw is 129 and d 3; a length bound of 2048 leaves 17 pieces per
+    # segment, which lifts the second round's share to 128 (> 126): both rounds'
+    # shares then still cover the work, and no segment overflows its pieces.
+    from .pa_testlib import Dev, oracle_decode_rows
+    b = W.long_quantised("fp8")
+    d = Dev(b)
+    full = pa.pa_decode(d.pool, d.q, d.bt, d.lens, b.max_seq_len, b.scale).clone()
+    low = pa.pa_decode(d.pool, d.q, d.bt, d.lens, 2048, b.scale)
+    torch.cuda.synchronize()
+    gap = max_err(low, full.float().cpu().numpy())
+    say(b.name, "bound 2048 vs true bound, max diff", gap)
+    assert gap <= TOL["fp8"]
+    rows = [0, 7, 15]
+    err = max_err(low[rows], oracle_decode_rows(b, rows))
+    say(b.name, "bound 2048, rows", rows, "max_err", err)
+    assert err <= TOL["fp8"]
