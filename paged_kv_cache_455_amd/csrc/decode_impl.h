@@ -575,22 +575,36 @@ __device__ __forceinline__ void merge_partitions(const DecodeArgs &a, int r, int
 // when it owns the whole segment, else a partial (m, l, acc) for "piece"
 // w - first_wave(segment), combined by the merge kernel.
 
+// Cross-lane integer steps of the split, all DPP moves between registers (a lane
+// shuffle goes through the LDS crossbar: six dependent ones cost about 0.3 us).
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ int dpp_i(int x) {  // lanes with no source (or masked rows) read 0
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, 0xf, false);
+}
+constexpr int kDppRowShr1 = 0x111;     // + n - 1: lane i <- lane i - n within 16 (none below)
+constexpr int kDppRowBcast15 = 0x142;  // rows 1, 2, 3 <- lane 15 of the row before
+constexpr int kDppRowBcast31 = 0x143;  // rows 2, 3 <- lane 31
+
+// The maximum over the wave (uniform): each 16-lane row folded in registers, then
+// the four row maxima read by readlane.
 __device__ __forceinline__ int wave_max_i(int x) {
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) x = max(x, __shfl_xor(x, m, kWave));
-  return x;
+  x = max(x, dpp_i<kDppXor1>(x));
+  x = max(x, dpp_i<kDppXor2>(x));
+  x = max(x, dpp_i<kDppHalfMirror>(x));  // quads agree: pairs quad 0 with quad 1
+  x = max(x, dpp_i<kDppMirror>(x));      // halves agree: pairs the two halves
+  return max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
 }
-__device__ __forceinline__ int wave_sum_i(int x) {
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m, kWave);
-  return x;
-}
+// Inclusive prefix sum over the lanes: a scan of each row by shifts of 1, 2, 4 and 8
+// (zeros shifted in), then each row's total carried into the rows after it.
 __device__ __forceinline__ int wave_incl_scan_i(int x, int lane) {
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int y = __shfl_up(x, d, kWave);
-    if (lane >= d) x += y;
-  }
+  (void)lane;
+  x += dpp_i<kDppRowShr1>(x);
+  x += dpp_i<kDppRowShr1 + 1>(x);
+  x += dpp_i<kDppRowShr1 + 3>(x);
+  x += dpp_i<kDppRowShr1 + 7>(x);
+  x += dpp_i<kDppRowBcast15, 0xa>(x);  // rows 1 and 3 take the totals of rows 0 and 2
+  x += dpp_i<kDppRowBcast31, 0xc>(x);  // rows 2 and 3 take the total of rows 0..1
   return x;
 }
 

@@ -52,6 +52,11 @@ static Residency resident_groups() {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kDecodeWaves * kWave, 0) !=
       hipSuccess)
     return Residency{0, 0};
+  // The VALU-path kernels run one workgroup per CU (a wave per SIMD) even where
+  // their registers would allow two: twice the waves split twice as many segments,
+  // and config 2 measured 98.0 against 95.2 us at two.  The 1-byte MFMA path keeps
+  // the two workgroups per CU it was tuned at.
+  if (!Q8Geom<KV, D, G>::kOn) per_cu = per_cu > 1 ? 1 : per_cu;
   per_cu = per_cu > 0 ? per_cu : 1;
   cached = Residency{cus * per_cu, per_cu};
   return cached;
