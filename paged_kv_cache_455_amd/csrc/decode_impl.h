@@ -28,6 +28,8 @@
 // (Q8Path below).
 #pragma once
 
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -1115,10 +1117,19 @@ typedef __bf16 b8v_t __attribute__((ext_vector_type(8)));
 typedef short s4v_t __attribute__((ext_vector_type(4)));
 typedef float f4v_t __attribute__((ext_vector_type(4)));
 
+// The same tile on MFMA for 16-bit pools (f16, bf16) at a group of 8, where the VALU
+// path's 8 heads of dot products and weighted sums per lane no longer keep up with
+// the loads (Llama-3-70B-shaped decode: 147 us against 98 us at a group of 4 for the
+// same K/V bytes): K enters the score product as stored; V is transposed by 16-bit
+// permutes; for f16 pools the P.V product runs in f16 (P as f16 hi + lo, scaled by
+// 2^10 so that small weights stay clear of f16's subnormals; the output takes the
+// 2^-10 back), for bf16 pools in bf16 as for the codes.
 template <int KV, int D, int G>
 struct Q8Geom {
-  static constexpr bool kOn = (KV == PA_FP8_E4M3 || KV == PA_I8) && G == 8 && D == 128;
+  static constexpr bool k16 = KV == PA_F16 || KV == PA_BF16;
+  static constexpr bool kOn = (KV == PA_FP8_E4M3 || KV == PA_I8 || k16) && G == 8 && D == 128;
 };
+constexpr float kF16PScale = 1024.f;  // f16 pools: P enters the P.V product times 2^10
 
 // Codes 2*HI and 2*HI + 1 of word w as two exact 16-bit values (T16 = PA_BF16 or
 // PA_F16) packed in one word, the lower code in the low half.
@@ -1169,29 +1180,52 @@ struct Q8Tile {
   u32x2 v[4];    // value row 4*g16 + i: dims [8*c16, +8)
   float ks, vs;  // the tile's K and V scales
 };
+struct Q16Tile {
+  u32x4 k[4];    // key row c16: dims q8_dim0(kk, g16) .. +7, the A operand of k-step kk
+  u32x4 v[4];    // value row 4*g16 + i: dims [8*c16, +8)
+};
+template <int KV>
+using Q8TileOf = std::conditional_t<Q8Geom<KV, 128, 8>::k16, Q16Tile, Q8Tile>;
 
 struct Q8Acc {
   f4v_t o[8];  // o[e][i] = O[head 4*g16 + i][dim 8*c16 + e]
   float m, l;  // head c16: running max (log2 units), this lane's running sum
 };
 
+// f16 P.V product (f16 pools at a group of 8)
+__device__ __forceinline__ f4v_t mfma_pv_f16(const u32x2 &p, const u32x2 &v, const f4v_t &c) {
+  typedef _Float16 h4v_t __attribute__((ext_vector_type(4)));
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4v_t, p),
+                                               __builtin_bit_cast(h4v_t, v), c, 0, 0, 0);
+}
+
 template <int KV, int QT, bool MASK>
-__device__ __forceinline__ void q8_tile(Q8Acc &st, const u32x4 *qb, const Q8Tile &t,
+__device__ __forceinline__ void q8_tile(Q8Acc &st, const u32x4 *qb, const Q8TileOf<KV> &t,
                                         float qk_scale, int valid_rows, int g16) {
+  constexpr bool k16 = Q8Geom<KV, 128, 8>::k16;
   constexpr int T16 = QT == PA_F16 ? PA_F16 : PA_BF16;
   f4v_t sacc = f4v_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    const u32x4 &kw = kk < 2 ? t.k0 : t.k1;
-    const uint32_t w0 = kw[2 * (kk & 1)], w1 = kw[2 * (kk & 1) + 1];
     u32x4 ka;
-    ka[0] = codes2_to_16<KV, T16, false>(w0);
-    ka[1] = codes2_to_16<KV, T16, true>(w0);
-    ka[2] = codes2_to_16<KV, T16, false>(w1);
-    ka[3] = codes2_to_16<KV, T16, true>(w1);
+    if constexpr (k16) {
+      ka = t.k[kk];  // as stored
+    } else {
+      const u32x4 &kw = kk < 2 ? t.k0 : t.k1;
+      const uint32_t w0 = kw[2 * (kk & 1)], w1 = kw[2 * (kk & 1) + 1];
+      ka[0] = codes2_to_16<KV, T16, false>(w0);
+      ka[1] = codes2_to_16<KV, T16, true>(w0);
+      ka[2] = codes2_to_16<KV, T16, false>(w1);
+      ka[3] = codes2_to_16<KV, T16, true>(w1);
+    }
     sacc = mfma_qk<QT>(ka, qb[kk], sacc);
   }
-  const float qs = qk_scale * t.ks;
+  float ks = 1.f, vs = KV == PA_F16 ? kF16PScale : 1.f;
+  if constexpr (!k16) {
+    ks = t.ks;
+    vs = t.vs;
+  }
+  const float qs = qk_scale * ks;
   bool ok[4];
   float sv[4];
   float mx = kNegBig;
@@ -1223,14 +1257,44 @@ __device__ __forceinline__ void q8_tile(Q8Acc &st, const u32x4 *qb, const Q8Tile
     float p = fast_exp2(sv[i] - mn);
     if constexpr (MASK) p = ok[i] ? p : 0.f;
     psum += p;
-    pv[i] = p * t.vs;
+    pv[i] = p * vs;
   }
   st.l += psum;
   u32x2 ph, pl;
-  ph[0] = pack_bf16(pv[0], pv[1]);
-  ph[1] = pack_bf16(pv[2], pv[3]);
-  pl[0] = pack_bf16(pv[0] - bf16_lo(ph[0]), pv[1] - bf16_hi(ph[0]));
-  pl[1] = pack_bf16(pv[2] - bf16_lo(ph[1]), pv[3] - bf16_hi(ph[1]));
+  if constexpr (KV == PA_F16) {
+    auto pack_h = [](float x, float y) { return __builtin_bit_cast(uint32_t, h2_t{(_Float16)x, (_Float16)y}); };
+    ph[0] = pack_h(pv[0], pv[1]);
+    ph[1] = pack_h(pv[2], pv[3]);
+    pl[0] = pack_h(pv[0] - f16_lo(ph[0]), pv[1] - f16_hi(ph[0]));
+    pl[1] = pack_h(pv[2] - f16_lo(ph[1]), pv[3] - f16_hi(ph[1]));
+  } else {
+    ph[0] = pack_bf16(pv[0], pv[1]);
+    ph[1] = pack_bf16(pv[2], pv[3]);
+    pl[0] = pack_bf16(pv[0] - bf16_lo(ph[0]), pv[1] - bf16_hi(ph[0]));
+    pl[1] = pack_bf16(pv[2] - bf16_lo(ph[1]), pv[3] - bf16_hi(ph[1]));
+  }
+  if constexpr (k16) {
+    // value rows past the context may hold anything (NaN included): zero their bits
+    u32x4 vr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vr[i] = ok[i] ? t.v[i] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      // keys 0..3 of dim 8*c16 + e: the low or high halves of word e/2 of the rows
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      u32x2 vb;
+      vb[0] = __builtin_amdgcn_perm(vr[1][e >> 1], vr[0][e >> 1], sel);
+      vb[1] = __builtin_amdgcn_perm(vr[3][e >> 1], vr[2][e >> 1], sel);
+      if constexpr (KV == PA_F16) {
+        st.o[e] = mfma_pv_f16(ph, vb, st.o[e]);
+        st.o[e] = mfma_pv_f16(pl, vb, st.o[e]);
+      } else {
+        st.o[e] = mfma_pv(ph, vb, st.o[e]);
+        st.o[e] = mfma_pv(pl, vb, st.o[e]);
+      }
+    }
+    return;
+  }
 
   // value rows past the context may hold anything (NaN included): zero their bits
   uint32_t vr[4][2];
@@ -1264,9 +1328,10 @@ __device__ __forceinline__ void q8_tile(Q8Acc &st, const u32x4 *qb, const Q8Tile
 
 // Write the wave's result for (s, kv head h): the normalised output when single,
 // else the partial (m, l, acc) of `piece`.
-template <int QT>
+template <int KV, int QT>
 __device__ __forceinline__ void q8_emit(const DecodeArgs &a, const Q8Acc &st, int s, int h,
                                         bool single, int piece, int lane) {
+  constexpr float kOut = KV == PA_F16 ? 1.f / kF16PScale : 1.f;  // undo the P scale of f16 pools
   constexpr int D = 128, G = 8;
   const int g16 = lane >> 4, c16 = lane & 15;
   float L = st.l;
@@ -1285,7 +1350,7 @@ __device__ __forceinline__ void q8_emit(const DecodeArgs &a, const Q8Acc &st, in
     const int64_t row = (int64_t)s * a.num_q_heads + h * G + 4 * g16 + i;      // workspace
     const int64_t orow = qrow * a.num_q_heads + h * G + 4 * g16 + i;          // output
     if (single) {
-      const float inv = 1.f / Lh[i];
+      const float inv = kOut / Lh[i];
       u32x4 pk;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -1299,8 +1364,10 @@ __device__ __forceinline__ void q8_emit(const DecodeArgs &a, const Q8Acc &st, in
     } else {
       const int64_t r = row * a.max_parts + piece;
       float *dst = a.ws_acc + r * D + 8 * c16;
-      *reinterpret_cast<f4v_t *>(dst) = f4v_t{st.o[0][i], st.o[1][i], st.o[2][i], st.o[3][i]};
-      *reinterpret_cast<f4v_t *>(dst + 4) = f4v_t{st.o[4][i], st.o[5][i], st.o[6][i], st.o[7][i]};
+      *reinterpret_cast<f4v_t *>(dst) =
+          f4v_t{st.o[0][i], st.o[1][i], st.o[2][i], st.o[3][i]} * kOut;
+      *reinterpret_cast<f4v_t *>(dst + 4) =
+          f4v_t{st.o[4][i], st.o[5][i], st.o[6][i], st.o[7][i]} * kOut;
       if (c16 == 0) {
         a.ws_m[r] = mh[i];
         a.ws_l[r] = Lh[i];
@@ -1311,8 +1378,9 @@ __device__ __forceinline__ void q8_emit(const DecodeArgs &a, const Q8Acc &st, in
 
 template <int KV, int QT, bool NT>
 struct Q8Path {
-  static constexpr int D = 128, G = 8, kTileBytes = kBlock * D;
-  using Tile = Q8Tile;
+  static constexpr bool k16 = Q8Geom<KV, 128, 8>::k16;
+  static constexpr int D = 128, G = 8, E = k16 ? 2 : 1, kTileBytes = kBlock * D * E;
+  using Tile = Q8TileOf<KV>;
   const DecodeArgs &a;
   const int lane, g16, c16;
   const char *kbase, *vbase;
@@ -1321,18 +1389,39 @@ struct Q8Path {
 
   __device__ __forceinline__ Q8Path(const DecodeArgs &args, int ln)
       : a(args), lane(ln), g16(ln >> 4), c16(ln & 15),
-        kbase(reinterpret_cast<const char *>(args.k) + (ln & 15) * D + 16 * (ln >> 4)),
-        vbase(reinterpret_cast<const char *>(args.v) + 4 * (ln >> 4) * D + 8 * (ln & 15)) {}
+        kbase(reinterpret_cast<const char *>(args.k) + (ln & 15) * D * E + 16 * E * (ln >> 4)),
+        vbase(reinterpret_cast<const char *>(args.v) + 4 * (ln >> 4) * D * E + 8 * E * (ln & 15)) {}
 
-  __device__ __forceinline__ void load(Tile &t, int64_t tile, const StreamSeg &, int) {
-    const char *kp = kbase + tile * kTileBytes;
-    t.k0 = load_tile_part<u32x4, NT>(kp);
-    t.k1 = load_tile_part<u32x4, NT>(kp + 64);
-    const char *vp = vbase + tile * kTileBytes;
+  // Tile j of segment sg.  16-bit pools, with a fused append (k_new set): the
+  // newest row of the segment -- row tail - 1 of its last tile, not yet in the pool
+  // -- is read from k_new / v_new instead; every load is still issued, only its
+  // address differs.  (1-byte pools take their new rows through the quantised
+  // write before the decode.)
+  __device__ __forceinline__ void load(Tile &t, int64_t tile, const StreamSeg &sg, int j) {
+    if constexpr (k16) {
+      const int nr = (a.k_new != nullptr && j == sg.nblk - 1) ? sg.tail - 1 : -1;
+      const int64_t no = ((int64_t)sg.s * a.num_kv_heads + sg.h) * (D * E);
+      const char *kn = reinterpret_cast<const char *>(a.k_new) + no + 32 * g16;
+      const char *vn = reinterpret_cast<const char *>(a.v_new) + no + 16 * c16;
+      const char *kp = c16 == nr ? kn : kbase + tile * kTileBytes;
+      t.k[0] = load_tile_part<u32x4, NT>(kp);
+      t.k[1] = load_tile_part<u32x4, NT>(kp + 16);
+      t.k[2] = load_tile_part<u32x4, NT>(kp + 128);
+      t.k[3] = load_tile_part<u32x4, NT>(kp + 144);
+      const char *vp = vbase + tile * kTileBytes;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) t.v[i] = load_tile_part<u32x2, NT>(vp + i * D);
-    t.ks = a.k_scale[tile >> a.bs_shift];
-    t.vs = a.v_scale[tile >> a.bs_shift];
+      for (int i = 0; i < 4; ++i)
+        t.v[i] = load_tile_part<u32x4, NT>(4 * g16 + i == nr ? vn : vp + i * D * E);
+    } else {
+      const char *kp = kbase + tile * kTileBytes;
+      t.k0 = load_tile_part<u32x4, NT>(kp);
+      t.k1 = load_tile_part<u32x4, NT>(kp + 64);
+      const char *vp = vbase + tile * kTileBytes;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t.v[i] = load_tile_part<u32x2, NT>(vp + i * D);
+      t.ks = a.k_scale[tile >> a.bs_shift];
+      t.vs = a.v_scale[tile >> a.bs_shift];
+    }
   }
   __device__ __forceinline__ void prefetch_q(const StreamSeg &sg) {
 #pragma unroll
@@ -1360,7 +1449,7 @@ struct Q8Path {
       q8_tile<KV, QT, false>(st, qb, t, a.qk_scale, kBlock, g16);
   }
   __device__ __forceinline__ void emit(const StreamSeg &sg, bool single, int piece) {
-    q8_emit<QT>(a, st, sg.s, sg.h, single, piece, lane);
+    q8_emit<KV, QT>(a, st, sg.s, sg.h, single, piece, lane);
   }
 };
 

@@ -19,6 +19,13 @@ __global__ __launch_bounds__(kDecodeWaves *kWave, 2) void pa_decode_stream_q8_ke
   decode_stream_q8<KV, QT, NT>(a);
 }
 
+// 16-bit KV with a GQA group of 8 on the same MFMA tile: its tiles are twice the
+// bytes per lane, one wave per SIMD.
+template <int KV, int QT, bool NT>
+__global__ __launch_bounds__(kDecodeWaves *kWave) void pa_decode_stream_m16_kernel(DecodeArgs a) {
+  decode_stream_q8<KV, QT, NT>(a);
+}
+
 // One wave per (sequence, query head); four per workgroup.
 template <int QT, int D>
 __global__ __launch_bounds__(4 * kWave) void pa_decode_stream_merge_kernel(DecodeArgs a) {
@@ -29,7 +36,9 @@ __global__ __launch_bounds__(4 * kWave) void pa_decode_stream_merge_kernel(Decod
 
 template <int KV, int QT, int D, int G, bool NT>
 static constexpr auto stream_kernel() {
-  if constexpr (Q8Geom<KV, D, G>::kOn)
+  if constexpr (Q8Geom<KV, D, G>::kOn && Q8Geom<KV, D, G>::k16)
+    return pa_decode_stream_m16_kernel<KV, QT, NT>;
+  else if constexpr (Q8Geom<KV, D, G>::kOn)
     return pa_decode_stream_q8_kernel<KV, QT, NT>;
   else
     return pa_decode_stream_kernel<KV, QT, D, G, NT>;
@@ -54,9 +63,10 @@ static Residency resident_groups() {
     return Residency{0, 0};
   // The VALU-path kernels run one workgroup per CU (a wave per SIMD) even where
   // their registers would allow two: twice the waves split twice as many segments,
-  // and config 2 measured 98.0 against 95.2 us at two.  The 1-byte MFMA path keeps
-  // the two workgroups per CU it was tuned at.
-  if (!Q8Geom<KV, D, G>::kOn) per_cu = per_cu > 1 ? 1 : per_cu;
+  // and config 2 measured 98.0 against 95.2 us at two; the 16-bit MFMA tile too
+  // (99.5 against 105.6 us at a group of 8).  The 1-byte MFMA path keeps the two
+  // workgroups per CU it was tuned at.
+  if (!Q8Geom<KV, D, G>::kOn || Q8Geom<KV, D, G>::k16) per_cu = per_cu > 1 ? 1 : per_cu;
   per_cu = per_cu > 0 ? per_cu : 1;
   cached = Residency{cus * per_cu, per_cu};
   return cached;

@@ -86,6 +86,7 @@ CASES = [  # kv, Hq, Hkv, D, block size, contexts
     ("f16", 8, 8, 64, 16, [3, 16, 100, 257]),
     ("bf16", 16, 8, 128, 32, [2, 17, 48, 300, 1025]),
     ("f32", 16, 4, 128, 32, [1, 33, 64, 95]),
+    ("f16", 64, 8, 128, 16, [1, 2, 15, 16, 17, 31, 33, 129, 1000, 2049]),  # MFMA tile, f16 P.V
 ]
 
 
@@ -101,7 +102,8 @@ def test_fused_equals_unfused_and_oracle(kv, hq, hkv, d, bs, ctx):
 
 
 @pytest.mark.parametrize("kv,hq,hkv,d,bs", [("f16", 32, 8, 128, 16), ("bf16", 16, 8, 64, 32),
-                                           ("bf16", 8, 8, 128, 16), ("f16", 64, 8, 64, 32)])
+                                           ("bf16", 8, 8, 128, 16), ("f16", 64, 8, 64, 32),
+                                           ("f16", 64, 8, 128, 16), ("bf16", 64, 8, 128, 32)])
 def test_fused_peaked_data(kv, hq, hkv, d, bs):
     """Unscaled N(0,1) data (peaked softmax): the fused step against the unfused
     calls bit for bit, and against the oracle at one ulp of the output type."""

@@ -139,6 +139,7 @@ def test_decode_tiny_fp32_poisoned():
 @pytest.mark.parametrize("kv,qd,hq,hkv,hd", [
     ("f32", "f32", 4, 2, 64), ("f32", "f32", 8, 1, 128),
     ("f16", "f16", 32, 8, 128), ("f16", "f16", 8, 8, 64), ("f16", "f16", 16, 2, 128),
+    ("f16", "f16", 64, 8, 128), ("bf16", "bf16", 64, 8, 128),
     ("bf16", "bf16", 32, 8, 128), ("bf16", "bf16", 4, 4, 128),
     ("fp8", "bf16", 64, 8, 128), ("fp8", "f16", 8, 4, 64), ("fp8", "f16", 64, 8, 128),
     ("i8", "bf16", 64, 8, 128), ("i8", "f16", 16, 16, 128), ("i8", "f16", 32, 4, 128),
@@ -154,6 +155,7 @@ def test_decode_shapes_ragged(kv, qd, hq, hkv, hd):
 
 @pytest.mark.parametrize("kv,qd,hq,hkv,hd", [
     ("f16", "f16", 32, 8, 128), ("f16", "f16", 8, 8, 64), ("f16", "f16", 16, 2, 128),
+    ("f16", "f16", 64, 8, 128), ("bf16", "bf16", 16, 2, 128),
     ("bf16", "bf16", 32, 8, 128), ("bf16", "bf16", 4, 4, 128), ("bf16", "bf16", 3, 3, 64),
     ("fp8", "bf16", 64, 8, 128), ("fp8", "f16", 8, 4, 64),
     ("i8", "bf16", 64, 8, 128), ("i8", "f16", 16, 16, 128),
