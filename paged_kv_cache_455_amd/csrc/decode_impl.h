@@ -25,7 +25,7 @@
 // LPT lanes, after which the lanes hold finished scores for the P.V update; each
 // lane keeps its own running (max, sum, acc), merged across lanes at the end.
 // 1-byte KV with a GQA group of 8 runs both products of a tile on MFMA instead
-// (Q8Path below).
+// (MxPath below).
 #pragma once
 
 #include <type_traits>
@@ -1095,12 +1095,12 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a) {
   stream_run(a, path, w, lane);
 }
 
-// ---- 1-byte KV, GQA group 8, head_dim 128: both products on MFMA ----------------------
-// Against the group's 8 query heads, one (block, kv head) tile of 16 keys x 128 dims
+// ---- head_dim 128, 1-byte KV at GQA groups 2-8, 16-bit at 8: both products on MFMA --
+// Against the group's G query heads, one (block, kv head) tile of 16 keys x 128 dims
 // gives two small dense products, run on matrix cores with the heads padded to 16:
 //  * scores S^T[key][head] = K . Q^T on v_mfma_f32_16x16x32 (bf16, or f16 for f16
 //    queries; the codes convert exactly).  Lane (c16, g16) supplies key row c16,
-//    dims q8_dim0(kk, g16) .. +7 of k-step kk (two coalesced 16-byte loads per lane)
+//    dims mx_dim0(kk, g16) .. +7 of k-step kk (two coalesced 16-byte loads per lane)
 //    and receives the scores of keys 4*g16 .. +3 for head c16;
 //  * that is already the A-operand layout of O[head][dim] += P[head][key] . V[key][dim]
 //    on v_mfma_f32_16x16x16 bf16 (row c16, keys 4*g16 .. +3): the probabilities
@@ -1109,7 +1109,7 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a) {
 //  * the B operand (keys 4*g16 .. +3 of one dim) comes from four 8-byte loads of
 //    value rows 4*g16 + i, dims 8*c16 .. +7, transposed inside the lane by byte
 //    permutes and converted exactly to bf16; product e covers dims 8*c16 + e;
-//  * lane (c16, g16) accumulates O rows 4*g16 + i (heads; rows 8..15 are padding)
+//  * lane (c16, g16) accumulates O rows 4*g16 + i (heads; rows G..15 are padding)
 //    at dims 8*c16 + e.  Head c16's running max is the same in its four lanes; its
 //    running sum is kept per lane over that lane's keys and summed at the end.
 typedef _Float16 h8v_t __attribute__((ext_vector_type(8)));
@@ -1125,9 +1125,13 @@ typedef float f4v_t __attribute__((ext_vector_type(4)));
 // 2^10 so that small weights stay clear of f16's subnormals; the output takes the
 // 2^-10 back), for bf16 pools in bf16 as for the codes.
 template <int KV, int D, int G>
-struct Q8Geom {
+struct MxGeom {
   static constexpr bool k16 = KV == PA_F16 || KV == PA_BF16;
-  static constexpr bool kOn = (KV == PA_FP8_E4M3 || KV == PA_I8 || k16) && G == 8 && D == 128;
+  // 1-byte pools at groups of 2, 4 and 8 (the heads pad to 16 either way; at 4 the
+  // VALU path's per-code converts held fp8 to 3.3 TB/s); 16-bit pools at 8 only
+  // (at 4 and below their VALU path streams at the memory's rate)
+  static constexpr bool kOn =
+      D == 128 && (k16 ? G == 8 : ((KV == PA_FP8_E4M3 || KV == PA_I8) && (G == 2 || G == 4 || G == 8)));
 };
 constexpr float kF16PScale = 1024.f;  // f16 pools: P enters the P.V product times 2^10
 
@@ -1171,7 +1175,7 @@ __device__ __forceinline__ f4v_t mfma_pv(const u32x2 &p, const u32x2 &v, const f
 }
 
 // First of the 8 dims that lane group g16 supplies at k-step kk (same map for K and q).
-__device__ __forceinline__ int q8_dim0(int kk, int g16) {
+__device__ __forceinline__ int mx_dim0(int kk, int g16) {
   return (kk < 2 ? 0 : 64) + 16 * g16 + 8 * (kk & 1);
 }
 
@@ -1181,13 +1185,13 @@ struct Q8Tile {
   float ks, vs;  // the tile's K and V scales
 };
 struct Q16Tile {
-  u32x4 k[4];    // key row c16: dims q8_dim0(kk, g16) .. +7, the A operand of k-step kk
+  u32x4 k[4];    // key row c16: dims mx_dim0(kk, g16) .. +7, the A operand of k-step kk
   u32x4 v[4];    // value row 4*g16 + i: dims [8*c16, +8)
 };
 template <int KV>
-using Q8TileOf = std::conditional_t<Q8Geom<KV, 128, 8>::k16, Q16Tile, Q8Tile>;
+using MxTileOf = std::conditional_t<MxGeom<KV, 128, 8>::k16, Q16Tile, Q8Tile>;
 
-struct Q8Acc {
+struct MxAcc {
   f4v_t o[8];  // o[e][i] = O[head 4*g16 + i][dim 8*c16 + e]
   float m, l;  // head c16: running max (log2 units), this lane's running sum
 };
@@ -1200,9 +1204,9 @@ __device__ __forceinline__ f4v_t mfma_pv_f16(const u32x2 &p, const u32x2 &v, con
 }
 
 template <int KV, int QT, bool MASK>
-__device__ __forceinline__ void q8_tile(Q8Acc &st, const u32x4 *qb, const Q8TileOf<KV> &t,
+__device__ __forceinline__ void mx_tile(MxAcc &st, const u32x4 *qb, const MxTileOf<KV> &t,
                                         float qk_scale, int valid_rows, int g16) {
-  constexpr bool k16 = Q8Geom<KV, 128, 8>::k16;
+  constexpr bool k16 = MxGeom<KV, 128, 8>::k16;
   constexpr int T16 = QT == PA_F16 ? PA_F16 : PA_BF16;
   f4v_t sacc = f4v_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1328,11 +1332,11 @@ __device__ __forceinline__ void q8_tile(Q8Acc &st, const u32x4 *qb, const Q8Tile
 
 // Write the wave's result for (s, kv head h): the normalised output when single,
 // else the partial (m, l, acc) of `piece`.
-template <int KV, int QT>
-__device__ __forceinline__ void q8_emit(const DecodeArgs &a, const Q8Acc &st, int s, int h,
+template <int KV, int QT, int G>
+__device__ __forceinline__ void mx_emit(const DecodeArgs &a, const MxAcc &st, int s, int h,
                                         bool single, int piece, int lane) {
   constexpr float kOut = KV == PA_F16 ? 1.f / kF16PScale : 1.f;  // undo the P scale of f16 pools
-  constexpr int D = 128, G = 8;
+  constexpr int D = 128;
   const int g16 = lane >> 4, c16 = lane & 15;
   float L = st.l;
   L += xor_lanes<16>(L);
@@ -1343,10 +1347,11 @@ __device__ __forceinline__ void q8_emit(const DecodeArgs &a, const Q8Acc &st, in
     mh[i] = __shfl(st.m, 4 * g16 + i, kWave);
     Lh[i] = __shfl(L, 4 * g16 + i, kWave);
   }
-  if (g16 >= 2) return;  // padding heads
+  if (4 * g16 >= G) return;  // padding heads
   const int64_t qrow = decode_row(a, s);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    if (G < 4 && i >= G) break;
     const int64_t row = (int64_t)s * a.num_q_heads + h * G + 4 * g16 + i;      // workspace
     const int64_t orow = qrow * a.num_q_heads + h * G + 4 * g16 + i;          // output
     if (single) {
@@ -1376,18 +1381,18 @@ __device__ __forceinline__ void q8_emit(const DecodeArgs &a, const Q8Acc &st, in
   }
 }
 
-template <int KV, int QT, bool NT>
-struct Q8Path {
-  static constexpr bool k16 = Q8Geom<KV, 128, 8>::k16;
-  static constexpr int D = 128, G = 8, E = k16 ? 2 : 1, kTileBytes = kBlock * D * E;
-  using Tile = Q8TileOf<KV>;
+template <int KV, int QT, int G, bool NT>
+struct MxPath {
+  static constexpr bool k16 = MxGeom<KV, 128, 8>::k16;
+  static constexpr int D = 128, E = k16 ? 2 : 1, kTileBytes = kBlock * D * E;
+  using Tile = MxTileOf<KV>;
   const DecodeArgs &a;
   const int lane, g16, c16;
   const char *kbase, *vbase;
   u32x4 qb[4], qn[4];  // B operand per k-step: q[head c16][8 dims]; qn: next segment's
-  Q8Acc st;
+  MxAcc st;
 
-  __device__ __forceinline__ Q8Path(const DecodeArgs &args, int ln)
+  __device__ __forceinline__ MxPath(const DecodeArgs &args, int ln)
       : a(args), lane(ln), g16(ln >> 4), c16(ln & 15),
         kbase(reinterpret_cast<const char *>(args.k) + (ln & 15) * D * E + 16 * E * (ln >> 4)),
         vbase(reinterpret_cast<const char *>(args.v) + 4 * (ln >> 4) * D * E + 8 * E * (ln & 15)) {}
@@ -1431,7 +1436,7 @@ struct Q8Path {
                        ((decode_row(a, sg.s) * a.num_q_heads + sg.h * G + c16) * D) * 2;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        qn[kk] = *reinterpret_cast<const u32x4 *>(qp + q8_dim0(kk, g16) * 2);
+        qn[kk] = *reinterpret_cast<const u32x4 *>(qp + mx_dim0(kk, g16) * 2);
     }
   }
   __device__ __forceinline__ void begin_segment() {
@@ -1444,20 +1449,20 @@ struct Q8Path {
   }
   __device__ __forceinline__ void compute(const Tile &t, int valid, bool masked) {
     if (masked)
-      q8_tile<KV, QT, true>(st, qb, t, a.qk_scale, valid, g16);
+      mx_tile<KV, QT, true>(st, qb, t, a.qk_scale, valid, g16);
     else
-      q8_tile<KV, QT, false>(st, qb, t, a.qk_scale, kBlock, g16);
+      mx_tile<KV, QT, false>(st, qb, t, a.qk_scale, kBlock, g16);
   }
   __device__ __forceinline__ void emit(const StreamSeg &sg, bool single, int piece) {
-    q8_emit<KV, QT>(a, st, sg.s, sg.h, single, piece, lane);
+    mx_emit<KV, QT, G>(a, st, sg.s, sg.h, single, piece, lane);
   }
 };
 
-template <int KV, int QT, bool NT>
-__device__ __forceinline__ void decode_stream_q8(const DecodeArgs &a) {
+template <int KV, int QT, int G, bool NT>
+__device__ __forceinline__ void decode_stream_mx(const DecodeArgs &a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kDecodeWaves + threadIdx.x / kWave);
-  Q8Path<KV, QT, NT> path(a, lane);
+  MxPath<KV, QT, G, NT> path(a, lane);
   stream_run(a, path, w, lane);
 }
 

@@ -12,18 +12,18 @@ __global__ __launch_bounds__(kDecodeWaves *kWave) void pa_decode_stream_kernel(D
   decode_stream<KV, QT, D, G, NT>(a);
 }
 
-// 1-byte KV with a GQA group of 8 (both products on MFMA): its state fits two waves
-// per SIMD without spilling, which hides more of each wave's load latency.
-template <int KV, int QT, bool NT>
+// 1-byte KV with a GQA group of 2, 4 or 8 (both products on MFMA): its state fits
+// two waves per SIMD without spilling, which hides more of each wave's load latency.
+template <int KV, int QT, int G, bool NT>
 __global__ __launch_bounds__(kDecodeWaves *kWave, 2) void pa_decode_stream_q8_kernel(DecodeArgs a) {
-  decode_stream_q8<KV, QT, NT>(a);
+  decode_stream_mx<KV, QT, G, NT>(a);
 }
 
 // 16-bit KV with a GQA group of 8 on the same MFMA tile: its tiles are twice the
 // bytes per lane, one wave per SIMD.
-template <int KV, int QT, bool NT>
+template <int KV, int QT, int G, bool NT>
 __global__ __launch_bounds__(kDecodeWaves *kWave) void pa_decode_stream_m16_kernel(DecodeArgs a) {
-  decode_stream_q8<KV, QT, NT>(a);
+  decode_stream_mx<KV, QT, G, NT>(a);
 }
 
 // One wave per (sequence, query head); four per workgroup.
@@ -36,10 +36,10 @@ __global__ __launch_bounds__(4 * kWave) void pa_decode_stream_merge_kernel(Decod
 
 template <int KV, int QT, int D, int G, bool NT>
 static constexpr auto stream_kernel() {
-  if constexpr (Q8Geom<KV, D, G>::kOn && Q8Geom<KV, D, G>::k16)
-    return pa_decode_stream_m16_kernel<KV, QT, NT>;
-  else if constexpr (Q8Geom<KV, D, G>::kOn)
-    return pa_decode_stream_q8_kernel<KV, QT, NT>;
+  if constexpr (MxGeom<KV, D, G>::kOn && MxGeom<KV, D, G>::k16)
+    return pa_decode_stream_m16_kernel<KV, QT, G, NT>;
+  else if constexpr (MxGeom<KV, D, G>::kOn)
+    return pa_decode_stream_q8_kernel<KV, QT, G, NT>;
   else
     return pa_decode_stream_kernel<KV, QT, D, G, NT>;
 }
@@ -66,7 +66,7 @@ static Residency resident_groups() {
   // and config 2 measured 98.0 against 95.2 us at two; the 16-bit MFMA tile too
   // (99.5 against 105.6 us at a group of 8).  The 1-byte MFMA path keeps the two
   // workgroups per CU it was tuned at.
-  if (!Q8Geom<KV, D, G>::kOn || Q8Geom<KV, D, G>::k16) per_cu = per_cu > 1 ? 1 : per_cu;
+  if (!MxGeom<KV, D, G>::kOn || MxGeom<KV, D, G>::k16) per_cu = per_cu > 1 ? 1 : per_cu;
   per_cu = per_cu > 0 ? per_cu : 1;
   cached = Residency{cus * per_cu, per_cu};
   return cached;
