@@ -37,7 +37,8 @@ def _mirror_write(kv, k, v, ks, vs, kn, vn, slots):
 
 
 @pytest.mark.parametrize("kv,qd,hq,hkv,bs", [("f16", "f16", 32, 8, 16), ("bf16", "bf16", 16, 2, 32),
-                                             ("fp8", "bf16", 64, 8, 16), ("i8", "f16", 32, 4, 32)])
+                                             ("fp8", "bf16", 64, 8, 16), ("i8", "f16", 32, 4, 32),
+                                             ("fp8", "f16", 32, 8, 16)])
 def test_replays_match_eager_and_oracle(kv, qd, hq, hkv, bs):
     ctx0 = np.array([5, 100, 700, 1500, 33, 64, 16, 1])
     b = W.decode_batch(61, ctx0 + 1200, hq, hkv, 128, kv, qd, div=128 ** 0.5, with_new=True,
