@@ -1095,43 +1095,52 @@ __device__ __forceinline__ void decode_stream(const DecodeArgs &a) {
   stream_run(a, path, w, lane);
 }
 
-// ---- head_dim 128, 1-byte KV at GQA groups 2-8, 16-bit at 8: both products on MFMA --
-// Against the group's G query heads, one (block, kv head) tile of 16 keys x 128 dims
+// ---- head_dim 64 and 128, GQA groups 2-8: both products of a tile on MFMA ----------
+// Against the group's G query heads, one (block, kv head) tile of 16 keys x D dims
 // gives two small dense products, run on matrix cores with the heads padded to 16:
 //  * scores S^T[key][head] = K . Q^T on v_mfma_f32_16x16x32 (bf16, or f16 for f16
-//    queries; the codes convert exactly).  Lane (c16, g16) supplies key row c16,
-//    dims mx_dim0(kk, g16) .. +7 of k-step kk (two coalesced 16-byte loads per lane)
+//    queries; the codes convert exactly), D/32 k-steps.  Lane (c16, g16) supplies
+//    key row c16, dims mx_dim0(kk, g16) .. +7 of k-step kk (coalesced 16-byte loads)
 //    and receives the scores of keys 4*g16 .. +3 for head c16;
 //  * that is already the A-operand layout of O[head][dim] += P[head][key] . V[key][dim]
 //    on v_mfma_f32_16x16x16 bf16 (row c16, keys 4*g16 .. +3): the probabilities
 //    never leave the lane.  They enter with the tile's value scale folded in, split
 //    as bf16 hi + lo (hi + lo matches p to about 2^-17 relative);
-//  * the B operand (keys 4*g16 .. +3 of one dim) comes from four 8-byte loads of
-//    value rows 4*g16 + i, dims 8*c16 .. +7, transposed inside the lane by byte
-//    permutes and converted exactly to bf16; product e covers dims 8*c16 + e;
+//  * the B operand (keys 4*g16 .. +3 of one dim) comes from four loads of value
+//    rows 4*g16 + i, dims NE*c16 .. +NE-1 (NE = D/16), transposed inside the lane by
+//    byte permutes and converted exactly to bf16; product e covers dims NE*c16 + e;
 //  * lane (c16, g16) accumulates O rows 4*g16 + i (heads; rows G..15 are padding)
-//    at dims 8*c16 + e.  Head c16's running max is the same in its four lanes; its
+//    at dims NE*c16 + e.  Head c16's running max is the same in its four lanes; its
 //    running sum is kept per lane over that lane's keys and summed at the end.
 typedef _Float16 h8v_t __attribute__((ext_vector_type(8)));
 typedef __bf16 b8v_t __attribute__((ext_vector_type(8)));
 typedef short s4v_t __attribute__((ext_vector_type(4)));
 typedef float f4v_t __attribute__((ext_vector_type(4)));
 
-// The same tile on MFMA for 16-bit pools (f16, bf16) at a group of 8, where the VALU
-// path's 8 heads of dot products and weighted sums per lane no longer keep up with
-// the loads (Llama-3-70B-shaped decode: 147 us against 98 us at a group of 4 for the
-// same K/V bytes): K enters the score product as stored; V is transposed by 16-bit
+// 16-bit pools (f16, bf16) take the same tile, where the VALU path's dot products
+// and weighted sums per lane no longer keep up with the loads (Llama-3-70B-shaped
+// decode, a group of 8 at D 128: 147 us against 98 us at a group of 4 for the same
+// K/V bytes): K enters the score product as stored; V is transposed by 16-bit
 // permutes; for f16 pools the P.V product runs in f16 (P as f16 hi + lo, scaled by
 // 2^10 so that small weights stay clear of f16's subnormals; the output takes the
 // 2^-10 back), for bf16 pools in bf16 as for the codes.
 template <int KV, int D, int G>
 struct MxGeom {
   static constexpr bool k16 = KV == PA_F16 || KV == PA_BF16;
-  // 1-byte pools at groups of 2, 4 and 8 (the heads pad to 16 either way; at 4 the
-  // VALU path's per-code converts held fp8 to 3.3 TB/s); 16-bit pools at 8 only
-  // (at 4 and below their VALU path streams at the memory's rate)
-  static constexpr bool kOn =
-      D == 128 && (k16 ? G == 8 : ((KV == PA_FP8_E4M3 || KV == PA_I8) && (G == 2 || G == 4 || G == 8)));
+  static constexpr bool k8 = KV == PA_FP8_E4M3 || KV == PA_I8;
+  // D 128: 1-byte pools at groups of 2, 4 and 8 (at 4 the VALU path's per-code
+  // converts held fp8 to 3.3 TB/s), 16-bit pools at 8 only (at 4 and below their VALU
+  // path streams at the memory's rate).  D 64: both widths at groups of 2, 4 and 8,
+  // where the VALU path's per-key work over half the bytes held 16-bit pools to
+  // 2.8-4.6 TB/s and 1-byte pools to 1.2-2.7 TB/s.
+  static constexpr bool kOn = D == 128   ? (k16 ? G == 8 : (k8 && G >= 2))
+                              : D == 64 ? ((k16 || k8) && G >= 2)
+                                        : false;
+  static constexpr int NE = D / 16;  // P.V products per tile: dims per lane
+  static constexpr int KS = D / 32;  // k-steps of the score product
+  // workgroups per CU: two where a wave's K+V tile is at most 4 KiB (more waves keep
+  // more small loads in flight), else one
+  static constexpr int kPerCu = (k16 ? 2 : 1) * 2 * kBlock * D <= 4096 ? 2 : 1;
 };
 constexpr float kF16PScale = 1024.f;  // f16 pools: P enters the P.V product times 2^10
 
@@ -1174,48 +1183,69 @@ __device__ __forceinline__ f4v_t mfma_pv(const u32x2 &p, const u32x2 &v, const f
                                                    __builtin_bit_cast(s4v_t, v), c, 0, 0, 0);
 }
 
-// First of the 8 dims that lane group g16 supplies at k-step kk (same map for K and q).
+// First of the 8 dims that lane group g16 supplies at k-step kk (same map for K and
+// q): k-steps 2j and 2j + 1 cover dims [64j + 16*g16, +16).
 __device__ __forceinline__ int mx_dim0(int kk, int g16) {
-  return (kk < 2 ? 0 : 64) + 16 * g16 + 8 * (kk & 1);
+  return 64 * (kk >> 1) + 16 * g16 + 8 * (kk & 1);
 }
 
+// NW consecutive words at p (NW = 1, 2 or 4: one load).
+template <int NW, bool NT>
+__device__ __forceinline__ void load_words(uint32_t *w, const char *p) {
+  if constexpr (NW == 4) {
+    const u32x4 x = load_tile_part<u32x4, NT>(p);
+    w[0] = x[0]; w[1] = x[1]; w[2] = x[2]; w[3] = x[3];
+  } else if constexpr (NW == 2) {
+    const u32x2 x = load_tile_part<u32x2, NT>(p);
+    w[0] = x[0]; w[1] = x[1];
+  } else {
+    w[0] = load_tile_part<uint32_t, NT>(p);
+  }
+}
+
+// One tile's operands in lane (c16, g16).
+template <int D>
 struct Q8Tile {
-  u32x4 k0, k1;  // key row c16: dims [16*g16, +16) and [64 + 16*g16, +16)
-  u32x2 v[4];    // value row 4*g16 + i: dims [8*c16, +8)
-  float ks, vs;  // the tile's K and V scales
+  u32x4 k[D / 64];         // key row c16: dims [64j + 16*g16, +16), k-steps 2j, 2j + 1
+  uint32_t v[4][D / 64];   // value row 4*g16 + i: dims [(D/16)*c16, +D/16), one code a byte
+  float ks, vs;            // the tile's K and V scales
 };
+template <int D>
 struct Q16Tile {
-  u32x4 k[4];    // key row c16: dims mx_dim0(kk, g16) .. +7, the A operand of k-step kk
-  u32x4 v[4];    // value row 4*g16 + i: dims [8*c16, +8)
+  u32x4 k[D / 32];         // key row c16: dims mx_dim0(kk, g16) .. +7, the A operand of k-step kk
+  uint32_t v[4][D / 32];   // value row 4*g16 + i: dims [(D/16)*c16, +D/16), two a word
 };
-template <int KV>
-using MxTileOf = std::conditional_t<MxGeom<KV, 128, 8>::k16, Q16Tile, Q8Tile>;
+template <int KV, int D>
+using MxTileOf = std::conditional_t<MxGeom<KV, D, 8>::k16, Q16Tile<D>, Q8Tile<D>>;
 
+template <int D>
 struct MxAcc {
-  f4v_t o[8];  // o[e][i] = O[head 4*g16 + i][dim 8*c16 + e]
-  float m, l;  // head c16: running max (log2 units), this lane's running sum
+  f4v_t o[D / 16];  // o[e][i] = O[head 4*g16 + i][dim (D/16)*c16 + e]
+  float m, l;       // head c16: running max (log2 units), this lane's running sum
 };
 
-// f16 P.V product (f16 pools at a group of 8)
+// f16 P.V product (f16 pools)
 __device__ __forceinline__ f4v_t mfma_pv_f16(const u32x2 &p, const u32x2 &v, const f4v_t &c) {
   typedef _Float16 h4v_t __attribute__((ext_vector_type(4)));
   return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4v_t, p),
                                                __builtin_bit_cast(h4v_t, v), c, 0, 0, 0);
 }
 
-template <int KV, int QT, bool MASK>
-__device__ __forceinline__ void mx_tile(MxAcc &st, const u32x4 *qb, const MxTileOf<KV> &t,
+template <int KV, int QT, int D, bool MASK>
+__device__ __forceinline__ void mx_tile(MxAcc<D> &st, const u32x4 *qb, const MxTileOf<KV, D> &t,
                                         float qk_scale, int valid_rows, int g16) {
-  constexpr bool k16 = MxGeom<KV, 128, 8>::k16;
+  using Gm = MxGeom<KV, D, 8>;
+  constexpr bool k16 = Gm::k16;
+  constexpr int NE = Gm::NE, KS = Gm::KS;
   constexpr int T16 = QT == PA_F16 ? PA_F16 : PA_BF16;
   f4v_t sacc = f4v_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
+  for (int kk = 0; kk < KS; ++kk) {
     u32x4 ka;
     if constexpr (k16) {
       ka = t.k[kk];  // as stored
     } else {
-      const u32x4 &kw = kk < 2 ? t.k0 : t.k1;
+      const u32x4 &kw = t.k[kk >> 1];
       const uint32_t w0 = kw[2 * (kk & 1)], w1 = kw[2 * (kk & 1) + 1];
       ka[0] = codes2_to_16<KV, T16, false>(w0);
       ka[1] = codes2_to_16<KV, T16, true>(w0);
@@ -1249,7 +1279,7 @@ __device__ __forceinline__ void mx_tile(MxAcc &st, const u32x4 *qb, const MxTile
 #pragma unroll
     for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * g16 + i, kWave);
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
+    for (int e = 0; e < NE; ++e)
 #pragma unroll
       for (int i = 0; i < 4; ++i) st.o[e][i] *= ar[i];
   }
@@ -1279,12 +1309,15 @@ __device__ __forceinline__ void mx_tile(MxAcc &st, const u32x4 *qb, const MxTile
   }
   if constexpr (k16) {
     // value rows past the context may hold anything (NaN included): zero their bits
-    u32x4 vr[4];
+    constexpr int NW = D / 32;
+    uint32_t vr[4][NW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vr[i] = ok[i] ? t.v[i] : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      // keys 0..3 of dim 8*c16 + e: the low or high halves of word e/2 of the rows
+      for (int w = 0; w < NW; ++w) vr[i][w] = ok[i] ? t.v[i][w] : 0u;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      // keys 0..3 of dim NE*c16 + e: the low or high halves of word e/2 of the rows
       const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
       u32x2 vb;
       vb[0] = __builtin_amdgcn_perm(vr[1][e >> 1], vr[0][e >> 1], sel);
@@ -1301,14 +1334,14 @@ __device__ __forceinline__ void mx_tile(MxAcc &st, const u32x4 *qb, const MxTile
   }
 
   // value rows past the context may hold anything (NaN included): zero their bits
-  uint32_t vr[4][2];
+  constexpr int NW = D / 64;
+  uint32_t vr[4][NW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    vr[i][0] = ok[i] ? t.v[i][0] : 0u;
-    vr[i][1] = ok[i] ? t.v[i][1] : 0u;
-  }
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+    for (int w = 0; w < NW; ++w) vr[i][w] = ok[i] ? t.v[i][w] : 0u;
+#pragma unroll
+  for (int c = 0; c < NW; ++c) {
     // bytes (r0.b, r1.b, ...) interleaved, then one word per dim: keys 0..3 of dim 4c + m
     const uint32_t t01l = __builtin_amdgcn_perm(vr[1][c], vr[0][c], 0x05010400u);
     const uint32_t t01h = __builtin_amdgcn_perm(vr[1][c], vr[0][c], 0x07030602u);
@@ -1332,11 +1365,11 @@ __device__ __forceinline__ void mx_tile(MxAcc &st, const u32x4 *qb, const MxTile
 
 // Write the wave's result for (s, kv head h): the normalised output when single,
 // else the partial (m, l, acc) of `piece`.
-template <int KV, int QT, int G>
-__device__ __forceinline__ void mx_emit(const DecodeArgs &a, const MxAcc &st, int s, int h,
+template <int KV, int QT, int D, int G>
+__device__ __forceinline__ void mx_emit(const DecodeArgs &a, const MxAcc<D> &st, int s, int h,
                                         bool single, int piece, int lane) {
   constexpr float kOut = KV == PA_F16 ? 1.f / kF16PScale : 1.f;  // undo the P scale of f16 pools
-  constexpr int D = 128;
+  constexpr int NE = D / 16;
   const int g16 = lane >> 4, c16 = lane & 15;
   float L = st.l;
   L += xor_lanes<16>(L);
@@ -1356,23 +1389,28 @@ __device__ __forceinline__ void mx_emit(const DecodeArgs &a, const MxAcc &st, in
     const int64_t orow = qrow * a.num_q_heads + h * G + 4 * g16 + i;          // output
     if (single) {
       const float inv = kOut / Lh[i];
-      u32x4 pk;
+      uint32_t pk[NE / 2];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < NE / 2; ++e) {
         const float x = st.o[2 * e][i] * inv, y = st.o[2 * e + 1][i] * inv;
         if constexpr (QT == PA_F16)
           pk[e] = __builtin_bit_cast(uint32_t, h2_t{(_Float16)x, (_Float16)y});
         else
           pk[e] = pack_bf16(x, y);
       }
-      *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(a.out) + (orow * D + 8 * c16) * 2) = pk;
+      char *dst = reinterpret_cast<char *>(a.out) + (orow * D + NE * c16) * 2;
+      if constexpr (NE == 8)
+        *reinterpret_cast<u32x4 *>(dst) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+      else
+        *reinterpret_cast<u32x2 *>(dst) = u32x2{pk[0], pk[1]};
     } else {
       const int64_t r = row * a.max_parts + piece;
-      float *dst = a.ws_acc + r * D + 8 * c16;
-      *reinterpret_cast<f4v_t *>(dst) =
-          f4v_t{st.o[0][i], st.o[1][i], st.o[2][i], st.o[3][i]} * kOut;
-      *reinterpret_cast<f4v_t *>(dst + 4) =
-          f4v_t{st.o[4][i], st.o[5][i], st.o[6][i], st.o[7][i]} * kOut;
+      float *dst = a.ws_acc + r * D + NE * c16;
+#pragma unroll
+      for (int e4 = 0; e4 < NE / 4; ++e4)
+        *reinterpret_cast<f4v_t *>(dst + 4 * e4) =
+            f4v_t{st.o[4 * e4][i], st.o[4 * e4 + 1][i], st.o[4 * e4 + 2][i], st.o[4 * e4 + 3][i]} *
+            kOut;
       if (c16 == 0) {
         a.ws_m[r] = mh[i];
         a.ws_l[r] = Lh[i];
@@ -1381,21 +1419,23 @@ __device__ __forceinline__ void mx_emit(const DecodeArgs &a, const MxAcc &st, in
   }
 }
 
-template <int KV, int QT, int G, bool NT>
+template <int KV, int QT, int D, int G, bool NT>
 struct MxPath {
-  static constexpr bool k16 = MxGeom<KV, 128, 8>::k16;
-  static constexpr int D = 128, E = k16 ? 2 : 1, kTileBytes = kBlock * D * E;
-  using Tile = MxTileOf<KV>;
+  using Gm = MxGeom<KV, D, G>;
+  static constexpr bool k16 = Gm::k16;
+  static constexpr int E = k16 ? 2 : 1, KS = Gm::KS, NE = Gm::NE, kTileBytes = kBlock * D * E;
+  static constexpr int NWV = D * E / 64;  // words of a lane's value slice
+  using Tile = MxTileOf<KV, D>;
   const DecodeArgs &a;
   const int lane, g16, c16;
   const char *kbase, *vbase;
-  u32x4 qb[4], qn[4];  // B operand per k-step: q[head c16][8 dims]; qn: next segment's
-  MxAcc st;
+  u32x4 qb[KS], qn[KS];  // B operand per k-step: q[head c16][8 dims]; qn: next segment's
+  MxAcc<D> st;
 
   __device__ __forceinline__ MxPath(const DecodeArgs &args, int ln)
       : a(args), lane(ln), g16(ln >> 4), c16(ln & 15),
         kbase(reinterpret_cast<const char *>(args.k) + (ln & 15) * D * E + 16 * E * (ln >> 4)),
-        vbase(reinterpret_cast<const char *>(args.v) + 4 * (ln >> 4) * D * E + 8 * E * (ln & 15)) {}
+        vbase(reinterpret_cast<const char *>(args.v) + 4 * (ln >> 4) * D * E + NE * E * (ln & 15)) {}
 
   // Tile j of segment sg.  16-bit pools, with a fused append (k_new set): the
   // newest row of the segment -- row tail - 1 of its last tile, not yet in the pool
@@ -1406,63 +1446,62 @@ struct MxPath {
     if constexpr (k16) {
       const int nr = (a.k_new != nullptr && j == sg.nblk - 1) ? sg.tail - 1 : -1;
       const int64_t no = ((int64_t)sg.s * a.num_kv_heads + sg.h) * (D * E);
-      const char *kn = reinterpret_cast<const char *>(a.k_new) + no + 32 * g16;
-      const char *vn = reinterpret_cast<const char *>(a.v_new) + no + 16 * c16;
+      const char *kn = reinterpret_cast<const char *>(a.k_new) + no + 16 * E * g16;
+      const char *vn = reinterpret_cast<const char *>(a.v_new) + no + NE * E * c16;
       const char *kp = c16 == nr ? kn : kbase + tile * kTileBytes;
-      t.k[0] = load_tile_part<u32x4, NT>(kp);
-      t.k[1] = load_tile_part<u32x4, NT>(kp + 16);
-      t.k[2] = load_tile_part<u32x4, NT>(kp + 128);
-      t.k[3] = load_tile_part<u32x4, NT>(kp + 144);
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+        t.k[kk] = load_tile_part<u32x4, NT>(kp + (mx_dim0(kk, 0)) * E);
       const char *vp = vbase + tile * kTileBytes;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        t.v[i] = load_tile_part<u32x4, NT>(4 * g16 + i == nr ? vn : vp + i * D * E);
+        load_words<NWV, NT>(t.v[i], 4 * g16 + i == nr ? vn : vp + i * D * E);
     } else {
       const char *kp = kbase + tile * kTileBytes;
-      t.k0 = load_tile_part<u32x4, NT>(kp);
-      t.k1 = load_tile_part<u32x4, NT>(kp + 64);
+#pragma unroll
+      for (int j2 = 0; j2 < D / 64; ++j2) t.k[j2] = load_tile_part<u32x4, NT>(kp + 64 * j2);
       const char *vp = vbase + tile * kTileBytes;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) t.v[i] = load_tile_part<u32x2, NT>(vp + i * D);
+      for (int i = 0; i < 4; ++i) load_words<NWV, NT>(t.v[i], vp + i * D);
       t.ks = a.k_scale[tile >> a.bs_shift];
       t.vs = a.v_scale[tile >> a.bs_shift];
     }
   }
   __device__ __forceinline__ void prefetch_q(const StreamSeg &sg) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qn[kk] = u32x4{0, 0, 0, 0};
+    for (int kk = 0; kk < KS; ++kk) qn[kk] = u32x4{0, 0, 0, 0};
     if (c16 < G) {
       const char *qp = reinterpret_cast<const char *>(a.q) +
                        ((decode_row(a, sg.s) * a.num_q_heads + sg.h * G + c16) * D) * 2;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
+      for (int kk = 0; kk < KS; ++kk)
         qn[kk] = *reinterpret_cast<const u32x4 *>(qp + mx_dim0(kk, g16) * 2);
     }
   }
   __device__ __forceinline__ void begin_segment() {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qb[kk] = qn[kk];
+    for (int kk = 0; kk < KS; ++kk) qb[kk] = qn[kk];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) st.o[e] = f4v_t{0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < NE; ++e) st.o[e] = f4v_t{0.f, 0.f, 0.f, 0.f};
     st.m = kNegBig;
     st.l = 0.f;
   }
   __device__ __forceinline__ void compute(const Tile &t, int valid, bool masked) {
     if (masked)
-      mx_tile<KV, QT, true>(st, qb, t, a.qk_scale, valid, g16);
+      mx_tile<KV, QT, D, true>(st, qb, t, a.qk_scale, valid, g16);
     else
-      mx_tile<KV, QT, false>(st, qb, t, a.qk_scale, kBlock, g16);
+      mx_tile<KV, QT, D, false>(st, qb, t, a.qk_scale, kBlock, g16);
   }
   __device__ __forceinline__ void emit(const StreamSeg &sg, bool single, int piece) {
-    mx_emit<KV, QT, G>(a, st, sg.s, sg.h, single, piece, lane);
+    mx_emit<KV, QT, D, G>(a, st, sg.s, sg.h, single, piece, lane);
   }
 };
 
-template <int KV, int QT, int G, bool NT>
+template <int KV, int QT, int D, int G, bool NT>
 __device__ __forceinline__ void decode_stream_mx(const DecodeArgs &a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kDecodeWaves + threadIdx.x / kWave);
-  MxPath<KV, QT, G, NT> path(a, lane);
+  MxPath<KV, QT, D, G, NT> path(a, lane);
   stream_run(a, path, w, lane);
 }
 

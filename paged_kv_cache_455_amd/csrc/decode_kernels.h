@@ -12,18 +12,13 @@ __global__ __launch_bounds__(kDecodeWaves *kWave) void pa_decode_stream_kernel(D
   decode_stream<KV, QT, D, G, NT>(a);
 }
 
-// 1-byte KV with a GQA group of 2, 4 or 8 (both products on MFMA): its state fits
-// two waves per SIMD without spilling, which hides more of each wave's load latency.
-template <int KV, int QT, int G, bool NT>
-__global__ __launch_bounds__(kDecodeWaves *kWave, 2) void pa_decode_stream_q8_kernel(DecodeArgs a) {
-  decode_stream_mx<KV, QT, G, NT>(a);
-}
-
-// 16-bit KV with a GQA group of 8 on the same MFMA tile: its tiles are twice the
-// bytes per lane, one wave per SIMD.
-template <int KV, int QT, int G, bool NT>
-__global__ __launch_bounds__(kDecodeWaves *kWave) void pa_decode_stream_m16_kernel(DecodeArgs a) {
-  decode_stream_mx<KV, QT, G, NT>(a);
+// Both products on MFMA (MxGeom::kOn).  PER_CU workgroups per CU: two where a
+// wave's K+V tile is at most 4 KiB (1-byte pools; 16-bit ones at head_dim 64), whose
+// state then fits two waves per SIMD without spilling and hides more of each wave's
+// load latency; one for 16-bit pools at head_dim 128.
+template <int KV, int QT, int D, int G, bool NT, int PER_CU>
+__global__ __launch_bounds__(kDecodeWaves *kWave, PER_CU) void pa_decode_stream_mx_kernel(DecodeArgs a) {
+  decode_stream_mx<KV, QT, D, G, NT>(a);
 }
 
 // One wave per (sequence, query head); four per workgroup.
@@ -36,10 +31,8 @@ __global__ __launch_bounds__(4 * kWave) void pa_decode_stream_merge_kernel(Decod
 
 template <int KV, int QT, int D, int G, bool NT>
 static constexpr auto stream_kernel() {
-  if constexpr (MxGeom<KV, D, G>::kOn && MxGeom<KV, D, G>::k16)
-    return pa_decode_stream_m16_kernel<KV, QT, G, NT>;
-  else if constexpr (MxGeom<KV, D, G>::kOn)
-    return pa_decode_stream_q8_kernel<KV, QT, G, NT>;
+  if constexpr (MxGeom<KV, D, G>::kOn)
+    return pa_decode_stream_mx_kernel<KV, QT, D, G, NT, MxGeom<KV, D, G>::kPerCu>;
   else
     return pa_decode_stream_kernel<KV, QT, D, G, NT>;
 }
@@ -63,10 +56,11 @@ static Residency resident_groups() {
     return Residency{0, 0};
   // The VALU-path kernels run one workgroup per CU (a wave per SIMD) even where
   // their registers would allow two: twice the waves split twice as many segments,
-  // and config 2 measured 98.0 against 95.2 us at two; the 16-bit MFMA tile too
-  // (99.5 against 105.6 us at a group of 8).  The 1-byte MFMA path keeps the two
-  // workgroups per CU it was tuned at.
-  if (!MxGeom<KV, D, G>::kOn || MxGeom<KV, D, G>::k16) per_cu = per_cu > 1 ? 1 : per_cu;
+  // and config 2 measured 98.0 against 95.2 us at two; the 16-bit MFMA tile at
+  // head_dim 128 too (99.5 against 105.6 us at a group of 8).  The MFMA tiles of at
+  // most 4 KiB run two (the 16 x 32768-token fp8 decode: 179 against 198 us at one).
+  const int cap = MxGeom<KV, D, G>::kOn ? MxGeom<KV, D, G>::kPerCu : 1;
+  per_cu = per_cu > cap ? cap : per_cu;
   per_cu = per_cu > 0 ? per_cu : 1;
   cached = Residency{cus * per_cu, per_cu};
   return cached;

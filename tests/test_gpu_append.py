@@ -87,6 +87,8 @@ CASES = [  # kv, Hq, Hkv, D, block size, contexts
     ("bf16", 16, 8, 128, 32, [2, 17, 48, 300, 1025]),
     ("f32", 16, 4, 128, 32, [1, 33, 64, 95]),
     ("f16", 64, 8, 128, 16, [1, 2, 15, 16, 17, 31, 33, 129, 1000, 2049]),  # MFMA tile, f16 P.V
+    ("f16", 32, 8, 64, 16, [1, 2, 15, 16, 17, 31, 33, 129, 1000, 2049]),   # MFMA tile, D 64
+    ("bf16", 16, 8, 64, 32, [1, 31, 32, 33, 64, 65, 700, 2048]),
 ]
 
 

@@ -127,7 +127,8 @@ def test_quantised_write_bit_exact(kind):
     ("fp8", "f16", 8, 4, 64, False), ("i8", "bf16", 64, 8, 128, False),
     ("i8", "f16", 32, 4, 128, True), ("f16", "f16", 64, 8, 128, False),
     ("bf16", "bf16", 64, 8, 128, True), ("fp8", "bf16", 32, 8, 128, False),
-    ("i8", "f16", 16, 8, 128, True),
+    ("i8", "f16", 16, 8, 128, True), ("bf16", "bf16", 32, 8, 64, True),
+    ("i8", "f16", 64, 8, 64, False), ("f16", "f16", 64, 8, 64, False),
 ])
 def test_decode_ragged(kv, qd, hq, hkv, hd, shared):
     b = W.decode_batch(hq * 11 + hd, EDGES, hq, hkv, hd, kv, qd, poison=True, div=hd ** 0.5,

@@ -145,6 +145,8 @@ def test_decode_tiny_fp32_poisoned():
     ("i8", "bf16", 64, 8, 128), ("i8", "f16", 16, 16, 128), ("i8", "f16", 32, 4, 128),
     ("fp8", "bf16", 32, 8, 128), ("fp8", "f16", 16, 8, 128), ("i8", "bf16", 16, 8, 128),
     ("i8", "f16", 8, 2, 128),
+    ("f16", "f16", 32, 8, 64), ("bf16", "bf16", 64, 8, 64), ("f16", "f16", 16, 8, 64),
+    ("fp8", "bf16", 64, 8, 64), ("i8", "bf16", 32, 8, 64), ("fp8", "f16", 16, 8, 64),
 ])
 def test_decode_shapes_ragged(kv, qd, hq, hkv, hd):
     # contexts around block and partition edges (partitions are 8-32 blocks); data scaled
@@ -162,6 +164,7 @@ def test_decode_shapes_ragged(kv, qd, hq, hkv, hd):
     ("fp8", "bf16", 64, 8, 128), ("fp8", "f16", 8, 4, 64),
     ("i8", "bf16", 64, 8, 128), ("i8", "f16", 16, 16, 128),
     ("fp8", "bf16", 16, 8, 128), ("i8", "f16", 32, 8, 128),
+    ("f16", "f16", 64, 8, 64), ("i8", "bf16", 16, 8, 64),
 ])
 def test_decode_shapes_ragged_shared_pool(kv, qd, hq, hkv, hd):
     # A pool flagged as holding shared blocks (cached K/V loads): the same contexts as
@@ -208,16 +211,17 @@ def test_decode_peaked_every_group_and_head_dim(kv, hd, g):
 
 
 @pytest.mark.parametrize("kv,qd", [("fp8", "bf16"), ("i8", "f16")])
+@pytest.mark.parametrize("hd", [64, 128])
 @pytest.mark.parametrize("g", [1, 2, 4, 8])
-def test_decode_peaked_one_byte_every_group(kv, qd, g):
-    """1-byte pools, head_dim 128, every GQA group (1 on the VALU path, 2-8 on the
-    matrix-core tile with the heads padded to 16): unscaled N(0,1) data, contexts at
-    block and split edges, NaN past every context; per element the larger of the
-    1-byte tolerance and one ulp of the output."""
+def test_decode_peaked_one_byte_every_group(kv, qd, hd, g):
+    """1-byte pools, every GQA group (1 on the VALU path, 2-8 on the matrix-core
+    tile with the heads padded to 16): unscaled N(0,1) data, contexts at block and
+    split edges, NaN past every context; per element the larger of the 1-byte
+    tolerance and one ulp of the output."""
     ctx = [1, 2, 3, 15, 16, 17, 31, 100, 127, 128, 129, 511, 513, 1000, 2049, 3333]
     hkv = 2 if g == 8 else 4
-    b = W.decode_batch(500 + 10 * g, ctx, g * hkv, hkv, 128, kv, qd, poison=True,
-                       name=f"peaked-{kv}-{qd}-g{g}")
+    b = W.decode_batch(500 + 10 * g + hd, ctx, g * hkv, hkv, hd, kv, qd, poison=True,
+                       name=f"peaked-{kv}-{qd}-g{g}-d{hd}")
     b = poison_tails(b)
     out = run_decode(Dev(b))
     torch.cuda.synchronize()
@@ -295,11 +299,12 @@ def test_decode_deterministic_and_block_permutation_invariant():
 @pytest.mark.parametrize("kv,qd,hq,hkv", [("f16", "f16", 32, 8), ("bf16", "bf16", 16, 8),
                                            ("fp8", "bf16", 64, 8), ("i8", "f16", 32, 8),
                                            ("fp8", "f16", 32, 8), ("i8", "bf16", 16, 8)])
-def test_decode_cached_and_streamed_loads_agree(kv, qd, hq, hkv):
+@pytest.mark.parametrize("hd", [64, 128])
+def test_decode_cached_and_streamed_loads_agree(kv, qd, hq, hkv, hd):
     # the pool's shared-blocks flag only changes the cache hint of the K/V loads:
     # both kernels give the same bits, and both match the oracle
-    b = W.decode_batch(31, [1, 17, 300, 1024, 2100], hq, hkv, 128, kv, qd, poison=True,
-                       div=128 ** 0.5, name=f"hint-{kv}-{qd}")
+    b = W.decode_batch(31 + hd, [1, 17, 300, 1024, 2100], hq, hkv, hd, kv, qd, poison=True,
+                       div=hd ** 0.5, name=f"hint-{kv}-{qd}-d{hd}")
     b = poison_tails(b)
     streamed = run_decode(Dev(b, shared_blocks=False)).clone()
     cached = run_decode(Dev(b, shared_blocks=True)).clone()
