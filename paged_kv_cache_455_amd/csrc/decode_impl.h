@@ -1119,8 +1119,8 @@ typedef float f4v_t __attribute__((ext_vector_type(4)));
 
 // 16-bit pools (f16, bf16) take the same tile, where the VALU path's dot products
 // and weighted sums per lane no longer keep up with the loads (Llama-3-70B-shaped
-// decode, a group of 8 at D 128: 147 us against 98 us at a group of 4 for the same
-// K/V bytes): K enters the score product as stored; V is transposed by 16-bit
+// decode, a group of 8 at D 128, on the VALU path: 147 us against 98 us at a group of
+// 4 for the same K/V bytes): K enters the score product as stored; V is transposed by 16-bit
 // permutes; for f16 pools the P.V product runs in f16 (P as f16 hi + lo, scaled by
 // 2^10 so that small weights stay clear of f16's subnormals; the output takes the
 // 2^-10 back), for bf16 pools in bf16 as for the codes.
@@ -1129,11 +1129,13 @@ struct MxGeom {
   static constexpr bool k16 = KV == PA_F16 || KV == PA_BF16;
   static constexpr bool k8 = KV == PA_FP8_E4M3 || KV == PA_I8;
   // D 128: 1-byte pools at groups of 2, 4 and 8 (at 4 the VALU path's per-code
-  // converts held fp8 to 3.3 TB/s), 16-bit pools at 8 only (at 4 and below their VALU
-  // path streams at the memory's rate).  D 64: both widths at groups of 2, 4 and 8,
-  // where the VALU path's per-key work over half the bytes held 16-bit pools to
-  // 2.8-4.6 TB/s and 1-byte pools to 1.2-2.7 TB/s.
-  static constexpr bool kOn = D == 128   ? (k16 ? G == 8 : (k8 && G >= 2))
+  // converts held fp8 to 3.3 TB/s); 16-bit pools at 4 and 8 (at 4 the tile's lighter
+  // vector work leaves more of each wave's time to cover load latency: Llama-3-8B-
+  // shaped decode 94.6 -> 92.8 us, prefix sharing 158.6 -> 143.9 us), not at 2, where
+  // the two paths are level within a few percent either way.  D 64: both widths at
+  // groups of 2, 4 and 8, where the VALU path's per-key work over half the bytes held
+  // 16-bit pools to 2.8-4.6 TB/s and 1-byte pools to 1.2-2.7 TB/s.
+  static constexpr bool kOn = D == 128   ? (k16 ? G >= 4 : (k8 && G >= 2))
                               : D == 64 ? ((k16 || k8) && G >= 2)
                                         : false;
   static constexpr int NE = D / 16;  // P.V products per tile: dims per lane
@@ -1381,7 +1383,13 @@ __device__ __forceinline__ void mx_emit(const DecodeArgs &a, const MxAcc<D> &st,
     Lh[i] = __shfl(L, 4 * g16 + i, kWave);
   }
   if (4 * g16 >= G) return;  // padding heads
-  const int64_t qrow = decode_row(a, s);
+  // the output row: by a scalar read for 16-bit pools; 1-byte pools have the next
+  // tile's scales in flight as scalar loads, which that read's wait would drain
+  int64_t qrow;
+  if constexpr (MxGeom<KV, D, G>::k16)
+    qrow = single ? decode_row_uniform(a, s) : 0;
+  else
+    qrow = decode_row(a, s);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (G < 4 && i >= G) break;
