@@ -1124,6 +1124,15 @@ typedef float f4v_t __attribute__((ext_vector_type(4)));
 // permutes; for f16 pools the P.V product runs in f16 (P as f16 hi + lo, scaled by
 // 2^10 so that small weights stay clear of f16's subnormals; the output takes the
 // 2^-10 back), for bf16 pools in bf16 as for the codes.
+// Workgroups per CU of the balanced-split stream kernels (either path): two where a
+// wave's K+V tile is at most 4 KiB, i.e. 1-byte pools and 16-bit ones at head_dim
+// 64 (more waves keep more of the small loads in flight), else one.
+template <int KV, int D>
+constexpr int stream_per_cu() {
+  constexpr int E = KV == PA_F32 ? 4 : (KV == PA_F16 || KV == PA_BF16) ? 2 : 1;
+  return 2 * kBlock * D * E <= 4096 ? 2 : 1;
+}
+
 template <int KV, int D, int G>
 struct MxGeom {
   static constexpr bool k16 = KV == PA_F16 || KV == PA_BF16;
@@ -1140,9 +1149,7 @@ struct MxGeom {
                                         : false;
   static constexpr int NE = D / 16;  // P.V products per tile: dims per lane
   static constexpr int KS = D / 32;  // k-steps of the score product
-  // workgroups per CU: two where a wave's K+V tile is at most 4 KiB (more waves keep
-  // more small loads in flight), else one
-  static constexpr int kPerCu = (k16 ? 2 : 1) * 2 * kBlock * D <= 4096 ? 2 : 1;
+  static constexpr int kPerCu = stream_per_cu<KV, D>();
 };
 constexpr float kF16PScale = 1024.f;  // f16 pools: P enters the P.V product times 2^10
 

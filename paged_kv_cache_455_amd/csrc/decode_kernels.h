@@ -54,12 +54,13 @@ static Residency resident_groups() {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kDecodeWaves * kWave, 0) !=
       hipSuccess)
     return Residency{0, 0};
-  // The VALU-path kernels run one workgroup per CU (a wave per SIMD) even where
-  // their registers would allow two: twice the waves split twice as many segments,
-  // and config 2 measured 98.0 against 95.2 us at two; the 16-bit MFMA tile at
-  // head_dim 128 too (99.5 against 105.6 us at a group of 8).  The MFMA tiles of at
-  // most 4 KiB run two (the 16 x 32768-token fp8 decode: 179 against 198 us at one).
-  const int cap = MxGeom<KV, D, G>::kOn ? MxGeom<KV, D, G>::kPerCu : 1;
+  // Kernels whose K+V tile is 8 KiB or more run one workgroup per CU (a wave per
+  // SIMD) even where their registers would allow two: twice the waves split twice
+  // as many segments, and config 2 measured 98.0 against 95.2 us at two on the VALU
+  // path, the 16-bit MFMA tile 105.6 against 99.5 us at a group of 8.  Tiles of at
+  // most 4 KiB run two (the 16 x 32768-token fp8 decode: 179 against 198 us at one;
+  // MHA-shaped fp8 at head_dim 64 on the VALU path 52.3 against 36.4 us).
+  const int cap = stream_per_cu<KV, D>();
   per_cu = per_cu > cap ? cap : per_cu;
   per_cu = per_cu > 0 ? per_cu : 1;
   cached = Residency{cus * per_cu, per_cu};
