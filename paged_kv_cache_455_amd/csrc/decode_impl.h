@@ -1149,7 +1149,6 @@ struct MxGeom {
                                         : false;
   static constexpr int NE = D / 16;  // P.V products per tile: dims per lane
   static constexpr int KS = D / 32;  // k-steps of the score product
-  static constexpr int kPerCu = stream_per_cu<KV, D>();
 };
 constexpr float kF16PScale = 1024.f;  // f16 pools: P enters the P.V product times 2^10
 

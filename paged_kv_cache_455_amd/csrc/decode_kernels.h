@@ -12,10 +12,11 @@ __global__ __launch_bounds__(kDecodeWaves *kWave) void pa_decode_stream_kernel(D
   decode_stream<KV, QT, D, G, NT>(a);
 }
 
-// Both products on MFMA (MxGeom::kOn).  PER_CU workgroups per CU: two where a
-// wave's K+V tile is at most 4 KiB (1-byte pools; 16-bit ones at head_dim 64), whose
-// state then fits two waves per SIMD without spilling and hides more of each wave's
-// load latency; one for 16-bit pools at head_dim 128.
+// Both products on MFMA (MxGeom::kOn).  PER_CU workgroups per CU
+// (stream_kernel_per_cu): two where a wave's K+V tile is at most 4 KiB (1-byte
+// pools; 16-bit ones at head_dim 64) or the pool's blocks are shared, whose state
+// then fits two waves per SIMD without spilling and hides more of each wave's load
+// latency; else one.
 template <int KV, int QT, int D, int G, bool NT, int PER_CU>
 __global__ __launch_bounds__(kDecodeWaves *kWave, PER_CU) void pa_decode_stream_mx_kernel(DecodeArgs a) {
   decode_stream_mx<KV, QT, D, G, NT>(a);
@@ -29,10 +30,20 @@ __global__ __launch_bounds__(4 * kWave) void pa_decode_stream_merge_kernel(Decod
   merge_stream<QT, D>(a, row / a.num_q_heads, row % a.num_q_heads, threadIdx.x % kWave);
 }
 
+// Workgroups per CU of the stream kernel of (KV, D, G, NT): stream_per_cu's rule by
+// tile size, and two for the MFMA tile over a shared-block pool (cached loads), whose
+// hits in L2 and the Infinity Cache leave each wave waiting on latency more than on
+// HBM (prefix sharing, 16-bit at D 128: 143.5 against 138.8 us at two; the unshared
+// config-2 batch is 2.3 us slower at two).
+template <int KV, int D, int G, bool NT>
+constexpr int stream_kernel_per_cu() {
+  return MxGeom<KV, D, G>::kOn && !NT ? 2 : stream_per_cu<KV, D>();
+}
+
 template <int KV, int QT, int D, int G, bool NT>
 static constexpr auto stream_kernel() {
   if constexpr (MxGeom<KV, D, G>::kOn)
-    return pa_decode_stream_mx_kernel<KV, QT, D, G, NT, MxGeom<KV, D, G>::kPerCu>;
+    return pa_decode_stream_mx_kernel<KV, QT, D, G, NT, stream_kernel_per_cu<KV, D, G, NT>()>;
   else
     return pa_decode_stream_kernel<KV, QT, D, G, NT>;
 }
@@ -60,7 +71,7 @@ static Residency resident_groups() {
   // path, the 16-bit MFMA tile 105.6 against 99.5 us at a group of 8.  Tiles of at
   // most 4 KiB run two (the 16 x 32768-token fp8 decode: 179 against 198 us at one;
   // MHA-shaped fp8 at head_dim 64 on the VALU path 52.3 against 36.4 us).
-  const int cap = stream_per_cu<KV, D>();
+  const int cap = stream_kernel_per_cu<KV, D, G, NT>();
   per_cu = per_cu > cap ? cap : per_cu;
   per_cu = per_cu > 0 ? per_cu : 1;
   cached = Residency{cus * per_cu, per_cu};

@@ -114,6 +114,24 @@ def test_eager_decode_with_an_understated_length_bound():
         assert err <= TOL["f16"], (bound, err)
 
 
+@pytest.mark.parametrize("kv,qd,hq,hd", [("fp8", "bf16", 8, 128), ("i8", "f16", 8, 64),
+                                         ("bf16", "bf16", 8, 64)])
+def test_eager_decode_two_rounds_valu_path_understated_bound(kv, qd, hq, hd):
+    # MHA-shaped batches whose K+V tile is at most 4 KiB run the VALU path at two
+    # workgroups per CU, with the same two-round skew of the split: long and short
+    # contexts under a length bound far below the longest, against the oracle
+    b = W.decode_batch(63 + hd, [9000, 1, 40, 3000, 17, 2048, 12000, 5], hq, 8, hd, kv, qd,
+                       div=hd ** 0.5, name=f"two-round-valu-{kv}-d{hd}")
+    from .pa_testlib import Dev, oracle_decode_rows
+    d = Dev(b)
+    for bound in (256, b.max_seq_len):
+        out = pa.pa_decode(d.pool, d.q, d.bt, d.lens, bound, b.scale)
+        torch.cuda.synchronize()
+        err = max_err(out, oracle_decode_rows(b))
+        say(b.name, "bound", bound, "max_err", err)
+        assert err <= TOL[kv], (bound, err)
+
+
 def test_eager_decode_two_rounds_with_an_understated_length_bound():
     # The 1-byte decode runs two workgroups per CU, and the split gives the first
     # round tpw + d cost units per wave and the second tpw - d.  On the 16 x 32768
