@@ -14,9 +14,9 @@
 //    capacity streams an equal share of it, emitting a finished output for a
 //    segment it owns alone and a partial (m, l, acc) piece otherwise, merged by a
 //    second kernel;
-//  * the partitioned form (decode_partition; the mixed step's rows for fp32 and
-//    1-byte KV): one workgroup per (query row, kv head, context partition), 4
-//    waves taking blocks w, w+4, ... and merging through LDS.
+//  * the partitioned form (decode_partition; the mixed step's rows for fp32 KV):
+//    one workgroup per (query row, kv head, context partition), 4 waves taking
+//    blocks w, w+4, ... and merging through LDS.
 // In both, the GQA group of G query heads shares every K/V tile load; one
 // (block, kv head) tile is 16 x head_dim contiguous elements, and a wave-wide
 // load instruction reads 64 x 16 bytes (8 bytes for 1-byte codes) contiguous, so
@@ -24,8 +24,10 @@
 // and V alike; q.k partial sums are completed with DPP adds inside each row of
 // LPT lanes, after which the lanes hold finished scores for the P.V update; each
 // lane keeps its own running (max, sum, acc), merged across lanes at the end.
-// 1-byte KV with a GQA group of 8 runs both products of a tile on MFMA instead
-// (MxPath below).
+// Where that vector work per tile, not the loads, would set the pace -- 1-byte KV
+// at GQA groups 2-8, 16-bit KV at groups 4 and 8, both widths at head_dim 64 and
+// groups 2-8 (MxGeom) -- the balanced split runs both products of a tile on MFMA
+// instead (MxPath below).
 #pragma once
 
 #include <type_traits>
