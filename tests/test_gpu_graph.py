@@ -36,13 +36,14 @@ def _mirror_write(kv, k, v, ks, vs, kn, vn, slots):
     return k, v, ks, vs
 
 
-@pytest.mark.parametrize("kv,qd,hq,hkv,bs", [("f16", "f16", 32, 8, 16), ("bf16", "bf16", 16, 2, 32),
-                                             ("fp8", "bf16", 64, 8, 16), ("i8", "f16", 32, 4, 32),
-                                             ("fp8", "f16", 32, 8, 16)])
-def test_replays_match_eager_and_oracle(kv, qd, hq, hkv, bs):
+@pytest.mark.parametrize("kv,qd,hq,hkv,bs,hd", [("f16", "f16", 32, 8, 16, 128), ("bf16", "bf16", 16, 2, 32, 128),
+                                                ("fp8", "bf16", 64, 8, 16, 128), ("i8", "f16", 32, 4, 32, 128),
+                                                ("fp8", "f16", 32, 8, 16, 128), ("bf16", "bf16", 32, 8, 16, 64),
+                                                ("i8", "bf16", 64, 8, 32, 64)])
+def test_replays_match_eager_and_oracle(kv, qd, hq, hkv, bs, hd):
     ctx0 = np.array([5, 100, 700, 1500, 33, 64, 16, 1])
-    b = W.decode_batch(61, ctx0 + 1200, hq, hkv, 128, kv, qd, div=128 ** 0.5, with_new=True,
-                       name=f"graph-{kv}", block_size=bs)     # tables with room to grow
+    b = W.decode_batch(61, ctx0 + 1200, hq, hkv, hd, kv, qd, div=hd ** 0.5, with_new=True,
+                       name=f"graph-{kv}-d{hd}", block_size=bs)     # tables with room to grow
     say(b.name, "block", bs)
     S = b.num_seqs
     dev = lambda t: t.clone().cuda()
