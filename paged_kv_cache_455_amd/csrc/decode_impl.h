@@ -1526,23 +1526,31 @@ __device__ __forceinline__ void decode_stream_mx(const DecodeArgs &a) {
 // row of kv head h at its slot, the pool position of token n - 1 ("5688vip" chapter
 // 3, section 3.2: a new token's K/V goes at the end of the request's last block),
 // slot = block_tables[s][(n - 1) / bs] * bs + (n - 1) % bs.  Lanes 0..31 move K,
-// lanes 32..63 V, 16 bytes each (a row is at most 512 bytes).
+// lanes 32..63 V, 16 bytes each (a row is at most 512 bytes).  Two halves, so that
+// the caller can issue the row's load (which depends on nothing) together with its
+// own first loads, and the table read with its second.
 template <int D, int E>
-__device__ __forceinline__ void append_new_row(const DecodeArgs &a, int s, int h, int n, int lane) {
+__device__ __forceinline__ u32x4 append_load(const DecodeArgs &a, int s, int h, int lane) {
   constexpr int RB = D * E, CPR = RB / 16;
   static_assert(CPR <= 32, "row too wide");
+  const int c = lane & 31;
+  if (c >= CPR) return u32x4{0u, 0u, 0u, 0u};
+  const int64_t src = ((int64_t)s * a.num_kv_heads + h) * RB + c * 16;
+  return *reinterpret_cast<const u32x4 *>(
+      reinterpret_cast<const char *>(lane >= 32 ? a.v_new : a.k_new) + src);
+}
+template <int D, int E>
+__device__ __forceinline__ void append_store(const DecodeArgs &a, int s, int h, int n, int lane,
+                                             const u32x4 &row) {
+  constexpr int RB = D * E, CPR = RB / 16;
   const int bs = kBlock << a.bs_shift, p = n - 1;
   const int64_t blk = a.bt[(int64_t)s * a.max_blocks_per_seq + p / bs];
   const int64_t slot = blk * bs + p % bs;
   if (a.slots_out != nullptr && h == 0 && lane == 0) a.slots_out[s] = slot;
   const int c = lane & 31;
   if (c >= CPR) return;
-  const bool is_v = lane >= 32;
-  const int64_t src = ((int64_t)s * a.num_kv_heads + h) * RB + c * 16;
   const int64_t dst = ((blk * a.num_kv_heads + h) * bs + p % bs) * RB + c * 16;
-  const char *from = reinterpret_cast<const char *>(is_v ? a.v_new : a.k_new) + src;
-  char *to = reinterpret_cast<char *>(is_v ? a.pool_v : a.pool_k) + dst;
-  *reinterpret_cast<u32x4 *>(to) = *reinterpret_cast<const u32x4 *>(from);
+  *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(lane >= 32 ? a.pool_v : a.pool_k) + dst) = row;
 }
 
 // Second pass of the balanced split.  One wave per (sequence s, query head hq):
@@ -1553,6 +1561,14 @@ __device__ __forceinline__ void append_new_row(const DecodeArgs &a, int s, int h
 // Nothing to do where one wave owned the whole segment (pieces == 1).
 template <int QT, int D>
 __device__ __forceinline__ void merge_stream(const DecodeArgs &a, int s, int hq, int lane) {
+  // the split header and (fused append) the new K/V row, read beside the row's
+  // length (all in bounds)
+  const int h_t1 = a.hdr[0], h_t2 = a.hdr[1 + a.num_seqs], h_s = a.hdr[1 + s];
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int h = hq / G;
+  const bool append = a.k_new != nullptr && hq % G == 0;
+  u32x4 new_row = u32x4{0u, 0u, 0u, 0u};
+  if (append) new_row = append_load<D, dtype_bytes(QT)>(a, s, h, lane);
   if (a.qsl != nullptr && a.qsl[s + 1] - a.qsl[s] != 1) return;  // not a decode row
   const int n = a.ctx[s];
   const int64_t o = (decode_row(a, s) * a.num_q_heads + hq) * D;
@@ -1561,15 +1577,15 @@ __device__ __forceinline__ void merge_stream(const DecodeArgs &a, int s, int hq,
     if (a.slots_out != nullptr && hq == 0 && lane == 0) a.slots_out[s] = -1;
     return;
   }
-  const int G = a.num_q_heads / a.num_kv_heads;
-  const int h = hq / G;
-  if (a.k_new != nullptr && hq % G == 0) append_new_row<D, dtype_bytes(QT)>(a, s, h, n, lane);
   const int nblk = (n + kBlock - 1) / kBlock;
   // the split as stream_range made it
-  const SplitGeom sp{a.hdr[0], a.hdr[1 + a.num_seqs], a.skew > 0 ? a.num_waves / 2 : a.num_waves};
-  const int seg0 = a.hdr[1 + s] + h * (nblk + a.seg_cost) + a.seg_cost;
+  const SplitGeom sp{h_t1, h_t2, a.skew > 0 ? a.num_waves / 2 : a.num_waves};
+  const int seg0 = h_s + h * (nblk + a.seg_cost) + a.seg_cost;
   const int pieces = sp.wave_of(seg0 + nblk - 1) - sp.wave_of(seg0) + 1;
-  if (pieces <= 1) return;
+  if (pieces <= 1) {
+    if (append) append_store<D, dtype_bytes(QT)>(a, s, h, n, lane, new_row);
+    return;
+  }
   const int64_t r0 = ((int64_t)s * a.num_q_heads + hq) * a.max_parts;
   // acc: each wave-wide load brings PPL whole pieces, lane l taking dims
   // 4*(l % LP) .. +3 of piece PPL*j + l / LP (16 bytes a lane), so the NB loads in
@@ -1598,6 +1614,8 @@ __device__ __forceinline__ void merge_stream(const DecodeArgs &a, int s, int hq,
     }
   };
   load_acc(0);
+  // the append's table read goes out behind the pieces' loads
+  if (append) append_store<D, dtype_bytes(QT)>(a, s, h, n, lane, new_row);
   float M = mp;
   for (int p = lane + kWave; p < pieces; p += kWave) M = fmaxf(M, a.ws_m[r0 + p]);
   M = fmaxf(M, xor_lanes<1>(M));
