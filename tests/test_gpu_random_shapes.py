@@ -1,8 +1,7 @@
 """GPU parity over seeded random decode shapes and mixed steps: every KV type,
-head_dim 64 and 128,
-GQA groups 1-8, block sizes 16 and 32, shared-block (cached) and streamed pools,
-random batch sizes and context lengths mixed with block and split edges, NaN past
-every context.  Unscaled N(0,1) data ("peaked": the scores decide the output),
+head_dim 64 and 128, GQA groups 1-8, block sizes 16 and 32, shared-block (cached)
+and streamed pools, random batch sizes and context lengths mixed with block and
+split edges, NaN past every context.  Unscaled N(0,1) data ("peaked": the scores decide the output),
 each element held to the larger of its KV type's max-abs tolerance and one ulp of
 the output type at the oracle's value.  The cases cross the decode paths (VALU and
 matrix-core tiles, one or two workgroups per CU, the split's two-round skew) in
