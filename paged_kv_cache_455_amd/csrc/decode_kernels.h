@@ -33,8 +33,8 @@ __global__ __launch_bounds__(4 * kWave) void pa_decode_stream_merge_kernel(Decod
 // Workgroups per CU of the stream kernel of (KV, D, G, NT): stream_per_cu's rule by
 // tile size, and two for the MFMA tile over a shared-block pool (cached loads), whose
 // hits in L2 and the Infinity Cache leave each wave waiting on latency more than on
-// HBM (prefix sharing, 16-bit at D 128: 143.5 against 138.8 us at two; the unshared
-// config-2 batch is 2.3 us slower at two).
+// HBM (128 bf16 requests over a 1024-token shared prefix: 143.5 against 138.8 us at
+// two; the unshared Llama-3-8B-shaped decode layer is 2.3 us slower at two).
 template <int KV, int D, int G, bool NT>
 constexpr int stream_kernel_per_cu() {
   return MxGeom<KV, D, G>::kOn && !NT ? 2 : stream_per_cu<KV, D>();
@@ -67,8 +67,9 @@ static Residency resident_groups() {
     return Residency{0, 0};
   // Kernels whose K+V tile is 8 KiB or more run one workgroup per CU (a wave per
   // SIMD) even where their registers would allow two: twice the waves split twice
-  // as many segments, and config 2 measured 98.0 against 95.2 us at two on the VALU
-  // path, the 16-bit MFMA tile 105.6 against 99.5 us at a group of 8.  Tiles of at
+  // as many segments: the Llama-3-8B-shaped decode layer (64 sequences, 32/8 heads)
+  // measured 98.0 against 95.2 us at two on the VALU path, the 16-bit MFMA tile 105.6
+  // against 99.5 us at a group of 8.  Tiles of at
   // most 4 KiB run two (the 16 x 32768-token fp8 decode: 179 against 198 us at one;
   // MHA-shaped fp8 at head_dim 64 on the VALU path 52.3 against 36.4 us).
   const int cap = stream_kernel_per_cu<KV, D, G, NT>();

@@ -244,7 +244,7 @@ def decode_batch(seed: int, ctx, hq: int, hkv: int, d: int, kv: str, qd: str, *,
 
 
 # ----------------------------------------------------------------------------------
-# prefix sharing with forked requests (config 3)
+# prefix sharing with forked requests
 # ----------------------------------------------------------------------------------
 def fork_batch(seed: int, n_req: int, prefix_tokens: int, suffix_lo: int, suffix_hi: int,
                n_forks: int, hq: int, hkv: int, d: int, kv: str, qd: str, *, div: float = 1.0,
@@ -311,7 +311,7 @@ def fork_batch(seed: int, n_req: int, prefix_tokens: int, suffix_lo: int, suffix
 
 
 # ----------------------------------------------------------------------------------
-# mixed prefill chunks + decodes (config 4)
+# mixed prefill chunks + decodes
 # ----------------------------------------------------------------------------------
 def mixed_batch(seed: int, n_chunks: int, chunk_len: int, prior_lo: int, prior_hi: int,
                 n_dec: int, dec_median: float, dec_sigma: float, dec_lo: int, dec_hi: int,
